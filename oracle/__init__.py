@@ -1,0 +1,169 @@
+"""CPU oracle of the sparse MoE feed-forward layer (plain C, built with gcc).
+
+TEST INFRASTRUCTURE ONLY: only the tests, ``__graft_entry__.smoke()`` and the
+benchmark's ``cpu_baseline`` leg may import this package. It shares no code
+with the HIP library and never imports it.
+
+What the C code computes, and where each step comes from, is stated in the
+header of ``moe_oracle.c``. Every function here is argument marshalling
+around that C code. Parity of the oracle itself is pinned by the CPU tests
+against fp64 numpy evaluations, closed forms and invariants.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(_HERE, "moe_oracle.c")
+LIB = os.path.join(_HERE, "libmoe_oracle.so")
+
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (no fast-math, fma contraction off)."""
+    if force or not os.path.exists(LIB):
+        tmp = LIB + ".tmp"
+        cmd = ["gcc", "-O2", "-mfma", "-ffp-contract=off", "-fno-fast-math", "-fopenmp",
+               "-fPIC", "-shared", "-std=c11", SRC, "-o", tmp, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, LIB)
+    return LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB):
+            build(force=False)
+        lib = ctypes.CDLL(LIB)
+        vp, i64, i32, f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float
+        lib.oracle_router_logits.argtypes = [vp, vp, vp, i32, i64, i64, i64, vp]
+        lib.oracle_select_topk.argtypes = [vp, i64, i64, i32, f32, vp, vp]
+        lib.oracle_route.argtypes = [vp, i64, i32, i64, vp, vp, vp, vp]
+        lib.oracle_moe_tokens.argtypes = [vp, vp, vp, i32, i64, i64, vp, vp, i32, i32,
+                                          vp, vp, vp, vp, i64, vp]
+        lib.oracle_num_threads.argtypes = []
+        for f in (lib.oracle_router_logits, lib.oracle_select_topk, lib.oracle_route,
+                  lib.oracle_moe_tokens, lib.oracle_num_threads):
+            f.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def _dtype_code(a: np.ndarray) -> int:
+    if a.dtype == np.uint16:
+        return 0          # bf16 bit patterns
+    if a.dtype == np.float32:
+        return 1
+    raise TypeError(f"oracle takes bf16 bits (uint16) or float32, got {a.dtype}")
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _check(rc, what):
+    if rc != 0:
+        raise ValueError(f"oracle {what} rejected its arguments")
+
+
+def num_threads() -> int:
+    return _load().oracle_num_threads()
+
+
+def router_logits(hidden: np.ndarray, router_w: np.ndarray, bias: np.ndarray | None = None) -> np.ndarray:
+    """fp32 logits [T, E] in the canonical summation order (+ bias[e])."""
+    hidden = np.ascontiguousarray(hidden)
+    router_w = np.ascontiguousarray(router_w)
+    assert hidden.dtype == router_w.dtype
+    T, H = hidden.shape
+    E = router_w.shape[0]
+    assert router_w.shape == (E, H)
+    if bias is not None:
+        bias = np.ascontiguousarray(bias, dtype=np.float32)
+        assert bias.shape == (E,)
+    out = np.empty((T, E), dtype=np.float32)
+    _check(_load().oracle_router_logits(_p(hidden), _p(router_w), _p(bias), _dtype_code(hidden),
+                                        T, H, E, _p(out)), "router_logits")
+    return out
+
+
+def select_topk(logits: np.ndarray, k: int, routed_scale: float = 1.0):
+    """ids [T, k] int32 (slot order = rank order) and weights [T, k] float32."""
+    logits = np.ascontiguousarray(logits, dtype=np.float32)
+    T, E = logits.shape
+    ids = np.empty((T, k), dtype=np.int32)
+    w = np.empty((T, k), dtype=np.float32)
+    _check(_load().oracle_select_topk(_p(logits), T, E, int(k), float(routed_scale), _p(ids), _p(w)),
+           "select_topk")
+    return ids, w
+
+
+def route(ids: np.ndarray, E: int):
+    """counts [E], offsets [E+1], perm [T*k], inv [T*k] (all int32)."""
+    ids = np.ascontiguousarray(ids, dtype=np.int32)
+    T, k = ids.shape
+    counts = np.empty(E, dtype=np.int32)
+    offsets = np.empty(E + 1, dtype=np.int32)
+    perm = np.empty(T * k, dtype=np.int32)
+    inv = np.empty(T * k, dtype=np.int32)
+    _check(_load().oracle_route(_p(ids), T, int(k), int(E), _p(counts), _p(offsets), _p(perm), _p(inv)),
+           "route")
+    return counts, offsets, perm, inv
+
+
+def moe_tokens(hidden, gate_up, down, ids, weights, tokens=None, shared=()):
+    """Layer output (fp32) for the listed tokens; ``shared`` is a sequence of
+    (gate_up [2Is, H], down [H, Is]) pairs, each added unscaled."""
+    hidden = np.ascontiguousarray(hidden)
+    gate_up = np.ascontiguousarray(gate_up)
+    down = np.ascontiguousarray(down)
+    dt = _dtype_code(hidden)
+    assert gate_up.dtype == hidden.dtype and down.dtype == hidden.dtype
+    T, H = hidden.shape
+    E, twoI, H2 = gate_up.shape
+    I = twoI // 2
+    assert H2 == H and down.shape == (E, H, I)
+    ids = np.ascontiguousarray(ids, dtype=np.int32)
+    weights = np.ascontiguousarray(weights, dtype=np.float32)
+    k = ids.shape[1]
+    if tokens is None:
+        tokens = np.arange(T, dtype=np.int32)
+    tokens = np.ascontiguousarray(tokens, dtype=np.int32)
+    n_sh = len(shared)
+    keep = []
+    sgu = (ctypes.c_void_p * max(1, n_sh))()
+    sdn = (ctypes.c_void_p * max(1, n_sh))()
+    sI = np.zeros(max(1, n_sh), dtype=np.int64)
+    for s, (g, d) in enumerate(shared):
+        g = np.ascontiguousarray(g)
+        d = np.ascontiguousarray(d)
+        assert g.dtype == hidden.dtype and d.dtype == hidden.dtype
+        Is = g.shape[0] // 2
+        assert g.shape == (2 * Is, H) and d.shape == (H, Is)
+        keep += [g, d]
+        sgu[s] = g.ctypes.data
+        sdn[s] = d.ctypes.data
+        sI[s] = Is
+    out = np.empty((len(tokens), H), dtype=np.float32)
+    _check(_load().oracle_moe_tokens(_p(hidden), _p(gate_up), _p(down), dt, H, I, _p(ids), _p(weights),
+                                     int(k), n_sh, ctypes.cast(sgu, ctypes.c_void_p),
+                                     ctypes.cast(sdn, ctypes.c_void_p), _p(sI), _p(tokens),
+                                     len(tokens), _p(out)), "moe_tokens")
+    return out
+
+
+def moe_forward(hidden, router_w, gate_up, down, k, routed_scale=1.0, bias=None, shared=(),
+                tokens=None):
+    """Whole layer: routing for every token, outputs for ``tokens`` (all if None)."""
+    logits = router_logits(hidden, router_w, bias)
+    ids, w = select_topk(logits, k, routed_scale)
+    counts, offsets, perm, inv = route(ids, router_w.shape[0])
+    out = moe_tokens(hidden, gate_up, down, ids, w, tokens=tokens, shared=shared)
+    return dict(logits=logits, ids=ids, weights=w, counts=counts, offsets=offsets,
+                perm=perm, inv=inv, out=out)

@@ -1,0 +1,286 @@
+/*
+ * CPU oracle for the sparse Mixture-of-Experts feed-forward layer.
+ *
+ * TEST INFRASTRUCTURE ONLY. Nothing on the product path may include, link,
+ * load or call this file: only the tests, the smoke check and the benchmark's
+ * CPU-baseline leg use it. It shares no code, header, table or helper with
+ * the HIP library.
+ *
+ * What it computes, per token (the "eager" expert backend that the page
+ * "Transformer中的混合专家架构详解" (MoEs in Transformers), section on the
+ * experts backends, names as the correctness reference: loop over the
+ * selected experts and apply each one's projections):
+ *
+ *   1. router logits  l[e] = <x, Wr[e]> (+ b[e])          (PhiMoE page, sec. 6:
+ *                                                          a bias-free linear
+ *                                                          router; bias optional)
+ *   2. top-k experts by logit, ties to the lower index    (PhiMoE page, sec. 6:
+ *                                                          greedy top-1, mask,
+ *                                                          next; eval path)
+ *   3. weights = softmax over the k selected logits, times the routed scale
+ *                                                          (PhiMoE page, sec. 6;
+ *                                                          Instella page: scale 2.5)
+ *   4. expert SwiGLU: g = Wgu[e][0:I] x, u = Wgu[e][I:2I] x, h = silu(g)*u,
+ *      y = Wd[e] h                                         (PhiMoE page, sec. 2,
+ *                                                          item 3: packed gate_up,
+ *                                                          chunk(2), act(gate)*up)
+ *   5. out = sum_j w_j y_j  (+ every shared expert's SwiGLU output, unscaled)
+ *                                                          (GraniteMoeSWA page,
+ *                                                          decoder-layer section;
+ *                                                          Instella page, FarSkipMoE)
+ *   6. routing metadata: per-expert counts, exclusive offsets, and the stable
+ *      expert-major permutation of flat assignments a = t*k + j
+ *                                                          (MoEs in Transformers
+ *                                                          page: grouped_mm sorts
+ *                                                          tokens by expert id and
+ *                                                          groups them; PhiMoE
+ *                                                          page sec. 2 item 4:
+ *                                                          no token is dropped)
+ *
+ * Precision: inputs are bf16 bit patterns (dtype 0) widened exactly to fp32,
+ * or fp32 (dtype 1). Every sum accumulates in fp32 with fmaf in ascending
+ * index order. The router logit is the one exception to "ascending": the
+ * pages fix no summation order, yet the expert ids must be reproducible bit
+ * for bit, so the logit is DEFINED as the fp32 sum taken in this order:
+ * 64 partial sums P[0..63]; element i = 512*c + 8*L + v (v = 0..7) goes to
+ * P[L], visiting c ascending then v ascending; then, for d = 32, 16, 8, 4,
+ * 2, 1, every P[L] becomes P[L] + P[L ^ d]; the logit is P[0]. Softmax
+ * weights and SiLU are evaluated in fp64 and rounded to fp32.
+ *
+ * Build: gcc -O2 -mfma -ffp-contract=off -fopenmp -fPIC -shared (no fast-math).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define OR_OK 0
+#define OR_BAD -1
+
+static float widen(const void *base, int dtype, size_t i)
+{
+    if (dtype == 0) {
+        uint32_t u = (uint32_t)((const uint16_t *)base)[i] << 16;
+        float f;
+        memcpy(&f, &u, sizeof f);
+        return f;
+    }
+    return ((const float *)base)[i];
+}
+
+/* Logit of one (token, expert) pair in the order stated in the header. */
+static float router_dot(const void *X, const void *Wr, int dtype, int64_t t, int64_t e, int64_t H)
+{
+    float P[64];
+    for (int L = 0; L < 64; L++)
+        P[L] = 0.0f;
+    for (int64_t c = 0; c * 512 < H; c++)
+        for (int L = 0; L < 64; L++)
+            for (int v = 0; v < 8; v++) {
+                int64_t i = 512 * c + 8 * L + v;
+                if (i < H)
+                    P[L] = fmaf(widen(X, dtype, (size_t)(t * H + i)),
+                                widen(Wr, dtype, (size_t)(e * H + i)), P[L]);
+            }
+    for (int d = 32; d >= 1; d /= 2) {
+        float Q[64];
+        for (int L = 0; L < 64; L++)
+            Q[L] = P[L] + P[L ^ d];
+        memcpy(P, Q, sizeof P);
+    }
+    return P[0];
+}
+
+int oracle_router_logits(const void *X, const void *Wr, const float *bias, int dtype,
+                         int64_t T, int64_t H, int64_t E, float *logits)
+{
+    if (!X || !Wr || !logits || T < 0 || H <= 0 || E <= 0 || (dtype != 0 && dtype != 1))
+        return OR_BAD;
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; t++)
+        for (int64_t e = 0; e < E; e++) {
+            float l = router_dot(X, Wr, dtype, t, e, H);
+            if (bias)
+                l = l + bias[e];
+            logits[t * E + e] = l;
+        }
+    return OR_OK;
+}
+
+/* Expert a ranks before expert b iff l[a] > l[b], or l[a] == l[b] and a < b. */
+static int ranks_before(const float *l, int64_t a, int64_t b)
+{
+    return l[a] > l[b] || (l[a] == l[b] && a < b);
+}
+
+int oracle_select_topk(const float *logits, int64_t T, int64_t E, int k, float routed_scale,
+                       int32_t *ids, float *weights)
+{
+    if (!logits || !ids || !weights || T < 0 || E <= 0 || k < 1 || k > E || k > 256)
+        return OR_BAD;
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; t++) {
+        const float *l = logits + t * E;
+        /* greedy: take the best remaining expert k times */
+        for (int j = 0; j < k; j++) {
+            int64_t best = -1;
+            for (int64_t e = 0; e < E; e++) {
+                int taken = 0;
+                for (int q = 0; q < j; q++)
+                    if (ids[t * k + q] == e)
+                        taken = 1;
+                if (taken)
+                    continue;
+                if (best < 0 || ranks_before(l, e, best))
+                    best = e;
+            }
+            ids[t * k + j] = (int32_t)best;
+        }
+        /* softmax over the selected logits (shifted by the largest), renormalised */
+        double m = (double)l[ids[t * k]];
+        double p[256], s = 0.0;
+        for (int j = 0; j < k; j++) {
+            p[j] = exp((double)l[ids[t * k + j]] - m);
+            s += p[j];
+        }
+        for (int j = 0; j < k; j++)
+            weights[t * k + j] = (float)((double)routed_scale * p[j] / s);
+    }
+    return OR_OK;
+}
+
+int oracle_route(const int32_t *ids, int64_t T, int k, int64_t E, int32_t *counts,
+                 int32_t *offsets, int32_t *perm, int32_t *inv)
+{
+    if (!ids || !counts || !offsets || !perm || !inv || T < 0 || k < 1 || E <= 0)
+        return OR_BAD;
+    int64_t TK = T * k;
+    for (int64_t e = 0; e < E; e++)
+        counts[e] = 0;
+    for (int64_t a = 0; a < TK; a++) {
+        if (ids[a] < 0 || ids[a] >= E)
+            return OR_BAD;
+        counts[ids[a]]++;
+    }
+    offsets[0] = 0;
+    for (int64_t e = 0; e < E; e++)
+        offsets[e + 1] = offsets[e] + counts[e];
+    /* stable counting sort: assignments of one expert keep ascending a */
+    int32_t *next = (int32_t *)malloc(sizeof(int32_t) * (size_t)E);
+    if (!next)
+        return OR_BAD;
+    for (int64_t e = 0; e < E; e++)
+        next[e] = offsets[e];
+    for (int64_t a = 0; a < TK; a++) {
+        int32_t p = next[ids[a]]++;
+        perm[p] = (int32_t)a;
+        inv[a] = p;
+    }
+    free(next);
+    return OR_OK;
+}
+
+static double silu(double z) { return z / (1.0 + exp(-z)); }
+
+/* y = Wd h with h = silu(Wg x) * (Wu x); weights rows [0,I) gate, [I,2I) up. */
+static void swiglu_expert(const float *x, const void *gate_up, const void *down, int dtype,
+                          int64_t H, int64_t I, float *h, float *y)
+{
+    for (int64_t n = 0; n < I; n++) {
+        float g = 0.0f, u = 0.0f;
+        for (int64_t i = 0; i < H; i++) {
+            g = fmaf(widen(gate_up, dtype, (size_t)(n * H + i)), x[i], g);
+            u = fmaf(widen(gate_up, dtype, (size_t)((I + n) * H + i)), x[i], u);
+        }
+        h[n] = (float)(silu((double)g) * (double)u);
+    }
+    for (int64_t m = 0; m < H; m++) {
+        float acc = 0.0f;
+        for (int64_t n = 0; n < I; n++)
+            acc = fmaf(widen(down, dtype, (size_t)(m * I + n)), h[n], acc);
+        y[m] = acc;
+    }
+}
+
+/*
+ * Layer output for the listed tokens: out[r] = sum_j w[t,j] * FFN_{ids[t,j]}(x_t)
+ * (j ascending, fp32 fmaf) + sum_s SharedFFN_s(x_t), with t = tokens[r].
+ * gate_up is [E, 2I, H], down is [E, H, I]; shared expert s has gate_up
+ * [2*shared_I[s], H] and down [H, shared_I[s]].
+ */
+int oracle_moe_tokens(const void *X, const void *gate_up, const void *down, int dtype,
+                      int64_t H, int64_t I, const int32_t *ids, const float *weights, int k,
+                      int n_shared, const void *const *shared_gate_up,
+                      const void *const *shared_down, const int64_t *shared_I,
+                      const int32_t *tokens, int64_t n_tokens, float *out)
+{
+    if (!X || !gate_up || !down || !ids || !weights || !tokens || !out || H <= 0 || I <= 0 ||
+        k < 1 || n_shared < 0)
+        return OR_BAD;
+    int64_t Imax = I;
+    for (int s = 0; s < n_shared; s++)
+        if (shared_I[s] > Imax)
+            Imax = shared_I[s];
+    int bad = 0;
+#pragma omp parallel
+    {
+        float *x = (float *)malloc(sizeof(float) * (size_t)H);
+        float *y = (float *)malloc(sizeof(float) * (size_t)H);
+        float *h = (float *)malloc(sizeof(float) * (size_t)Imax);
+        if (!x || !y || !h) {
+#pragma omp atomic write
+            bad = 1;
+        } else {
+#pragma omp for schedule(dynamic, 1)
+            for (int64_t r = 0; r < n_tokens; r++) {
+                int64_t t = tokens[r];
+                for (int64_t i = 0; i < H; i++)
+                    x[i] = widen(X, dtype, (size_t)(t * H + i));
+                float *o = out + r * H;
+                for (int64_t m = 0; m < H; m++)
+                    o[m] = 0.0f;
+                for (int j = 0; j < k; j++) {
+                    int64_t e = ids[t * k + j];
+                    float w = weights[t * k + j];
+                    size_t gu_off = (size_t)e * (size_t)(2 * I * H);
+                    size_t dn_off = (size_t)e * (size_t)(H * I);
+                    const void *gu = dtype == 0 ? (const void *)((const uint16_t *)gate_up + gu_off)
+                                                : (const void *)((const float *)gate_up + gu_off);
+                    const void *dn = dtype == 0 ? (const void *)((const uint16_t *)down + dn_off)
+                                                : (const void *)((const float *)down + dn_off);
+                    swiglu_expert(x, gu, dn, dtype, H, I, h, y);
+                    for (int64_t m = 0; m < H; m++)
+                        o[m] = fmaf(w, y[m], o[m]);
+                }
+                for (int s = 0; s < n_shared; s++) {
+                    swiglu_expert(x, shared_gate_up[s], shared_down[s], dtype, H, shared_I[s], h, y);
+                    for (int64_t m = 0; m < H; m++)
+                        o[m] = o[m] + y[m];
+                }
+            }
+        }
+        free(x);
+        free(y);
+        free(h);
+    }
+    return bad ? OR_BAD : OR_OK;
+}
+
+/* Number of OpenMP threads the oracle runs on (reported beside its timings). */
+int oracle_num_threads(void)
+{
+    int n = 1;
+#pragma omp parallel
+    {
+#pragma omp single
+        {
+#ifdef _OPENMP
+            n = omp_get_num_threads();
+#endif
+        }
+    }
+    return n;
+}
