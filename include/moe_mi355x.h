@@ -1,0 +1,142 @@
+/*
+ * moe_mi355x.h -- C ABI of the sparse Mixture-of-Experts feed-forward layer
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * The layer is the block-sparse MoE of PhiMoE and its shared-expert
+ * variants:
+ *   - router: a bias-free linear layer from hidden size to the number of
+ *     experts ("深入解析 Transformers 中的 PhiMoE" page, section 6, call chain
+ *     of PhimoeSparseMoeBlock / PhimoeTopKRouter);
+ *   - top-k experts per token with softmax weights over the selected
+ *     experts (same page, section 6, sparsemixer at inference: greedy top-1,
+ *     mask it, take the next, softmax the selected weights);
+ *   - no token is ever dropped and no capacity padding is applied (same
+ *     page, section 2, item 4);
+ *   - experts are packed: gate_up_proj [E, 2I, H] (gate rows first, then up
+ *     rows) and down_proj [E, H, I]; each expert computes
+ *     down(silu(gate x) * up x) (same page, section 2, item 3);
+ *   - tokens are sorted by expert id and grouped so that one grouped GEMM
+ *     serves all experts ("Transformer中的混合专家架构详解" page, experts
+ *     backends section, grouped_mm; weight-loading section: kernels need the
+ *     experts packed in one contiguous tensor);
+ *   - optional always-on shared expert added to the routed output
+ *     (GraniteMoeSWA page, decoder-layer section: moe output + shared_mlp;
+ *     Instella page, FarSkipMoE: routed + shared, routed scaling factor).
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are DEVICE pointers owned by the caller; the
+ *     library never allocates or frees memory on the call path and keeps no
+ *     mutable global state (calls on different streams may overlap as long
+ *     as their buffers do not).
+ *   - Tensors are dense, row-major, with the shapes stated; base pointers
+ *     must be 16-byte aligned; H, I and shared_I must be multiples of 8.
+ *   - Every argument check runs before any HIP call; a rejected call has
+ *     enqueued nothing. Work is enqueued asynchronously on opts->stream and
+ *     no host synchronisation happens; device faults surface at the caller's
+ *     next synchronisation.
+ *   - Error details of the last failing call on the calling thread are
+ *     available from moe_last_error().
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum moe_status {
+    MOE_OK = 0,
+    MOE_ERR_INVALID_ARG = -1, /* bad shape, k, dtype, null pointer, aliasing  */
+    MOE_ERR_UNSUPPORTED = -2, /* valid request outside what this build serves */
+    MOE_ERR_WORKSPACE = -3,   /* workspace missing or smaller than required   */
+    MOE_ERR_ALIGNMENT = -4,   /* a pointer is not 16-byte aligned             */
+    MOE_ERR_HIP = -5          /* a HIP launch or runtime call failed          */
+} moe_status;
+
+typedef enum moe_dtype {
+    MOE_BF16 = 0, /* bf16 hidden, router, expert weights and output; fp32 accumulation */
+    MOE_F32 = 1   /* fp32 everywhere                                                */
+} moe_dtype;
+
+/* opts->flags bits: choose the expert-GEMM schedule (default: by shape). */
+#define MOE_FLAG_FORCE_TILED 0x1u  /* large-M tiles (prefill schedule)          */
+#define MOE_FLAG_FORCE_SKINNY 0x2u /* weight-streaming tiles (decode schedule)  */
+
+typedef struct moe_opts {
+    uint32_t struct_size;     /* = sizeof(moe_opts); set by moe_opts_init            */
+    int32_t dtype;            /* moe_dtype of hidden, router_w, gate_up, down, out,  */
+                              /* shared_gate_up and shared_down                      */
+    float routed_scale;       /* multiplies the routed weights only (default 1.0)   */
+    uint32_t flags;           /* MOE_FLAG_* bits, default 0                          */
+    const float *router_bias; /* [E] fp32 added to every logit row, or NULL          */
+    const void *shared_gate_up; /* [2*shared_I, H] (gate rows then up rows) or NULL  */
+    const void *shared_down;  /* [H, shared_I] or NULL                               */
+    int64_t shared_I;         /* intermediate size of the shared expert; 0 = none    */
+    /* Optional outputs (NULL = not written). */
+    float *router_logits;     /* [T, E] fp32 logits, bias included                   */
+    int32_t *topk_ids;        /* [T, k] selected experts, slot 0 = largest logit     */
+    float *topk_weights;      /* [T, k] renormalised weights times routed_scale      */
+    int32_t *expert_counts;   /* [E] assignments per expert                          */
+    int32_t *expert_offsets;  /* [E+1] exclusive prefix sum of expert_counts         */
+    int32_t *perm;            /* [T*k] sorted position -> flat assignment t*k+j      */
+    int32_t *inv_perm;        /* [T*k] flat assignment -> sorted position            */
+    /* Scratch memory, at least moe_workspace_bytes(...) bytes, 256-byte aligned. */
+    void *workspace;
+    size_t workspace_bytes;
+    void *stream;             /* hipStream_t to enqueue on; NULL = default stream    */
+} moe_opts;
+
+/* Fills *opts with defaults: dtype MOE_BF16, routed_scale 1, everything else 0. */
+void moe_opts_init(moe_opts *opts);
+
+/*
+ * Bytes of workspace moe_forward needs for these sizes and options (only
+ * dtype, shared_I and flags of opts are read; opts may be NULL for the
+ * defaults). Returns a negative moe_status when the sizes are invalid.
+ * Pure host arithmetic: no HIP call.
+ */
+int64_t moe_workspace_bytes(int64_t T, int64_t H, int64_t I, int64_t E, int32_t k,
+                            const moe_opts *opts);
+
+/*
+ * out[T, H] = sum over the k experts selected for each token of
+ *             w[t, j] * down_e(silu(gate_e x_t) * up_e x_t)
+ *             (+ shared expert output when opts->shared_I > 0).
+ *
+ * hidden   [T, H]       token activations
+ * router_w [E, H]       router weight (nn.Linear layout [out, in])
+ * gate_up  [E, 2I, H]   rows [0, I) gate projection, rows [I, 2I) up projection
+ * down     [E, H, I]    down projection (nn.Linear layout [out, in])
+ * out      [T, H]       written in full; must not overlap any input
+ *
+ * Sizes: T >= 0 (T = 0 is a successful no-op), 1 <= k <= E <= 256, H, I >= 8
+ * and multiples of 8, T*k < 2^31.
+ *
+ * Routing is reproducible bit for bit. The logit of expert e is an fp32 sum
+ * of products hidden[t,i]*router_w[e,i] taken in this order: 64 partial sums
+ * P[0..63], element i = 512c + 8L + v (v = 0..7) fused-multiply-added into
+ * P[L] with c ascending, then v ascending; then for d = 32, 16, 8, 4, 2, 1
+ * every P[L] becomes P[L] + P[L xor d]; the logit is P[0] + router_bias[e].
+ * Experts rank by logit, ties to the lower index; slot j of a token holds
+ * its j-th ranked expert. Weights are exp(l_j - l_0) / sum_i exp(l_i - l_0)
+ * over the selected experts, times routed_scale. Assignments are grouped by
+ * expert, ascending t*k+j inside each group.
+ *
+ * Returns MOE_OK or a negative moe_status; on error nothing was enqueued
+ * unless the status is MOE_ERR_HIP (a launch failed part-way).
+ */
+int moe_forward(const void *hidden, const void *router_w, const void *gate_up, const void *down,
+                int64_t T, int64_t H, int64_t I, int64_t E, int32_t k, const moe_opts *opts,
+                void *out);
+
+/* Message describing the last failing call on this thread ("" if none). */
+const char *moe_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_H */

@@ -1,0 +1,201 @@
+"""Python binding of libmoe_mi355x.so, the MI355X sparse-MoE layer.
+
+Argument marshalling only: every step of the layer runs in the library's HIP
+kernels. PyTorch supplies device memory and the current stream. The library
+must be built (``python -m sparse_mixture_experts_logits_amd.build``); if it is
+missing, every call raises -- there is no fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+__all__ = ["moe_forward", "workspace_bytes", "MoeError", "load_library", "LIB_PATH",
+           "FLAG_FORCE_TILED", "FLAG_FORCE_SKINNY", "bf16_bits_to_tensor", "EXPORTS"]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_mi355x.so")
+
+MOE_BF16 = 0
+MOE_F32 = 1
+FLAG_FORCE_TILED = 0x1
+FLAG_FORCE_SKINNY = 0x2
+EXPORTS = ("moe_opts_init", "moe_workspace_bytes", "moe_forward", "moe_last_error")
+
+STATUS = {0: "MOE_OK", -1: "MOE_ERR_INVALID_ARG", -2: "MOE_ERR_UNSUPPORTED", -3: "MOE_ERR_WORKSPACE",
+          -4: "MOE_ERR_ALIGNMENT", -5: "MOE_ERR_HIP"}
+
+
+class MoeOpts(ctypes.Structure):
+    """Mirror of ``moe_opts`` in include/moe_mi355x.h."""
+    _fields_ = [
+        ("struct_size", ctypes.c_uint32),
+        ("dtype", ctypes.c_int32),
+        ("routed_scale", ctypes.c_float),
+        ("flags", ctypes.c_uint32),
+        ("router_bias", ctypes.c_void_p),
+        ("shared_gate_up", ctypes.c_void_p),
+        ("shared_down", ctypes.c_void_p),
+        ("shared_I", ctypes.c_int64),
+        ("router_logits", ctypes.c_void_p),
+        ("topk_ids", ctypes.c_void_p),
+        ("topk_weights", ctypes.c_void_p),
+        ("expert_counts", ctypes.c_void_p),
+        ("expert_offsets", ctypes.c_void_p),
+        ("perm", ctypes.c_void_p),
+        ("inv_perm", ctypes.c_void_p),
+        ("workspace", ctypes.c_void_p),
+        ("workspace_bytes", ctypes.c_size_t),
+        ("stream", ctypes.c_void_p),
+    ]
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+_lib = None
+
+
+def load_library():
+    """Load the in-tree HIP library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise FileNotFoundError(
+                f"{LIB_PATH} is missing; build it with `python -m sparse_mixture_experts_logits_amd.build`")
+        lib = ctypes.CDLL(LIB_PATH)
+        vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+        lib.moe_opts_init.argtypes = [ctypes.POINTER(MoeOpts)]
+        lib.moe_opts_init.restype = None
+        lib.moe_workspace_bytes.argtypes = [i64, i64, i64, i64, i32, ctypes.POINTER(MoeOpts)]
+        lib.moe_workspace_bytes.restype = i64
+        lib.moe_forward.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i32, ctypes.POINTER(MoeOpts), vp]
+        lib.moe_forward.restype = ctypes.c_int
+        lib.moe_last_error.argtypes = []
+        lib.moe_last_error.restype = ctypes.c_char_p
+        _lib = lib
+    return _lib
+
+
+def new_opts() -> MoeOpts:
+    o = MoeOpts()
+    load_library().moe_opts_init(ctypes.byref(o))
+    return o
+
+
+def last_error() -> str:
+    return load_library().moe_last_error().decode()
+
+
+def workspace_bytes(T, H, I, E, k, dtype=MOE_BF16, shared_I=0, flags=0) -> int:
+    o = new_opts()
+    o.dtype = dtype
+    o.shared_I = shared_I
+    o.flags = flags
+    n = load_library().moe_workspace_bytes(T, H, I, E, k, ctypes.byref(o))
+    if n < 0:
+        raise MoeError(int(n), last_error())
+    return int(n)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def bf16_bits_to_tensor(a: np.ndarray, device="cuda"):
+    """uint16 bf16 bit patterns (or float32) -> torch tensor on ``device``."""
+    import torch
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(device)
+    return torch.from_numpy(a).to(device)
+
+
+def moe_forward(hidden, router_w, gate_up, down, k: int, *, routed_scale: float = 1.0, router_bias=None,
+                shared_gate_up=None, shared_down=None, flags: int = 0, return_routing: bool = False,
+                out=None, workspace=None, stream=None):
+    """Run the MoE layer on torch tensors already on the GPU.
+
+    hidden [T, H], router_w [E, H], gate_up [E, 2I, H], down [E, H, I] (all
+    bf16 or all fp32, contiguous); router_bias [E] fp32; shared_gate_up
+    [2Is, H], shared_down [H, Is]. Returns out [T, H] (and a dict of routing
+    tensors when ``return_routing``). Work is enqueued on ``stream`` (default:
+    torch's current stream)."""
+    import torch
+    lib = load_library()
+    T, H = hidden.shape
+    E, twoI, _ = gate_up.shape
+    I = twoI // 2
+    o = new_opts()
+    if hidden.dtype == torch.bfloat16:
+        o.dtype = MOE_BF16
+    elif hidden.dtype == torch.float32:
+        o.dtype = MOE_F32
+    else:
+        raise TypeError(f"unsupported dtype {hidden.dtype}")
+    tensors = [hidden, router_w, gate_up, down] + [t for t in (shared_gate_up, shared_down) if t is not None]
+    for t in tensors:
+        if t.dtype != hidden.dtype or not t.is_contiguous() or not t.is_cuda:
+            raise ValueError("all tensors must be contiguous CUDA tensors of one dtype")
+    if router_w.shape != (E, H) or gate_up.shape != (E, 2 * I, H) or down.shape != (E, H, I):
+        raise ValueError("shape mismatch among hidden, router_w, gate_up, down")
+    o.routed_scale = float(routed_scale)
+    o.flags = int(flags)
+    if router_bias is not None:
+        router_bias = router_bias.to(dtype=torch.float32).contiguous()
+        o.router_bias = router_bias.data_ptr()
+    if shared_gate_up is not None:
+        Is = shared_gate_up.shape[0] // 2
+        if shared_gate_up.shape != (2 * Is, H) or shared_down is None or shared_down.shape != (H, Is):
+            raise ValueError("shared expert shapes must be [2Is, H] and [H, Is]")
+        o.shared_gate_up = shared_gate_up.data_ptr()
+        o.shared_down = shared_down.data_ptr()
+        o.shared_I = Is
+    dev = hidden.device
+    if out is None:
+        out = torch.empty((T, H), dtype=hidden.dtype, device=dev)
+    routing = None
+    if return_routing:
+        routing = dict(
+            logits=torch.empty((T, E), dtype=torch.float32, device=dev),
+            ids=torch.empty((T, k), dtype=torch.int32, device=dev),
+            weights=torch.empty((T, k), dtype=torch.float32, device=dev),
+            counts=torch.empty((E,), dtype=torch.int32, device=dev),
+            offsets=torch.empty((E + 1,), dtype=torch.int32, device=dev),
+            perm=torch.empty((T * k,), dtype=torch.int32, device=dev),
+            inv=torch.empty((T * k,), dtype=torch.int32, device=dev),
+        )
+        o.router_logits = routing["logits"].data_ptr()
+        o.topk_ids = routing["ids"].data_ptr()
+        o.topk_weights = routing["weights"].data_ptr()
+        o.expert_counts = routing["counts"].data_ptr()
+        o.expert_offsets = routing["offsets"].data_ptr()
+        o.perm = routing["perm"].data_ptr()
+        o.inv_perm = routing["inv"].data_ptr()
+    need = lib.moe_workspace_bytes(T, H, I, E, k, ctypes.byref(o))
+    if need < 0:
+        raise MoeError(int(need), last_error())
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
+    o.workspace = workspace.data_ptr()
+    o.workspace_bytes = workspace.numel()
+    current = torch.cuda.current_stream(dev)
+    if stream is None:
+        stream = current
+    if stream != current:
+        # buffers allocated here belong to the current stream's pool
+        for t in (router_bias, workspace, out, *(routing.values() if routing else ())):
+            if t is not None:
+                t.record_stream(stream)
+    o.stream = stream.cuda_stream
+    rc = lib.moe_forward(_ptr(hidden), _ptr(router_w), _ptr(gate_up), _ptr(down), T, H, I, E, int(k),
+                         ctypes.byref(o), _ptr(out))
+    if rc != 0:
+        raise MoeError(rc, last_error())
+    if return_routing:
+        return out, routing
+    return out

@@ -1,0 +1,316 @@
+// C ABI of the MoE layer: argument checks, workspace layout and the kernel
+// sequence on the caller's stream. See include/moe_mi355x.h for the contract.
+#include "moe_mi355x.h"
+#include "moe_internal.h"
+
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+namespace {
+
+thread_local char g_err[512];
+
+int fail(int code, const char *fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+bool overlaps(const void *a, uint64_t na, const void *b, uint64_t nb)
+{
+    if (!a || !b || na == 0 || nb == 0) return false;
+    const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+    return a0 < b0 + nb && b0 < a0 + na;
+}
+
+bool debug_sync()
+{
+    static int v = -1;
+    if (v < 0) {
+        const char *s = getenv("MOE_DEBUG_SYNC");
+        v = (s && s[0] == '1') ? 1 : 0;
+    }
+    return v == 1;
+}
+
+constexpr int64_t kAlign = 256;
+
+int64_t align_up(int64_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// Shape checks shared by moe_workspace_bytes and moe_forward (no HIP call).
+int check_shape(int64_t T, int64_t H, int64_t I, int64_t E, int32_t k, const moe_opts *opts)
+{
+    if (opts && opts->struct_size != sizeof(moe_opts))
+        return fail(MOE_ERR_INVALID_ARG, "opts->struct_size is %u, expected %zu (call moe_opts_init)",
+                    opts->struct_size, sizeof(moe_opts));
+    const int dtype = opts ? opts->dtype : MOE_BF16;
+    if (dtype != MOE_BF16 && dtype != MOE_F32)
+        return fail(MOE_ERR_INVALID_ARG, "unknown dtype %d", dtype);
+    if (T < 0) return fail(MOE_ERR_INVALID_ARG, "T = %lld is negative", (long long)T);
+    if (E < 1 || E > moe::kMaxExperts)
+        return fail(MOE_ERR_INVALID_ARG, "E = %lld outside [1, %d]", (long long)E, moe::kMaxExperts);
+    if (k < 1 || k > E) return fail(MOE_ERR_INVALID_ARG, "k = %d outside [1, E = %lld]", k, (long long)E);
+    if (H < 8 || H % 8) return fail(MOE_ERR_INVALID_ARG, "H = %lld must be a positive multiple of 8", (long long)H);
+    if (I < 8 || I % 8) return fail(MOE_ERR_INVALID_ARG, "I = %lld must be a positive multiple of 8", (long long)I);
+    if (H > (1 << 24) || I > (1 << 24))
+        return fail(MOE_ERR_UNSUPPORTED, "H = %lld or I = %lld above 2^24", (long long)H, (long long)I);
+    if (T * (int64_t)k >= ((int64_t)1 << 31))
+        return fail(MOE_ERR_UNSUPPORTED, "T*k = %lld must be below 2^31", (long long)(T * k));
+    // 32-bit element offsets inside one expert / one activation tensor
+    if (2 * I * H >= ((int64_t)1 << 31) || T * H >= ((int64_t)1 << 31) || T * (int64_t)k * I >= ((int64_t)1 << 31))
+        return fail(MOE_ERR_UNSUPPORTED, "a single expert or activation tensor exceeds 2^31 elements");
+    if (opts) {
+        if (opts->shared_I < 0 || (opts->shared_I > 0 && opts->shared_I % 8))
+            return fail(MOE_ERR_INVALID_ARG, "shared_I = %lld must be 0 or a positive multiple of 8",
+                        (long long)opts->shared_I);
+        if (opts->shared_I > (1 << 24)) return fail(MOE_ERR_UNSUPPORTED, "shared_I above 2^24");
+        if (opts->flags & ~(MOE_FLAG_FORCE_TILED | MOE_FLAG_FORCE_SKINNY))
+            return fail(MOE_ERR_INVALID_ARG, "unknown flag bits 0x%x", opts->flags);
+        if ((opts->flags & MOE_FLAG_FORCE_TILED) && (opts->flags & MOE_FLAG_FORCE_SKINNY))
+            return fail(MOE_ERR_INVALID_ARG, "MOE_FLAG_FORCE_TILED and MOE_FLAG_FORCE_SKINNY both set");
+    }
+    return MOE_OK;
+}
+
+moe::Shape make_shape(int64_t T, int64_t H, int64_t I, int64_t E, int32_t k, const moe_opts *opts)
+{
+    moe::Shape s;
+    s.T = T;
+    s.H = H;
+    s.I = I;
+    s.E = E;
+    s.k = k;
+    s.sharedI = opts ? opts->shared_I : 0;
+    s.dtype = opts ? opts->dtype : MOE_BF16;
+    s.nblk = (int)((T + moe::kRouterTokensPerBlock - 1) / moe::kRouterTokensPerBlock);
+    s.tileBM = moe::tiled_block_m();
+    s.maxTiles = (T * k) / s.tileBM + E + 1;
+    return s;
+}
+
+}  // namespace
+
+namespace moe {
+
+int64_t workspace_layout(const Shape &s, void *base, Workspace *ws)
+{
+    int64_t off = 0;
+    auto take = [&](int64_t bytes) -> void * {
+        off = align_up(off);
+        void *p = base ? (void *)((char *)base + off) : nullptr;
+        off += bytes;
+        return p;
+    };
+    const int64_t TK = s.T * s.k;
+    const int64_t es = s.dtype == MOE_BF16 ? 2 : 4;
+    Workspace w;
+    w.ids = (int32_t *)take(TK * 4);
+    w.wts = (float *)take(TK * 4);
+    w.blk_counts = (int32_t *)take((int64_t)s.nblk * s.E * 4);
+    w.blk_base = (int32_t *)take((int64_t)s.nblk * s.E * 4);
+    w.counts = (int32_t *)take(s.E * 4);
+    w.offsets = (int32_t *)take((s.E + 1) * 4);
+    w.tile_start = (int32_t *)take((s.E + 1) * 4);
+    w.tiles = (MTile *)take(s.maxTiles * (int64_t)sizeof(MTile));
+    w.perm = (int32_t *)take(TK * 4);
+    w.inv = (int32_t *)take(TK * 4);
+    w.row_token = (int32_t *)take(TK * 4);
+    w.row_weight = (float *)take(TK * 4);
+    w.row_expert = (int32_t *)take(TK * 4);
+    w.h = take(TK * s.I * es);
+    w.slot = (float *)take(TK * s.H * 4);
+    w.sh_h = s.sharedI > 0 ? take(s.T * s.sharedI * es) : nullptr;
+    w.sh_y = s.sharedI > 0 ? (float *)take(s.T * s.H * 4) : nullptr;
+    if (ws) *ws = w;
+    return align_up(off);
+}
+
+}  // namespace moe
+
+extern "C" {
+
+void moe_opts_init(moe_opts *opts)
+{
+    if (!opts) return;
+    memset(opts, 0, sizeof *opts);
+    opts->struct_size = sizeof(moe_opts);
+    opts->dtype = MOE_BF16;
+    opts->routed_scale = 1.0f;
+}
+
+const char *moe_last_error(void) { return g_err; }
+
+int64_t moe_workspace_bytes(int64_t T, int64_t H, int64_t I, int64_t E, int32_t k, const moe_opts *opts)
+{
+    g_err[0] = 0;
+    const int rc = check_shape(T, H, I, E, k, opts);
+    if (rc != MOE_OK) return rc;
+    const moe::Shape s = make_shape(T, H, I, E, k, opts);
+    return moe::workspace_layout(s, nullptr, nullptr);
+}
+
+int moe_forward(const void *hidden, const void *router_w, const void *gate_up, const void *down,
+                int64_t T, int64_t H, int64_t I, int64_t E, int32_t k, const moe_opts *opts, void *out)
+{
+    g_err[0] = 0;
+    if (!opts) return fail(MOE_ERR_INVALID_ARG, "opts is NULL");
+    int rc = check_shape(T, H, I, E, k, opts);
+    if (rc != MOE_OK) return rc;
+    if (!isfinite(opts->routed_scale)) return fail(MOE_ERR_INVALID_ARG, "routed_scale is not finite");
+    if (T == 0) return MOE_OK;
+
+    if (!hidden || !router_w || !gate_up || !down || !out)
+        return fail(MOE_ERR_INVALID_ARG, "hidden, router_w, gate_up, down and out must be non-NULL");
+    const bool shared = opts->shared_I > 0;
+    if (shared && (!opts->shared_gate_up || !opts->shared_down))
+        return fail(MOE_ERR_INVALID_ARG, "shared_I > 0 needs shared_gate_up and shared_down");
+    const void *tens[] = {hidden, router_w, gate_up, down, out, opts->shared_gate_up, opts->shared_down};
+    for (const void *p : tens)
+        if (p && !aligned(p, 16)) return fail(MOE_ERR_ALIGNMENT, "tensor pointer %p is not 16-byte aligned", p);
+    const void *small[] = {opts->router_bias, opts->router_logits, opts->topk_ids, opts->topk_weights,
+                           opts->expert_counts, opts->expert_offsets, opts->perm, opts->inv_perm};
+    for (const void *p : small)
+        if (p && !aligned(p, 4)) return fail(MOE_ERR_ALIGNMENT, "output pointer %p is not 4-byte aligned", p);
+
+    const uint64_t es = opts->dtype == MOE_BF16 ? 2 : 4;
+    const uint64_t out_bytes = (uint64_t)T * H * es;
+    struct Range {
+        const void *p;
+        uint64_t n;
+    } ins[] = {{hidden, (uint64_t)T * H * es},
+               {router_w, (uint64_t)E * H * es},
+               {gate_up, (uint64_t)E * 2 * I * H * es},
+               {down, (uint64_t)E * H * I * es},
+               {opts->shared_gate_up, shared ? (uint64_t)2 * opts->shared_I * H * es : 0},
+               {opts->shared_down, shared ? (uint64_t)H * opts->shared_I * es : 0},
+               {opts->router_bias, (uint64_t)E * 4},
+               {opts->workspace, opts->workspace_bytes}};
+    for (const Range &r : ins)
+        if (overlaps(out, out_bytes, r.p, r.n)) return fail(MOE_ERR_INVALID_ARG, "out overlaps an input or the workspace");
+
+    const moe::Shape s = make_shape(T, H, I, E, k, opts);
+    const int64_t need = moe::workspace_layout(s, nullptr, nullptr);
+    if (!opts->workspace || (int64_t)opts->workspace_bytes < need)
+        return fail(MOE_ERR_WORKSPACE, "workspace of %zu bytes at %p; %lld bytes needed", opts->workspace_bytes,
+                    opts->workspace, (long long)need);
+    if (!aligned(opts->workspace, 256)) return fail(MOE_ERR_ALIGNMENT, "workspace is not 256-byte aligned");
+
+    moe::Workspace ws;
+    moe::workspace_layout(s, opts->workspace, &ws);
+    hipStream_t st = (hipStream_t)opts->stream;
+
+    const bool f32 = opts->dtype == MOE_F32;
+    bool skinny;
+    if (opts->flags & MOE_FLAG_FORCE_SKINNY) skinny = true;
+    else if (opts->flags & MOE_FLAG_FORCE_TILED) skinny = false;
+    else skinny = T * k <= 32 * E;  // about 32 rows per expert or fewer: stream the weights
+
+    hipError_t e = hipSuccess;
+    int step = 0;
+    auto check = [&](hipError_t err, const char *what) -> int {
+        step++;
+        if (err == hipSuccess && debug_sync()) err = hipStreamSynchronize(st);
+        if (err != hipSuccess)
+            return fail(MOE_ERR_HIP, "%s (step %d) failed: %s", what, step, hipGetErrorString(err));
+        return MOE_OK;
+    };
+
+    if ((rc = check(moe::launch_router_topk(s, hidden, router_w, opts->router_bias, opts->routed_scale,
+                                            opts->router_logits, ws, st),
+                    "router_topk")))
+        return rc;
+    if (opts->topk_ids || opts->topk_weights) {
+        if (opts->topk_ids &&
+            (e = hipMemcpyAsync(opts->topk_ids, ws.ids, (size_t)(T * k * 4), hipMemcpyDeviceToDevice, st)) != hipSuccess)
+            return check(e, "copy topk_ids");
+        if (opts->topk_weights &&
+            (e = hipMemcpyAsync(opts->topk_weights, ws.wts, (size_t)(T * k * 4), hipMemcpyDeviceToDevice, st)) != hipSuccess)
+            return check(e, "copy topk_weights");
+    }
+    if ((rc = check(moe::launch_route_scan(s, opts->expert_counts, opts->expert_offsets, ws, st), "route_scan")))
+        return rc;
+    if ((rc = check(moe::launch_route_permute(s, opts->perm, opts->inv_perm, ws, st), "route_permute")))
+        return rc;
+
+    moe::GemmProblem gu;
+    gu.A = hidden;
+    gu.a_rows = ws.row_token;
+    gu.W = gate_up;
+    gu.w_expert_stride = 2 * I * H;
+    gu.K = H;
+    gu.N = I;
+    gu.C = ws.h;
+    gu.c_rows = nullptr;
+    gu.c_scale = nullptr;
+    gu.counts = ws.counts;
+    gu.offsets = ws.offsets;
+    gu.row_expert = ws.row_expert;
+    gu.tiles = ws.tiles;
+    gu.tile_start = ws.tile_start;
+    gu.E = E;
+    gu.dense_rows = 0;
+    gu.total_rows = T * k;
+
+    moe::GemmProblem dn = gu;
+    dn.A = ws.h;
+    dn.a_rows = nullptr;
+    dn.W = down;
+    dn.w_expert_stride = H * I;
+    dn.K = I;
+    dn.N = H;
+    dn.C = ws.slot;
+    dn.c_rows = ws.perm;
+    dn.c_scale = ws.row_weight;
+
+    if (f32) {
+        if ((rc = check(moe::launch_gate_up_f32(gu, st), "gate_up f32"))) return rc;
+        if ((rc = check(moe::launch_down_f32(dn, st), "down f32"))) return rc;
+    } else if (skinny) {
+        if ((rc = check(moe::launch_gate_up_skinny(gu, st), "gate_up skinny"))) return rc;
+        if ((rc = check(moe::launch_down_skinny(dn, st), "down skinny"))) return rc;
+    } else {
+        if ((rc = check(moe::launch_gate_up_tiled(gu, st), "gate_up tiled"))) return rc;
+        if ((rc = check(moe::launch_down_tiled(dn, st), "down tiled"))) return rc;
+    }
+
+    if (shared) {
+        moe::GemmProblem sg = gu;
+        sg.a_rows = nullptr;
+        sg.W = opts->shared_gate_up;
+        sg.w_expert_stride = 0;
+        sg.N = opts->shared_I;
+        sg.C = ws.sh_h;
+        sg.dense_rows = T;
+        sg.total_rows = T;
+        moe::GemmProblem sd = sg;
+        sd.A = ws.sh_h;
+        sd.W = opts->shared_down;
+        sd.K = opts->shared_I;
+        sd.N = H;
+        sd.C = ws.sh_y;
+        const bool sh_skinny = (opts->flags & MOE_FLAG_FORCE_SKINNY) ||
+                               (!(opts->flags & MOE_FLAG_FORCE_TILED) && T <= 32);
+        if (f32) {
+            if ((rc = check(moe::launch_gate_up_f32(sg, st), "shared gate_up f32"))) return rc;
+            if ((rc = check(moe::launch_down_f32(sd, st), "shared down f32"))) return rc;
+        } else if (sh_skinny) {
+            if ((rc = check(moe::launch_gate_up_skinny(sg, st), "shared gate_up skinny"))) return rc;
+            if ((rc = check(moe::launch_down_skinny(sd, st), "shared down skinny"))) return rc;
+        } else {
+            if ((rc = check(moe::launch_gate_up_tiled(sg, st), "shared gate_up tiled"))) return rc;
+            if ((rc = check(moe::launch_down_tiled(sd, st), "shared down tiled"))) return rc;
+        }
+    }
+    if ((rc = check(moe::launch_combine(s, ws.slot, shared ? ws.sh_y : nullptr, out, st), "combine"))) return rc;
+    return MOE_OK;
+}
+
+}  // extern "C"

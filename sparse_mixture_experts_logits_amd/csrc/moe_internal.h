@@ -1,0 +1,130 @@
+// Internal declarations shared by the HIP translation units of the MoE
+// library: device helpers, workspace layout and kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+// ------------------------------------------------------------------ device helpers
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
+
+struct alignas(16) u32x4 {
+    uint32_t x, y, z, w;
+};
+
+__device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xffff0000u); }
+
+// fp32 -> bf16 bits, round to nearest even (inputs are finite).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    return (u + (((u >> 16) & 1u) + 0x7fffu)) >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
+{
+    return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+
+__device__ __forceinline__ float silu_f32(float g) { return g / (1.0f + __expf(-g)); }
+
+// ------------------------------------------------------------------ routing constants
+
+constexpr int kRouterTokensPerBlock = 16;  // 4 waves x 4 tokens
+constexpr int kMaxExperts = 256;
+
+// Device tile of the large-M grouped GEMM: rows [row0, row0 + rows) of the
+// expert-sorted assignment list, all belonging to expert `expert`.
+struct alignas(16) MTile {
+    int32_t expert;
+    int32_t row0;
+    int32_t rows;
+    int32_t pad;
+};
+
+// ------------------------------------------------------------------ workspace
+
+struct Workspace {
+    int32_t *ids;          // [TK] selected experts, flat t*k+j
+    float *wts;            // [TK] routed weights (x routed_scale)
+    int32_t *blk_counts;   // [nblk][E] per-router-block histogram
+    int32_t *blk_base;     // [nblk][E] first sorted position of each block's run
+    int32_t *counts;       // [E]
+    int32_t *offsets;      // [E+1]
+    int32_t *tile_start;   // [E+1] first M-tile of each expert (large-M schedule)
+    MTile *tiles;          // [max_tiles]
+    int32_t *perm;         // [TK] sorted position -> flat assignment
+    int32_t *inv;          // [TK] flat assignment -> sorted position
+    int32_t *row_token;    // [TK] sorted position -> token
+    float *row_weight;     // [TK] sorted position -> routed weight
+    int32_t *row_expert;   // [TK] sorted position -> expert
+    void *h;               // [TK, I] activation of the routed experts (bf16 or f32)
+    float *slot;           // [TK, H] weighted routed outputs, flat-assignment order
+    void *sh_h;            // [T, shared_I] shared-expert activation
+    float *sh_y;           // [T, H] shared-expert output
+};
+
+struct Shape {
+    int64_t T, H, I, E;
+    int k;
+    int64_t sharedI;
+    int dtype;       // 0 bf16, 1 f32
+    int nblk;        // router blocks
+    int tileBM;      // rows per M-tile of the large-M schedule
+    int64_t maxTiles;
+};
+
+// Byte layout of the workspace; returns total bytes, fills ws when base != null.
+int64_t workspace_layout(const Shape &s, void *base, Workspace *ws);
+
+// ------------------------------------------------------------------ launchers (return hipError_t)
+
+hipError_t launch_router_topk(const Shape &s, const void *X, const void *Wr, const float *bias,
+                              float routed_scale, float *logits_out, const Workspace &ws,
+                              hipStream_t st);
+hipError_t launch_route_scan(const Shape &s, int32_t *counts_out, int32_t *offsets_out,
+                             const Workspace &ws, hipStream_t st);
+hipError_t launch_route_permute(const Shape &s, int32_t *perm_out, int32_t *inv_out,
+                                const Workspace &ws, hipStream_t st);
+
+// Grouped expert GEMMs. `dense_rows` > 0 selects the dense form used by the
+// shared expert: one group, rows [0, dense_rows), identity row maps.
+struct GemmProblem {
+    const void *A;           // gate_up: hidden [T, K]; down: h [rows, K]
+    const int32_t *a_rows;   // gate_up: sorted position -> token (null = identity)
+    const void *W;           // packed weights
+    int64_t w_expert_stride; // elements between experts (0 for dense)
+    int64_t K;               // reduction length
+    int64_t N;               // gate_up: I (h columns); down: H
+    void *C;                 // gate_up: h [rows, N]; down: fp32 [.., N]
+    const int32_t *c_rows;   // down: sorted position -> output row (null = identity)
+    const float *c_scale;    // down: sorted position -> weight (null = 1)
+    const int32_t *counts;   // [E] rows per expert (null in dense form)
+    const int32_t *offsets;  // [E+1]
+    const int32_t *row_expert;  // [rows] (fp32 path)
+    const MTile *tiles;      // large-M schedule
+    const int32_t *tile_start;  // [E+1]
+    int64_t E;
+    int64_t dense_rows;
+    int64_t total_rows;      // host-known number of rows (TK or T)
+};
+
+hipError_t launch_gate_up_tiled(const GemmProblem &p, hipStream_t st);
+hipError_t launch_down_tiled(const GemmProblem &p, hipStream_t st);
+hipError_t launch_gate_up_skinny(const GemmProblem &p, hipStream_t st);
+hipError_t launch_down_skinny(const GemmProblem &p, hipStream_t st);
+hipError_t launch_gate_up_f32(const GemmProblem &p, hipStream_t st);
+hipError_t launch_down_f32(const GemmProblem &p, hipStream_t st);
+
+int tiled_block_m();
+
+hipError_t launch_combine(const Shape &s, const float *slot, const float *sh_y, void *out,
+                          hipStream_t st);
+
+}  // namespace moe

@@ -1,0 +1,345 @@
+// Router, top-k selection and the expert-major permutation.
+//
+// Router: a bias-free linear layer hidden -> experts, top-k by logit with
+// the weights renormalised over the selected experts ("深入解析 Transformers
+// 中的 PhiMoE" page, section 6: PhimoeTopKRouter and sparsemixer at
+// inference). Permutation: assignments sorted by expert id and grouped, as
+// the grouped_mm experts backend does ("Transformer中的混合专家架构详解" page,
+// experts backends section), with no token dropped (PhiMoE page, section 2,
+// item 4).
+//
+// Bit-exactness: the logit is the fp32 sum in the fixed order stated in
+// moe_mi355x.h (lane L of a wave owns elements 512c + 8L + v, c then v
+// ascending, then an xor butterfly 32..1). This translation unit is built
+// with -ffp-contract=off and uses explicit fmaf, so the compiler cannot
+// change that order. Counts come from integer atomics (order-independent)
+// and the permutation from explicit stable ranks, so ids, counts, offsets
+// and perm are identical on every run.
+#include "moe_internal.h"
+
+#include <float.h>
+#include <limits.h>
+
+namespace moe {
+
+namespace {
+
+constexpr int kTPW = 4;  // tokens per wave in the router
+constexpr int kEG = 16;  // experts accumulated per pass
+
+template <typename Tin>
+struct RowLoader;
+
+template <>
+struct RowLoader<__bf16> {
+    // 8 consecutive elements starting at element i of a bf16 row
+    __device__ __forceinline__ static void load8(const __bf16 *row, int64_t i, float (&v)[8])
+    {
+        u32x4 q = *reinterpret_cast<const u32x4 *>(row + i);
+        v[0] = bf16_lo(q.x); v[1] = bf16_hi(q.x);
+        v[2] = bf16_lo(q.y); v[3] = bf16_hi(q.y);
+        v[4] = bf16_lo(q.z); v[5] = bf16_hi(q.z);
+        v[6] = bf16_lo(q.w); v[7] = bf16_hi(q.w);
+    }
+};
+
+template <>
+struct RowLoader<float> {
+    __device__ __forceinline__ static void load8(const float *row, int64_t i, float (&v)[8])
+    {
+        float4 a = *reinterpret_cast<const float4 *>(row + i);
+        float4 b = *reinterpret_cast<const float4 *>(row + i + 4);
+        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+        v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    }
+};
+
+// (va, ia) ranks before (vb, ib): larger logit first, then lower expert index.
+__device__ __forceinline__ bool ranks_before(float va, int ia, float vb, int ib)
+{
+    return va > vb || (va == vb && ia < ib);
+}
+
+template <typename Tin>
+__global__ __launch_bounds__(256) void router_topk_kernel(
+    const Tin *__restrict__ X, const Tin *__restrict__ Wr, const float *__restrict__ bias, int T,
+    int H, int E, int k, float routed_scale, int32_t *__restrict__ ids, float *__restrict__ wts,
+    float *__restrict__ logits_out, int32_t *__restrict__ blk_counts)
+{
+    __shared__ float s_logit[kRouterTokensPerBlock][kMaxExperts];
+    __shared__ float s_sel[4][kMaxExperts];
+    __shared__ int s_hist[kMaxExperts];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int tblk = blockIdx.x * kRouterTokensPerBlock;
+    const int tw0 = tblk + wave * kTPW;
+
+    for (int e = threadIdx.x; e < E; e += 256) s_hist[e] = 0;
+
+    // ---- logits: each lane accumulates its 8-element slices in order
+    const Tin *xrow[kTPW];
+#pragma unroll
+    for (int j = 0; j < kTPW; j++) {
+        int t = tw0 + j;
+        t = t < T ? t : T - 1;  // rows past T repeat a valid row; their results are dropped
+        xrow[j] = X + (int64_t)t * H;
+    }
+    for (int eg = 0; eg < E; eg += kEG) {
+        float acc[kTPW][kEG];
+#pragma unroll
+        for (int j = 0; j < kTPW; j++)
+#pragma unroll
+            for (int q = 0; q < kEG; q++) acc[j][q] = 0.0f;
+        for (int c = 0; c * 512 < H; c++) {
+            const int64_t i0 = (int64_t)c * 512 + lane * 8;
+            if (i0 < H) {  // H is a multiple of 8: a slice is all valid or all absent
+                float xv[kTPW][8];
+#pragma unroll
+                for (int j = 0; j < kTPW; j++) RowLoader<Tin>::load8(xrow[j], i0, xv[j]);
+#pragma unroll
+                for (int q = 0; q < kEG; q++) {
+                    const int e = eg + q;
+                    if (e < E) {
+                        float wv[8];
+                        RowLoader<Tin>::load8(Wr + (int64_t)e * H, i0, wv);
+#pragma unroll
+                        for (int j = 0; j < kTPW; j++)
+#pragma unroll
+                            for (int v = 0; v < 8; v++) acc[j][q] = __builtin_fmaf(xv[j][v], wv[v], acc[j][q]);
+                    }
+                }
+            }
+        }
+        // xor butterfly over the 64 lanes: P[L] <- P[L] + P[L ^ d], d = 32..1
+#pragma unroll
+        for (int j = 0; j < kTPW; j++)
+#pragma unroll
+            for (int q = 0; q < kEG; q++) {
+                float v = acc[j][q];
+#pragma unroll
+                for (int d = 32; d >= 1; d >>= 1) v = v + __shfl_xor(v, d, 64);
+                acc[j][q] = v;
+            }
+        if (lane == 0) {
+#pragma unroll
+            for (int j = 0; j < kTPW; j++)
+#pragma unroll
+                for (int q = 0; q < kEG; q++) {
+                    const int e = eg + q;
+                    if (e < E) {
+                        float l = acc[j][q];
+                        if (bias) l = l + bias[e];
+                        s_logit[wave * kTPW + j][e] = l;
+                    }
+                }
+        }
+    }
+    __syncthreads();
+
+    // ---- optional logits output
+    if (logits_out) {
+        for (int idx = threadIdx.x; idx < kRouterTokensPerBlock * E; idx += 256) {
+            const int j = idx / E, e = idx - j * E;
+            const int t = tblk + j;
+            if (t < T) logits_out[(int64_t)t * E + e] = s_logit[j][e];
+        }
+    }
+
+    // ---- top-k per token: k rounds of a wave-wide arg-max under the ranking rule
+    for (int j = 0; j < kTPW; j++) {
+        const int t = tw0 + j;
+        if (t >= T) break;  // wave-uniform
+        const float *lrow = s_logit[wave * kTPW + j];
+        float v[4];
+        bool taken[4];
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+            const int e = lane + 64 * q;
+            v[q] = e < E ? lrow[e] : -FLT_MAX;
+            taken[q] = e >= E;
+        }
+        for (int s = 0; s < k; s++) {
+            float bv = -FLT_MAX;
+            int bi = INT_MAX;
+#pragma unroll
+            for (int q = 0; q < 4; q++) {
+                const int e = lane + 64 * q;
+                if (!taken[q] && ranks_before(v[q], e, bv, bi)) {
+                    bv = v[q];
+                    bi = e;
+                }
+            }
+#pragma unroll
+            for (int d = 32; d >= 1; d >>= 1) {
+                const float ov = __shfl_xor(bv, d, 64);
+                const int oi = __shfl_xor(bi, d, 64);
+                if (ranks_before(ov, oi, bv, bi)) {
+                    bv = ov;
+                    bi = oi;
+                }
+            }
+            // every lane now holds the winner (bv, bi)
+#pragma unroll
+            for (int q = 0; q < 4; q++)
+                if (lane + 64 * q == bi) taken[q] = true;
+            if (lane == 0) {
+                ids[(int64_t)t * k + s] = bi;
+                s_sel[wave][s] = bv;
+                atomicAdd(&s_hist[bi], 1);
+            }
+        }
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+        // weights: exp(l_s - l_0) / sum, times the routed scale
+        const float m = s_sel[wave][0];
+        float psum = 0.0f;
+        for (int s = lane; s < k; s += 64) psum += __expf(s_sel[wave][s] - m);
+#pragma unroll
+        for (int d = 32; d >= 1; d >>= 1) psum += __shfl_xor(psum, d, 64);
+        for (int s = lane; s < k; s += 64)
+            wts[(int64_t)t * k + s] = routed_scale * (__expf(s_sel[wave][s] - m) / psum);
+        __builtin_amdgcn_wave_barrier();
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < E; e += 256) blk_counts[(int64_t)blockIdx.x * E + e] = s_hist[e];
+}
+
+// One workgroup: expert totals, exclusive offsets, per-block bases and the
+// M-tile list of the large-M schedule.
+__global__ __launch_bounds__(1024) void route_scan_kernel(
+    const int32_t *__restrict__ blk_counts, int nblk, int E, int BM, int32_t *__restrict__ counts,
+    int32_t *__restrict__ offsets, int32_t *__restrict__ blk_base, int32_t *__restrict__ tile_start,
+    MTile *__restrict__ tiles, int32_t *__restrict__ counts_out, int32_t *__restrict__ offsets_out)
+{
+    __shared__ int s_part[1024];
+    __shared__ int s_cnt[kMaxExperts];
+    __shared__ int s_off[kMaxExperts + 1];
+    __shared__ int s_ts[kMaxExperts + 1];
+
+    const int tid = threadIdx.x;
+    const int G = 1024 / E;  // E <= 256 so G >= 4
+    const int g = tid / E, e = tid - (tid / E) * E;
+    const int chunk = (nblk + G - 1) / G;
+    const int b0 = g * chunk;
+    const int b1 = min(nblk, b0 + chunk);
+    if (g < G) {
+        int s = 0;
+        for (int b = b0; b < b1; b++) s += blk_counts[(int64_t)b * E + e];
+        s_part[g * E + e] = s;
+    }
+    __syncthreads();
+    if (tid < E) {
+        int run = 0;
+        for (int gg = 0; gg < G; gg++) {
+            const int c = s_part[gg * E + tid];
+            s_part[gg * E + tid] = run;
+            run += c;
+        }
+        s_cnt[tid] = run;
+    }
+    __syncthreads();
+    if (tid == 0) {
+        s_off[0] = 0;
+        s_ts[0] = 0;
+        for (int x = 0; x < E; x++) {
+            s_off[x + 1] = s_off[x] + s_cnt[x];
+            s_ts[x + 1] = s_ts[x] + (s_cnt[x] + BM - 1) / BM;
+        }
+    }
+    __syncthreads();
+    if (g < G) {
+        int base = s_off[e] + s_part[g * E + e];
+        for (int b = b0; b < b1; b++) {
+            blk_base[(int64_t)b * E + e] = base;
+            base += blk_counts[(int64_t)b * E + e];
+        }
+    }
+    if (tid < E) {
+        counts[tid] = s_cnt[tid];
+        if (counts_out) counts_out[tid] = s_cnt[tid];
+        const int nt = (s_cnt[tid] + BM - 1) / BM;
+        for (int i = 0; i < nt; i++) {
+            MTile m;
+            m.expert = tid;
+            m.row0 = s_off[tid] + i * BM;
+            m.rows = min(BM, s_cnt[tid] - i * BM);
+            m.pad = 0;
+            tiles[s_ts[tid] + i] = m;
+        }
+    }
+    if (tid <= E) {
+        offsets[tid] = s_off[tid];
+        tile_start[tid] = s_ts[tid];
+        if (offsets_out) offsets_out[tid] = s_off[tid];
+    }
+}
+
+// Scatter: assignment a of router block b goes to sorted position
+// blk_base[b][e] + (number of earlier assignments of block b with expert e).
+__global__ __launch_bounds__(256) void route_permute_kernel(
+    const int32_t *__restrict__ ids, const float *__restrict__ wts, const int32_t *__restrict__ blk_base,
+    int T, int k, int E, int32_t *__restrict__ perm, int32_t *__restrict__ inv,
+    int32_t *__restrict__ row_token, float *__restrict__ row_weight, int32_t *__restrict__ row_expert,
+    int32_t *__restrict__ perm_out, int32_t *__restrict__ inv_out)
+{
+    __shared__ int s_ids[kRouterTokensPerBlock * kMaxExperts];
+    const int t0 = blockIdx.x * kRouterTokensPerBlock;
+    const int nt = min(kRouterTokensPerBlock, T - t0);
+    const int n = nt * k;
+    const int64_t a0 = (int64_t)t0 * k;
+    for (int i = threadIdx.x; i < n; i += 256) s_ids[i] = ids[a0 + i];
+    __syncthreads();
+    for (int i = threadIdx.x; i < n; i += 256) {
+        const int e = s_ids[i];
+        int r = 0;
+        for (int j = 0; j < i; j++) r += (s_ids[j] == e);
+        const int p = blk_base[(int64_t)blockIdx.x * E + e] + r;
+        const int a = (int)(a0 + i);
+        perm[p] = a;
+        inv[a] = p;
+        row_token[p] = a / k;
+        row_weight[p] = wts[a];
+        row_expert[p] = e;
+        if (perm_out) perm_out[p] = a;
+        if (inv_out) inv_out[a] = p;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_router_topk(const Shape &s, const void *X, const void *Wr, const float *bias,
+                              float routed_scale, float *logits_out, const Workspace &ws,
+                              hipStream_t st)
+{
+    dim3 grid(s.nblk), block(256);
+    if (s.dtype == 0)
+        hipLaunchKernelGGL(router_topk_kernel<__bf16>, grid, block, 0, st, (const __bf16 *)X,
+                           (const __bf16 *)Wr, bias, (int)s.T, (int)s.H, (int)s.E, s.k, routed_scale,
+                           ws.ids, ws.wts, logits_out, ws.blk_counts);
+    else
+        hipLaunchKernelGGL(router_topk_kernel<float>, grid, block, 0, st, (const float *)X,
+                           (const float *)Wr, bias, (int)s.T, (int)s.H, (int)s.E, s.k, routed_scale,
+                           ws.ids, ws.wts, logits_out, ws.blk_counts);
+    return hipGetLastError();
+}
+
+hipError_t launch_route_scan(const Shape &s, int32_t *counts_out, int32_t *offsets_out,
+                             const Workspace &ws, hipStream_t st)
+{
+    hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(1024), 0, st, ws.blk_counts, s.nblk,
+                       (int)s.E, s.tileBM, ws.counts, ws.offsets, ws.blk_base, ws.tile_start,
+                       ws.tiles, counts_out, offsets_out);
+    return hipGetLastError();
+}
+
+hipError_t launch_route_permute(const Shape &s, int32_t *perm_out, int32_t *inv_out,
+                                const Workspace &ws, hipStream_t st)
+{
+    hipLaunchKernelGGL(route_permute_kernel, dim3(s.nblk), dim3(256), 0, st, ws.ids, ws.wts,
+                       ws.blk_base, (int)s.T, s.k, (int)s.E, ws.perm, ws.inv, ws.row_token,
+                       ws.row_weight, ws.row_expert, perm_out, inv_out);
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,156 @@
+"""C-ABI checks that need no GPU: the library loads, exports every entry point
+its header declares, mirrors the options struct, sizes the workspace, and
+rejects bad arguments before making any HIP call (so only invalid calls are
+made here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import sparse_mixture_experts_logits_amd as moe
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_mi355x.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(moe.LIB_PATH), reason="library not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_\w+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    lib = moe.load_library()
+    names = declared_functions()
+    assert set(names) == set(moe.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_opts_struct_mirror_matches_library():
+    o = moe.new_opts()
+    assert o.struct_size == ctypes.sizeof(moe.MoeOpts)
+    assert o.dtype == 0 and o.routed_scale == 1.0 and o.flags == 0 and o.workspace is None
+
+
+def test_workspace_bytes_valid_and_monotone():
+    a = moe.workspace_bytes(32, 4096, 6400, 16, 2)
+    b = moe.workspace_bytes(4096, 4096, 6400, 16, 2)
+    c = moe.workspace_bytes(4096, 4096, 6400, 16, 2, shared_I=1024)
+    assert 0 < a < b < c
+    assert a % 256 == 0 and b % 256 == 0
+    # h (bf16) and the fp32 slots dominate: T*k*(2I + 4H) bytes
+    assert b >= 4096 * 2 * (2 * 6400 + 4 * 4096)
+    assert moe.workspace_bytes(0, 64, 64, 4, 2) >= 0
+
+
+@pytest.mark.parametrize("T,H,I,E,k,msg", [
+    (4, 4096, 6400, 16, 0, "k = 0"),
+    (4, 4096, 6400, 16, 17, "k = 17"),
+    (4, 4100, 6400, 16, 2, "H = 4100"),
+    (4, 4096, 6404, 16, 2, "I = 6404"),
+    (4, 4096, 6400, 257, 2, "E = 257"),
+    (-1, 4096, 6400, 16, 2, "T = -1"),
+])
+def test_workspace_bytes_rejects_bad_sizes(T, H, I, E, k, msg):
+    with pytest.raises(moe.MoeError) as ei:
+        moe.workspace_bytes(T, H, I, E, k)
+    assert ei.value.status == -1 and msg in str(ei.value)
+
+
+def call(T=4, H=64, I=32, E=4, k=2, opts=None, ptrs=None, out=None):
+    """moe_forward with fake device addresses: only argument checks may run."""
+    lib = moe.load_library()
+    base = 1 << 40
+    p = ptrs or dict(hidden=base, router_w=base + (1 << 30), gate_up=base + (2 << 30), down=base + (3 << 30))
+    if out is None:
+        out = base + (4 << 30)
+    o = opts if opts is not None else moe.new_opts()
+    vp = ctypes.c_void_p
+    rc = lib.moe_forward(vp(p["hidden"]), vp(p["router_w"]), vp(p["gate_up"]), vp(p["down"]), T, H, I, E, k,
+                         ctypes.byref(o) if o is not False else None, vp(out))
+    return rc, moe.last_error()
+
+
+def good_opts(nbytes=1 << 30):
+    o = moe.new_opts()
+    o.workspace = (1 << 40) + (8 << 30)
+    o.workspace_bytes = nbytes
+    return o
+
+
+def test_rejects_null_opts():
+    assert call(opts=False)[0] == -1
+
+
+def test_rejects_wrong_struct_size():
+    o = good_opts()
+    o.struct_size = 64
+    rc, msg = call(opts=o)
+    assert rc == -1 and "struct_size" in msg
+
+
+def test_rejects_bad_k_and_dtype():
+    assert call(k=5, opts=good_opts())[0] == -1
+    o = good_opts()
+    o.dtype = 7
+    assert call(opts=o)[0] == -1
+
+
+def test_zero_tokens_succeeds_without_pointers():
+    rc, _ = call(T=0, opts=good_opts(), ptrs=dict(hidden=0, router_w=0, gate_up=0, down=0), out=0)
+    assert rc == 0
+
+
+def test_rejects_null_and_misaligned_pointers():
+    base = 1 << 40
+    p = dict(hidden=0, router_w=base + (1 << 30), gate_up=base + (2 << 30), down=base + (3 << 30))
+    assert call(opts=good_opts(), ptrs=p)[0] == -1
+    p["hidden"] = base + 8
+    rc, msg = call(opts=good_opts(), ptrs=p)
+    assert rc == -4 and "aligned" in msg
+
+
+def test_rejects_small_or_missing_workspace():
+    rc, msg = call(opts=good_opts(nbytes=100))
+    assert rc == -3 and "needed" in msg
+    o = good_opts()
+    o.workspace = None
+    assert call(opts=o)[0] == -3
+    o = good_opts()
+    o.workspace = (1 << 40) + (8 << 30) + 16
+    assert call(opts=o)[0] == -4
+
+
+def test_rejects_output_aliasing_an_input():
+    base = 1 << 40
+    rc, msg = call(opts=good_opts(), out=base + 64)
+    assert rc == -1 and "overlaps" in msg
+
+
+def test_rejects_shared_expert_without_weights_and_bad_flags():
+    o = good_opts()
+    o.shared_I = 16
+    assert call(opts=o)[0] == -1
+    o = good_opts()
+    o.shared_I = 12
+    assert call(opts=o)[0] == -1
+    o = good_opts()
+    o.flags = moe.FLAG_FORCE_TILED | moe.FLAG_FORCE_SKINNY
+    assert call(opts=o)[0] == -1
+    o = good_opts()
+    o.flags = 0x80
+    assert call(opts=o)[0] == -1
+    o = good_opts()
+    o.routed_scale = float("nan")
+    assert call(opts=o)[0] == -1
+
+
+def test_missing_library_raises(tmp_path, monkeypatch):
+    monkeypatch.setattr(moe, "_lib", None)
+    monkeypatch.setattr(moe, "LIB_PATH", str(tmp_path / "absent.so"))
+    with pytest.raises(FileNotFoundError):
+        moe.load_library()

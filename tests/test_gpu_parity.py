@@ -1,0 +1,215 @@
+"""GPU parity: the HIP library against the CPU oracle on the same seeded inputs.
+
+Bar (per output): expert ids, counts, offsets and the permutation bit-exact;
+router logits bit-exact (both sides use the same fp32 order); routed weights
+within 2e-6 relative (exp rounding); layer output within
+max|out - ref| <= 2e-2 * max|ref| (bf16 inputs and output, fp32 accumulation).
+Full-size workloads check routing over every token and the output on a fixed
+sample of tokens that the oracle computes one by one.
+"""
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+import sparse_mixture_experts_logits_amd as moe  # noqa: E402
+
+OUT_TOL = 2e-2
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    moe.load_library()
+    yield
+
+
+# ------------------------------------------------------------------ helpers
+
+_host_cache = {}
+_dev_cache = {}
+
+
+def host_inputs(name):
+    if name not in _host_cache:
+        wl = W.BY_NAME[name]
+        donor = next((v for v in _host_cache.values() if W._same_weights(v.wl, wl)), None)
+        _host_cache[name] = W.make_inputs(wl, weights_from=donor)
+    return _host_cache[name]
+
+
+def dev(a):
+    key = (id(a), a.shape)
+    if key not in _dev_cache:
+        _dev_cache[key] = (a, moe.bf16_bits_to_tensor(a))
+    return _dev_cache[key][1]
+
+
+def run_gpu(inp, flags=0, T=None, shared=True):
+    wl = inp.wl
+    sgu = sdn = None
+    if shared and inp.shared_gate_up:
+        gu, dn = inp.shared_concat()
+        sgu, sdn = dev(gu), dev(dn)
+    bias = None if inp.bias is None else torch.from_numpy(inp.bias).cuda()
+    out, r = moe.moe_forward(dev(inp.hidden), dev(inp.router_w), dev(inp.gate_up), dev(inp.down), wl.k,
+                             routed_scale=wl.routed_scale, router_bias=bias, shared_gate_up=sgu,
+                             shared_down=sdn, flags=flags, return_routing=True)
+    torch.cuda.synchronize()
+    out = out.float().cpu().numpy()
+    r = {k: v.cpu().numpy() for k, v in r.items()}
+    return out, r
+
+
+def oracle_routing(inp):
+    wl = inp.wl
+    logits = oracle.router_logits(inp.hidden, inp.router_w, inp.bias)
+    ids, w = oracle.select_topk(logits, wl.k, wl.routed_scale)
+    counts, offsets, perm, inv = oracle.route(ids, wl.E)
+    return dict(logits=logits, ids=ids, weights=w, counts=counts, offsets=offsets, perm=perm, inv=inv)
+
+
+def oracle_out(inp, ref, tokens):
+    shared = list(zip(inp.shared_gate_up, inp.shared_down))
+    return oracle.moe_tokens(inp.hidden, inp.gate_up, inp.down, ref["ids"], ref["weights"],
+                             tokens=tokens, shared=shared)
+
+
+def check_routing(got, ref, what):
+    for key in ("ids", "counts", "offsets", "perm", "inv"):
+        assert np.array_equal(got[key], ref[key]), f"{what}: {key} differs"
+    assert np.array_equal(got["logits"].view(np.uint32), ref["logits"].view(np.uint32)), f"{what}: logits differ"
+    assert np.allclose(got["weights"], ref["weights"], rtol=2e-6, atol=1e-7), f"{what}: weights differ"
+
+
+def check_out(got, ref, what):
+    err = np.max(np.abs(got - ref))
+    scale = np.max(np.abs(ref))
+    rms = np.sqrt(np.mean((got - ref) ** 2)) / max(np.sqrt(np.mean(ref ** 2)), 1e-30)
+    _say(f"  {what}: max|err|/max|ref| = {err / scale:.3e}, rel rms = {rms:.3e}")
+    assert np.all(np.isfinite(got)), f"{what}: non-finite output"
+    assert err <= OUT_TOL * scale, f"{what}: max|err| {err:.4g} > {OUT_TOL} * {scale:.4g}"
+    return err / scale
+
+
+def sample_tokens(T, n=32):
+    if T <= n:
+        return np.arange(T, dtype=np.int32)
+    s = set(range(8)) | set(range(T - 8, T)) | set(np.linspace(0, T - 1, n - 16).astype(int).tolist())
+    return np.array(sorted(s), dtype=np.int32)
+
+
+# ------------------------------------------------------------------ small shapes, every output element
+
+SMALL = [
+    # name, kwargs for custom_inputs: ragged tails in M, N and K; several tiles per expert
+    ("ragged_bf16", dict(T=700, H=328, I=200, E=4, k=2)),
+    ("multi_tile_bf16", dict(T=1100, H=256, I=384, E=6, k=3)),
+    ("fine_grained_bf16", dict(T=96, H=192, I=64, E=32, k=6, routed_scale=2.5)),
+    ("shared_bf16", dict(T=130, H=136, I=72, E=8, k=2, n_shared=2, shared_I=40, routed_scale=0.5)),
+    ("biased_bf16", dict(T=257, H=512, I=128, E=16, k=2, bias=((0, 6.0), (13, -30.0), (14, -30.0), (15, -30.0)))),
+    ("single_expert_bf16", dict(T=40, H=64, I=48, E=1, k=1)),
+    ("k_equals_E_bf16", dict(T=50, H=64, I=32, E=5, k=5)),
+    ("one_token_bf16", dict(T=1, H=4096, I=256, E=16, k=2)),
+    ("f32_small", dict(T=77, H=96, I=40, E=5, k=2, dtype="f32", n_shared=1, shared_I=24)),
+]
+
+
+@pytest.mark.parametrize("name,kw", SMALL, ids=[s[0] for s in SMALL])
+@pytest.mark.parametrize("flags", [0, moe.FLAG_FORCE_TILED, moe.FLAG_FORCE_SKINNY], ids=["auto", "tiled", "skinny"])
+def test_small_full_parity(name, kw, flags):
+    _say(f"case {name} flags={flags}")
+    inp = W.custom_inputs(**kw, std_weight=0.05 if kw.get("dtype") != "f32" else 0.1)
+    ref = oracle_routing(inp)
+    out, got = run_gpu(inp, flags=flags)
+    check_routing(got, ref, name)
+    r_out = oracle_out(inp, ref, np.arange(inp.wl.T, dtype=np.int32))
+    rel = check_out(out, r_out, name)
+    if inp.wl.dtype == "f32":
+        assert rel < 1e-4
+
+
+def test_tiny_workload_full_parity():
+    inp = host_inputs("tiny_f32")
+    ref = oracle_routing(inp)
+    out, got = run_gpu(inp)
+    check_routing(got, ref, "tiny_f32")
+    r_out = oracle_out(inp, ref, np.arange(inp.wl.T, dtype=np.int32))
+    assert check_out(out, r_out, "tiny_f32") < 1e-4
+
+
+def test_router_ties_and_zero_router():
+    inp = W.custom_inputs(T=200, H=256, I=64, E=8, k=3)
+    wr = inp.router_w.copy()
+    wr[5] = wr[2]
+    wr[7] = wr[2]
+    inp.router_w = wr
+    ref = oracle_routing(inp)
+    _, got = run_gpu(inp)
+    check_routing(got, ref, "tied rows")
+    inp.router_w = np.zeros_like(wr)
+    ref = oracle_routing(inp)
+    out, got = run_gpu(inp)
+    check_routing(got, ref, "zero router")
+    assert np.all(got["ids"] == np.arange(3))
+
+
+def test_zero_tokens_is_a_no_op():
+    inp = W.custom_inputs(T=4, H=64, I=32, E=4, k=2)
+    h = dev(inp.hidden)[:0]
+    out = moe.moe_forward(h, dev(inp.router_w), dev(inp.gate_up), dev(inp.down), 2)
+    torch.cuda.synchronize()
+    assert out.shape == (0, 64)
+
+
+def test_run_to_run_bitwise_identical():
+    inp = W.custom_inputs(T=1100, H=256, I=384, E=6, k=3)
+    a, ra = run_gpu(inp)
+    b, rb = run_gpu(inp)
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    for key in ra:
+        assert np.array_equal(ra[key], rb[key])
+
+
+# ------------------------------------------------------------------ full-size workloads
+
+FULL = ["phimoe_decode", "phimoe_prefill", "instella_fine", "phimoe_skewed"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_workload(name):
+    _say(f"case {name}")
+    inp = host_inputs(name)
+    ref = oracle_routing(inp)
+    out, got = run_gpu(inp)
+    check_routing(got, ref, name)
+    if name == "phimoe_skewed":
+        frac0 = ref["counts"][0] / ref["counts"].sum()
+        _say(f"  expert 0 share {frac0:.3f}, counts {ref['counts'].tolist()}")
+        assert ref["counts"][13:].sum() == 0 and 0.45 < frac0 <= 0.5
+    toks = sample_tokens(inp.wl.T)
+    r_out = oracle_out(inp, ref, toks)
+    check_out(out[toks], r_out, name)
+
+
+@pytest.mark.parametrize("name,flags", [("phimoe_decode", moe.FLAG_FORCE_TILED),
+                                        ("instella_fine", moe.FLAG_FORCE_SKINNY)])
+def test_full_size_other_schedule(name, flags):
+    _say(f"case {name} flags={flags}")
+    inp = host_inputs(name)
+    ref = oracle_routing(inp)
+    out, got = run_gpu(inp, flags=flags)
+    check_routing(got, ref, name)
+    toks = sample_tokens(inp.wl.T, 16)
+    check_out(out[toks], oracle_out(inp, ref, toks), name)

@@ -162,14 +162,29 @@ class Inputs:
         return gu, dn
 
 
-def make_inputs(wl: Workload | str, T: int | None = None) -> Inputs:
+def _same_weights(a: Workload, b: Workload) -> bool:
+    return (a.seed, a.H, a.I, a.E, a.dtype, a.std_weight, a.n_shared, a.shared_I) == \
+        (b.seed, b.H, b.I, b.E, b.dtype, b.std_weight, b.n_shared, b.shared_I)
+
+
+def make_inputs(wl: Workload | str, T: int | None = None, weights_from: Inputs | None = None) -> Inputs:
     """Draw the inputs of a workload. ``T`` overrides the token count (hidden
-    rows are a prefix of the full workload's hidden stream when smaller)."""
+    rows are a prefix of the full workload's hidden stream when smaller).
+    ``weights_from`` reuses the weight arrays of another workload's inputs
+    when they come from the same draws (same seed, shapes and deviation)."""
     if isinstance(wl, str):
         wl = BY_NAME[wl]
     T = wl.T if T is None else T
     dt = wl.dtype
     hidden = draw(wl.seed, HIDDEN_BASE + wl.index, (T, wl.H), wl.std_hidden, dt)
+    if weights_from is not None and _same_weights(weights_from.wl, wl):
+        w = weights_from
+        bias = None
+        if wl.bias:
+            bias = np.zeros(wl.E, dtype=np.float32)
+            for e, v in wl.bias:
+                bias[e] = np.float32(v)
+        return Inputs(wl, hidden, w.router_w, w.gate_up, w.down, bias, w.shared_gate_up, w.shared_down)
     router_w = draw(wl.seed, TID_ROUTER, (wl.E, wl.H), wl.std_weight, dt)
     gate_up = draw(wl.seed, TID_GATE_UP, (wl.E, 2 * wl.I, wl.H), wl.std_weight, dt)
     down = draw(wl.seed, TID_DOWN, (wl.E, wl.H, wl.I), wl.std_weight, dt)
