@@ -1,6 +1,279 @@
-"""Benchmark of the sparse MoE feed-forward layer (placeholder, filled in below)."""
+"""Benchmark of the MI355X sparse-MoE layer (one GPU).
+
+One step is one moe_forward call -- router, top-k, permutation, gate_up GEMM
+with fused SiLU*up, down GEMM with the weighted scatter, combine -- over one
+batch of seeded synthetic tokens already resident in HBM. Prints ONE JSON
+line on stdout.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+Default workload: the PhiMoE decode step (T=32, H=4096, I=6400, E=16, top-2),
+a weight-bandwidth-bound case. The PhiMoE prefill chunk (T=4096) is measured
+in the same run and reported under "prefill" (MFMA-bound). Every timed call
+records stage events, so the per-kernel durations and the roofline figures
+come from the same timed region.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0         # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+FP32_PEAK_TFLOPS = 157.3       # MI355X fp32 vector
+METRIC = "MoE layer tokens/sec + % of bf16 MFMA peak (prefill) / % HBM BW (decode)"
+KERNEL_SOURCES = {"gate_up": ("gemm_skinny.hip", "gemm_tiled.hip"), "down": ("gemm_skinny.hip", "gemm_tiled.hip")}
 
 
 def decode_tokens_per_s_bound(bandwidth_Bps: float, bytes_per_token: float) -> float:
     """Bandwidth-bound decode rate: every token streams its active weights once."""
     return bandwidth_Bps / bytes_per_token
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ------------------------------------------------------------------ algorithmic work
+
+def work(wl, counts):
+    """Algorithmic FLOPs and bytes of the layer and of its two expert GEMMs.
+
+    Bytes count what the method itself must move once: weights of experts that
+    received tokens, hidden, router weights and the output for the layer; for
+    a GEMM kernel, its weights once plus its input and output activations once
+    (gate_up: hidden in, h out; down: h in, fp32 weighted slots out)."""
+    es = 2 if wl.dtype == "bf16" else 4
+    T, H, I, E, k = wl.T, wl.H, wl.I, wl.E, wl.k
+    TK = T * k
+    hit = int(sum(1 for c in counts if c > 0))
+    Is = wl.n_shared * wl.shared_I
+    f_gu = 2.0 * TK * 2 * I * H
+    f_dn = 2.0 * TK * H * I
+    f_router = 2.0 * T * H * E
+    f_shared = 2.0 * T * 3 * Is * H
+    b_gu = hit * 2 * I * H * es + T * H * es + TK * I * es
+    b_dn = hit * H * I * es + TK * I * es + TK * H * 4
+    b_layer = hit * 3 * I * H * es + 2 * T * H * es + E * H * es + 3 * Is * H * es
+    return dict(hit=hit, flop_layer=f_gu + f_dn + f_router + f_shared, bytes_layer=b_layer,
+                flop_gate_up=f_gu, bytes_gate_up=b_gu, flop_down=f_dn, bytes_down=b_dn)
+
+
+def source_hash(names):
+    h = hashlib.sha256()
+    for n in sorted(set(names)):
+        with open(os.path.join(ROOT, "sparse_mixture_experts_logits_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        d = json.load(open(path))
+    except (OSError, ValueError):
+        return None
+    if d.get("source_hash") != source_hash(KERNEL_SOURCES[kernel]):
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+# ------------------------------------------------------------------ GPU timing
+
+def run_workload(name, steps, warmup):
+    import torch
+    import numpy as np
+    import sparse_mixture_experts_logits_amd as moe
+    import workloads as W
+
+    wl = W.BY_NAME[name]
+    t0 = time.time()
+    inp = W.make_inputs(wl, weights_from=_INPUT_CACHE.get("weights"))
+    _INPUT_CACHE.setdefault("weights", inp)
+    log(f"[bench] {name}: inputs drawn in {time.time() - t0:.1f}s")
+    dev = torch.device("cuda", 0)
+    d = lambda a: moe.bf16_bits_to_tensor(a, dev)  # noqa: E731
+    key = id(inp.gate_up)
+    if key not in _DEV_CACHE:
+        _DEV_CACHE.clear()
+        _DEV_CACHE[key] = (d(inp.router_w), d(inp.gate_up), d(inp.down))
+    router_w, gate_up, down = _DEV_CACHE[key]
+    hidden = d(inp.hidden)
+    sgu = sdn = None
+    if inp.shared_gate_up:
+        gu, dn = inp.shared_concat()
+        sgu, sdn = d(gu), d(dn)
+    bias = None if inp.bias is None else torch.from_numpy(inp.bias).to(dev)
+    kw = dict(routed_scale=wl.routed_scale, router_bias=bias, shared_gate_up=sgu, shared_down=sdn)
+
+    out = torch.empty((wl.T, wl.H), dtype=hidden.dtype, device=dev)
+    need = moe.workspace_bytes(wl.T, wl.H, wl.I, wl.E, wl.k, shared_I=sgu.shape[0] // 2 if sgu is not None else 0,
+                               dtype=0 if wl.dtype == "bf16" else 1)
+    ws = torch.empty((need,), dtype=torch.uint8, device=dev)
+    _, routing = moe.moe_forward(hidden, router_w, gate_up, down, wl.k, return_routing=True, out=out,
+                                 workspace=ws, **kw)
+    torch.cuda.synchronize()
+    counts = routing["counts"].cpu().numpy().tolist()
+
+    nev = moe.STAGE_EVENTS
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(steps)]
+    for evs in events:
+        for e in evs:
+            e.record()  # creates the underlying hipEvent_t
+    torch.cuda.synchronize()
+    handles = [(ctypes.c_void_p * nev)(*[e.cuda_event for e in evs]) for evs in events]
+
+    for _ in range(warmup):
+        moe.moe_forward(hidden, router_w, gate_up, down, wl.k, out=out, workspace=ws, **kw)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # timed region (one rank: the barrier is the synchronize)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record()
+    for i in range(steps):
+        moe.moe_forward(hidden, router_w, gate_up, down, wl.k, out=out, workspace=ws, stage_events=handles[i], **kw)
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_ms = start.elapsed_time(end)
+    stage_ms = np.zeros(nev - 1)
+    for evs in events:
+        for j in range(nev - 1):
+            stage_ms[j] += evs[j].elapsed_time(evs[j + 1])
+    stage_ms /= steps
+    return dict(wl=wl, counts=counts, wall_s=wall, gpu_ms=gpu_ms, steps=steps,
+                stages=dict(zip(moe.STAGES, stage_ms.tolist())), inp=inp)
+
+
+_INPUT_CACHE = {}
+_DEV_CACHE = {}
+
+
+def roofline_of(res):
+    """Roofline of the dominant expert GEMM (the stage with the largest time)."""
+    wl = res["wl"]
+    w = work(wl, res["counts"])
+    st = res["stages"]
+    kernel = "gate_up" if st["gate_up"] >= st["down"] else "down"
+    dur_s = st[kernel] / 1e3
+    decode = wl.T * wl.k <= 32 * wl.E
+    if decode:
+        achieved = w[f"bytes_{kernel}"] / dur_s / 1e9
+        r = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBPS, unit="GB/s",
+                 frac=round(achieved / HBM_PEAK_GBPS, 4))
+    else:
+        peak = BF16_PEAK_TFLOPS if wl.dtype == "bf16" else FP32_PEAK_TFLOPS
+        achieved = w[f"flop_{kernel}"] / dur_s / 1e12
+        r = dict(bound="mfma", achieved=round(achieved, 1), peak=peak, unit="TFLOP/s",
+                 frac=round(achieved / peak, 4))
+    tr = measured_traffic(kernel, wl.name)
+    r["traffic"] = tr
+    r["kernel"] = kernel
+    r["avg_launch_ms"] = round(st[kernel], 4)
+    return r, w
+
+
+def layer_summary(res, w):
+    wl = res["wl"]
+    ms = res["wall_s"] * 1e3 / res["steps"]
+    s = ms / 1e3
+    return dict(ms_per_step=round(ms, 4), tokens_per_s=round(wl.T / s, 1),
+                tflops=round(w["flop_layer"] / s / 1e12, 2), gbps=round(w["bytes_layer"] / s / 1e9, 1),
+                frac_hbm=round(w["bytes_layer"] / s / 1e9 / HBM_PEAK_GBPS, 4),
+                frac_mfma=round(w["flop_layer"] / s / 1e12 / BF16_PEAK_TFLOPS, 4),
+                experts_hit=w["hit"], stages_ms={k: round(v, 4) for k, v in res["stages"].items()})
+
+
+# ------------------------------------------------------------------ CPU oracle baseline
+
+def cpu_baseline(res, max_tokens):
+    import numpy as np
+    import oracle
+    inp = res["inp"]
+    wl = inp.wl
+    n = min(wl.T, max_tokens)
+    toks = np.arange(n, dtype=np.int32)
+    t0 = time.perf_counter()
+    logits = oracle.router_logits(inp.hidden[:n], inp.router_w, inp.bias)
+    ids, wts = oracle.select_topk(logits, wl.k, wl.routed_scale)
+    oracle.route(ids, wl.E)
+    shared = list(zip(inp.shared_gate_up, inp.shared_down))
+    oracle.moe_tokens(inp.hidden[:n], inp.gate_up, inp.down, ids, wts, tokens=toks, shared=shared)
+    dt = time.perf_counter() - t0
+    what = "all" if n == wl.T else "the first"
+    return dict(value=round(n / dt, 3), unit="tokens/s", cores=oracle.num_threads(), kind="oracle",
+                sample=f"{what} {n} tokens of {wl.name} (routing + every selected expert FFN), {dt:.1f} s")
+
+
+# ------------------------------------------------------------------ main
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="phimoe_decode")
+    ap.add_argument("--prefill-steps", type=int, default=20)
+    ap.add_argument("--no-prefill", action="store_true", help="skip the secondary prefill measurement")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-tokens", type=int, default=32)
+    args = ap.parse_args(argv)
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the layer here has no multi-GPU path (run with --gpus 1).",
+              file=sys.stderr)
+        return 2
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+
+    res = run_workload(args.workload, args.steps, args.warmup)
+    roof, w = roofline_of(res)
+    lay = layer_summary(res, w)
+    wl = res["wl"]
+    line = {
+        "metric": METRIC,
+        "value": lay["tokens_per_s"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": lay["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic (seeded normal draws; no checkpoint)",
+        "config": {"workload": wl.name, "T": wl.T, "H": wl.H, "I": wl.I, "E": wl.E, "k": wl.k,
+                   "routed_scale": wl.routed_scale, "shared_I": wl.n_shared * wl.shared_I,
+                   "parallelism": "single GPU"},
+        "roofline": roof,
+        "layer": lay,
+    }
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline(res, args.cpu_tokens)
+    if not args.no_prefill and args.workload != "phimoe_prefill":
+        pres = run_workload("phimoe_prefill", args.prefill_steps, 3)
+        proof, pw = roofline_of(pres)
+        line["prefill"] = dict(workload="phimoe_prefill", roofline=proof, layer=layer_summary(pres, pw))
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -87,7 +87,27 @@ typedef struct moe_opts {
     void *workspace;
     size_t workspace_bytes;
     void *stream;             /* hipStream_t to enqueue on; NULL = default stream    */
+    /* Optional stage timing: MOE_NUM_STAGE_EVENTS caller-created hipEvent_t
+     * handles (or NULL). Event 0 is recorded on the stream before the first
+     * kernel and event i+1 after stage i (see MOE_STAGE_*), so the time of
+     * stage i is the elapsed time between events i and i+1. Stages that do
+     * not run (no shared expert) take zero time. */
+    void *const *stage_events;
 } moe_opts;
+
+/* Stages of moe_forward, in launch order. */
+enum {
+    MOE_STAGE_ROUTER = 0,        /* router logits, top-k, weights, block histogram */
+    MOE_STAGE_SCAN = 1,          /* expert counts, offsets, tile list              */
+    MOE_STAGE_PERMUTE = 2,       /* stable expert-major permutation                */
+    MOE_STAGE_GATE_UP = 3,       /* routed gate_up GEMM with fused silu(gate)*up   */
+    MOE_STAGE_DOWN = 4,          /* routed down GEMM, weighted slot scatter        */
+    MOE_STAGE_SHARED_GATE_UP = 5,
+    MOE_STAGE_SHARED_DOWN = 6,
+    MOE_STAGE_COMBINE = 7,       /* ordered slot sum (+ shared), output rounding   */
+    MOE_NUM_STAGES = 8,
+    MOE_NUM_STAGE_EVENTS = 9
+};
 
 /* Fills *opts with defaults: dtype MOE_BF16, routed_scale 1, everything else 0. */
 void moe_opts_init(moe_opts *opts);

@@ -22,6 +22,8 @@ MOE_F32 = 1
 FLAG_FORCE_TILED = 0x1
 FLAG_FORCE_SKINNY = 0x2
 EXPORTS = ("moe_opts_init", "moe_workspace_bytes", "moe_forward", "moe_last_error")
+STAGES = ("router", "scan", "permute", "gate_up", "down", "shared_gate_up", "shared_down", "combine")
+STAGE_EVENTS = len(STAGES) + 1
 
 STATUS = {0: "MOE_OK", -1: "MOE_ERR_INVALID_ARG", -2: "MOE_ERR_UNSUPPORTED", -3: "MOE_ERR_WORKSPACE",
           -4: "MOE_ERR_ALIGNMENT", -5: "MOE_ERR_HIP"}
@@ -48,6 +50,7 @@ class MoeOpts(ctypes.Structure):
         ("workspace", ctypes.c_void_p),
         ("workspace_bytes", ctypes.c_size_t),
         ("stream", ctypes.c_void_p),
+        ("stage_events", ctypes.c_void_p),
     ]
 
 
@@ -67,6 +70,10 @@ def load_library():
         if not os.path.exists(LIB_PATH):
             raise FileNotFoundError(
                 f"{LIB_PATH} is missing; build it with `python -m sparse_mixture_experts_logits_amd.build`")
+        try:  # bind to the HIP runtime torch ships (same soname) when torch is present
+            import torch  # noqa: F401
+        except ImportError:  # pragma: no cover
+            pass
         lib = ctypes.CDLL(LIB_PATH)
         vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
         lib.moe_opts_init.argtypes = [ctypes.POINTER(MoeOpts)]
@@ -117,7 +124,7 @@ def bf16_bits_to_tensor(a: np.ndarray, device="cuda"):
 
 def moe_forward(hidden, router_w, gate_up, down, k: int, *, routed_scale: float = 1.0, router_bias=None,
                 shared_gate_up=None, shared_down=None, flags: int = 0, return_routing: bool = False,
-                out=None, workspace=None, stream=None):
+                out=None, workspace=None, stream=None, stage_events=None):
     """Run the MoE layer on torch tensors already on the GPU.
 
     hidden [T, H], router_w [E, H], gate_up [E, 2I, H], down [E, H, I] (all
@@ -192,6 +199,8 @@ def moe_forward(hidden, router_w, gate_up, down, k: int, *, routed_scale: float 
             if t is not None:
                 t.record_stream(stream)
     o.stream = stream.cuda_stream
+    if stage_events is not None:
+        o.stage_events = ctypes.cast(stage_events, ctypes.c_void_p)
     rc = lib.moe_forward(_ptr(hidden), _ptr(router_w), _ptr(gate_up), _ptr(down), T, H, I, E, int(k),
                          ctypes.byref(o), _ptr(out))
     if rc != 0:

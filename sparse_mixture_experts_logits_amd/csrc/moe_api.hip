@@ -222,10 +222,18 @@ int moe_forward(const void *hidden, const void *router_w, const void *gate_up, c
             return fail(MOE_ERR_HIP, "%s (step %d) failed: %s", what, step, hipGetErrorString(err));
         return MOE_OK;
     };
+    // stage boundary i (0 = before the first kernel); no-op without events
+    auto mark = [&](int i) -> int {
+        if (!opts->stage_events) return MOE_OK;
+        hipError_t err = hipEventRecord((hipEvent_t)opts->stage_events[i], st);
+        if (err != hipSuccess) return fail(MOE_ERR_HIP, "hipEventRecord(stage %d): %s", i, hipGetErrorString(err));
+        return MOE_OK;
+    };
+    if ((rc = mark(0))) return rc;
 
     if ((rc = check(moe::launch_router_topk(s, hidden, router_w, opts->router_bias, opts->routed_scale,
                                             opts->router_logits, ws, st),
-                    "router_topk")))
+                    "router_topk")) || (rc = mark(1 + MOE_STAGE_ROUTER)))
         return rc;
     if (opts->topk_ids || opts->topk_weights) {
         if (opts->topk_ids &&
@@ -235,9 +243,11 @@ int moe_forward(const void *hidden, const void *router_w, const void *gate_up, c
             (e = hipMemcpyAsync(opts->topk_weights, ws.wts, (size_t)(T * k * 4), hipMemcpyDeviceToDevice, st)) != hipSuccess)
             return check(e, "copy topk_weights");
     }
-    if ((rc = check(moe::launch_route_scan(s, opts->expert_counts, opts->expert_offsets, ws, st), "route_scan")))
+    if ((rc = check(moe::launch_route_scan(s, opts->expert_counts, opts->expert_offsets, ws, st), "route_scan")) ||
+        (rc = mark(1 + MOE_STAGE_SCAN)))
         return rc;
-    if ((rc = check(moe::launch_route_permute(s, opts->perm, opts->inv_perm, ws, st), "route_permute")))
+    if ((rc = check(moe::launch_route_permute(s, opts->perm, opts->inv_perm, ws, st), "route_permute")) ||
+        (rc = mark(1 + MOE_STAGE_PERMUTE)))
         return rc;
 
     moe::GemmProblem gu;
@@ -270,16 +280,14 @@ int moe_forward(const void *hidden, const void *router_w, const void *gate_up, c
     dn.c_rows = ws.perm;
     dn.c_scale = ws.row_weight;
 
-    if (f32) {
-        if ((rc = check(moe::launch_gate_up_f32(gu, st), "gate_up f32"))) return rc;
-        if ((rc = check(moe::launch_down_f32(dn, st), "down f32"))) return rc;
-    } else if (skinny) {
-        if ((rc = check(moe::launch_gate_up_skinny(gu, st), "gate_up skinny"))) return rc;
-        if ((rc = check(moe::launch_down_skinny(dn, st), "down skinny"))) return rc;
-    } else {
-        if ((rc = check(moe::launch_gate_up_tiled(gu, st), "gate_up tiled"))) return rc;
-        if ((rc = check(moe::launch_down_tiled(dn, st), "down tiled"))) return rc;
-    }
+    if (f32) rc = check(moe::launch_gate_up_f32(gu, st), "gate_up f32");
+    else if (skinny) rc = check(moe::launch_gate_up_skinny(gu, st), "gate_up skinny");
+    else rc = check(moe::launch_gate_up_tiled(gu, st), "gate_up tiled");
+    if (rc || (rc = mark(1 + MOE_STAGE_GATE_UP))) return rc;
+    if (f32) rc = check(moe::launch_down_f32(dn, st), "down f32");
+    else if (skinny) rc = check(moe::launch_down_skinny(dn, st), "down skinny");
+    else rc = check(moe::launch_down_tiled(dn, st), "down tiled");
+    if (rc || (rc = mark(1 + MOE_STAGE_DOWN))) return rc;
 
     if (shared) {
         moe::GemmProblem sg = gu;
@@ -298,18 +306,20 @@ int moe_forward(const void *hidden, const void *router_w, const void *gate_up, c
         sd.C = ws.sh_y;
         const bool sh_skinny = (opts->flags & MOE_FLAG_FORCE_SKINNY) ||
                                (!(opts->flags & MOE_FLAG_FORCE_TILED) && T <= 32);
-        if (f32) {
-            if ((rc = check(moe::launch_gate_up_f32(sg, st), "shared gate_up f32"))) return rc;
-            if ((rc = check(moe::launch_down_f32(sd, st), "shared down f32"))) return rc;
-        } else if (sh_skinny) {
-            if ((rc = check(moe::launch_gate_up_skinny(sg, st), "shared gate_up skinny"))) return rc;
-            if ((rc = check(moe::launch_down_skinny(sd, st), "shared down skinny"))) return rc;
-        } else {
-            if ((rc = check(moe::launch_gate_up_tiled(sg, st), "shared gate_up tiled"))) return rc;
-            if ((rc = check(moe::launch_down_tiled(sd, st), "shared down tiled"))) return rc;
-        }
+        if (f32) rc = check(moe::launch_gate_up_f32(sg, st), "shared gate_up f32");
+        else if (sh_skinny) rc = check(moe::launch_gate_up_skinny(sg, st), "shared gate_up skinny");
+        else rc = check(moe::launch_gate_up_tiled(sg, st), "shared gate_up tiled");
+        if (rc || (rc = mark(1 + MOE_STAGE_SHARED_GATE_UP))) return rc;
+        if (f32) rc = check(moe::launch_down_f32(sd, st), "shared down f32");
+        else if (sh_skinny) rc = check(moe::launch_down_skinny(sd, st), "shared down skinny");
+        else rc = check(moe::launch_down_tiled(sd, st), "shared down tiled");
+        if (rc || (rc = mark(1 + MOE_STAGE_SHARED_DOWN))) return rc;
+    } else {
+        if ((rc = mark(1 + MOE_STAGE_SHARED_GATE_UP)) || (rc = mark(1 + MOE_STAGE_SHARED_DOWN))) return rc;
     }
-    if ((rc = check(moe::launch_combine(s, ws.slot, shared ? ws.sh_y : nullptr, out, st), "combine"))) return rc;
+    if ((rc = check(moe::launch_combine(s, ws.slot, shared ? ws.sh_y : nullptr, out, st), "combine")) ||
+        (rc = mark(1 + MOE_STAGE_COMBINE)))
+        return rc;
     return MOE_OK;
 }
 
