@@ -91,7 +91,7 @@ typedef struct moe_opts {
      * handles (or NULL). Event 0 is recorded on the stream before the first
      * kernel and event i+1 after stage i (see MOE_STAGE_*), so the time of
      * stage i is the elapsed time between events i and i+1. Stages that do
-     * not run (no shared expert) take zero time. */
+     * not run (no shared expert) take zero time. NULL entries are skipped. */
     void *const *stage_events;
 } moe_opts;
 

@@ -5,12 +5,16 @@
 // "Transformer中的混合专家架构详解" page, section "from dense to sparse":
 // decode speed ~ memory bandwidth / bytes of active weights). So the roles
 // swap: weight rows are the MFMA M side (16 rows per v_mfma_f32_16x16x32_bf16)
-// and the expert's tokens are the N side (16 per group, two groups per pass).
-//   * Each lane streams 64 contiguous bytes of one weight row per step; the
-//     reduction index is permuted identically for weights and tokens, which
-//     leaves the dot products unchanged.
-//   * A workgroup owns 16 output rows (gate_up: 16 gate + the matching 16 up
-//     rows) and splits K over its 4 waves; partial sums meet in LDS in wave
+// and the expert's tokens are the N side (groups of 16).
+//   * Loads are shaped for HBM, not for the MFMA: one load instruction reads
+//     4 whole 256-byte row segments (16 lanes per row, non-temporal). Each
+//     wave writes them to its own LDS tile and reads MFMA fragments back with
+//     an xor swizzle that keeps both directions free of bank conflicts.
+//   * The next step's loads (weights and the token fragments) are issued as
+//     soon as the current step's data is in LDS and registers, so one step is
+//     always in flight per wave.
+//   * A workgroup owns 32 weight rows (gate_up: 16 gate + the matching 16 up
+//     rows; down: 32 consecutive rows) and splits K over its waves; partial sums meet in LDS in wave
 //     order, so the result does not depend on timing.
 //   * Experts with no tokens exit before reading anything, so only the
 //     weights of experts that received tokens are read.
@@ -20,7 +24,20 @@ namespace moe {
 
 namespace {
 
-constexpr int KB = 128;  // reduction elements per lane-group step (4 x 32)
+constexpr int KB = 128;  // reduction elements per step: 256 bytes of each row
+#ifndef MOE_SKINNY_WAVES
+#define MOE_SKINNY_WAVES 4
+#endif
+#ifndef MOE_SKINNY_PD_GU
+#define MOE_SKINNY_PD_GU 1
+#endif
+#ifndef MOE_SKINNY_PD_DN
+#define MOE_SKINNY_PD_DN 1
+#endif
+#ifndef MOE_SKINNY_DOWN_BLOCKS
+#define MOE_SKINNY_DOWN_BLOCKS 2
+#endif
+constexpr int SW = MOE_SKINNY_WAVES;  // waves per workgroup, splitting K
 
 struct SkinnyParams {
     const __bf16 *A;
@@ -39,12 +56,20 @@ struct SkinnyParams {
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8_t, v); }
 
+// 16-byte chunk c (0..15) of row r (0..31) in a wave's LDS tile of 256-byte rows
+__device__ __forceinline__ int tswz(int r, int c) { return r * 16 + (c ^ (r & 15)); }
+
 template <bool GATEUP>
-__global__ __launch_bounds__(256) void skinny_gemm_kernel(SkinnyParams p)
+__global__ __launch_bounds__(SW * 64) void skinny_gemm_kernel(SkinnyParams p)
 {
-    constexpr int NG = 2;  // token groups of 16 per pass
-    constexpr int NW = GATEUP ? 2 : 1;
-    __shared__ f32x4_t s_red[4][NG][NW][64];
+    constexpr int PD = GATEUP ? MOE_SKINNY_PD_GU : MOE_SKINNY_PD_DN;  // steps of weights in flight
+    // 16-row MFMA blocks per workgroup: gate_up takes 16 gate + the matching 16
+    // up rows; down takes MOE_SKINNY_DOWN_BLOCKS consecutive blocks of 16 rows
+    constexpr int NW = GATEUP ? 2 : MOE_SKINNY_DOWN_BLOCKS;
+    constexpr int NR = 16 * NW;         // weight rows per step
+    constexpr int NL = NR / 4;          // load instructions per step
+    __shared__ u32x4 s_w[SW][NR * 16];
+    __shared__ f32x4_t s_red[SW][NW][64];
 
     const int e = p.counts ? (int)blockIdx.y : 0;
     const int M = p.counts ? p.counts[e] : p.dense_rows;
@@ -53,102 +78,128 @@ __global__ __launch_bounds__(256) void skinny_gemm_kernel(SkinnyParams p)
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    const int n0 = blockIdx.x * 16;
-    const int lgrp = lane >> 4;  // which 32-element quarter of a 128-element step
+    const int n0 = blockIdx.x * (GATEUP ? 16 : 16 * NW);
+    const int lgrp = lane >> 4;
+    const int l16 = lane & 15;
 
     const int nkb = (p.K + KB - 1) / KB;
-    const int kb_lo = wave * nkb / 4;
-    const int kb_hi = (wave + 1) * nkb / 4;
+    const int kb_lo = wave * nkb / SW;
+    const int kb_hi = (wave + 1) * nkb / SW;
 
-    const int wr = n0 + (lane & 15);
-    const int wrc = wr < p.N ? wr : 0;
-    const __bf16 *wbase = p.W + (int64_t)e * p.w_expert_stride;
-    const __bf16 *wg = wbase + (int64_t)wrc * p.K + lgrp * 32;
-    const __bf16 *wu = GATEUP ? wg + (int64_t)p.N * p.K : wg;
+    // load instruction i covers tile rows 4i..4i+3; this lane: row 4i + lgrp, chunk l16
+    // element offsets inside one expert fit in 32 bits (2*I*H < 2^31 is checked on the host)
+    const __bf16 *wbase = p.W + (int64_t)e * p.w_expert_stride + l16 * 8;
+    uint32_t woff[NL];
+#pragma unroll
+    for (int i = 0; i < NL; i++) {
+        const int tr = 4 * i + lgrp;  // tile row
+        int mrow;
+        if (GATEUP) {
+            const int n = n0 + (tr & 15);
+            const int nc = n < p.N ? n : 0;
+            mrow = (tr < 16) ? nc : p.N + nc;  // gate rows, then up rows
+        } else {
+            const int n = n0 + tr;
+            mrow = n < p.N ? n : 0;
+        }
+        woff[i] = (uint32_t)mrow * (uint32_t)p.K;
+    }
+    u32x4 *tile = s_w[wave];
     const u32x4 zero = {0u, 0u, 0u, 0u};
 
-    for (int pass = 0; pass < M; pass += 16 * NG) {
-        const __bf16 *xp[NG];
-        bool xv[NG];
-#pragma unroll
-        for (int g = 0; g < NG; g++) {
-            const int q = pass + g * 16 + (lane & 15);
-            xv[g] = q < M;
-            const int qc = q < M ? q : M - 1;
-            const int64_t src = p.a_rows ? (int64_t)p.a_rows[row0 + qc] : (int64_t)(row0 + qc);
-            xp[g] = p.A + src * p.K + lgrp * 32;
-        }
-        const bool g1 = pass + 16 < M;  // second token group present (wave-uniform)
+    for (int pass = 0; pass < M; pass += 16) {
+        const int q = pass + l16;
+        const bool xv = q < M;
+        const int qc = xv ? q : M - 1;
+        const int64_t src = p.a_rows ? (int64_t)p.a_rows[row0 + qc] : (int64_t)(row0 + qc);
+        const __bf16 *xp = p.A + src * p.K + lgrp * 8;
 
-        f32x4_t acc[NG][NW];
+        f32x4_t acc[NW];
 #pragma unroll
-        for (int g = 0; g < NG; g++)
-#pragma unroll
-            for (int w = 0; w < NW; w++) acc[g][w] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int w = 0; w < NW; w++) acc[w] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-        for (int kb = kb_lo; kb < kb_hi; kb++) {
+        u32x4 st[PD][NL];
+        u32x4 xs[PD][4];
+        // weights of step kb and the token fragments it needs (MFMA j takes chunk 4j + lgrp)
+        auto gload = [&](int kb, int b) {
             const int k = kb * KB;
-            u32x4 a[NW][4], b[NG][4];
+            const bool ok = k + l16 * 8 < p.K;
+#pragma unroll
+            for (int i = 0; i < NL; i++) st[b][i] = ok ? load_nt16(wbase + woff[i] + k) : zero;
 #pragma unroll
             for (int j = 0; j < 4; j++) {
-                const bool ok = k + lgrp * 32 + j * 8 < p.K;
-                a[0][j] = ok ? *reinterpret_cast<const u32x4 *>(wg + k + j * 8) : zero;
-                if (GATEUP) a[NW - 1][j] = ok ? *reinterpret_cast<const u32x4 *>(wu + k + j * 8) : zero;
-                b[0][j] = (ok && xv[0]) ? *reinterpret_cast<const u32x4 *>(xp[0] + k + j * 8) : zero;
-                if (g1) b[1][j] = (ok && xv[1]) ? *reinterpret_cast<const u32x4 *>(xp[1] + k + j * 8) : zero;
+                const bool okx = xv && (k + (4 * j + lgrp) * 8 < p.K);
+                xs[b][j] = okx ? *reinterpret_cast<const u32x4 *>(xp + k + j * 32) : zero;
             }
+        };
+        // one reduction step from staging buffer b (a compile-time index after unrolling)
+        auto step = [&](int kb, int b) {
+#pragma unroll
+            for (int i = 0; i < NL; i++) tile[tswz(4 * i + lgrp, l16)] = st[b][i];
+            u32x4 xb[4];
+#pragma unroll
+            for (int j = 0; j < 4; j++) xb[j] = xs[b][j];
+            if (kb + PD < kb_hi) gload(kb + PD, b);
 #pragma unroll
             for (int j = 0; j < 4; j++) {
-#pragma unroll
-                for (int w = 0; w < NW; w++)
-                    acc[0][w] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[w][j]), as_bf16x8(b[0][j]),
-                                                                        acc[0][w], 0, 0, 0);
-                if (g1) {
-#pragma unroll
-                    for (int w = 0; w < NW; w++)
-                        acc[1][w] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                            as_bf16x8(a[w][j]), as_bf16x8(b[1][j]), acc[1][w], 0, 0, 0);
-                }
-            }
-        }
-
-        // ---- split-K reduction across the 4 waves, in wave order
-#pragma unroll
-        for (int g = 0; g < NG; g++)
-#pragma unroll
-            for (int w = 0; w < NW; w++) s_red[wave][g][w][lane] = acc[g][w];
-        __syncthreads();
-        if (wave == 0) {
-#pragma unroll
-            for (int g = 0; g < NG; g++) {
-                if (g == 1 && !g1) break;
-                f32x4_t s[NW];
 #pragma unroll
                 for (int w = 0; w < NW; w++) {
-                    s[w] = s_red[0][g][w][lane];
-#pragma unroll
-                    for (int v = 1; v < 4; v++) {
-                        const f32x4_t o = s_red[v][g][w][lane];
-                        s[w][0] += o[0]; s[w][1] += o[1]; s[w][2] += o[2]; s[w][3] += o[3];
-                    }
+                    const u32x4 a = tile[tswz(16 * w + l16, 4 * j + lgrp)];
+                    acc[w] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(xb[j]), acc[w], 0, 0, 0);
                 }
-                const int q = pass + g * 16 + (lane & 15);
-                const int c = n0 + 4 * lgrp;  // 4 consecutive output columns
-                if (q < M && c < p.N) {
-                    const int pos = row0 + q;
-                    if (GATEUP) {
+            }
+        };
+#pragma unroll
+        for (int b = 0; b < PD; b++)
+            if (kb_lo + b < kb_hi) gload(kb_lo + b, b);
+        int kb = kb_lo;
+        for (; kb + PD <= kb_hi; kb += PD) {
+#pragma unroll
+            for (int b = 0; b < PD; b++) step(kb + b, b);
+        }
+#pragma unroll
+        for (int b = 0; b < PD - 1; b++)
+            if (kb + b < kb_hi) step(kb + b, b);
+
+        // ---- split-K reduction across the waves, in wave order
+#pragma unroll
+        for (int w = 0; w < NW; w++) s_red[wave][w][lane] = acc[w];
+        __syncthreads();
+        if (wave == 0) {
+            f32x4_t sm[NW];
+#pragma unroll
+            for (int w = 0; w < NW; w++) {
+                sm[w] = s_red[0][w][lane];
+#pragma unroll
+                for (int v = 1; v < SW; v++) {
+                    const f32x4_t o = s_red[v][w][lane];
+                    sm[w][0] += o[0]; sm[w][1] += o[1]; sm[w][2] += o[2]; sm[w][3] += o[3];
+                }
+            }
+            // lane: token column l16, output rows 4*lgrp + 0..3 of each 16-row block
+            if (xv) {
+                const int pos = row0 + q;
+                if (GATEUP) {
+                    const int c = n0 + 4 * lgrp;
+                    if (c < p.N) {
                         float hv[4];
 #pragma unroll
-                        for (int i = 0; i < 4; i++) hv[i] = silu_f32(s[0][i]) * s[NW - 1][i];
+                        for (int i = 0; i < 4; i++) hv[i] = silu_f32(sm[0][i]) * sm[1][i];
                         uint2 packed;
                         packed.x = pack_bf16x2(hv[0], hv[1]);
                         packed.y = pack_bf16x2(hv[2], hv[3]);
                         *reinterpret_cast<uint2 *>(reinterpret_cast<__bf16 *>(p.C) + (int64_t)pos * p.N + c) = packed;
-                    } else {
-                        const int64_t orow = p.c_rows ? (int64_t)p.c_rows[pos] : (int64_t)pos;
-                        const float sc = p.c_scale ? p.c_scale[pos] : 1.0f;
-                        float4 y = make_float4(s[0][0] * sc, s[0][1] * sc, s[0][2] * sc, s[0][3] * sc);
-                        *reinterpret_cast<float4 *>(reinterpret_cast<float *>(p.C) + orow * p.N + c) = y;
+                    }
+                } else {
+                    const int64_t orow = p.c_rows ? (int64_t)p.c_rows[pos] : (int64_t)pos;
+                    const float sc = p.c_scale ? p.c_scale[pos] : 1.0f;
+#pragma unroll
+                    for (int w = 0; w < NW; w++) {
+                        const int c = n0 + 16 * w + 4 * lgrp;
+                        if (c < p.N) {
+                            float4 y = make_float4(sm[w][0] * sc, sm[w][1] * sc, sm[w][2] * sc, sm[w][3] * sc);
+                            *reinterpret_cast<float4 *>(reinterpret_cast<float *>(p.C) + orow * p.N + c) = y;
+                        }
                     }
                 }
             }
@@ -181,15 +232,16 @@ hipError_t launch_gate_up_skinny(const GemmProblem &g, hipStream_t st)
 {
     SkinnyParams s = make_params(g);
     dim3 grid((unsigned)((g.N + 15) / 16), g.dense_rows > 0 ? 1u : (unsigned)g.E);
-    hipLaunchKernelGGL(skinny_gemm_kernel<true>, grid, dim3(256), 0, st, s);
+    hipLaunchKernelGGL(skinny_gemm_kernel<true>, grid, dim3(SW * 64), 0, st, s);
     return hipGetLastError();
 }
 
 hipError_t launch_down_skinny(const GemmProblem &g, hipStream_t st)
 {
     SkinnyParams s = make_params(g);
-    dim3 grid((unsigned)((g.N + 15) / 16), g.dense_rows > 0 ? 1u : (unsigned)g.E);
-    hipLaunchKernelGGL(skinny_gemm_kernel<false>, grid, dim3(256), 0, st, s);
+    constexpr int rows = 16 * MOE_SKINNY_DOWN_BLOCKS;
+    dim3 grid((unsigned)((g.N + rows - 1) / rows), g.dense_rows > 0 ? 1u : (unsigned)g.E);
+    hipLaunchKernelGGL(skinny_gemm_kernel<false>, grid, dim3(SW * 64), 0, st, s);
     return hipGetLastError();
 }
 

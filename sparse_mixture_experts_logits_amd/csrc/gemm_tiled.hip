@@ -42,7 +42,14 @@ struct TiledParams {
     int NB;  // N-blocks
 };
 
-__device__ __forceinline__ int swz(int row, int ch) { return row * 8 + (ch ^ (row & 7)); }
+// LDS tile layout: rows of 128 bytes (8 chunks of 16 bytes). The chunk index
+// is xor-ed with (row / 2) mod 8 so that the 16 lanes a ds_read_b128 serves
+// per cycle (16 consecutive rows, one chunk column) hit 16 distinct 16-byte
+// bank groups of the 64-bank LDS.
+#ifndef MOE_TILED_SWZ_SHIFT
+#define MOE_TILED_SWZ_SHIFT 1
+#endif
+__device__ __forceinline__ int swz(int row, int ch) { return row * 8 + (ch ^ ((row >> MOE_TILED_SWZ_SHIFT) & 7)); }
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8_t, v); }
 

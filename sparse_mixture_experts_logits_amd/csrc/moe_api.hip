@@ -90,7 +90,8 @@ moe::Shape make_shape(int64_t T, int64_t H, int64_t I, int64_t E, int32_t k, con
     s.k = k;
     s.sharedI = opts ? opts->shared_I : 0;
     s.dtype = opts ? opts->dtype : MOE_BF16;
-    s.nblk = (int)((T + moe::kRouterTokensPerBlock - 1) / moe::kRouterTokensPerBlock);
+    s.rtok = T <= 1024 ? 4 : 16;  // small T: more router blocks, shorter chains per wave
+    s.nblk = (int)((T + s.rtok - 1) / s.rtok);
     s.tileBM = moe::tiled_block_m();
     s.maxTiles = (T * k) / s.tileBM + E + 1;
     return s;
@@ -213,7 +214,6 @@ int moe_forward(const void *hidden, const void *router_w, const void *gate_up, c
     else if (opts->flags & MOE_FLAG_FORCE_TILED) skinny = false;
     else skinny = T * k <= 32 * E;  // about 32 rows per expert or fewer: stream the weights
 
-    hipError_t e = hipSuccess;
     int step = 0;
     auto check = [&](hipError_t err, const char *what) -> int {
         step++;
@@ -224,7 +224,7 @@ int moe_forward(const void *hidden, const void *router_w, const void *gate_up, c
     };
     // stage boundary i (0 = before the first kernel); no-op without events
     auto mark = [&](int i) -> int {
-        if (!opts->stage_events) return MOE_OK;
+        if (!opts->stage_events || !opts->stage_events[i]) return MOE_OK;
         hipError_t err = hipEventRecord((hipEvent_t)opts->stage_events[i], st);
         if (err != hipSuccess) return fail(MOE_ERR_HIP, "hipEventRecord(stage %d): %s", i, hipGetErrorString(err));
         return MOE_OK;
@@ -232,17 +232,9 @@ int moe_forward(const void *hidden, const void *router_w, const void *gate_up, c
     if ((rc = mark(0))) return rc;
 
     if ((rc = check(moe::launch_router_topk(s, hidden, router_w, opts->router_bias, opts->routed_scale,
-                                            opts->router_logits, ws, st),
+                                            opts->router_logits, opts->topk_ids, opts->topk_weights, ws, st),
                     "router_topk")) || (rc = mark(1 + MOE_STAGE_ROUTER)))
         return rc;
-    if (opts->topk_ids || opts->topk_weights) {
-        if (opts->topk_ids &&
-            (e = hipMemcpyAsync(opts->topk_ids, ws.ids, (size_t)(T * k * 4), hipMemcpyDeviceToDevice, st)) != hipSuccess)
-            return check(e, "copy topk_ids");
-        if (opts->topk_weights &&
-            (e = hipMemcpyAsync(opts->topk_weights, ws.wts, (size_t)(T * k * 4), hipMemcpyDeviceToDevice, st)) != hipSuccess)
-            return check(e, "copy topk_weights");
-    }
     if ((rc = check(moe::launch_route_scan(s, opts->expert_counts, opts->expert_offsets, ws, st), "route_scan")) ||
         (rc = mark(1 + MOE_STAGE_SCAN)))
         return rc;

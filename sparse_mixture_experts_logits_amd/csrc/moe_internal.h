@@ -17,6 +17,15 @@ struct alignas(16) u32x4 {
     uint32_t x, y, z, w;
 };
 
+typedef uint32_t u32x4v_t __attribute__((ext_vector_type(4)));
+
+// 16-byte load marked non-temporal (streamed data that is read once).
+__device__ __forceinline__ u32x4 load_nt16(const void *p)
+{
+    const u32x4v_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4v_t *>(p));
+    return u32x4{v.x, v.y, v.z, v.w};
+}
+
 __device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xffff0000u); }
 
@@ -36,7 +45,7 @@ __device__ __forceinline__ float silu_f32(float g) { return g / (1.0f + __expf(-
 
 // ------------------------------------------------------------------ routing constants
 
-constexpr int kRouterTokensPerBlock = 16;  // 4 waves x 4 tokens
+constexpr int kRouterMaxTokensPerBlock = 16;  // tokens per router block: 4 (small T) or 16
 constexpr int kMaxExperts = 256;
 
 // Device tile of the large-M grouped GEMM: rows [row0, row0 + rows) of the
@@ -75,6 +84,7 @@ struct Shape {
     int k;
     int64_t sharedI;
     int dtype;       // 0 bf16, 1 f32
+    int rtok;        // tokens per router block (4 or 16)
     int nblk;        // router blocks
     int tileBM;      // rows per M-tile of the large-M schedule
     int64_t maxTiles;
@@ -86,8 +96,8 @@ int64_t workspace_layout(const Shape &s, void *base, Workspace *ws);
 // ------------------------------------------------------------------ launchers (return hipError_t)
 
 hipError_t launch_router_topk(const Shape &s, const void *X, const void *Wr, const float *bias,
-                              float routed_scale, float *logits_out, const Workspace &ws,
-                              hipStream_t st);
+                              float routed_scale, float *logits_out, int32_t *ids_out, float *wts_out,
+                              const Workspace &ws, hipStream_t st);
 hipError_t launch_route_scan(const Shape &s, int32_t *counts_out, int32_t *offsets_out,
                              const Workspace &ws, hipStream_t st);
 hipError_t launch_route_permute(const Shape &s, int32_t *perm_out, int32_t *inv_out,

@@ -24,9 +24,6 @@ namespace moe {
 
 namespace {
 
-constexpr int kTPW = 4;  // tokens per wave in the router
-constexpr int kEG = 16;  // experts accumulated per pass
-
 template <typename Tin>
 struct RowLoader;
 
@@ -60,86 +57,101 @@ __device__ __forceinline__ bool ranks_before(float va, int ia, float vb, int ib)
     return va > vb || (va == vb && ia < ib);
 }
 
-template <typename Tin>
+// One workgroup routes RT tokens. The 4 waves split the experts; each wave
+// takes TG tokens x 4 experts at a time so every loaded slice of hidden and
+// router weights feeds several dot products, and all loads of a 512-element
+// chunk are issued before its fmas.
+template <typename Tin, int RT>
 __global__ __launch_bounds__(256) void router_topk_kernel(
     const Tin *__restrict__ X, const Tin *__restrict__ Wr, const float *__restrict__ bias, int T,
     int H, int E, int k, float routed_scale, int32_t *__restrict__ ids, float *__restrict__ wts,
-    float *__restrict__ logits_out, int32_t *__restrict__ blk_counts)
+    int32_t *__restrict__ ids_out, float *__restrict__ wts_out, float *__restrict__ logits_out,
+    int32_t *__restrict__ blk_counts)
 {
-    __shared__ float s_logit[kRouterTokensPerBlock][kMaxExperts];
+    constexpr int TG = RT < 8 ? RT : 8;  // tokens per pass
+    constexpr int EG = 4;                // experts per pass
+    __shared__ float s_logit[RT][kMaxExperts];
     __shared__ float s_sel[4][kMaxExperts];
     __shared__ int s_hist[kMaxExperts];
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    const int tblk = blockIdx.x * kRouterTokensPerBlock;
-    const int tw0 = tblk + wave * kTPW;
+    const int tblk = blockIdx.x * RT;
 
     for (int e = threadIdx.x; e < E; e += 256) s_hist[e] = 0;
 
-    // ---- logits: each lane accumulates its 8-element slices in order
-    const Tin *xrow[kTPW];
+    // ---- logits
+    const int epw = (E + 3) / 4;
+    const int e_lo = wave * epw;
+    const int e_hi = min(E, e_lo + epw);
+    const int nchunk = (H + 511) / 512;
+    for (int tg = 0; tg < RT; tg += TG) {
+        const Tin *xrow[TG];
 #pragma unroll
-    for (int j = 0; j < kTPW; j++) {
-        int t = tw0 + j;
-        t = t < T ? t : T - 1;  // rows past T repeat a valid row; their results are dropped
-        xrow[j] = X + (int64_t)t * H;
-    }
-    for (int eg = 0; eg < E; eg += kEG) {
-        float acc[kTPW][kEG];
-#pragma unroll
-        for (int j = 0; j < kTPW; j++)
-#pragma unroll
-            for (int q = 0; q < kEG; q++) acc[j][q] = 0.0f;
-        for (int c = 0; c * 512 < H; c++) {
-            const int64_t i0 = (int64_t)c * 512 + lane * 8;
-            if (i0 < H) {  // H is a multiple of 8: a slice is all valid or all absent
-                float xv[kTPW][8];
-#pragma unroll
-                for (int j = 0; j < kTPW; j++) RowLoader<Tin>::load8(xrow[j], i0, xv[j]);
-#pragma unroll
-                for (int q = 0; q < kEG; q++) {
-                    const int e = eg + q;
-                    if (e < E) {
-                        float wv[8];
-                        RowLoader<Tin>::load8(Wr + (int64_t)e * H, i0, wv);
-#pragma unroll
-                        for (int j = 0; j < kTPW; j++)
-#pragma unroll
-                            for (int v = 0; v < 8; v++) acc[j][q] = __builtin_fmaf(xv[j][v], wv[v], acc[j][q]);
-                    }
-                }
-            }
+        for (int j = 0; j < TG; j++) {
+            int t = tblk + tg + j;
+            t = t < T ? t : T - 1;  // rows past T repeat a valid row; results dropped
+            xrow[j] = X + (int64_t)t * H;
         }
-        // xor butterfly over the 64 lanes: P[L] <- P[L] + P[L ^ d], d = 32..1
+        for (int es = e_lo; es < e_hi; es += EG) {
+            const Tin *wrow[EG];
 #pragma unroll
-        for (int j = 0; j < kTPW; j++)
-#pragma unroll
-            for (int q = 0; q < kEG; q++) {
-                float v = acc[j][q];
-#pragma unroll
-                for (int d = 32; d >= 1; d >>= 1) v = v + __shfl_xor(v, d, 64);
-                acc[j][q] = v;
+            for (int q = 0; q < EG; q++) {
+                const int e = min(es + q, E - 1);  // clamped rows are computed and dropped
+                wrow[q] = Wr + (int64_t)e * H;
             }
-        if (lane == 0) {
+            float acc[TG][EG];
 #pragma unroll
-            for (int j = 0; j < kTPW; j++)
+            for (int j = 0; j < TG; j++)
 #pragma unroll
-                for (int q = 0; q < kEG; q++) {
-                    const int e = eg + q;
-                    if (e < E) {
-                        float l = acc[j][q];
-                        if (bias) l = l + bias[e];
-                        s_logit[wave * kTPW + j][e] = l;
-                    }
+                for (int q = 0; q < EG; q++) acc[j][q] = 0.0f;
+#pragma unroll 2
+            for (int c = 0; c < nchunk; c++) {
+                const int64_t i0 = (int64_t)c * 512 + lane * 8;
+                if (i0 < H) {  // H is a multiple of 8: a slice is all valid or all absent
+                    float xv[TG][8], wv[EG][8];
+#pragma unroll
+                    for (int j = 0; j < TG; j++) RowLoader<Tin>::load8(xrow[j], i0, xv[j]);
+#pragma unroll
+                    for (int q = 0; q < EG; q++) RowLoader<Tin>::load8(wrow[q], i0, wv[q]);
+#pragma unroll
+                    for (int j = 0; j < TG; j++)
+#pragma unroll
+                        for (int q = 0; q < EG; q++)
+#pragma unroll
+                            for (int v = 0; v < 8; v++) acc[j][q] = __builtin_fmaf(xv[j][v], wv[q][v], acc[j][q]);
                 }
+            }
+            // xor butterfly over the 64 lanes: P[L] <- P[L] + P[L ^ d], d = 32..1
+#pragma unroll
+            for (int j = 0; j < TG; j++)
+#pragma unroll
+                for (int q = 0; q < EG; q++) {
+                    float v = acc[j][q];
+#pragma unroll
+                    for (int d = 32; d >= 1; d >>= 1) v = v + __shfl_xor(v, d, 64);
+                    acc[j][q] = v;
+                }
+            if (lane == 0) {
+#pragma unroll
+                for (int j = 0; j < TG; j++)
+#pragma unroll
+                    for (int q = 0; q < EG; q++) {
+                        const int e = es + q;
+                        if (e < e_hi) {
+                            float l = acc[j][q];
+                            if (bias) l = l + bias[e];
+                            s_logit[tg + j][e] = l;
+                        }
+                    }
+            }
         }
     }
     __syncthreads();
 
     // ---- optional logits output
     if (logits_out) {
-        for (int idx = threadIdx.x; idx < kRouterTokensPerBlock * E; idx += 256) {
+        for (int idx = threadIdx.x; idx < RT * E; idx += 256) {
             const int j = idx / E, e = idx - j * E;
             const int t = tblk + j;
             if (t < T) logits_out[(int64_t)t * E + e] = s_logit[j][e];
@@ -147,10 +159,10 @@ __global__ __launch_bounds__(256) void router_topk_kernel(
     }
 
     // ---- top-k per token: k rounds of a wave-wide arg-max under the ranking rule
-    for (int j = 0; j < kTPW; j++) {
-        const int t = tw0 + j;
+    for (int j = wave; j < RT; j += 4) {
+        const int t = tblk + j;
         if (t >= T) break;  // wave-uniform
-        const float *lrow = s_logit[wave * kTPW + j];
+        const float *lrow = s_logit[j];
         float v[4];
         bool taken[4];
 #pragma unroll
@@ -185,6 +197,7 @@ __global__ __launch_bounds__(256) void router_topk_kernel(
                 if (lane + 64 * q == bi) taken[q] = true;
             if (lane == 0) {
                 ids[(int64_t)t * k + s] = bi;
+                if (ids_out) ids_out[(int64_t)t * k + s] = bi;
                 s_sel[wave][s] = bv;
                 atomicAdd(&s_hist[bi], 1);
             }
@@ -197,8 +210,11 @@ __global__ __launch_bounds__(256) void router_topk_kernel(
         for (int s = lane; s < k; s += 64) psum += __expf(s_sel[wave][s] - m);
 #pragma unroll
         for (int d = 32; d >= 1; d >>= 1) psum += __shfl_xor(psum, d, 64);
-        for (int s = lane; s < k; s += 64)
-            wts[(int64_t)t * k + s] = routed_scale * (__expf(s_sel[wave][s] - m) / psum);
+        for (int s = lane; s < k; s += 64) {
+            const float w = routed_scale * (__expf(s_sel[wave][s] - m) / psum);
+            wts[(int64_t)t * k + s] = w;
+            if (wts_out) wts_out[(int64_t)t * k + s] = w;
+        }
         __builtin_amdgcn_wave_barrier();
     }
     __syncthreads();
@@ -279,13 +295,13 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(
 // blk_base[b][e] + (number of earlier assignments of block b with expert e).
 __global__ __launch_bounds__(256) void route_permute_kernel(
     const int32_t *__restrict__ ids, const float *__restrict__ wts, const int32_t *__restrict__ blk_base,
-    int T, int k, int E, int32_t *__restrict__ perm, int32_t *__restrict__ inv,
+    int T, int k, int E, int RT, int32_t *__restrict__ perm, int32_t *__restrict__ inv,
     int32_t *__restrict__ row_token, float *__restrict__ row_weight, int32_t *__restrict__ row_expert,
     int32_t *__restrict__ perm_out, int32_t *__restrict__ inv_out)
 {
-    __shared__ int s_ids[kRouterTokensPerBlock * kMaxExperts];
-    const int t0 = blockIdx.x * kRouterTokensPerBlock;
-    const int nt = min(kRouterTokensPerBlock, T - t0);
+    __shared__ int s_ids[kRouterMaxTokensPerBlock * kMaxExperts];
+    const int t0 = blockIdx.x * RT;
+    const int nt = min(RT, T - t0);
     const int n = nt * k;
     const int64_t a0 = (int64_t)t0 * k;
     for (int i = threadIdx.x; i < n; i += 256) s_ids[i] = ids[a0 + i];
@@ -309,18 +325,22 @@ __global__ __launch_bounds__(256) void route_permute_kernel(
 }  // namespace
 
 hipError_t launch_router_topk(const Shape &s, const void *X, const void *Wr, const float *bias,
-                              float routed_scale, float *logits_out, const Workspace &ws,
-                              hipStream_t st)
+                              float routed_scale, float *logits_out, int32_t *ids_out, float *wts_out,
+                              const Workspace &ws, hipStream_t st)
 {
     dim3 grid(s.nblk), block(256);
-    if (s.dtype == 0)
-        hipLaunchKernelGGL(router_topk_kernel<__bf16>, grid, block, 0, st, (const __bf16 *)X,
-                           (const __bf16 *)Wr, bias, (int)s.T, (int)s.H, (int)s.E, s.k, routed_scale,
-                           ws.ids, ws.wts, logits_out, ws.blk_counts);
-    else
-        hipLaunchKernelGGL(router_topk_kernel<float>, grid, block, 0, st, (const float *)X,
-                           (const float *)Wr, bias, (int)s.T, (int)s.H, (int)s.E, s.k, routed_scale,
-                           ws.ids, ws.wts, logits_out, ws.blk_counts);
+#define MOE_ROUTER_LAUNCH(TIN, RT)                                                                      \
+    hipLaunchKernelGGL((router_topk_kernel<TIN, RT>), grid, block, 0, st, (const TIN *)X, (const TIN *)Wr, \
+                       bias, (int)s.T, (int)s.H, (int)s.E, s.k, routed_scale, ws.ids, ws.wts, ids_out,  \
+                       wts_out, logits_out, ws.blk_counts)
+    if (s.dtype == 0) {
+        if (s.rtok == 4) MOE_ROUTER_LAUNCH(__bf16, 4);
+        else MOE_ROUTER_LAUNCH(__bf16, 16);
+    } else {
+        if (s.rtok == 4) MOE_ROUTER_LAUNCH(float, 4);
+        else MOE_ROUTER_LAUNCH(float, 16);
+    }
+#undef MOE_ROUTER_LAUNCH
     return hipGetLastError();
 }
 
@@ -337,7 +357,7 @@ hipError_t launch_route_permute(const Shape &s, int32_t *perm_out, int32_t *inv_
                                 const Workspace &ws, hipStream_t st)
 {
     hipLaunchKernelGGL(route_permute_kernel, dim3(s.nblk), dim3(256), 0, st, ws.ids, ws.wts,
-                       ws.blk_base, (int)s.T, s.k, (int)s.E, ws.perm, ws.inv, ws.row_token,
+                       ws.blk_base, (int)s.T, s.k, (int)s.E, s.rtok, ws.perm, ws.inv, ws.row_token,
                        ws.row_weight, ws.row_expert, perm_out, inv_out);
     return hipGetLastError();
 }
