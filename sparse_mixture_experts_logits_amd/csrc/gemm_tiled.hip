@@ -23,7 +23,8 @@ namespace moe {
 
 namespace {
 
-constexpr int BK = 64;  // bf16 elements per k-tile (128 bytes per row)
+constexpr int BK = 32;     // bf16 elements per k-stage (64 bytes per row)
+constexpr int STAGES = 4;  // LDS ring depth: three stages in flight while one is consumed
 
 struct TiledParams {
     const __bf16 *A;
@@ -42,30 +43,41 @@ struct TiledParams {
     int NB;  // N-blocks
 };
 
-// LDS tile layout: rows of 128 bytes (8 chunks of 16 bytes). The chunk index
-// is xor-ed with (row / 2) mod 8 so that the 16 lanes a ds_read_b128 serves
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void global_void_t;
+
+// LDS stage layout: rows of 64 bytes (4 chunks of 16 bytes); chunk c of row r
+// sits at chunk slot c ^ ((r >> 2) & 3), so the 16 lanes a ds_read_b128 serves
 // per cycle (16 consecutive rows, one chunk column) hit 16 distinct 16-byte
 // bank groups of the 64-bank LDS.
-#ifndef MOE_TILED_SWZ_SHIFT
-#define MOE_TILED_SWZ_SHIFT 1
-#endif
-__device__ __forceinline__ int swz(int row, int ch) { return row * 8 + (ch ^ ((row >> MOE_TILED_SWZ_SHIFT) & 7)); }
+__device__ __forceinline__ int lds_slot(int r, int c) { return r * 4 + (c ^ ((r >> 2) & 3)); }
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8_t, v); }
+
+// Wait until at most N vector-memory operations of this wave are outstanding
+// (global_load_lds stages are counted there), then barrier. The memory clobber
+// keeps the compiler from moving LDS accesses across it.
+template <int N>
+__device__ __forceinline__ void wait_vm_barrier()
+{
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
 
 template <int BM, int BN, int WM, int WN, bool GATEUP>
 __global__ __launch_bounds__(WM *WN * 64) void tiled_gemm_kernel(TiledParams p)
 {
     constexpr int NT = WM * WN * 64;
-    constexpr int A_CH = BM * 8 / NT;
-    constexpr int B_CH = BN * 8 / NT;
+    constexpr int NWAVE = WM * WN;
     constexpr int RM = BM / WM / 32;
     constexpr int RN = BN / WN / 32;
-    static_assert(A_CH >= 1 && B_CH >= 1 && RM >= 1 && RN >= 1, "tile shape");
+    constexpr int A_INS = BM / 16 / NWAVE;  // 16-row DMA instructions per wave per stage
+    constexpr int B_INS = BN / 16 / NWAVE;
+    constexpr int LOADS = A_INS + B_INS;    // vector-memory ops per wave per stage
+    static_assert(A_INS >= 1 && B_INS >= 1 && RM >= 1 && RN >= 1, "tile shape");
     static_assert(!GATEUP || (RN % 2 == 0), "gate/up pairing needs an even RN");
 
-    __shared__ u32x4 sA[2][BM * 8];
-    __shared__ u32x4 sB[2][BN * 8];
+    __shared__ u32x4 sA[STAGES][BM * 4];
+    __shared__ u32x4 sB[STAGES][BN * 4];
     __shared__ int s_ts[kMaxExperts + 1];
 
     const int tid = threadIdx.x;
@@ -73,7 +85,6 @@ __global__ __launch_bounds__(WM *WN * 64) void tiled_gemm_kernel(TiledParams p)
     const int wave = tid >> 6;
     const int wm = wave / WN;
     const int wn = wave - wm * WN;
-    const int ch = tid & 7;
 
     int n_mtiles;
     if (p.tiles) {
@@ -88,13 +99,18 @@ __global__ __launch_bounds__(WM *WN * 64) void tiled_gemm_kernel(TiledParams p)
     const int nx = G >> 3;
     const int xcd = blockIdx.x & 7;
     const int li = blockIdx.x >> 3;
+    const int nk = (p.K + BK - 1) / BK;
+
+    // DMA lane geometry: instruction i of this wave fills LDS rows
+    // 16*(wave*INS + i) + lane/4, chunk slot lane%4 (logical chunk lc below)
+    const int drow = lane >> 2;
 
     for (int r = 0;; r++) {
         const int id = r * G + xcd * nx + li;
         if (id >= total) break;
 
         // ---- decode tile id -> (expert, M-tile, N-block)
-        int e, mt, nb, row0, rows;
+        int e, nb, row0, rows;
         if (p.tiles) {
             int lo = 0, hi = p.E;  // find e: s_ts[e]*NB <= id < s_ts[e+1]*NB
             while (hi - lo > 1) {
@@ -105,32 +121,34 @@ __global__ __launch_bounds__(WM *WN * 64) void tiled_gemm_kernel(TiledParams p)
             const int nte = s_ts[e + 1] - s_ts[e];
             const int local = id - s_ts[e] * p.NB;
             nb = local / nte;
-            mt = s_ts[e] + (local - nb * nte);
-            const MTile t = p.tiles[mt];
+            const MTile t = p.tiles[s_ts[e] + (local - nb * nte)];
             row0 = t.row0;
             rows = t.rows;
         } else {
             e = 0;
             nb = id / n_mtiles;
-            mt = id - nb * n_mtiles;
+            const int mt = id - nb * n_mtiles;
             row0 = mt * BM;
             rows = min(BM, p.dense_rows - row0);
         }
 
-        // ---- per-thread source rows
-        const __bf16 *aptr[A_CH];
+        // ---- per-lane DMA source rows (rows past the tile repeat row 0; dropped later)
+        const __bf16 *asrc[A_INS];
+        int alc[A_INS];
 #pragma unroll
-        for (int i = 0; i < A_CH; i++) {
-            const int rr = (tid >> 3) + i * (NT / 8);
+        for (int i = 0; i < A_INS; i++) {
+            const int rr = 16 * (wave * A_INS + i) + drow;
             const int rc = rr < rows ? rr : 0;
             const int64_t src = p.a_rows ? (int64_t)p.a_rows[row0 + rc] : (int64_t)(row0 + rc);
-            aptr[i] = p.A + src * p.K + ch * 8;
+            alc[i] = (lane & 3) ^ ((rr >> 2) & 3);
+            asrc[i] = p.A + src * p.K + alc[i] * 8;
         }
         const __bf16 *wbase = p.W + (int64_t)e * p.w_expert_stride;
-        const __bf16 *bptr[B_CH];
+        const __bf16 *bsrc[B_INS];
+        int blc[B_INS];
 #pragma unroll
-        for (int i = 0; i < B_CH; i++) {
-            const int rr = (tid >> 3) + i * (NT / 8);
+        for (int i = 0; i < B_INS; i++) {
+            const int rr = 16 * (wave * B_INS + i) + drow;
             int wrow;
             if (GATEUP) {
                 const int half = BN / 2;
@@ -141,8 +159,30 @@ __global__ __launch_bounds__(WM *WN * 64) void tiled_gemm_kernel(TiledParams p)
                 const int n = nb * BN + rr;
                 wrow = n < p.N ? n : 0;
             }
-            bptr[i] = wbase + (int64_t)wrow * p.K + ch * 8;
+            blc[i] = (lane & 3) ^ ((rr >> 2) & 3);
+            bsrc[i] = wbase + (int64_t)wrow * p.K + blc[i] * 8;
         }
+
+        // stage kt -> LDS buffer b: every lane copies 16 bytes; chunks past K are zero-filled
+        auto issue = [&](int kt, int b) {
+            const int k0 = kt * BK;
+#pragma unroll
+            for (int i = 0; i < A_INS; i++) {
+                u32x4 *dst = &sA[b][(wave * A_INS + i) * 64];
+                if (k0 + alc[i] * 8 < p.K)
+                    __builtin_amdgcn_global_load_lds((global_void_t *)(asrc[i] + k0), (lds_void_t *)dst, 16, 0, 0);
+                else
+                    dst[lane] = u32x4{0u, 0u, 0u, 0u};
+            }
+#pragma unroll
+            for (int i = 0; i < B_INS; i++) {
+                u32x4 *dst = &sB[b][(wave * B_INS + i) * 64];
+                if (k0 + blc[i] * 8 < p.K)
+                    __builtin_amdgcn_global_load_lds((global_void_t *)(bsrc[i] + k0), (lds_void_t *)dst, 16, 0, 0);
+                else
+                    dst[lane] = u32x4{0u, 0u, 0u, 0u};
+            }
+        };
 
         f32x16_t acc[RM][RN];
 #pragma unroll
@@ -152,43 +192,15 @@ __global__ __launch_bounds__(WM *WN * 64) void tiled_gemm_kernel(TiledParams p)
 #pragma unroll
                 for (int q = 0; q < 16; q++) acc[i][j][q] = 0.0f;
 
-        const int nk = (p.K + BK - 1) / BK;
-        u32x4 ra[A_CH], rb[B_CH];
-        const u32x4 zero = {0u, 0u, 0u, 0u};
-
-        auto gload = [&](int kt) {
-            const int k0 = kt * BK;
-            const bool ok = k0 + ch * 8 < p.K;
-#pragma unroll
-            for (int i = 0; i < A_CH; i++)
-                ra[i] = ok ? *reinterpret_cast<const u32x4 *>(aptr[i] + k0) : zero;
-#pragma unroll
-            for (int i = 0; i < B_CH; i++)
-                rb[i] = ok ? *reinterpret_cast<const u32x4 *>(bptr[i] + k0) : zero;
-        };
-        auto lstore = [&](int buf) {
-#pragma unroll
-            for (int i = 0; i < A_CH; i++) sA[buf][swz((tid >> 3) + i * (NT / 8), ch)] = ra[i];
-#pragma unroll
-            for (int i = 0; i < B_CH; i++) sB[buf][swz((tid >> 3) + i * (NT / 8), ch)] = rb[i];
-        };
-
-        __syncthreads();  // previous tile's readers are done with the buffers
-        gload(0);
-        lstore(0);
-        __syncthreads();
-
-        for (int kt = 0; kt < nk; kt++) {
-            const int buf = kt & 1;
-            if (kt + 1 < nk) gload(kt + 1);
+        auto compute = [&](int b) {
 #pragma unroll
             for (int kk = 0; kk < BK / 16; kk++) {
                 bf16x8_t af[RM], bf[RN];
-                const int chk = kk * 2 + (lane >> 5);
+                const int c = kk * 2 + (lane >> 5);
 #pragma unroll
                 for (int i = 0; i < RM; i++) {
                     const int row = wm * (BM / WM) + i * 32 + (lane & 31);
-                    af[i] = as_bf16x8(sA[buf][swz(row, chk)]);
+                    af[i] = as_bf16x8(sA[b][lds_slot(row, c)]);
                 }
 #pragma unroll
                 for (int j = 0; j < RN; j++) {
@@ -200,7 +212,7 @@ __global__ __launch_bounds__(WM *WN * 64) void tiled_gemm_kernel(TiledParams p)
                         row = wn * (BN / WN) + j * 32;
                     }
                     row += lane & 31;
-                    bf[j] = as_bf16x8(sB[buf][swz(row, chk)]);
+                    bf[j] = as_bf16x8(sB[b][lds_slot(row, c)]);
                 }
 #pragma unroll
                 for (int i = 0; i < RM; i++)
@@ -208,9 +220,32 @@ __global__ __launch_bounds__(WM *WN * 64) void tiled_gemm_kernel(TiledParams p)
                     for (int j = 0; j < RN; j++)
                         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
             }
-            if (kt + 1 < nk) lstore(buf ^ 1);
-            __syncthreads();
+        };
+
+        // all waves are done with the previous tile's stages before refilling them
+        wait_vm_barrier<0>();
+#pragma unroll
+        for (int s = 0; s < STAGES - 1; s++)
+            if (s < nk) issue(s, s);
+
+        // stage kt lives in buffer kt % STAGES; the loop is unrolled by STAGES so
+        // buffer indices are compile-time constants
+        auto step = [&](int kt, int b) {
+            const int ahead = min(STAGES - 2, nk - 1 - kt);  // issued stages after kt
+            if (ahead >= 2) wait_vm_barrier<2 * LOADS>();
+            else if (ahead == 1) wait_vm_barrier<LOADS>();
+            else wait_vm_barrier<0>();
+            if (kt + STAGES - 1 < nk) issue(kt + STAGES - 1, (b + STAGES - 1) % STAGES);
+            compute(b);
+        };
+        int kt = 0;
+        for (; kt + STAGES <= nk; kt += STAGES) {
+#pragma unroll
+            for (int b = 0; b < STAGES; b++) step(kt + b, b);
         }
+#pragma unroll
+        for (int b = 0; b < STAGES - 1; b++)
+            if (kt + b < nk) step(kt + b, b);
 
         // ---- epilogue
         if (GATEUP) {
