@@ -15,7 +15,9 @@ import numpy as np
 __all__ = ["moe_forward", "workspace_bytes", "MoeError", "load_library", "LIB_PATH",
            "FLAG_FORCE_TILED", "FLAG_FORCE_SKINNY", "bf16_bits_to_tensor", "EXPORTS"]
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_mi355x.so")
+# MOE_MI355X_LIB may point at another build of the same library (tuning builds)
+LIB_PATH = os.environ.get("MOE_MI355X_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                                             "libmoe_mi355x.so")
 
 MOE_BF16 = 0
 MOE_F32 = 1

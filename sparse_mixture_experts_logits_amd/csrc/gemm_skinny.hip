@@ -77,7 +77,7 @@ __global__ __launch_bounds__(SW * 64) void skinny_gemm_kernel(SkinnyParams p)
     const int row0 = p.counts ? p.offsets[e] : 0;
 
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
     const int n0 = blockIdx.x * (GATEUP ? 16 : 16 * NW);
     const int lgrp = lane >> 4;
     const int l16 = lane & 15;

@@ -23,8 +23,17 @@ namespace moe {
 
 namespace {
 
-constexpr int BK = 32;     // bf16 elements per k-stage (64 bytes per row)
-constexpr int STAGES = 4;  // LDS ring depth: three stages in flight while one is consumed
+#ifndef MOE_TILED_BK
+#define MOE_TILED_BK 32
+#endif
+#ifndef MOE_TILED_STAGES
+#define MOE_TILED_STAGES 4
+#endif
+constexpr int BK = MOE_TILED_BK;          // bf16 elements per k-stage (2*BK bytes per row)
+constexpr int STAGES = MOE_TILED_STAGES;  // LDS ring depth
+constexpr int CH = BK / 8;                // 16-byte chunks per row of a stage
+constexpr int RPI = 64 / CH;              // rows filled by one 64-lane copy instruction
+static_assert(CH == 4 || CH == 8, "stage rows of 64 or 128 bytes");
 
 struct TiledParams {
     const __bf16 *A;
@@ -46,11 +55,13 @@ struct TiledParams {
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) void global_void_t;
 
-// LDS stage layout: rows of 64 bytes (4 chunks of 16 bytes); chunk c of row r
-// sits at chunk slot c ^ ((r >> 2) & 3), so the 16 lanes a ds_read_b128 serves
-// per cycle (16 consecutive rows, one chunk column) hit 16 distinct 16-byte
-// bank groups of the 64-bank LDS.
-__device__ __forceinline__ int lds_slot(int r, int c) { return r * 4 + (c ^ ((r >> 2) & 3)); }
+// LDS stage layout: rows of CH chunks of 16 bytes; chunk c of row r sits at
+// slot c ^ swz(r) with swz(r) = (r >> 2) & 3 for 64-byte rows and (r >> 1) & 7
+// for 128-byte rows, so the 16 lanes a ds_read_b128 serves per cycle (16
+// consecutive rows, one chunk column) hit 16 distinct 16-byte bank groups of
+// the 64-bank LDS.
+__device__ __forceinline__ int lds_swz(int r) { return CH == 4 ? ((r >> 2) & 3) : ((r >> 1) & 7); }
+__device__ __forceinline__ int lds_slot(int r, int c) { return r * CH + (c ^ lds_swz(r)); }
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8_t, v); }
 
@@ -63,6 +74,20 @@ __device__ __forceinline__ void wait_vm_barrier()
     asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
+// Direct-to-LDS copy of 16 bytes per lane: lane i writes LDS bytes
+// [lds + 16 i, lds + 16 i + 16). Issued from inline assembly so that the
+// compiler does not treat every later LDS read as possibly aliasing the copy
+// (it would wait for all copies in flight before each read and serialize the
+// ring); completion is tracked by wait_vm_barrier's explicit vmcnt instead.
+// The copy has no register result; it only reads the address operands.
+__device__ __forceinline__ void dma16(const void *gptr, uint32_t lds)
+{
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(lds)
+                 : "memory", "m0");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void *p) { return (uint32_t)(uintptr_t)p; }
+
 template <int BM, int BN, int WM, int WN, bool GATEUP>
 __global__ __launch_bounds__(WM *WN * 64) void tiled_gemm_kernel(TiledParams p)
 {
@@ -70,19 +95,19 @@ __global__ __launch_bounds__(WM *WN * 64) void tiled_gemm_kernel(TiledParams p)
     constexpr int NWAVE = WM * WN;
     constexpr int RM = BM / WM / 32;
     constexpr int RN = BN / WN / 32;
-    constexpr int A_INS = BM / 16 / NWAVE;  // 16-row DMA instructions per wave per stage
-    constexpr int B_INS = BN / 16 / NWAVE;
+    constexpr int A_INS = BM / RPI / NWAVE;  // copy instructions per wave per stage
+    constexpr int B_INS = BN / RPI / NWAVE;
     constexpr int LOADS = A_INS + B_INS;    // vector-memory ops per wave per stage
     static_assert(A_INS >= 1 && B_INS >= 1 && RM >= 1 && RN >= 1, "tile shape");
     static_assert(!GATEUP || (RN % 2 == 0), "gate/up pairing needs an even RN");
 
-    __shared__ u32x4 sA[STAGES][BM * 4];
-    __shared__ u32x4 sB[STAGES][BN * 4];
+    __shared__ u32x4 sA[STAGES][BM * CH];
+    __shared__ u32x4 sB[STAGES][BN * CH];
     __shared__ int s_ts[kMaxExperts + 1];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
     const int wm = wave / WN;
     const int wn = wave - wm * WN;
 
@@ -101,9 +126,9 @@ __global__ __launch_bounds__(WM *WN * 64) void tiled_gemm_kernel(TiledParams p)
     const int li = blockIdx.x >> 3;
     const int nk = (p.K + BK - 1) / BK;
 
-    // DMA lane geometry: instruction i of this wave fills LDS rows
-    // 16*(wave*INS + i) + lane/4, chunk slot lane%4 (logical chunk lc below)
-    const int drow = lane >> 2;
+    // copy geometry: instruction i of this wave fills LDS rows
+    // RPI*(wave*INS + i) + lane/CH, chunk slot lane%CH (logical chunk lc below)
+    const int drow = lane / CH;
 
     for (int r = 0;; r++) {
         const int id = r * G + xcd * nx + li;
@@ -137,10 +162,10 @@ __global__ __launch_bounds__(WM *WN * 64) void tiled_gemm_kernel(TiledParams p)
         int alc[A_INS];
 #pragma unroll
         for (int i = 0; i < A_INS; i++) {
-            const int rr = 16 * (wave * A_INS + i) + drow;
+            const int rr = RPI * (wave * A_INS + i) + drow;
             const int rc = rr < rows ? rr : 0;
             const int64_t src = p.a_rows ? (int64_t)p.a_rows[row0 + rc] : (int64_t)(row0 + rc);
-            alc[i] = (lane & 3) ^ ((rr >> 2) & 3);
+            alc[i] = (lane % CH) ^ lds_swz(rr);
             asrc[i] = p.A + src * p.K + alc[i] * 8;
         }
         const __bf16 *wbase = p.W + (int64_t)e * p.w_expert_stride;
@@ -148,7 +173,7 @@ __global__ __launch_bounds__(WM *WN * 64) void tiled_gemm_kernel(TiledParams p)
         int blc[B_INS];
 #pragma unroll
         for (int i = 0; i < B_INS; i++) {
-            const int rr = 16 * (wave * B_INS + i) + drow;
+            const int rr = RPI * (wave * B_INS + i) + drow;
             int wrow;
             if (GATEUP) {
                 const int half = BN / 2;
@@ -159,18 +184,28 @@ __global__ __launch_bounds__(WM *WN * 64) void tiled_gemm_kernel(TiledParams p)
                 const int n = nb * BN + rr;
                 wrow = n < p.N ? n : 0;
             }
-            blc[i] = (lane & 3) ^ ((rr >> 2) & 3);
+            blc[i] = (lane % CH) ^ lds_swz(rr);
             bsrc[i] = wbase + (int64_t)wrow * p.K + blc[i] * 8;
         }
 
-        // stage kt -> LDS buffer b: every lane copies 16 bytes; chunks past K are zero-filled
+        // stage kt -> LDS buffer b: every lane copies 16 bytes. Only a final
+        // partial stage (K not a multiple of BK) masks lanes; they zero-fill.
         auto issue = [&](int kt, int b) {
+            const int k0 = kt * BK;
+#pragma unroll
+            for (int i = 0; i < A_INS; i++)
+                dma16(asrc[i] + k0, lds_addr(&sA[b][(wave * A_INS + i) * 64]));
+#pragma unroll
+            for (int i = 0; i < B_INS; i++)
+                dma16(bsrc[i] + k0, lds_addr(&sB[b][(wave * B_INS + i) * 64]));
+        };
+        auto issue_tail = [&](int kt, int b) {
             const int k0 = kt * BK;
 #pragma unroll
             for (int i = 0; i < A_INS; i++) {
                 u32x4 *dst = &sA[b][(wave * A_INS + i) * 64];
                 if (k0 + alc[i] * 8 < p.K)
-                    __builtin_amdgcn_global_load_lds((global_void_t *)(asrc[i] + k0), (lds_void_t *)dst, 16, 0, 0);
+                    dma16(asrc[i] + k0, lds_addr(dst));
                 else
                     dst[lane] = u32x4{0u, 0u, 0u, 0u};
             }
@@ -178,10 +213,15 @@ __global__ __launch_bounds__(WM *WN * 64) void tiled_gemm_kernel(TiledParams p)
             for (int i = 0; i < B_INS; i++) {
                 u32x4 *dst = &sB[b][(wave * B_INS + i) * 64];
                 if (k0 + blc[i] * 8 < p.K)
-                    __builtin_amdgcn_global_load_lds((global_void_t *)(bsrc[i] + k0), (lds_void_t *)dst, 16, 0, 0);
+                    dma16(bsrc[i] + k0, lds_addr(dst));
                 else
                     dst[lane] = u32x4{0u, 0u, 0u, 0u};
             }
+        };
+        const bool ragged = (p.K % BK) != 0;
+        auto issue_any = [&](int kt, int b) {
+            if (ragged && kt == nk - 1) issue_tail(kt, b);
+            else issue(kt, b);
         };
 
         f32x16_t acc[RM][RN];
@@ -226,26 +266,33 @@ __global__ __launch_bounds__(WM *WN * 64) void tiled_gemm_kernel(TiledParams p)
         wait_vm_barrier<0>();
 #pragma unroll
         for (int s = 0; s < STAGES - 1; s++)
-            if (s < nk) issue(s, s);
+            if (s < nk) issue_any(s, s);
 
-        // stage kt lives in buffer kt % STAGES; the loop is unrolled by STAGES so
-        // buffer indices are compile-time constants
-        auto step = [&](int kt, int b) {
-            const int ahead = min(STAGES - 2, nk - 1 - kt);  // issued stages after kt
-            if (ahead >= 2) wait_vm_barrier<2 * LOADS>();
+        // Steady state: stage kt is consumed while stages kt+1, kt+2 are in
+        // flight and stage kt+3 is issued into the buffer stage kt-1 used.
+        // Unrolled by STAGES so every buffer index is a compile-time constant.
+        int kt = 0;
+        for (; kt + 2 * STAGES - 1 <= nk; kt += STAGES) {
+#pragma unroll
+            for (int b = 0; b < STAGES; b++) {
+                wait_vm_barrier<(STAGES - 2) * LOADS>();
+                if (ragged && kt + b + STAGES - 1 == nk - 1) issue_tail(kt + b + STAGES - 1, (b + STAGES - 1) % STAGES);
+                else issue(kt + b + STAGES - 1, (b + STAGES - 1) % STAGES);
+                compute(b);
+            }
+        }
+        // Drain: fewer than 2*STAGES-1 stages remain (kt is a multiple of STAGES,
+        // so stage kt + b lives in buffer b).
+#pragma unroll
+        for (int b = 0; b < 2 * STAGES - 1; b++) {
+            if (kt + b >= nk) break;
+            const int ahead = min(STAGES - 2, nk - 1 - (kt + b));
+            if (ahead >= 2 && STAGES >= 4) wait_vm_barrier<(STAGES >= 4 ? 2 : 0) * LOADS>();
             else if (ahead == 1) wait_vm_barrier<LOADS>();
             else wait_vm_barrier<0>();
-            if (kt + STAGES - 1 < nk) issue(kt + STAGES - 1, (b + STAGES - 1) % STAGES);
-            compute(b);
-        };
-        int kt = 0;
-        for (; kt + STAGES <= nk; kt += STAGES) {
-#pragma unroll
-            for (int b = 0; b < STAGES; b++) step(kt + b, b);
+            if (kt + b + STAGES - 1 < nk) issue_any(kt + b + STAGES - 1, (b + STAGES - 1) % STAGES);
+            compute(b % STAGES);
         }
-#pragma unroll
-        for (int b = 0; b < STAGES - 1; b++)
-            if (kt + b < nk) step(kt + b, b);
 
         // ---- epilogue
         if (GATEUP) {
@@ -285,6 +332,254 @@ __global__ __launch_bounds__(WM *WN * 64) void tiled_gemm_kernel(TiledParams p)
                         }
                     }
                 }
+        }
+    }
+}
+
+// Software-pipelined variant: 4 waves, 128 tokens x 128 weight rows per wave
+// (accumulators live in AGPRs), fragments double-buffered across the two
+// 16-wide halves of a stage. Iteration kt: read half 1 of stage kt while the
+// MFMAs of half 0 run; then wait for stage kt+1 and barrier (everyone has
+// finished reading stage kt-1, whose buffer the copy of stage kt+3 reuses);
+// issue that copy; read half 0 of stage kt+1 while the MFMAs of half 1 run.
+// The MFMA takes weight rows as its A operand and tokens as B, so a lane of
+// the 32x32 result holds one token and 4 consecutive output columns per
+// group of 4 registers: the epilogue writes packed 8-byte (h) or 16-byte
+// (weighted fp32 slot) chunks and looks up each token's row once.
+template <int BM, int BN, bool GATEUP>
+__global__ __launch_bounds__(256) void tiled_pp_kernel(TiledParams p)
+{
+    constexpr int WM = 2, WN = 2, NT = 256, NWAVE = 4;
+    constexpr int RT = BM / WM / 32;  // 32-token blocks per wave
+    constexpr int RW = BN / WN / 32;  // 32-weight-row blocks per wave
+    constexpr int A_INS = BM / RPI / NWAVE;
+    constexpr int B_INS = BN / RPI / NWAVE;
+    constexpr int LOADS = A_INS + B_INS;
+    static_assert(!GATEUP || (RW % 2 == 0), "gate/up pairing needs an even RW");
+
+    static_assert(BK == 32 && STAGES >= 3, "the pipelined schedule reads two 16-wide halves per stage");
+    __shared__ u32x4 sA[STAGES][BM * CH];  // token rows
+    __shared__ u32x4 sB[STAGES][BN * CH];  // weight rows
+    __shared__ int s_ts[kMaxExperts + 1];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+    const int wm = wave / WN;
+    const int wn = wave - wm * WN;
+
+    int n_mtiles;
+    if (p.tiles) {
+        for (int e = tid; e <= p.E; e += NT) s_ts[e] = p.tile_start[e];
+        __syncthreads();
+        n_mtiles = s_ts[p.E];
+    } else {
+        n_mtiles = (p.dense_rows + BM - 1) / BM;
+    }
+    const int total = n_mtiles * p.NB;
+    const int G = gridDim.x;
+    const int nx = G >> 3;
+    const int xcd = blockIdx.x & 7;
+    const int li = blockIdx.x >> 3;
+    const int nk = (p.K + BK - 1) / BK;
+    const bool ragged = (p.K % BK) != 0;
+    const int drow = lane / CH;
+
+    // Fragment addressing. Every fragment row is (multiple of 32) + lane%32, so
+    // the swizzle term depends on the lane only and a fragment's LDS index is
+    // (block row + lane row) * CH + (chunk ^ swizzle): the block part is a
+    // compile-time constant per block.
+    const int sw = lds_swz(lane & 31);
+    const int lrow = (lane & 31) * CH;
+    int xo[BK / 16];
+#pragma unroll
+    for (int h = 0; h < BK / 16; h++) xo[h] = lrow + ((2 * h + (lane >> 5)) ^ sw);
+    auto t_blk = [&](int i) { return (wm * (BM / WM) + i * 32) * CH; };
+    auto w_blk = [&](int j) {
+        int row;
+        if (GATEUP) {
+            constexpr int HW = BN / 2 / WN;
+            row = (j < RW / 2) ? wn * HW + j * 32 : BN / 2 + wn * HW + (j - RW / 2) * 32;
+        } else {
+            row = wn * (BN / WN) + j * 32;
+        }
+        return row * CH;
+    };
+
+    for (int r = 0;; r++) {
+        const int id = r * G + xcd * nx + li;
+        if (id >= total) break;
+
+        int e, nb, row0, rows;
+        if (p.tiles) {
+            int lo = 0, hi = p.E;
+            while (hi - lo > 1) {
+                const int mid = (lo + hi) >> 1;
+                if (s_ts[mid] * p.NB <= id) lo = mid; else hi = mid;
+            }
+            e = lo;
+            const int nte = s_ts[e + 1] - s_ts[e];
+            const int local = id - s_ts[e] * p.NB;
+            nb = local / nte;
+            const MTile t = p.tiles[s_ts[e] + (local - nb * nte)];
+            row0 = t.row0;
+            rows = t.rows;
+        } else {
+            e = 0;
+            nb = id / n_mtiles;
+            const int mt = id - nb * n_mtiles;
+            row0 = mt * BM;
+            rows = min(BM, p.dense_rows - row0);
+        }
+
+        // element offsets of the lane's DMA rows: activations are < 2^31
+        // elements and one expert's weights are < 2^31 elements (host checks)
+        uint32_t aoff[A_INS];
+        int alc[A_INS];
+#pragma unroll
+        for (int i = 0; i < A_INS; i++) {
+            const int rr = RPI * (wave * A_INS + i) + drow;
+            const int rc = rr < rows ? rr : 0;
+            const uint32_t src = p.a_rows ? (uint32_t)p.a_rows[row0 + rc] : (uint32_t)(row0 + rc);
+            alc[i] = (lane % CH) ^ lds_swz(rr);
+            aoff[i] = src * (uint32_t)p.K + alc[i] * 8;
+        }
+        const __bf16 *wbase = p.W + (int64_t)e * p.w_expert_stride;
+        uint32_t boff[B_INS];
+        int blc[B_INS];
+#pragma unroll
+        for (int i = 0; i < B_INS; i++) {
+            const int rr = RPI * (wave * B_INS + i) + drow;
+            int wrow;
+            if (GATEUP) {
+                const int half = BN / 2;
+                const int n = nb * half + (rr < half ? rr : rr - half);
+                const int nc = n < p.N ? n : 0;
+                wrow = rr < half ? nc : p.N + nc;
+            } else {
+                const int n = nb * BN + rr;
+                wrow = n < p.N ? n : 0;
+            }
+            blc[i] = (lane % CH) ^ lds_swz(rr);
+            boff[i] = (uint32_t)wrow * (uint32_t)p.K + blc[i] * 8;
+        }
+
+        auto issue = [&](int kt, int b) {
+            const int k0 = kt * BK;
+            if (ragged && kt == nk - 1) {
+#pragma unroll
+                for (int i = 0; i < A_INS; i++) {
+                    u32x4 *dst = &sA[b][(wave * A_INS + i) * 64];  // 64 chunks per instruction
+                    if (k0 + alc[i] * 8 < p.K) dma16(p.A + aoff[i] + k0, lds_addr(dst));
+                    else dst[lane] = u32x4{0u, 0u, 0u, 0u};
+                }
+#pragma unroll
+                for (int i = 0; i < B_INS; i++) {
+                    u32x4 *dst = &sB[b][(wave * B_INS + i) * 64];
+                    if (k0 + blc[i] * 8 < p.K) dma16(wbase + boff[i] + k0, lds_addr(dst));
+                    else dst[lane] = u32x4{0u, 0u, 0u, 0u};
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < A_INS; i++) dma16(p.A + aoff[i] + k0, lds_addr(&sA[b][(wave * A_INS + i) * 64]));
+#pragma unroll
+                for (int i = 0; i < B_INS; i++) dma16(wbase + boff[i] + k0, lds_addr(&sB[b][(wave * B_INS + i) * 64]));
+            }
+        };
+
+        f32x16_t acc[RW][RT];
+#pragma unroll
+        for (int j = 0; j < RW; j++)
+#pragma unroll
+            for (int i = 0; i < RT; i++)
+#pragma unroll
+                for (int q = 0; q < 16; q++) acc[j][i][q] = 0.0f;
+
+        bf16x8_t ft[2][RT], fw[2][RW];
+        // fragments of half h (k16 step) of the stage in buffer b into set f
+        auto frag = [&](int b, int h, int f) {
+            const u32x4 *pa = &sA[b][xo[h]];
+            const u32x4 *pb = &sB[b][xo[h]];
+#pragma unroll
+            for (int i = 0; i < RT; i++) ft[f][i] = as_bf16x8(pa[t_blk(i)]);
+#pragma unroll
+            for (int j = 0; j < RW; j++) fw[f][j] = as_bf16x8(pb[w_blk(j)]);
+        };
+        auto mma = [&](int f) {
+#pragma unroll
+            for (int j = 0; j < RW; j++)
+#pragma unroll
+                for (int i = 0; i < RT; i++)
+                    acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[f][j], ft[f][i], acc[j][i], 0, 0, 0);
+        };
+
+        wait_vm_barrier<0>();  // previous tile fully consumed
+#pragma unroll
+        for (int s = 0; s < STAGES - 1; s++)
+            if (s < nk) issue(s, s);
+        // stage 0 complete (stages 1 and 2 may still be in flight)
+        if (nk >= 3) wait_vm_barrier<2 * LOADS>();
+        else if (nk == 2) wait_vm_barrier<LOADS>();
+        else wait_vm_barrier<0>();
+        frag(0, 0, 0);
+
+        auto iter = [&](int kt, int b) {
+            frag(b, 1, 1);
+            mma(0);
+            if (kt + 1 < nk) {
+                // stage kt+1 must be complete; stage kt+2 may stay in flight
+                if (kt + 2 < nk) wait_vm_barrier<LOADS>();
+                else wait_vm_barrier<0>();
+                if (kt + STAGES - 1 < nk) issue(kt + STAGES - 1, (b + STAGES - 1) % STAGES);
+                frag((b + 1) % STAGES, 0, 0);
+            }
+            mma(1);
+        };
+#pragma unroll 1
+        for (int kt = 0; kt < nk; kt++) iter(kt, kt % STAGES);
+
+        // ---- epilogue: lane = one token of each 32-token block, 4 columns per group
+#pragma unroll
+        for (int i = 0; i < RT; i++) {
+            const int t = wm * (BM / WM) + i * 32 + (lane & 31);
+            if (t < rows) {
+                const int pos = row0 + t;
+                if (GATEUP) {
+                    constexpr int HW = BN / 2 / WN;
+                    uint16_t *Hh = reinterpret_cast<uint16_t *>(p.C) + (int64_t)pos * p.N;
+#pragma unroll
+                    for (int j = 0; j < RW / 2; j++)
+#pragma unroll
+                        for (int g4 = 0; g4 < 4; g4++) {
+                            const int c = nb * (BN / 2) + wn * HW + j * 32 + 8 * g4 + 4 * (lane >> 5);
+                            if (c < p.N) {
+                                float hv[4];
+#pragma unroll
+                                for (int u = 0; u < 4; u++)
+                                    hv[u] = silu_f32(acc[j][i][4 * g4 + u]) * acc[j + RW / 2][i][4 * g4 + u];
+                                uint2 pk;
+                                pk.x = pack_bf16x2(hv[0], hv[1]);
+                                pk.y = pack_bf16x2(hv[2], hv[3]);
+                                *reinterpret_cast<uint2 *>(Hh + c) = pk;
+                            }
+                        }
+                } else {
+                    const int64_t orow = p.c_rows ? (int64_t)p.c_rows[pos] : (int64_t)pos;
+                    const float sc = p.c_scale ? p.c_scale[pos] : 1.0f;
+                    float *Y = reinterpret_cast<float *>(p.C) + orow * p.N;
+#pragma unroll
+                    for (int j = 0; j < RW; j++)
+#pragma unroll
+                        for (int g4 = 0; g4 < 4; g4++) {
+                            const int m = nb * BN + wn * (BN / WN) + j * 32 + 8 * g4 + 4 * (lane >> 5);
+                            if (m < p.N) {
+                                float4 y = make_float4(acc[j][i][4 * g4] * sc, acc[j][i][4 * g4 + 1] * sc,
+                                                       acc[j][i][4 * g4 + 2] * sc, acc[j][i][4 * g4 + 3] * sc);
+                                *reinterpret_cast<float4 *>(Y + m) = y;
+                            }
+                        }
+                }
+            }
         }
     }
 }
@@ -331,12 +626,20 @@ TiledParams make_params(const GemmProblem &g, int NB)
 
 int tiled_block_m() { return kBM; }
 
+#ifndef MOE_TILED_PP
+#define MOE_TILED_PP 0
+#endif
+
 hipError_t launch_gate_up_tiled(const GemmProblem &g, hipStream_t st)
 {
     const int NB = (int)((g.N + kBN / 2 - 1) / (kBN / 2));
     TiledParams t = make_params(g, NB);
+#if MOE_TILED_PP
+    hipLaunchKernelGGL((tiled_pp_kernel<kBM, kBN, true>), dim3(persistent_grid()), dim3(256), 0, st, t);
+#else
     hipLaunchKernelGGL((tiled_gemm_kernel<kBM, kBN, kWM, kWN, true>), dim3(persistent_grid()),
                        dim3(kWM * kWN * 64), 0, st, t);
+#endif
     return hipGetLastError();
 }
 
@@ -344,8 +647,12 @@ hipError_t launch_down_tiled(const GemmProblem &g, hipStream_t st)
 {
     const int NB = (int)((g.N + kBN - 1) / kBN);
     TiledParams t = make_params(g, NB);
+#if MOE_TILED_PP
+    hipLaunchKernelGGL((tiled_pp_kernel<kBM, kBN, false>), dim3(persistent_grid()), dim3(256), 0, st, t);
+#else
     hipLaunchKernelGGL((tiled_gemm_kernel<kBM, kBN, kWM, kWN, false>), dim3(persistent_grid()),
                        dim3(kWM * kWN * 64), 0, st, t);
+#endif
     return hipGetLastError();
 }
 

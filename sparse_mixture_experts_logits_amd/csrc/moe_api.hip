@@ -90,7 +90,7 @@ moe::Shape make_shape(int64_t T, int64_t H, int64_t I, int64_t E, int32_t k, con
     s.k = k;
     s.sharedI = opts ? opts->shared_I : 0;
     s.dtype = opts ? opts->dtype : MOE_BF16;
-    s.rtok = T <= 1024 ? 4 : 16;  // small T: more router blocks, shorter chains per wave
+    s.rtok = 4;  // tokens per router block: many short blocks keep every CU busy
     s.nblk = (int)((T + s.rtok - 1) / s.rtok);
     s.tileBM = moe::tiled_block_m();
     s.maxTiles = (T * k) / s.tileBM + E + 1;
@@ -282,12 +282,15 @@ int moe_forward(const void *hidden, const void *router_w, const void *gate_up, c
     if (rc || (rc = mark(1 + MOE_STAGE_DOWN))) return rc;
 
     if (shared) {
+        // shared expert: a dense problem over all T tokens with weight 1
         moe::GemmProblem sg = gu;
         sg.a_rows = nullptr;
         sg.W = opts->shared_gate_up;
         sg.w_expert_stride = 0;
         sg.N = opts->shared_I;
         sg.C = ws.sh_h;
+        sg.c_rows = nullptr;
+        sg.c_scale = nullptr;
         sg.dense_rows = T;
         sg.total_rows = T;
         moe::GemmProblem sd = sg;

@@ -75,7 +75,7 @@ __global__ __launch_bounds__(256) void router_topk_kernel(
     __shared__ int s_hist[kMaxExperts];
 
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
     const int tblk = blockIdx.x * RT;
 
     for (int e = threadIdx.x; e < E; e += 256) s_hist[e] = 0;
