@@ -9,9 +9,14 @@ line on stdout.
 
 Default workload: the PhiMoE decode step (T=32, H=4096, I=6400, E=16, top-2),
 a weight-bandwidth-bound case. The PhiMoE prefill chunk (T=4096) is measured
-in the same run and reported under "prefill" (MFMA-bound). Every timed call
-records stage events, so the per-kernel durations and the roofline figures
-come from the same timed region.
+in the same run and reported under "prefill" (MFMA-bound). A short untimed
+pilot with events at every stage boundary finds the dominant kernel; every
+timed call then records HIP events around that kernel on the library's
+stream, so the roofline figures come from the timed region itself.
+
+Other modes: --copy-calibration (a 1 GiB device copy, for scaling rocprofv3
+FETCH_SIZE / WRITE_SIZE) and --write-traffic (summarise those counter runs
+into profiles/).
 """
 from __future__ import annotations
 
@@ -76,6 +81,66 @@ def source_hash(names):
     return h.hexdigest()[:16]
 
 
+def copy_calibration(nbytes=1 << 30, reps=3):
+    """A plain device copy of known size, for scaling FETCH_SIZE / WRITE_SIZE."""
+    import torch
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": nbytes, "reps": reps}), flush=True)
+
+
+def _counter_rows(path):
+    import csv
+    import glob
+    rows = []
+    for f in glob.glob(os.path.join(path, "**", "*counter_collection.csv"), recursive=True):
+        rows += list(csv.DictReader(open(f)))
+    return rows
+
+
+def write_traffic(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, kernel, workload, regex, copy_bytes,
+                  command):
+    """Summarise rocprofv3 FETCH_SIZE / WRITE_SIZE runs of one kernel into
+    profiles/<kernel>_<workload>_traffic.json, scaled by the same counters on a
+    plain copy of copy_bytes (read copy_bytes, write copy_bytes)."""
+    import re
+    rx = re.compile(regex)
+
+    def avg(rows, counter, name_rx=None):
+        v = [float(r["Counter_Value"]) for r in rows
+             if r["Counter_Name"] == counter and (name_rx is None or name_rx.search(r["Kernel_Name"]))]
+        return sum(v) / len(v) if v else None, len(v)
+
+    def copy_avg(rows, counter):
+        # the largest dispatches of the calibration run are the copies
+        v = sorted(float(r["Counter_Value"]) for r in rows if r["Counter_Name"] == counter)
+        top = [x for x in v if x >= 0.5 * v[-1]] if v else []
+        return sum(top) / len(top) if top else None
+
+    f_k, nf = avg(_counter_rows(fetch_dir), "FETCH_SIZE", rx)
+    w_k, nw = avg(_counter_rows(write_dir), "WRITE_SIZE", rx)
+    f_c = copy_avg(_counter_rows(copy_fetch_dir), "FETCH_SIZE")
+    w_c = copy_avg(_counter_rows(copy_write_dir), "WRITE_SIZE")
+    ff = copy_bytes / (f_c * 1024.0)
+    fw = copy_bytes / (w_c * 1024.0)
+    d = {
+        "kernel": kernel, "workload": workload, "kernel_regex": regex,
+        "fetch_size_kib_per_launch": f_k, "write_size_kib_per_launch": w_k, "launches": [nf, nw],
+        "copy_calibration": {"bytes": copy_bytes, "fetch_kib": f_c, "write_kib": w_c,
+                             "fetch_factor": ff, "write_factor": fw},
+        "hbm_bytes_per_launch": f_k * 1024.0 * ff + w_k * 1024.0 * fw,
+        "source_hash": source_hash(KERNEL_SOURCES[kernel]),
+        "command": command,
+    }
+    out = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.json")
+    with open(out, "w") as fh:
+        json.dump(d, fh, indent=1)
+    print(json.dumps(d))
+
+
 def measured_traffic(kernel, workload):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it
     was taken on the current kernel source; else None."""
@@ -129,19 +194,41 @@ def run_workload(name, steps, warmup):
     counts = routing["counts"].cpu().numpy().tolist()
 
     nev = moe.STAGE_EVENTS
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(steps)]
-    for evs in events:
-        for e in evs:
-            e.record()  # creates the underlying hipEvent_t
-    torch.cuda.synchronize()
-    handles = [(ctypes.c_void_p * nev)(*[e.cuda_event for e in evs]) for evs in events]
+
+    def event_sets(n):
+        sets = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(n)]
+        for evs in sets:
+            for e in evs:
+                e.record()  # creates the underlying hipEvent_t
+        torch.cuda.synchronize()
+        return sets
 
     for _ in range(warmup):
         moe.moe_forward(hidden, router_w, gate_up, down, wl.k, out=out, workspace=ws, **kw)
     torch.cuda.synchronize()
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    # timed region (one rank: the barrier is the synchronize)
+
+    # pilot (untimed): every stage boundary, to find the dominant stage
+    pilot = event_sets(5)
+    for evs in pilot:
+        h = (ctypes.c_void_p * nev)(*[e.cuda_event for e in evs])
+        moe.moe_forward(hidden, router_w, gate_up, down, wl.k, out=out, workspace=ws, stage_events=h, **kw)
     torch.cuda.synchronize()
+    stage_ms = np.zeros(nev - 1)
+    for evs in pilot:
+        for j in range(nev - 1):
+            stage_ms[j] += evs[j].elapsed_time(evs[j + 1])
+    stage_ms /= len(pilot)
+    dom = int(np.argmax(stage_ms))
+
+    # timed region: only the two events around the dominant stage are recorded
+    events = event_sets(steps)
+    handles = []
+    for evs in events:
+        arr = [None] * nev
+        arr[dom], arr[dom + 1] = evs[dom].cuda_event, evs[dom + 1].cuda_event
+        handles.append((ctypes.c_void_p * nev)(*arr))
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()  # one rank: the barrier is the synchronize
     t0 = time.perf_counter()
     start.record()
     for i in range(steps):
@@ -150,13 +237,11 @@ def run_workload(name, steps, warmup):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     gpu_ms = start.elapsed_time(end)
-    stage_ms = np.zeros(nev - 1)
-    for evs in events:
-        for j in range(nev - 1):
-            stage_ms[j] += evs[j].elapsed_time(evs[j + 1])
-    stage_ms /= steps
-    return dict(wl=wl, counts=counts, wall_s=wall, gpu_ms=gpu_ms, steps=steps,
-                stages=dict(zip(moe.STAGES, stage_ms.tolist())), inp=inp)
+    dom_ms = sum(evs[dom].elapsed_time(evs[dom + 1]) for evs in events) / steps
+    stages = dict(zip(moe.STAGES, stage_ms.tolist()))
+    stages[moe.STAGES[dom]] = dom_ms  # live value from the timed region
+    return dict(wl=wl, counts=counts, wall_s=wall, gpu_ms=gpu_ms, steps=steps, stages=stages,
+                dominant=moe.STAGES[dom], inp=inp)
 
 
 _INPUT_CACHE = {}
@@ -168,7 +253,9 @@ def roofline_of(res):
     wl = res["wl"]
     w = work(wl, res["counts"])
     st = res["stages"]
-    kernel = "gate_up" if st["gate_up"] >= st["down"] else "down"
+    kernel = res["dominant"]
+    if kernel not in ("gate_up", "down"):  # the expert GEMMs dominate every workload here
+        kernel = "gate_up" if st["gate_up"] >= st["down"] else "down"
     dur_s = st[kernel] / 1e3
     decode = wl.T * wl.k <= 32 * wl.E
     if decode:
@@ -184,6 +271,7 @@ def roofline_of(res):
     r["traffic"] = tr
     r["kernel"] = kernel
     r["avg_launch_ms"] = round(st[kernel], 4)
+    r["timing"] = "HIP events around this kernel on the library's stream, every timed step"
     return r, w
 
 
@@ -231,7 +319,20 @@ def main(argv=None):
     ap.add_argument("--no-prefill", action="store_true", help="skip the secondary prefill measurement")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-tokens", type=int, default=32)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a 1 GiB device copy (counter calibration under rocprofv3)")
+    ap.add_argument("--write-traffic", nargs=7, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR",
+                                                         "COPY_WRITE_DIR", "KERNEL", "WORKLOAD", "REGEX"),
+                    help="summarise rocprofv3 FETCH_SIZE/WRITE_SIZE runs into profiles/")
+    ap.add_argument("--command", default="", help="command line recorded with --write-traffic")
     args = ap.parse_args(argv)
+    if args.write_traffic:
+        fd, wd, cfd, cwd, kernel, workload, regex = args.write_traffic
+        write_traffic(fd, wd, cfd, cwd, kernel, workload, regex, 1 << 30, args.command)
+        return 0
+    if args.copy_calibration:
+        copy_calibration()
+        return 0
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the layer here has no multi-GPU path (run with --gpus 1).",
               file=sys.stderr)
