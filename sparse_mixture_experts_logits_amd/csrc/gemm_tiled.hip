@@ -26,6 +26,18 @@ namespace {
 #ifndef MOE_TILED_BK
 #define MOE_TILED_BK 32
 #endif
+#ifndef MOE_TILED_INTERLEAVE
+#define MOE_TILED_INTERLEAVE 1
+#endif
+#ifndef MOE_TILED_BM
+#define MOE_TILED_BM 256
+#define MOE_TILED_BN 256
+#define MOE_TILED_WM 4
+#define MOE_TILED_WN 2
+#endif
+#ifndef MOE_TILED_OCC
+#define MOE_TILED_OCC 1
+#endif
 #ifndef MOE_TILED_STAGES
 #define MOE_TILED_STAGES 4
 #endif
@@ -89,7 +101,7 @@ __device__ __forceinline__ void dma16(const void *gptr, uint32_t lds)
 __device__ __forceinline__ uint32_t lds_addr(const void *p) { return (uint32_t)(uintptr_t)p; }
 
 template <int BM, int BN, int WM, int WN, bool GATEUP>
-__global__ __launch_bounds__(WM *WN * 64) void tiled_gemm_kernel(TiledParams p)
+__global__ __launch_bounds__(WM *WN * 64, MOE_TILED_OCC) void tiled_gemm_kernel(TiledParams p)
 {
     constexpr int NT = WM * WN * 64;
     constexpr int NWAVE = WM * WN;
@@ -103,7 +115,6 @@ __global__ __launch_bounds__(WM *WN * 64) void tiled_gemm_kernel(TiledParams p)
 
     __shared__ u32x4 sA[STAGES][BM * CH];
     __shared__ u32x4 sB[STAGES][BN * CH];
-    __shared__ int s_ts[kMaxExperts + 1];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -111,10 +122,11 @@ __global__ __launch_bounds__(WM *WN * 64) void tiled_gemm_kernel(TiledParams p)
     const int wm = wave / WN;
     const int wn = wave - wm * WN;
 
+    // first M-tile of each expert (read through the scalar cache, so the
+    // whole LDS is left to the stage ring)
+    const int32_t *s_ts = p.tile_start;
     int n_mtiles;
     if (p.tiles) {
-        for (int e = tid; e <= p.E; e += NT) s_ts[e] = p.tile_start[e];
-        __syncthreads();
         n_mtiles = s_ts[p.E];
     } else {
         n_mtiles = (p.dense_rows + BM - 1) / BM;
@@ -232,6 +244,50 @@ __global__ __launch_bounds__(WM *WN * 64) void tiled_gemm_kernel(TiledParams p)
 #pragma unroll
                 for (int q = 0; q < 16; q++) acc[i][j][q] = 0.0f;
 
+        // copy instruction q (A rows first, then B rows) of stage kt into buffer b
+        auto issue_one = [&](int kt, int b, int q) {
+            const int k0 = kt * BK;
+            if (q < A_INS) dma16(asrc[q] + k0, lds_addr(&sA[b][(wave * A_INS + q) * 64]));
+            else dma16(bsrc[q - A_INS] + k0, lds_addr(&sB[b][(wave * B_INS + q - A_INS) * 64]));
+        };
+        // Consume stage buffer b. When nkt >= 0, the copies of stage nkt into
+        // buffer nb are spread between the MFMAs, one copy per MFMA_PER_COPY
+        // MFMAs, so the copy engine never holds up the fragment reads.
+        auto compute_with = [&](int b, int nkt, int nb) {
+            constexpr int NMMA = (BK / 16) * RM * RN;
+            constexpr int PER = NMMA / LOADS > 0 ? NMMA / LOADS : 1;
+            static_assert(PER * LOADS <= NMMA, "every copy finds an MFMA slot");
+#pragma unroll
+            for (int kk = 0; kk < BK / 16; kk++) {
+                bf16x8_t af[RM], bf[RN];
+                const int c = kk * 2 + (lane >> 5);
+#pragma unroll
+                for (int i = 0; i < RM; i++) {
+                    const int row = wm * (BM / WM) + i * 32 + (lane & 31);
+                    af[i] = as_bf16x8(sA[b][lds_slot(row, c)]);
+                }
+#pragma unroll
+                for (int j = 0; j < RN; j++) {
+                    int row;
+                    if (GATEUP) {
+                        constexpr int HW = BN / 2 / WN;
+                        row = (j < RN / 2) ? wn * HW + j * 32 : BN / 2 + wn * HW + (j - RN / 2) * 32;
+                    } else {
+                        row = wn * (BN / WN) + j * 32;
+                    }
+                    row += lane & 31;
+                    bf[j] = as_bf16x8(sB[b][lds_slot(row, c)]);
+                }
+#pragma unroll
+                for (int i = 0; i < RM; i++)
+#pragma unroll
+                    for (int j = 0; j < RN; j++) {
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
+                        const int mi = (kk * RM + i) * RN + j;  // compile-time after unrolling
+                        if ((mi + 1) % PER == 0 && (mi + 1) / PER - 1 < LOADS) issue_one(nkt, nb, (mi + 1) / PER - 1);
+                    }
+            }
+        };
         auto compute = [&](int b) {
 #pragma unroll
             for (int kk = 0; kk < BK / 16; kk++) {
@@ -271,14 +327,20 @@ __global__ __launch_bounds__(WM *WN * 64) void tiled_gemm_kernel(TiledParams p)
         // Steady state: stage kt is consumed while stages kt+1, kt+2 are in
         // flight and stage kt+3 is issued into the buffer stage kt-1 used.
         // Unrolled by STAGES so every buffer index is a compile-time constant.
+        // (a ragged last stage is always left to the drain)
         int kt = 0;
-        for (; kt + 2 * STAGES - 1 <= nk; kt += STAGES) {
+        const int steady_last = nk - (ragged ? 1 : 0);
+        for (; kt + 2 * STAGES - 1 <= steady_last; kt += STAGES) {
 #pragma unroll
             for (int b = 0; b < STAGES; b++) {
                 wait_vm_barrier<(STAGES - 2) * LOADS>();
-                if (ragged && kt + b + STAGES - 1 == nk - 1) issue_tail(kt + b + STAGES - 1, (b + STAGES - 1) % STAGES);
-                else issue(kt + b + STAGES - 1, (b + STAGES - 1) % STAGES);
+                const int nkt = kt + b + STAGES - 1, nb = (b + STAGES - 1) % STAGES;
+#if MOE_TILED_INTERLEAVE
+                compute_with(b, nkt, nb);
+#else
+                issue(nkt, nb);
                 compute(b);
+#endif
             }
         }
         // Drain: fewer than 2*STAGES-1 stages remain (kt is a multiple of STAGES,
@@ -336,13 +398,14 @@ __global__ __launch_bounds__(WM *WN * 64) void tiled_gemm_kernel(TiledParams p)
     }
 }
 
-// Software-pipelined variant: 4 waves, 128 tokens x 128 weight rows per wave
-// (accumulators live in AGPRs), fragments double-buffered across the two
-// 16-wide halves of a stage. Iteration kt: read half 1 of stage kt while the
-// MFMAs of half 0 run; then wait for stage kt+1 and barrier (everyone has
-// finished reading stage kt-1, whose buffer the copy of stage kt+3 reuses);
-// issue that copy; read half 0 of stage kt+1 while the MFMAs of half 1 run.
-// The MFMA takes weight rows as its A operand and tokens as B, so a lane of
+// Software-pipelined variant: 4 waves (one per SIMD), 128 tokens x 128
+// weight rows per wave (accumulators live in AGPRs), fragments
+// double-buffered across the two 16-wide halves of a stage, with the barrier
+// between the halves and each stage's copies split over both halves (the
+// schedule is spelled out above the steady-state loop). Per stage it reads
+// 64 KB of fragments from LDS against 96 KB for the 8-wave kernel; it is
+// faster on the balanced prefill shapes and slower on the down GEMM of
+// skewed routing, so it is off by default. The MFMA takes weight rows as its A operand and tokens as B, so a lane of
 // the 32x32 result holds one token and 4 consecutive output columns per
 // group of 4 registers: the epilogue writes packed 8-byte (h) or 16-byte
 // (weighted fp32 slot) chunks and looks up each token's row once.
@@ -360,7 +423,6 @@ __global__ __launch_bounds__(256) void tiled_pp_kernel(TiledParams p)
     static_assert(BK == 32 && STAGES >= 3, "the pipelined schedule reads two 16-wide halves per stage");
     __shared__ u32x4 sA[STAGES][BM * CH];  // token rows
     __shared__ u32x4 sB[STAGES][BN * CH];  // weight rows
-    __shared__ int s_ts[kMaxExperts + 1];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -368,10 +430,11 @@ __global__ __launch_bounds__(256) void tiled_pp_kernel(TiledParams p)
     const int wm = wave / WN;
     const int wn = wave - wm * WN;
 
+    // first M-tile of each expert (read through the scalar cache, so the
+    // whole LDS is left to the stage ring)
+    const int32_t *s_ts = p.tile_start;
     int n_mtiles;
     if (p.tiles) {
-        for (int e = tid; e <= p.E; e += NT) s_ts[e] = p.tile_start[e];
-        __syncthreads();
         n_mtiles = s_ts[p.E];
     } else {
         n_mtiles = (p.dense_rows + BM - 1) / BM;
@@ -464,26 +527,28 @@ __global__ __launch_bounds__(256) void tiled_pp_kernel(TiledParams p)
             boff[i] = (uint32_t)wrow * (uint32_t)p.K + blc[i] * 8;
         }
 
-        auto issue = [&](int kt, int b) {
+        // copy q (A rows first, then B rows; 64 chunks of 16 bytes each) of
+        // stage kt into buffer b. Only a final partial stage masks lanes (they
+        // zero-fill); every copy instruction still issues, since chunk 0 of
+        // each of its rows is always in range, so each stage is exactly
+        // LOADS vector-memory operations for the vmcnt waits below.
+        auto copy_full = [&](int kt, int b, int q) {
             const int k0 = kt * BK;
+            if (q < A_INS) dma16(p.A + aoff[q] + k0, lds_addr(&sA[b][(wave * A_INS + q) * 64]));
+            else dma16(wbase + boff[q - A_INS] + k0, lds_addr(&sB[b][(wave * B_INS + q - A_INS) * 64]));
+        };
+        auto copy_any = [&](int kt, int b, int q) {
             if (ragged && kt == nk - 1) {
-#pragma unroll
-                for (int i = 0; i < A_INS; i++) {
-                    u32x4 *dst = &sA[b][(wave * A_INS + i) * 64];  // 64 chunks per instruction
-                    if (k0 + alc[i] * 8 < p.K) dma16(p.A + aoff[i] + k0, lds_addr(dst));
-                    else dst[lane] = u32x4{0u, 0u, 0u, 0u};
-                }
-#pragma unroll
-                for (int i = 0; i < B_INS; i++) {
-                    u32x4 *dst = &sB[b][(wave * B_INS + i) * 64];
-                    if (k0 + blc[i] * 8 < p.K) dma16(wbase + boff[i] + k0, lds_addr(dst));
-                    else dst[lane] = u32x4{0u, 0u, 0u, 0u};
-                }
+                const int k0 = kt * BK;
+                u32x4 *dst = q < A_INS ? &sA[b][(wave * A_INS + q) * 64] : &sB[b][(wave * B_INS + q - A_INS) * 64];
+                const int lc = q < A_INS ? alc[q] : blc[q - A_INS];
+                if (k0 + lc * 8 < p.K)
+                    dma16(q < A_INS ? (const void *)(p.A + aoff[q] + k0) : (const void *)(wbase + boff[q - A_INS] + k0),
+                          lds_addr(dst));
+                else
+                    dst[lane] = u32x4{0u, 0u, 0u, 0u};
             } else {
-#pragma unroll
-                for (int i = 0; i < A_INS; i++) dma16(p.A + aoff[i] + k0, lds_addr(&sA[b][(wave * A_INS + i) * 64]));
-#pragma unroll
-                for (int i = 0; i < B_INS; i++) dma16(wbase + boff[i] + k0, lds_addr(&sB[b][(wave * B_INS + i) * 64]));
+                copy_full(kt, b, q);
             }
         };
 
@@ -505,38 +570,130 @@ __global__ __launch_bounds__(256) void tiled_pp_kernel(TiledParams p)
 #pragma unroll
             for (int j = 0; j < RW; j++) fw[f][j] = as_bf16x8(pb[w_blk(j)]);
         };
-        auto mma = [&](int f) {
+        // MFMAs of fragment set f. With copies, copies q0 .. q0+HALF-1 of
+        // stage nkt into buffer nbuf go out between them, one every PER MFMAs
+        // (compile-time slots), so the vector-memory path is fed evenly.
+        constexpr int HALF = LOADS / 2;
+        static_assert(LOADS % 2 == 0, "copies split evenly over the two halves of a stage");
+        auto mma = [&](int f, bool copies, int nkt, int nbuf, int q0) {
+            constexpr int NM = RW * RT;
+            constexpr int PER = NM / HALF > 0 ? NM / HALF : 1;
+            constexpr int INL = NM / PER < HALF ? NM / PER : HALF;
 #pragma unroll
             for (int j = 0; j < RW; j++)
 #pragma unroll
-                for (int i = 0; i < RT; i++)
+                for (int i = 0; i < RT; i++) {
+                    const int mi = j * RT + i;  // compile-time after unrolling
+                    if (copies && mi % PER == 0 && mi / PER < INL) copy_full(nkt, nbuf, q0 + mi / PER);
                     acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[f][j], ft[f][i], acc[j][i], 0, 0, 0);
+                }
+#pragma unroll
+            for (int q = INL; q < HALF; q++)
+                if (copies) copy_full(nkt, nbuf, q0 + q);
         };
 
+        // One 16-wide half in steady state, in a fixed instruction order: the
+        // MFMAs of fragment set f, one fragment read (half rh of buffer rb into
+        // set g) after each of the first RT+RW MFMAs, and the copies q0 ..
+        // q0+HALF-1 of stage nkt into buffer nbuf after every second MFMA of
+        // the rest. Scheduling fences pin the order: left to itself the
+        // compiler bunches the reads and the copies, and a wave that queues
+        // many LDS or memory instructions at once stops issuing MFMAs.
+        auto half_step = [&](int f, int rb, int rh, int g, int nkt, int nbuf, int q0) {
+            constexpr int NM = RW * RT;
+            constexpr int NR = RT + RW;
+            static_assert(NR + 2 * HALF <= NM + 1, "reads and copies fit between the MFMAs");
+            const u32x4 *pa = &sA[rb][xo[rh]];
+            const u32x4 *pb = &sB[rb][xo[rh]];
+            // read r after MFMA r; copy c after MFMA NR + 2c (compile-time slots)
+            auto read_at = [&](int mi) { return mi < NR ? mi : -1; };
+            auto copy_at = [&](int mi) {
+                return ((mi - NR) >= 0 && (mi - NR) % 2 == 0 && (mi - NR) / 2 < HALF) ? (mi - NR) / 2 : -1;
+            };
+#pragma unroll
+            for (int mi = 0; mi < NM; mi++) {
+                const int j = mi / RT, i = mi % RT;
+                acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[f][j], ft[f][i], acc[j][i], 0, 0, 0);
+                __builtin_amdgcn_sched_barrier(0);
+                const int r = read_at(mi);
+                if (r >= 0 && r < RT) {
+                    ft[g][r] = as_bf16x8(pa[t_blk(r)]);
+                    __builtin_amdgcn_sched_barrier(0);
+                } else if (r >= RT) {
+                    fw[g][r - RT] = as_bf16x8(pb[w_blk(r - RT)]);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                const int c = copy_at(mi);
+                if (c >= 0) {
+                    copy_full(nkt, nbuf, q0 + c);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+        };
+
+        // Schedule of stage s (buffer s % STAGES). The barrier sits between
+        // the two 16-wide halves: before it, the second half of s is read and
+        // the first half's MFMAs run; after it (stage s+1 has landed and
+        // every wave is done with buffer s), the first half of s+1 is read
+        // while the second half's MFMAs run. Copies of stage s+STAGES go
+        // into buffer s in two parts: the first during the second half of s,
+        // the rest during the first half of s+1, so copy traffic is spread
+        // over the whole stage.
         wait_vm_barrier<0>();  // previous tile fully consumed
 #pragma unroll
-        for (int s = 0; s < STAGES - 1; s++)
-            if (s < nk) issue(s, s);
-        // stage 0 complete (stages 1 and 2 may still be in flight)
-        if (nk >= 3) wait_vm_barrier<2 * LOADS>();
+        for (int st = 0; st < STAGES - 1; st++)
+            if (st < nk)
+#pragma unroll
+                for (int q = 0; q < LOADS; q++) copy_any(st, st, q);
+        if (STAGES - 1 < nk)
+#pragma unroll
+            for (int q = 0; q < HALF; q++) copy_any(STAGES - 1, STAGES - 1, q);
+        // stage 0 landed: what may stay in flight is everything issued for later stages
+        if (nk >= STAGES) wait_vm_barrier<(STAGES - 2) * LOADS + HALF>();
+        else if (nk == 3 && STAGES >= 4) wait_vm_barrier<2 * LOADS>();
         else if (nk == 2) wait_vm_barrier<LOADS>();
         else wait_vm_barrier<0>();
         frag(0, 0, 0);
 
-        auto iter = [&](int kt, int b) {
-            frag(b, 1, 1);
-            mma(0);
-            if (kt + 1 < nk) {
-                // stage kt+1 must be complete; stage kt+2 may stay in flight
-                if (kt + 2 < nk) wait_vm_barrier<LOADS>();
-                else wait_vm_barrier<0>();
-                if (kt + STAGES - 1 < nk) issue(kt + STAGES - 1, (b + STAGES - 1) % STAGES);
-                frag((b + 1) % STAGES, 0, 0);
+        // Steady state, unrolled by STAGES so buffer indices are constants;
+        // every stage it copies is a full one. Scheduling fences keep each
+        // fragment read ahead of the MFMAs it overlaps (the compiler would
+        // otherwise sink the reads below them).
+        int kt = 0;
+        const int steady_last = nk - (ragged ? 1 : 0);
+        for (; kt + 2 * STAGES <= steady_last; kt += STAGES) {
+#pragma unroll
+            for (int b = 0; b < STAGES; b++) {
+                __builtin_amdgcn_sched_barrier(0);
+                half_step(0, b, 1, 1, kt + b + STAGES - 1, (b + STAGES - 1) % STAGES, HALF);
+                __builtin_amdgcn_sched_barrier(0);
+                wait_vm_barrier<(STAGES - 2) * LOADS>();
+                __builtin_amdgcn_sched_barrier(0);
+                half_step(1, (b + 1) % STAGES, 0, 0, kt + b + STAGES, b, 0);
+                __builtin_amdgcn_sched_barrier(0);
             }
-            mma(1);
-        };
+        }
+        // Drain: same schedule with run-time buffers and exact waits.
 #pragma unroll 1
-        for (int kt = 0; kt < nk; kt++) iter(kt, kt % STAGES);
+        for (; kt < nk; kt++) {
+            const int b = kt % STAGES;
+            frag(b, 1, 1);
+            if (kt + STAGES - 1 < nk)
+#pragma unroll
+                for (int q = HALF; q < LOADS; q++) copy_any(kt + STAGES - 1, (kt + STAGES - 1) % STAGES, q);
+            mma(0, false, 0, 0, 0);
+            if (kt + 1 < nk) {
+                const int beyond = min(nk - 1, kt + STAGES - 1) - (kt + 1);  // later stages, all issued
+                if (beyond >= 2 && STAGES >= 4) wait_vm_barrier<(STAGES >= 4 ? 2 : 0) * LOADS>();
+                else if (beyond >= 1) wait_vm_barrier<LOADS>();
+                else wait_vm_barrier<0>();
+                frag((b + 1) % STAGES, 0, 0);
+                if (kt + STAGES < nk)
+#pragma unroll
+                    for (int q = 0; q < HALF; q++) copy_any(kt + STAGES, b, q);
+            }
+            mma(1, false, 0, 0, 0);
+        }
 
         // ---- epilogue: lane = one token of each 32-token block, 4 columns per group
 #pragma unroll
@@ -585,10 +742,10 @@ __global__ __launch_bounds__(256) void tiled_pp_kernel(TiledParams p)
 }
 
 // Tile configuration of the large-M schedule.
-constexpr int kBM = 256;
-constexpr int kBN = 256;
-constexpr int kWM = 4;
-constexpr int kWN = 2;
+constexpr int kBM = MOE_TILED_BM;
+constexpr int kBN = MOE_TILED_BN;
+constexpr int kWM = MOE_TILED_WM;
+constexpr int kWN = MOE_TILED_WN;
 
 int persistent_grid()
 {
@@ -599,7 +756,7 @@ int persistent_grid()
             hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
             cus = 256;
     }
-    return ((cus + 7) / 8) * 8;
+    return ((cus + 7) / 8) * 8 * MOE_TILED_OCC;
 }
 
 TiledParams make_params(const GemmProblem &g, int NB)
