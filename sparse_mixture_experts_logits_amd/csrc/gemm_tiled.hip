@@ -29,15 +29,6 @@ namespace {
 #ifndef MOE_TILED_INTERLEAVE
 #define MOE_TILED_INTERLEAVE 1
 #endif
-#ifndef MOE_TILED_BM
-#define MOE_TILED_BM 256
-#define MOE_TILED_BN 256
-#define MOE_TILED_WM 4
-#define MOE_TILED_WN 2
-#endif
-#ifndef MOE_TILED_OCC
-#define MOE_TILED_OCC 1
-#endif
 #ifndef MOE_TILED_STAGES
 #define MOE_TILED_STAGES 4
 #endif
@@ -100,8 +91,8 @@ __device__ __forceinline__ void dma16(const void *gptr, uint32_t lds)
 
 __device__ __forceinline__ uint32_t lds_addr(const void *p) { return (uint32_t)(uintptr_t)p; }
 
-template <int BM, int BN, int WM, int WN, bool GATEUP>
-__global__ __launch_bounds__(WM *WN * 64, MOE_TILED_OCC) void tiled_gemm_kernel(TiledParams p)
+template <int BM, int BN, int WM, int WN, int OCC, bool GATEUP>
+__global__ __launch_bounds__(WM *WN * 64, OCC) void tiled_gemm_kernel(TiledParams p)
 {
     constexpr int NT = WM * WN * 64;
     constexpr int NWAVE = WM * WN;
@@ -741,13 +732,8 @@ __global__ __launch_bounds__(256) void tiled_pp_kernel(TiledParams p)
     }
 }
 
-// Tile configuration of the large-M schedule.
-constexpr int kBM = MOE_TILED_BM;
-constexpr int kBN = MOE_TILED_BN;
-constexpr int kWM = MOE_TILED_WM;
-constexpr int kWN = MOE_TILED_WN;
-
-int persistent_grid()
+// Persistent grid: OCC workgroups per CU, rounded to whole XCD rounds.
+int persistent_grid(int occ)
 {
     static int cus = 0;
     if (!cus) {
@@ -756,7 +742,7 @@ int persistent_grid()
             hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
             cus = 256;
     }
-    return ((cus + 7) / 8) * 8 * MOE_TILED_OCC;
+    return ((cus + 7) / 8) * 8 * occ;
 }
 
 TiledParams make_params(const GemmProblem &g, int NB)
@@ -779,38 +765,49 @@ TiledParams make_params(const GemmProblem &g, int NB)
     return t;
 }
 
-}  // namespace
-
-int tiled_block_m() { return kBM; }
+template <int BM, int BN, int WM, int WN, int OCC, bool GATEUP>
+hipError_t launch_cfg(const GemmProblem &g, hipStream_t st)
+{
+    const int cols = GATEUP ? BN / 2 : BN;  // output columns per N-block
+    TiledParams t = make_params(g, (int)((g.N + cols - 1) / cols));
+    hipLaunchKernelGGL((tiled_gemm_kernel<BM, BN, WM, WN, OCC, GATEUP>), dim3(persistent_grid(OCC)),
+                       dim3(WM * WN * 64), 0, st, t);
+    return hipGetLastError();
+}
 
 #ifndef MOE_TILED_PP
 #define MOE_TILED_PP 0
 #endif
 
+template <bool GATEUP>
+hipError_t launch_pp(const GemmProblem &g, hipStream_t st)
+{
+    const int cols = GATEUP ? 128 : 256;
+    TiledParams t = make_params(g, (int)((g.N + cols - 1) / cols));
+    hipLaunchKernelGGL((tiled_pp_kernel<256, 256, GATEUP>), dim3(persistent_grid(1)), dim3(256), 0, st, t);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+// Routed experts: 256x256 tiles, 8 waves, one workgroup per CU; the M-tile
+// list is built for this height. Dense problems (the shared expert, all T
+// rows) use smaller tiles so that a few thousand rows still fill the CUs:
+// 128x256 (gate_up) and 128x128 with two workgroups per CU (down).
+int tiled_block_m() { return 256; }
+
 hipError_t launch_gate_up_tiled(const GemmProblem &g, hipStream_t st)
 {
-    const int NB = (int)((g.N + kBN / 2 - 1) / (kBN / 2));
-    TiledParams t = make_params(g, NB);
-#if MOE_TILED_PP
-    hipLaunchKernelGGL((tiled_pp_kernel<kBM, kBN, true>), dim3(persistent_grid()), dim3(256), 0, st, t);
-#else
-    hipLaunchKernelGGL((tiled_gemm_kernel<kBM, kBN, kWM, kWN, true>), dim3(persistent_grid()),
-                       dim3(kWM * kWN * 64), 0, st, t);
-#endif
-    return hipGetLastError();
+    if (g.dense_rows > 0) return launch_cfg<128, 256, 2, 2, 1, true>(g, st);
+    if (MOE_TILED_PP) return launch_pp<true>(g, st);
+    return launch_cfg<256, 256, 4, 2, 1, true>(g, st);
 }
 
 hipError_t launch_down_tiled(const GemmProblem &g, hipStream_t st)
 {
-    const int NB = (int)((g.N + kBN - 1) / kBN);
-    TiledParams t = make_params(g, NB);
-#if MOE_TILED_PP
-    hipLaunchKernelGGL((tiled_pp_kernel<kBM, kBN, false>), dim3(persistent_grid()), dim3(256), 0, st, t);
-#else
-    hipLaunchKernelGGL((tiled_gemm_kernel<kBM, kBN, kWM, kWN, false>), dim3(persistent_grid()),
-                       dim3(kWM * kWN * 64), 0, st, t);
-#endif
-    return hipGetLastError();
+    if (g.dense_rows > 0) return launch_cfg<128, 128, 2, 2, 2, false>(g, st);
+    if (MOE_TILED_PP) return launch_pp<false>(g, st);
+    return launch_cfg<256, 256, 4, 2, 1, false>(g, st);
 }
 
 }  // namespace moe

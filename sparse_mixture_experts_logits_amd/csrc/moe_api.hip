@@ -90,7 +90,9 @@ moe::Shape make_shape(int64_t T, int64_t H, int64_t I, int64_t E, int32_t k, con
     s.k = k;
     s.sharedI = opts ? opts->shared_I : 0;
     s.dtype = opts ? opts->dtype : MOE_BF16;
-    s.rtok = 4;  // tokens per router block: many short blocks keep every CU busy
+    // tokens per router block: one token per block while T alone does not
+    // fill the CUs, else 4 (many short blocks keep every CU busy)
+    s.rtok = T <= 256 ? 1 : 4;
     s.nblk = (int)((T + s.rtok - 1) / s.rtok);
     s.tileBM = moe::tiled_block_m();
     s.maxTiles = (T * k) / s.tileBM + E + 1;

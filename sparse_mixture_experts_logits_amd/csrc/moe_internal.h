@@ -45,7 +45,7 @@ __device__ __forceinline__ float silu_f32(float g) { return g / (1.0f + __expf(-
 
 // ------------------------------------------------------------------ routing constants
 
-constexpr int kRouterMaxTokensPerBlock = 16;  // tokens per router block: 4 (small T) or 16
+constexpr int kRouterMaxTokensPerBlock = 4;  // tokens per router block: 1 or 4
 constexpr int kMaxExperts = 256;
 
 // Device tile of the large-M grouped GEMM: rows [row0, row0 + rows) of the
@@ -84,7 +84,7 @@ struct Shape {
     int k;
     int64_t sharedI;
     int dtype;       // 0 bf16, 1 f32
-    int rtok;        // tokens per router block (4 or 16)
+    int rtok;        // tokens per router block (1 or 4)
     int nblk;        // router blocks
     int tileBM;      // rows per M-tile of the large-M schedule
     int64_t maxTiles;

@@ -24,30 +24,33 @@ namespace moe {
 
 namespace {
 
+// A slice of 8 consecutive row elements as loaded (bf16: one 16-byte load,
+// widened to fp32 exactly only when used, so more slices fit in flight).
 template <typename Tin>
-struct RowLoader;
+struct Slice;
 
 template <>
-struct RowLoader<__bf16> {
-    // 8 consecutive elements starting at element i of a bf16 row
-    __device__ __forceinline__ static void load8(const __bf16 *row, int64_t i, float (&v)[8])
+struct Slice<__bf16> {
+    u32x4 q;
+    __device__ __forceinline__ void load(const __bf16 *row, int64_t i) { q = *reinterpret_cast<const u32x4 *>(row + i); }
+    __device__ __forceinline__ float at(int v) const
     {
-        u32x4 q = *reinterpret_cast<const u32x4 *>(row + i);
-        v[0] = bf16_lo(q.x); v[1] = bf16_hi(q.x);
-        v[2] = bf16_lo(q.y); v[3] = bf16_hi(q.y);
-        v[4] = bf16_lo(q.z); v[5] = bf16_hi(q.z);
-        v[6] = bf16_lo(q.w); v[7] = bf16_hi(q.w);
+        const uint32_t w = v < 2 ? q.x : v < 4 ? q.y : v < 6 ? q.z : q.w;
+        return (v & 1) ? bf16_hi(w) : bf16_lo(w);
     }
 };
 
 template <>
-struct RowLoader<float> {
-    __device__ __forceinline__ static void load8(const float *row, int64_t i, float (&v)[8])
+struct Slice<float> {
+    float4 a, b;
+    __device__ __forceinline__ void load(const float *row, int64_t i)
     {
-        float4 a = *reinterpret_cast<const float4 *>(row + i);
-        float4 b = *reinterpret_cast<const float4 *>(row + i + 4);
-        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-        v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+        a = *reinterpret_cast<const float4 *>(row + i);
+        b = *reinterpret_cast<const float4 *>(row + i + 4);
+    }
+    __device__ __forceinline__ float at(int v) const
+    {
+        return v == 0 ? a.x : v == 1 ? a.y : v == 2 ? a.z : v == 3 ? a.w : v == 4 ? b.x : v == 5 ? b.y : v == 6 ? b.z : b.w;
     }
 };
 
@@ -105,21 +108,33 @@ __global__ __launch_bounds__(256) void router_topk_kernel(
             for (int j = 0; j < TG; j++)
 #pragma unroll
                 for (int q = 0; q < EG; q++) acc[j][q] = 0.0f;
-#pragma unroll 2
-            for (int c = 0; c < nchunk; c++) {
-                const int64_t i0 = (int64_t)c * 512 + lane * 8;
-                if (i0 < H) {  // H is a multiple of 8: a slice is all valid or all absent
-                    float xv[TG][8], wv[EG][8];
+            // CU chunks per step: every load of a step is issued before its
+            // fmas, which still run in chunk order
+            constexpr int CU = TG == 1 ? 8 : 2;
+            for (int c0 = 0; c0 < nchunk; c0 += CU) {
+                Slice<Tin> xv[CU][TG], wv[CU][EG];
 #pragma unroll
-                    for (int j = 0; j < TG; j++) RowLoader<Tin>::load8(xrow[j], i0, xv[j]);
+                for (int u = 0; u < CU; u++) {
+                    const int64_t i0 = (int64_t)(c0 + u) * 512 + lane * 8;
+                    if (i0 < H) {  // H is a multiple of 8: a slice is all valid or all absent
 #pragma unroll
-                    for (int q = 0; q < EG; q++) RowLoader<Tin>::load8(wrow[q], i0, wv[q]);
+                        for (int j = 0; j < TG; j++) xv[u][j].load(xrow[j], i0);
 #pragma unroll
-                    for (int j = 0; j < TG; j++)
+                        for (int q = 0; q < EG; q++) wv[u][q].load(wrow[q], i0);
+                    }
+                }
 #pragma unroll
-                        for (int q = 0; q < EG; q++)
+                for (int u = 0; u < CU; u++) {
+                    const int64_t i0 = (int64_t)(c0 + u) * 512 + lane * 8;
+                    if (i0 < H) {
 #pragma unroll
-                            for (int v = 0; v < 8; v++) acc[j][q] = __builtin_fmaf(xv[j][v], wv[q][v], acc[j][q]);
+                        for (int j = 0; j < TG; j++)
+#pragma unroll
+                            for (int q = 0; q < EG; q++)
+#pragma unroll
+                                for (int v = 0; v < 8; v++)
+                                    acc[j][q] = __builtin_fmaf(xv[u][j].at(v), wv[u][q].at(v), acc[j][q]);
+                    }
                 }
             }
             // xor butterfly over the 64 lanes: P[L] <- P[L] + P[L ^ d], d = 32..1
@@ -241,7 +256,15 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(
     const int b1 = min(nblk, b0 + chunk);
     if (g < G) {
         int s = 0;
-        for (int b = b0; b < b1; b++) s += blk_counts[(int64_t)b * E + e];
+        int b = b0;
+        for (; b + 8 <= b1; b += 8) {  // eight independent loads per step
+            int v[8];
+#pragma unroll
+            for (int u = 0; u < 8; u++) v[u] = blk_counts[(int64_t)(b + u) * E + e];
+#pragma unroll
+            for (int u = 0; u < 8; u++) s += v[u];
+        }
+        for (; b < b1; b++) s += blk_counts[(int64_t)b * E + e];
         s_part[g * E + e] = s;
     }
     __syncthreads();
@@ -266,7 +289,18 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(
     __syncthreads();
     if (g < G) {
         int base = s_off[e] + s_part[g * E + e];
-        for (int b = b0; b < b1; b++) {
+        int b = b0;
+        for (; b + 8 <= b1; b += 8) {
+            int v[8];
+#pragma unroll
+            for (int u = 0; u < 8; u++) v[u] = blk_counts[(int64_t)(b + u) * E + e];
+#pragma unroll
+            for (int u = 0; u < 8; u++) {
+                blk_base[(int64_t)(b + u) * E + e] = base;
+                base += v[u];
+            }
+        }
+        for (; b < b1; b++) {
             blk_base[(int64_t)b * E + e] = base;
             base += blk_counts[(int64_t)b * E + e];
         }
@@ -333,12 +367,13 @@ hipError_t launch_router_topk(const Shape &s, const void *X, const void *Wr, con
     hipLaunchKernelGGL((router_topk_kernel<TIN, RT>), grid, block, 0, st, (const TIN *)X, (const TIN *)Wr, \
                        bias, (int)s.T, (int)s.H, (int)s.E, s.k, routed_scale, ws.ids, ws.wts, ids_out,  \
                        wts_out, logits_out, ws.blk_counts)
+    static_assert(kRouterMaxTokensPerBlock == 4, "router blocks of 1 or 4 tokens");
     if (s.dtype == 0) {
-        if (s.rtok == 4) MOE_ROUTER_LAUNCH(__bf16, 4);
-        else MOE_ROUTER_LAUNCH(__bf16, 16);
+        if (s.rtok == 1) MOE_ROUTER_LAUNCH(__bf16, 1);
+        else MOE_ROUTER_LAUNCH(__bf16, 4);
     } else {
-        if (s.rtok == 4) MOE_ROUTER_LAUNCH(float, 4);
-        else MOE_ROUTER_LAUNCH(float, 16);
+        if (s.rtok == 1) MOE_ROUTER_LAUNCH(float, 1);
+        else MOE_ROUTER_LAUNCH(float, 4);
     }
 #undef MOE_ROUTER_LAUNCH
     return hipGetLastError();
