@@ -9,7 +9,10 @@ line on stdout.
 
 Default workload: the PhiMoE decode step (T=32, H=4096, I=6400, E=16, top-2),
 a weight-bandwidth-bound case. The PhiMoE prefill chunk (T=4096) is measured
-in the same run and reported under "prefill" (MFMA-bound). A short untimed
+in the same run and reported under "prefill" (MFMA-bound), and the decode
+step with FP8 (E4M3, per-row scaled) expert weights under "decode_fp8" (a
+different weight storage, so never the headline value; --fp8 makes it the
+main line, marked in its config). A short untimed
 pilot with events at every stage boundary finds the dominant kernel; every
 timed call then records HIP events around that kernel on the library's
 stream, so the roofline figures come from the timed region itself.
@@ -50,13 +53,14 @@ def log(*a):
 
 # ------------------------------------------------------------------ algorithmic work
 
-def work(wl, counts):
+def work(wl, counts, fp8=False):
     """Algorithmic FLOPs and bytes of the layer and of its two expert GEMMs.
 
     Bytes count what the method itself must move once: weights of experts that
     received tokens, hidden, router weights and the output for the layer; for
     a GEMM kernel, its weights once plus its input and output activations once
-    (gate_up: hidden in, h out; down: h in, fp32 weighted slots out)."""
+    (gate_up: hidden in, h out; down: h in, fp32 weighted slots out). With
+    FP8 expert weights a weight is one byte plus its row's 4-byte scale."""
     es = 2 if wl.dtype == "bf16" else 4
     T, H, I, E, k = wl.T, wl.H, wl.I, wl.E, wl.k
     TK = T * k
@@ -66,9 +70,11 @@ def work(wl, counts):
     f_dn = 2.0 * TK * H * I
     f_router = 2.0 * T * H * E
     f_shared = 2.0 * T * 3 * Is * H
-    b_gu = hit * 2 * I * H * es + T * H * es + TK * I * es
-    b_dn = hit * H * I * es + TK * I * es + TK * H * 4
-    b_layer = hit * 3 * I * H * es + 2 * T * H * es + E * H * es + 3 * Is * H * es
+    w_gu = hit * (2 * I * H + 2 * I * 4) if fp8 else hit * 2 * I * H * es
+    w_dn = hit * (H * I + H * 4) if fp8 else hit * H * I * es
+    b_gu = w_gu + T * H * es + TK * I * es
+    b_dn = w_dn + TK * I * es + TK * H * 4
+    b_layer = w_gu + w_dn + 2 * T * H * es + E * H * es + 3 * Is * H * es
     return dict(hit=hit, flop_layer=f_gu + f_dn + f_router + f_shared, bytes_layer=b_layer,
                 flop_gate_up=f_gu, bytes_gate_up=b_gu, flop_down=f_dn, bytes_down=b_dn)
 
@@ -158,7 +164,7 @@ def measured_traffic(kernel, workload):
 
 # ------------------------------------------------------------------ GPU timing
 
-def run_workload(name, steps, warmup):
+def run_workload(name, steps, warmup, fp8=False):
     import torch
     import numpy as np
     import sparse_mixture_experts_logits_amd as moe
@@ -177,12 +183,17 @@ def run_workload(name, steps, warmup):
         _DEV_CACHE[key] = (d(inp.router_w), d(inp.gate_up), d(inp.down))
     router_w, gate_up, down = _DEV_CACHE[key]
     hidden = d(inp.hidden)
+    scales = {}
+    if fp8:  # quantise the routed experts once, outside the timed region
+        gate_up, gs = moe.quantize_fp8_rows(gate_up)
+        down, ds = moe.quantize_fp8_rows(down)
+        scales = dict(gate_up_scale=gs, down_scale=ds)
     sgu = sdn = None
     if inp.shared_gate_up:
         gu, dn = inp.shared_concat()
         sgu, sdn = d(gu), d(dn)
     bias = None if inp.bias is None else torch.from_numpy(inp.bias).to(dev)
-    kw = dict(routed_scale=wl.routed_scale, router_bias=bias, shared_gate_up=sgu, shared_down=sdn)
+    kw = dict(routed_scale=wl.routed_scale, router_bias=bias, shared_gate_up=sgu, shared_down=sdn, **scales)
 
     out = torch.empty((wl.T, wl.H), dtype=hidden.dtype, device=dev)
     need = moe.workspace_bytes(wl.T, wl.H, wl.I, wl.E, wl.k, shared_I=sgu.shape[0] // 2 if sgu is not None else 0,
@@ -241,7 +252,7 @@ def run_workload(name, steps, warmup):
     stages = dict(zip(moe.STAGES, stage_ms.tolist()))
     stages[moe.STAGES[dom]] = dom_ms  # live value from the timed region
     return dict(wl=wl, counts=counts, wall_s=wall, gpu_ms=gpu_ms, steps=steps, stages=stages,
-                dominant=moe.STAGES[dom], inp=inp)
+                dominant=moe.STAGES[dom], inp=inp, fp8=fp8)
 
 
 _INPUT_CACHE = {}
@@ -251,7 +262,7 @@ _DEV_CACHE = {}
 def roofline_of(res):
     """Roofline of the dominant expert GEMM (the stage with the largest time)."""
     wl = res["wl"]
-    w = work(wl, res["counts"])
+    w = work(wl, res["counts"], fp8=res["fp8"])
     st = res["stages"]
     kernel = res["dominant"]
     if kernel not in ("gate_up", "down"):  # the expert GEMMs dominate every workload here
@@ -267,7 +278,7 @@ def roofline_of(res):
         achieved = w[f"flop_{kernel}"] / dur_s / 1e12
         r = dict(bound="mfma", achieved=round(achieved, 1), peak=peak, unit="TFLOP/s",
                  frac=round(achieved / peak, 4))
-    tr = measured_traffic(kernel, wl.name)
+    tr = measured_traffic(kernel, wl.name + ("_fp8" if res["fp8"] else ""))
     r["traffic"] = tr
     r["kernel"] = kernel
     r["avg_launch_ms"] = round(st[kernel], 4)
@@ -318,6 +329,8 @@ def main(argv=None):
     ap.add_argument("--prefill-steps", type=int, default=20)
     ap.add_argument("--no-prefill", action="store_true", help="skip the secondary prefill measurement")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-fp8", action="store_true", help="skip the secondary FP8-weight decode measurement")
+    ap.add_argument("--fp8", action="store_true", help="time the main workload with FP8 expert weights")
     ap.add_argument("--cpu-tokens", type=int, default=32)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a 1 GiB device copy (counter calibration under rocprofv3)")
@@ -343,7 +356,7 @@ def main(argv=None):
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
 
-    res = run_workload(args.workload, args.steps, args.warmup)
+    res = run_workload(args.workload, args.steps, args.warmup, fp8=args.fp8)
     roof, w = roofline_of(res)
     lay = layer_summary(res, w)
     wl = res["wl"]
@@ -362,12 +375,18 @@ def main(argv=None):
         "data": "synthetic (seeded normal draws; no checkpoint)",
         "config": {"workload": wl.name, "T": wl.T, "H": wl.H, "I": wl.I, "E": wl.E, "k": wl.k,
                    "routed_scale": wl.routed_scale, "shared_I": wl.n_shared * wl.shared_I,
-                   "parallelism": "single GPU"},
+                   "parallelism": "single GPU",
+                   **({"expert_weights": "fp8_e4m3_row_scaled"} if args.fp8 else {})},
         "roofline": roof,
         "layer": lay,
     }
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(res, args.cpu_tokens)
+    if not args.no_fp8 and not args.fp8 and args.workload == "phimoe_decode":
+        fres = run_workload("phimoe_decode", args.steps, args.warmup, fp8=True)
+        froof, fw = roofline_of(fres)
+        line["decode_fp8"] = dict(workload="phimoe_decode", weights="OCP FP8 E4M3, one fp32 scale per row",
+                                  roofline=froof, layer=layer_summary(fres, fw))
     if not args.no_prefill and args.workload != "phimoe_prefill":
         pres = run_workload("phimoe_prefill", args.prefill_steps, 3)
         proof, pw = roofline_of(pres)

@@ -61,6 +61,14 @@ typedef enum moe_dtype {
     MOE_F32 = 1   /* fp32 everywhere                                                */
 } moe_dtype;
 
+/* Storage of the routed experts' weights (gate_up, down). */
+typedef enum moe_weight_format {
+    MOE_WEIGHTS_NATIVE = 0,  /* same dtype as the activations (opts->dtype)          */
+    MOE_WEIGHTS_FP8_E4M3 = 1 /* one byte per weight, OCP FP8 E4M3, plus one fp32    */
+                             /* scale per weight row: w = e4m3(q) * scale (see      */
+                             /* moe_quantize_fp8_rows); bf16 activations only        */
+} moe_weight_format;
+
 /* opts->flags bits: choose the expert-GEMM schedule (default: by shape). */
 #define MOE_FLAG_FORCE_TILED 0x1u  /* large-M tiles (prefill schedule)          */
 #define MOE_FLAG_FORCE_SKINNY 0x2u /* weight-streaming tiles (decode schedule)  */
@@ -93,6 +101,18 @@ typedef struct moe_opts {
      * stage i is the elapsed time between events i and i+1. Stages that do
      * not run (no shared expert) take zero time. NULL entries are skipped. */
     void *const *stage_events;
+    /* Routed expert weights stored as FP8 (moe_weight_format; default native).
+     * With MOE_WEIGHTS_FP8_E4M3, gate_up is bytes [E, 2I, H] and down bytes
+     * [E, H, I], each row scaled by gate_up_scale [E, 2I] / down_scale [E, H]
+     * (fp32); H and I must be multiples of 16. This is the storage that
+     * halves the bytes a decode step streams (MoEs in Transformers page,
+     * section on why MoEs are fast: decode speed ~ bandwidth / bytes of the
+     * active weights; per-expert quantisation once experts are packed). The
+     * shared expert stays in opts->dtype. Every schedule streams the weights
+     * (the weight-streaming kernels), so MOE_FLAG_FORCE_TILED is rejected. */
+    int32_t weight_format;
+    const float *gate_up_scale;
+    const float *down_scale;
 } moe_opts;
 
 /* Stages of moe_forward, in launch order. */
@@ -151,6 +171,23 @@ int64_t moe_workspace_bytes(int64_t T, int64_t H, int64_t I, int64_t E, int32_t 
 int moe_forward(const void *hidden, const void *router_w, const void *gate_up, const void *down,
                 int64_t T, int64_t H, int64_t I, int64_t E, int32_t k, const moe_opts *opts,
                 void *out);
+
+/*
+ * Per-row FP8 quantisation of a bf16 matrix w [rows, cols] (for instance the
+ * packed gate_up viewed as [E*2I, H], or down as [E*H, I]):
+ *   a = max_i |w[r, i]|,  scale[r] = a / 448 (fp32 division; 1 when a = 0),
+ *   q[r, i] = the OCP FP8 E4M3 value nearest to w[r, i] / scale[r] (fp32
+ *             division), ties to the even code, saturating at +-448; zero
+ *             is stored as 0x00.
+ * E4M3: sign bit, 4 exponent bits with bias 7, 3 mantissa bits; exponent
+ * field 0 holds the subnormals m * 2^-9; 0x7F / 0xFF are NaN (never
+ * produced). 448 is the largest finite magnitude.
+ * q [rows, cols] bytes and scale [rows] fp32 are device outputs; cols >= 16
+ * and a multiple of 16; w and q 16-byte aligned. Asynchronous on stream
+ * (hipStream_t, NULL = default). Returns MOE_OK or a negative moe_status
+ * (argument checks run before any HIP call).
+ */
+int moe_quantize_fp8_rows(const void *w, int64_t rows, int64_t cols, void *q, float *scale, void *stream);
 
 /* Message describing the last failing call on this thread ("" if none). */
 const char *moe_last_error(void);

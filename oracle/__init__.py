@@ -48,8 +48,13 @@ def _load():
         lib.oracle_moe_tokens.argtypes = [vp, vp, vp, i32, i64, i64, vp, vp, i32, i32,
                                           vp, vp, vp, vp, i64, vp]
         lib.oracle_num_threads.argtypes = []
+        lib.oracle_e4m3_values.argtypes = [vp]
+        lib.oracle_quantize_e4m3_rows.argtypes = [vp, i64, i64, vp, vp]
+        lib.oracle_moe_tokens_e4m3.argtypes = [vp, vp, vp, vp, vp, i64, i64, vp, vp, i32, i32,
+                                               vp, vp, vp, vp, i64, vp]
         for f in (lib.oracle_router_logits, lib.oracle_select_topk, lib.oracle_route,
-                  lib.oracle_moe_tokens, lib.oracle_num_threads):
+                  lib.oracle_moe_tokens, lib.oracle_num_threads, lib.oracle_e4m3_values,
+                  lib.oracle_quantize_e4m3_rows, lib.oracle_moe_tokens_e4m3):
             f.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -156,6 +161,82 @@ def moe_tokens(hidden, gate_up, down, ids, weights, tokens=None, shared=()):
                                      ctypes.cast(sdn, ctypes.c_void_p), _p(sI), _p(tokens),
                                      len(tokens), _p(out)), "moe_tokens")
     return out
+
+
+def e4m3_values() -> np.ndarray:
+    """Value of each of the 256 E4M3 codes (fp64; NaN for 0x7F and 0xFF)."""
+    out = np.empty(256, dtype=np.float64)
+    _check(_load().oracle_e4m3_values(_p(out)), "e4m3_values")
+    return out
+
+
+def quantize_e4m3_rows(w: np.ndarray):
+    """Per-row E4M3 quantisation of bf16 bits w [..., cols] -> (q uint8, scale fp32 [...])."""
+    w = np.ascontiguousarray(w)
+    assert w.dtype == np.uint16
+    cols = w.shape[-1]
+    rows = w.size // cols
+    q = np.empty(w.shape, dtype=np.uint8)
+    scale = np.empty(w.shape[:-1], dtype=np.float32)
+    _check(_load().oracle_quantize_e4m3_rows(_p(w), rows, cols, _p(q), _p(scale)), "quantize_e4m3_rows")
+    return q, scale
+
+
+def moe_tokens_e4m3(hidden, gate_up_q, gu_scale, down_q, dn_scale, ids, weights, tokens=None, shared=()):
+    """moe_tokens with E4M3 routed-expert weights (bf16 activations and shared experts)."""
+    hidden = np.ascontiguousarray(hidden)
+    assert hidden.dtype == np.uint16
+    gate_up_q = np.ascontiguousarray(gate_up_q, dtype=np.uint8)
+    down_q = np.ascontiguousarray(down_q, dtype=np.uint8)
+    gu_scale = np.ascontiguousarray(gu_scale, dtype=np.float32)
+    dn_scale = np.ascontiguousarray(dn_scale, dtype=np.float32)
+    T, H = hidden.shape
+    E, twoI, H2 = gate_up_q.shape
+    I = twoI // 2
+    assert H2 == H and down_q.shape == (E, H, I)
+    assert gu_scale.shape == (E, 2 * I) and dn_scale.shape == (E, H)
+    ids = np.ascontiguousarray(ids, dtype=np.int32)
+    weights = np.ascontiguousarray(weights, dtype=np.float32)
+    k = ids.shape[1]
+    if tokens is None:
+        tokens = np.arange(T, dtype=np.int32)
+    tokens = np.ascontiguousarray(tokens, dtype=np.int32)
+    n_sh = len(shared)
+    keep = []
+    sgu = (ctypes.c_void_p * max(1, n_sh))()
+    sdn = (ctypes.c_void_p * max(1, n_sh))()
+    sI = np.zeros(max(1, n_sh), dtype=np.int64)
+    for s, (g, d) in enumerate(shared):
+        g = np.ascontiguousarray(g)
+        d = np.ascontiguousarray(d)
+        assert g.dtype == np.uint16 and d.dtype == np.uint16
+        Is = g.shape[0] // 2
+        assert g.shape == (2 * Is, H) and d.shape == (H, Is)
+        keep += [g, d]
+        sgu[s] = g.ctypes.data
+        sdn[s] = d.ctypes.data
+        sI[s] = Is
+    out = np.empty((len(tokens), H), dtype=np.float32)
+    _check(_load().oracle_moe_tokens_e4m3(_p(hidden), _p(gate_up_q), _p(gu_scale), _p(down_q), _p(dn_scale),
+                                          H, I, _p(ids), _p(weights), int(k), n_sh,
+                                          ctypes.cast(sgu, ctypes.c_void_p), ctypes.cast(sdn, ctypes.c_void_p),
+                                          _p(sI), _p(tokens), len(tokens), _p(out)), "moe_tokens_e4m3")
+    return out
+
+
+def moe_forward_e4m3(hidden, router_w, gate_up, down, k, routed_scale=1.0, bias=None, shared=(),
+                     tokens=None):
+    """Whole layer with the routed experts quantised to E4M3 per row (bf16
+    weights in, quantised here): routing as moe_forward, outputs for
+    ``tokens``. Returns the routing, the outputs and the quantised weights."""
+    logits = router_logits(hidden, router_w, bias)
+    ids, w = select_topk(logits, k, routed_scale)
+    counts, offsets, perm, inv = route(ids, router_w.shape[0])
+    gq, gs = quantize_e4m3_rows(gate_up)
+    dq, ds = quantize_e4m3_rows(down)
+    out = moe_tokens_e4m3(hidden, gq, gs, dq, ds, ids, w, tokens=tokens, shared=shared)
+    return dict(logits=logits, ids=ids, weights=w, counts=counts, offsets=offsets, perm=perm, inv=inv,
+                out=out, gate_up_q=gq, gate_up_scale=gs, down_q=dq, down_scale=ds)
 
 
 def moe_forward(hidden, router_w, gate_up, down, k, routed_scale=1.0, bias=None, shared=(),

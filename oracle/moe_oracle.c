@@ -269,6 +269,178 @@ int oracle_moe_tokens(const void *X, const void *gate_up, const void *down, int 
     return bad ? OR_BAD : OR_OK;
 }
 
+/*
+ * FP8 expert weights (the low-precision decode storage: the MoEs in
+ * Transformers page, section on why MoEs are fast, prices decode at memory
+ * bandwidth over the bytes of the active weights and notes that a native
+ * low-precision format is faster still; its weight-loading section ties
+ * per-expert quantisation to packed experts). The pages fix no format; the
+ * reading taken here is OCP FP8 E4M3 with one fp32 scale per weight row.
+ *
+ * E4M3 byte b: sign = bit 7, exponent field e = bits 6..3 (bias 7), mantissa
+ * m = bits 2..0; e = 0 holds the subnormals m * 2^-9, otherwise the value is
+ * (1 + m/8) * 2^(e-7); e = 15 with m = 7 is NaN. Largest finite: 448.
+ */
+static double e4m3_value(uint8_t b)
+{
+    int sgn = b >> 7, e = (b >> 3) & 15, m = b & 7;
+    if (e == 15 && m == 7)
+        return NAN;
+    double v = e == 0 ? ldexp((double)m, -9) : ldexp((double)(8 + m), e - 10);
+    return sgn ? -v : v;
+}
+
+/* The value table of all 256 codes (NaN for the two NaN codes). */
+int oracle_e4m3_values(double *out256)
+{
+    if (!out256)
+        return OR_BAD;
+    for (int b = 0; b < 256; b++)
+        out256[b] = e4m3_value((uint8_t)b);
+    return OR_OK;
+}
+
+/*
+ * Per-row quantisation of bf16 rows: a = max |w|, scale = a / 448 (fp32
+ * division), q = the code whose value is nearest to w / scale (fp32
+ * division), ties to the even code, saturating at 448; zero -> 0x00. A row
+ * with a < 448 * 2^-126 (its scale would be subnormal) is stored as zeros
+ * with scale 1. The nearest code is found by bisection over the 127
+ * non-negative finite values, which increase with the code.
+ */
+int oracle_quantize_e4m3_rows(const uint16_t *w, int64_t rows, int64_t cols, uint8_t *q, float *scale)
+{
+    if (!w || !q || !scale || rows < 0 || cols < 1)
+        return OR_BAD;
+    double pos[127];
+    for (int c = 0; c < 127; c++)
+        pos[c] = e4m3_value((uint8_t)c);
+    const float min_row_max = 448.0f * ldexpf(1.0f, -126);
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; r++) {
+        float a = 0.0f;
+        for (int64_t i = 0; i < cols; i++) {
+            float x = fabsf(widen(w, 0, (size_t)(r * cols + i)));
+            if (x > a)
+                a = x;
+        }
+        int zero_row = !(a >= min_row_max);
+        float sc = zero_row ? 1.0f : a / 448.0f;
+        scale[r] = sc;
+        for (int64_t i = 0; i < cols; i++) {
+            uint8_t code = 0;
+            if (!zero_row) {
+                float v = widen(w, 0, (size_t)(r * cols + i)) / sc;
+                double av = fabs((double)v);
+                int c;
+                if (av >= pos[126]) {
+                    c = 126;
+                } else {
+                    int lo = 0, hi = 126; /* pos[lo] <= av < pos[hi] */
+                    while (hi - lo > 1) {
+                        int mid = (lo + hi) / 2;
+                        if (pos[mid] <= av)
+                            lo = mid;
+                        else
+                            hi = mid;
+                    }
+                    double dlo = av - pos[lo], dhi = pos[hi] - av;
+                    c = dlo < dhi ? lo : dhi < dlo ? hi : ((lo & 1) ? hi : lo);
+                }
+                code = c == 0 ? 0 : (uint8_t)((v < 0 ? 0x80 : 0) | c);
+            }
+            q[r * cols + i] = code;
+        }
+    }
+    return OR_OK;
+}
+
+/* The expert SwiGLU with E4M3 weights: each weight is fl32(value(q) * row
+ * scale) (the product of a 4-bit and a 24-bit significand is exact in fp64,
+ * so this is one rounding); tab[] holds value(q) for every code. */
+static void swiglu_expert_e4m3(const double *tab, const float *x, const uint8_t *gate_up,
+                               const float *gu_scale, const uint8_t *down, const float *dn_scale,
+                               int64_t H, int64_t I, float *h, float *y)
+{
+    for (int64_t n = 0; n < I; n++) {
+        float g = 0.0f, u = 0.0f;
+        for (int64_t i = 0; i < H; i++) {
+            float wg = (float)(tab[gate_up[n * H + i]] * (double)gu_scale[n]);
+            float wu = (float)(tab[gate_up[(I + n) * H + i]] * (double)gu_scale[I + n]);
+            g = fmaf(wg, x[i], g);
+            u = fmaf(wu, x[i], u);
+        }
+        h[n] = (float)(silu((double)g) * (double)u);
+    }
+    for (int64_t m = 0; m < H; m++) {
+        float acc = 0.0f;
+        for (int64_t n = 0; n < I; n++)
+            acc = fmaf((float)(tab[down[m * I + n]] * (double)dn_scale[m]), h[n], acc);
+        y[m] = acc;
+    }
+}
+
+/*
+ * Same layer as oracle_moe_tokens with the routed experts stored as E4M3
+ * bytes gate_up [E, 2I, H], down [E, H, I] and fp32 row scales
+ * gu_scale [E, 2I], dn_scale [E, H]; activations and shared experts bf16.
+ */
+int oracle_moe_tokens_e4m3(const uint16_t *X, const uint8_t *gate_up, const float *gu_scale,
+                           const uint8_t *down, const float *dn_scale, int64_t H, int64_t I,
+                           const int32_t *ids, const float *weights, int k, int n_shared,
+                           const void *const *shared_gate_up, const void *const *shared_down,
+                           const int64_t *shared_I, const int32_t *tokens, int64_t n_tokens, float *out)
+{
+    if (!X || !gate_up || !gu_scale || !down || !dn_scale || !ids || !weights || !tokens || !out ||
+        H <= 0 || I <= 0 || k < 1 || n_shared < 0)
+        return OR_BAD;
+    double tab[256];
+    for (int b = 0; b < 256; b++)
+        tab[b] = e4m3_value((uint8_t)b);
+    int64_t Imax = I;
+    for (int s = 0; s < n_shared; s++)
+        if (shared_I[s] > Imax)
+            Imax = shared_I[s];
+    int bad = 0;
+#pragma omp parallel
+    {
+        float *x = (float *)malloc(sizeof(float) * (size_t)H);
+        float *y = (float *)malloc(sizeof(float) * (size_t)H);
+        float *h = (float *)malloc(sizeof(float) * (size_t)Imax);
+        if (!x || !y || !h) {
+#pragma omp atomic write
+            bad = 1;
+        } else {
+#pragma omp for schedule(dynamic, 1)
+            for (int64_t r = 0; r < n_tokens; r++) {
+                int64_t t = tokens[r];
+                for (int64_t i = 0; i < H; i++)
+                    x[i] = widen(X, 0, (size_t)(t * H + i));
+                float *o = out + r * H;
+                for (int64_t m = 0; m < H; m++)
+                    o[m] = 0.0f;
+                for (int j = 0; j < k; j++) {
+                    int64_t e = ids[t * k + j];
+                    float w = weights[t * k + j];
+                    swiglu_expert_e4m3(tab, x, gate_up + (size_t)e * (size_t)(2 * I * H), gu_scale + e * 2 * I,
+                                       down + (size_t)e * (size_t)(H * I), dn_scale + e * H, H, I, h, y);
+                    for (int64_t m = 0; m < H; m++)
+                        o[m] = fmaf(w, y[m], o[m]);
+                }
+                for (int s = 0; s < n_shared; s++) {
+                    swiglu_expert(x, shared_gate_up[s], shared_down[s], 0, H, shared_I[s], h, y);
+                    for (int64_t m = 0; m < H; m++)
+                        o[m] = o[m] + y[m];
+                }
+            }
+        }
+        free(x);
+        free(y);
+        free(h);
+    }
+    return bad ? OR_BAD : OR_OK;
+}
+
 /* Number of OpenMP threads the oracle runs on (reported beside its timings). */
 int oracle_num_threads(void)
 {

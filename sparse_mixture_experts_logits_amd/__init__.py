@@ -12,8 +12,9 @@ import os
 
 import numpy as np
 
-__all__ = ["moe_forward", "workspace_bytes", "MoeError", "load_library", "LIB_PATH",
-           "FLAG_FORCE_TILED", "FLAG_FORCE_SKINNY", "bf16_bits_to_tensor", "EXPORTS"]
+__all__ = ["moe_forward", "workspace_bytes", "quantize_fp8_rows", "MoeError", "load_library", "LIB_PATH",
+           "FLAG_FORCE_TILED", "FLAG_FORCE_SKINNY", "WEIGHTS_NATIVE", "WEIGHTS_FP8_E4M3",
+           "bf16_bits_to_tensor", "EXPORTS"]
 
 # MOE_MI355X_LIB may point at another build of the same library (tuning builds)
 LIB_PATH = os.environ.get("MOE_MI355X_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
@@ -23,7 +24,9 @@ MOE_BF16 = 0
 MOE_F32 = 1
 FLAG_FORCE_TILED = 0x1
 FLAG_FORCE_SKINNY = 0x2
-EXPORTS = ("moe_opts_init", "moe_workspace_bytes", "moe_forward", "moe_last_error")
+WEIGHTS_NATIVE = 0
+WEIGHTS_FP8_E4M3 = 1
+EXPORTS = ("moe_opts_init", "moe_workspace_bytes", "moe_forward", "moe_quantize_fp8_rows", "moe_last_error")
 STAGES = ("router", "scan", "permute", "gate_up", "down", "shared_gate_up", "shared_down", "combine")
 STAGE_EVENTS = len(STAGES) + 1
 
@@ -53,6 +56,9 @@ class MoeOpts(ctypes.Structure):
         ("workspace_bytes", ctypes.c_size_t),
         ("stream", ctypes.c_void_p),
         ("stage_events", ctypes.c_void_p),
+        ("weight_format", ctypes.c_int32),
+        ("gate_up_scale", ctypes.c_void_p),
+        ("down_scale", ctypes.c_void_p),
     ]
 
 
@@ -84,6 +90,8 @@ def load_library():
         lib.moe_workspace_bytes.restype = i64
         lib.moe_forward.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i32, ctypes.POINTER(MoeOpts), vp]
         lib.moe_forward.restype = ctypes.c_int
+        lib.moe_quantize_fp8_rows.argtypes = [vp, i64, i64, vp, vp, vp]
+        lib.moe_quantize_fp8_rows.restype = ctypes.c_int
         lib.moe_last_error.argtypes = []
         lib.moe_last_error.restype = ctypes.c_char_p
         _lib = lib
@@ -124,16 +132,38 @@ def bf16_bits_to_tensor(a: np.ndarray, device="cuda"):
     return torch.from_numpy(a).to(device)
 
 
+def quantize_fp8_rows(w, stream=None):
+    """Per-row FP8 E4M3 quantisation of a contiguous bf16 CUDA tensor viewed
+    as [rows, cols] (cols = last dimension): returns (q uint8 of w's shape,
+    scale fp32 of w's leading shape) with w ~= e4m3(q) * scale."""
+    import torch
+    if w.dtype != torch.bfloat16 or not w.is_contiguous() or not w.is_cuda:
+        raise ValueError("w must be a contiguous bf16 CUDA tensor")
+    cols = w.shape[-1]
+    rows = w.numel() // cols if cols else 0
+    q = torch.empty(w.shape, dtype=torch.uint8, device=w.device)
+    scale = torch.empty(w.shape[:-1], dtype=torch.float32, device=w.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(w.device)
+    rc = load_library().moe_quantize_fp8_rows(_ptr(w), rows, cols, _ptr(q), _ptr(scale),
+                                              ctypes.c_void_p(stream.cuda_stream))
+    if rc != 0:
+        raise MoeError(rc, last_error())
+    return q, scale
+
+
 def moe_forward(hidden, router_w, gate_up, down, k: int, *, routed_scale: float = 1.0, router_bias=None,
                 shared_gate_up=None, shared_down=None, flags: int = 0, return_routing: bool = False,
-                out=None, workspace=None, stream=None, stage_events=None):
+                out=None, workspace=None, stream=None, stage_events=None, gate_up_scale=None, down_scale=None):
     """Run the MoE layer on torch tensors already on the GPU.
 
     hidden [T, H], router_w [E, H], gate_up [E, 2I, H], down [E, H, I] (all
     bf16 or all fp32, contiguous); router_bias [E] fp32; shared_gate_up
-    [2Is, H], shared_down [H, Is]. Returns out [T, H] (and a dict of routing
-    tensors when ``return_routing``). Work is enqueued on ``stream`` (default:
-    torch's current stream)."""
+    [2Is, H], shared_down [H, Is]. FP8 expert weights: gate_up and down as
+    uint8 E4M3 codes with gate_up_scale [E, 2I] and down_scale [E, H] (fp32,
+    from quantize_fp8_rows); activations bf16. Returns out [T, H] (and a dict
+    of routing tensors when ``return_routing``). Work is enqueued on
+    ``stream`` (default: torch's current stream)."""
     import torch
     lib = load_library()
     T, H = hidden.shape
@@ -146,10 +176,25 @@ def moe_forward(hidden, router_w, gate_up, down, k: int, *, routed_scale: float 
         o.dtype = MOE_F32
     else:
         raise TypeError(f"unsupported dtype {hidden.dtype}")
-    tensors = [hidden, router_w, gate_up, down] + [t for t in (shared_gate_up, shared_down) if t is not None]
-    for t in tensors:
-        if t.dtype != hidden.dtype or not t.is_contiguous() or not t.is_cuda:
-            raise ValueError("all tensors must be contiguous CUDA tensors of one dtype")
+    w8 = gate_up.dtype == torch.uint8
+    if w8:
+        if down.dtype != torch.uint8 or gate_up_scale is None or down_scale is None:
+            raise ValueError("FP8 weights need uint8 gate_up and down plus gate_up_scale and down_scale")
+        gate_up_scale = gate_up_scale.to(dtype=torch.float32).contiguous()
+        down_scale = down_scale.to(dtype=torch.float32).contiguous()
+        if gate_up_scale.shape != (E, 2 * I) or down_scale.shape != (E, H):
+            raise ValueError("gate_up_scale must be [E, 2I] and down_scale [E, H]")
+        o.weight_format = WEIGHTS_FP8_E4M3
+        o.gate_up_scale = gate_up_scale.data_ptr()
+        o.down_scale = down_scale.data_ptr()
+    acts = [hidden, router_w] + [t for t in (shared_gate_up, shared_down) if t is not None]
+    acts += [] if w8 else [gate_up, down]
+    for t in acts + ([gate_up, down] if w8 else []):
+        if not t.is_contiguous() or not t.is_cuda:
+            raise ValueError("all tensors must be contiguous CUDA tensors")
+    for t in acts:
+        if t.dtype != hidden.dtype:
+            raise ValueError("activations, router and native-format weights must share one dtype")
     if router_w.shape != (E, H) or gate_up.shape != (E, 2 * I, H) or down.shape != (E, H, I):
         raise ValueError("shape mismatch among hidden, router_w, gate_up, down")
     o.routed_scale = float(routed_scale)
@@ -197,7 +242,7 @@ def moe_forward(hidden, router_w, gate_up, down, k: int, *, routed_scale: float 
         stream = current
     if stream != current:
         # buffers allocated here belong to the current stream's pool
-        for t in (router_bias, workspace, out, *(routing.values() if routing else ())):
+        for t in (router_bias, workspace, out, gate_up_scale, down_scale, *(routing.values() if routing else ())):
             if t is not None:
                 t.record_stream(stream)
     o.stream = stream.cuda_stream

@@ -25,7 +25,7 @@ COMMON = [
     "-Wno-unused-result",
 ]
 # the router's fp32 summation order is part of its contract
-PER_FILE = {"router.hip": ["-ffp-contract=off"]}
+PER_FILE = {"router.hip": ["-ffp-contract=off"], "quant.hip": ["-ffp-contract=off"]}
 
 
 def sources():

@@ -18,6 +18,11 @@
 //     order, so the result does not depend on timing.
 //   * Experts with no tokens exit before reading anything, so only the
 //     weights of experts that received tokens are read.
+//   * FP8 weights (one byte each, OCP E4M3, one fp32 scale per weight row):
+//     the same 256-byte row segments now hold 256 weights; each 16-byte
+//     chunk is widened to two bf16 MFMA fragments in registers (exact: every
+//     E4M3 value is a bf16 value) and the row scale multiplies the
+//     accumulated sum in the epilogue, so a decode step reads half the bytes.
 #include "moe_internal.h"
 
 namespace moe {
@@ -34,15 +39,23 @@ constexpr int KB = 128;  // reduction elements per step: 256 bytes of each row
 #ifndef MOE_SKINNY_PD_DN
 #define MOE_SKINNY_PD_DN 1
 #endif
+#ifndef MOE_SKINNY_PD_W8
+#define MOE_SKINNY_PD_W8 1
+#endif
 #ifndef MOE_SKINNY_DOWN_BLOCKS
 #define MOE_SKINNY_DOWN_BLOCKS 2
 #endif
-constexpr int SW = MOE_SKINNY_WAVES;  // waves per workgroup, splitting K
+#ifndef MOE_SKINNY_WAVES_W8
+#define MOE_SKINNY_WAVES_W8 4
+#endif
+constexpr int SW_BF = MOE_SKINNY_WAVES;     // waves per workgroup, splitting K (bf16 weights)
+constexpr int SW_W8 = MOE_SKINNY_WAVES_W8;  // the same for E4M3 weights
 
 struct SkinnyParams {
     const __bf16 *A;
     const int32_t *a_rows;
-    const __bf16 *W;
+    const void *W;             // bf16 or E4M3 bytes
+    const float *w_scale;      // E4M3: [E, rows per expert] scales, else null
     int64_t w_expert_stride;
     int K;
     int N;
@@ -56,13 +69,36 @@ struct SkinnyParams {
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8_t, v); }
 
+// Two fp32 values that are exact bf16 values -> packed bf16 pair.
+__device__ __forceinline__ uint32_t pack_hi16(float lo, float hi)
+{
+    return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
+}
+
+// Eight E4M3 weights (two 32-bit words, byte 0 first) -> eight bf16.
+__device__ __forceinline__ u32x4 e4m3x8_to_bf16(uint32_t w0, uint32_t w1)
+{
+    const auto a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w0, false);
+    const auto b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w0, true);
+    const auto c = __builtin_amdgcn_cvt_pk_f32_fp8((int)w1, false);
+    const auto d = __builtin_amdgcn_cvt_pk_f32_fp8((int)w1, true);
+    return u32x4{pack_hi16(a[0], a[1]), pack_hi16(b[0], b[1]), pack_hi16(c[0], c[1]), pack_hi16(d[0], d[1])};
+}
+
 // 16-byte chunk c (0..15) of row r (0..31) in a wave's LDS tile of 256-byte rows
 __device__ __forceinline__ int tswz(int r, int c) { return r * 16 + (c ^ (r & 15)); }
 
-template <bool GATEUP>
-__global__ __launch_bounds__(SW * 64) void skinny_gemm_kernel(SkinnyParams p)
+#ifndef MOE_SKINNY_W8_OCC
+#define MOE_SKINNY_W8_OCC 1
+#endif
+template <bool GATEUP, bool W8>
+__global__ __launch_bounds__((W8 ? SW_W8 : SW_BF) * 64, W8 ? MOE_SKINNY_W8_OCC : 1) void skinny_gemm_kernel(SkinnyParams p)
 {
-    constexpr int PD = GATEUP ? MOE_SKINNY_PD_GU : MOE_SKINNY_PD_DN;  // steps of weights in flight
+    constexpr int SW = W8 ? SW_W8 : SW_BF;
+    constexpr int PD = W8 ? MOE_SKINNY_PD_W8 : GATEUP ? MOE_SKINNY_PD_GU : MOE_SKINNY_PD_DN;  // steps in flight
+    constexpr int KS = W8 ? 2 * KB : KB;  // reduction elements per step (256 bytes of each row)
+    constexpr int EPC = W8 ? 16 : 8;      // elements per 16-byte chunk
+    constexpr int XF = W8 ? 8 : 4;        // token fragments per step
     // 16-row MFMA blocks per workgroup: gate_up takes 16 gate + the matching 16
     // up rows; down takes MOE_SKINNY_DOWN_BLOCKS consecutive blocks of 16 rows
     constexpr int NW = GATEUP ? 2 : MOE_SKINNY_DOWN_BLOCKS;
@@ -82,13 +118,14 @@ __global__ __launch_bounds__(SW * 64) void skinny_gemm_kernel(SkinnyParams p)
     const int lgrp = lane >> 4;
     const int l16 = lane & 15;
 
-    const int nkb = (p.K + KB - 1) / KB;
+    const int nkb = (p.K + KS - 1) / KS;
     const int kb_lo = wave * nkb / SW;
     const int kb_hi = (wave + 1) * nkb / SW;
 
     // load instruction i covers tile rows 4i..4i+3; this lane: row 4i + lgrp, chunk l16
     // element offsets inside one expert fit in 32 bits (2*I*H < 2^31 is checked on the host)
-    const __bf16 *wbase = p.W + (int64_t)e * p.w_expert_stride + l16 * 8;
+    const uint8_t *wbase =
+        reinterpret_cast<const uint8_t *>(p.W) + ((int64_t)e * p.w_expert_stride + l16 * EPC) * (W8 ? 1 : 2);
     uint32_t woff[NL];
 #pragma unroll
     for (int i = 0; i < NL; i++) {
@@ -102,7 +139,7 @@ __global__ __launch_bounds__(SW * 64) void skinny_gemm_kernel(SkinnyParams p)
             const int n = n0 + tr;
             mrow = n < p.N ? n : 0;
         }
-        woff[i] = (uint32_t)mrow * (uint32_t)p.K;
+        woff[i] = (uint32_t)mrow * (uint32_t)p.K * (W8 ? 1u : 2u);  // bytes
     }
     u32x4 *tile = s_w[wave];
     const u32x4 zero = {0u, 0u, 0u, 0u};
@@ -112,40 +149,52 @@ __global__ __launch_bounds__(SW * 64) void skinny_gemm_kernel(SkinnyParams p)
         const bool xv = q < M;
         const int qc = xv ? q : M - 1;
         const int64_t src = p.a_rows ? (int64_t)p.a_rows[row0 + qc] : (int64_t)(row0 + qc);
-        const __bf16 *xp = p.A + src * p.K + lgrp * 8;
+        const __bf16 *xp = p.A + src * p.K + lgrp * EPC;
 
         f32x4_t acc[NW];
 #pragma unroll
         for (int w = 0; w < NW; w++) acc[w] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
         u32x4 st[PD][NL];
-        u32x4 xs[PD][4];
-        // weights of step kb and the token fragments it needs (MFMA j takes chunk 4j + lgrp)
+        u32x4 xs[PD][XF];
+        // weights of step kb and the token fragments it needs: MFMA j takes
+        // chunk 4j + lgrp (bf16: 8 elements; E4M3: 16 elements, as two MFMAs
+        // over its halves, fragment 2j + half)
         auto gload = [&](int kb, int b) {
-            const int k = kb * KB;
-            const bool ok = k + l16 * 8 < p.K;
+            const int k = kb * KS;
+            const bool ok = k + l16 * EPC < p.K;
+            const uint32_t kbytes = (uint32_t)k * (W8 ? 1u : 2u);
 #pragma unroll
-            for (int i = 0; i < NL; i++) st[b][i] = ok ? load_nt16(wbase + woff[i] + k) : zero;
+            for (int i = 0; i < NL; i++) st[b][i] = ok ? load_nt16(wbase + woff[i] + kbytes) : zero;
 #pragma unroll
-            for (int j = 0; j < 4; j++) {
-                const bool okx = xv && (k + (4 * j + lgrp) * 8 < p.K);
-                xs[b][j] = okx ? *reinterpret_cast<const u32x4 *>(xp + k + j * 32) : zero;
+            for (int f = 0; f < XF; f++) {
+                const int j = W8 ? f / 2 : f;
+                const int off = W8 ? j * 64 + (f % 2) * 8 : j * 32;
+                const bool okx = xv && (k + (4 * j + lgrp) * EPC < p.K);
+                xs[b][f] = okx ? *reinterpret_cast<const u32x4 *>(xp + k + off) : zero;
             }
         };
         // one reduction step from staging buffer b (a compile-time index after unrolling)
         auto step = [&](int kb, int b) {
 #pragma unroll
             for (int i = 0; i < NL; i++) tile[tswz(4 * i + lgrp, l16)] = st[b][i];
-            u32x4 xb[4];
+            u32x4 xb[XF];
 #pragma unroll
-            for (int j = 0; j < 4; j++) xb[j] = xs[b][j];
+            for (int f = 0; f < XF; f++) xb[f] = xs[b][f];
             if (kb + PD < kb_hi) gload(kb + PD, b);
 #pragma unroll
             for (int j = 0; j < 4; j++) {
 #pragma unroll
                 for (int w = 0; w < NW; w++) {
                     const u32x4 a = tile[tswz(16 * w + l16, 4 * j + lgrp)];
-                    acc[w] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(xb[j]), acc[w], 0, 0, 0);
+                    if (W8) {
+                        acc[w] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(e4m3x8_to_bf16(a.x, a.y)),
+                                                                         as_bf16x8(xb[2 * j]), acc[w], 0, 0, 0);
+                        acc[w] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(e4m3x8_to_bf16(a.z, a.w)),
+                                                                         as_bf16x8(xb[2 * j + 1]), acc[w], 0, 0, 0);
+                    } else {
+                        acc[w] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(xb[j]), acc[w], 0, 0, 0);
+                    }
                 }
             }
         };
@@ -177,6 +226,17 @@ __global__ __launch_bounds__(SW * 64) void skinny_gemm_kernel(SkinnyParams p)
                 }
             }
             // lane: token column l16, output rows 4*lgrp + 0..3 of each 16-row block
+            if (W8) {  // weight-row scales (E4M3 storage)
+                const float *sc = p.w_scale + (int64_t)e * (GATEUP ? 2 * p.N : p.N);
+#pragma unroll
+                for (int w = 0; w < NW; w++)
+#pragma unroll
+                    for (int i = 0; i < 4; i++) {
+                        const int r = GATEUP ? n0 + 4 * lgrp + i + w * p.N : n0 + 16 * w + 4 * lgrp + i;
+                        const bool in = GATEUP ? n0 + 4 * lgrp + i < p.N : r < p.N;
+                        sm[w][i] *= in ? sc[r] : 0.0f;
+                    }
+            }
             if (xv) {
                 const int pos = row0 + q;
                 if (GATEUP) {
@@ -213,7 +273,8 @@ SkinnyParams make_params(const GemmProblem &g)
     SkinnyParams s;
     s.A = (const __bf16 *)g.A;
     s.a_rows = g.a_rows;
-    s.W = (const __bf16 *)g.W;
+    s.W = g.W;
+    s.w_scale = g.w_scale;
     s.w_expert_stride = g.w_expert_stride;
     s.K = (int)g.K;
     s.N = (int)g.N;
@@ -232,7 +293,8 @@ hipError_t launch_gate_up_skinny(const GemmProblem &g, hipStream_t st)
 {
     SkinnyParams s = make_params(g);
     dim3 grid((unsigned)((g.N + 15) / 16), g.dense_rows > 0 ? 1u : (unsigned)g.E);
-    hipLaunchKernelGGL(skinny_gemm_kernel<true>, grid, dim3(SW * 64), 0, st, s);
+    if (g.w_scale) hipLaunchKernelGGL((skinny_gemm_kernel<true, true>), grid, dim3(SW_W8 * 64), 0, st, s);
+    else hipLaunchKernelGGL((skinny_gemm_kernel<true, false>), grid, dim3(SW_BF * 64), 0, st, s);
     return hipGetLastError();
 }
 
@@ -241,7 +303,8 @@ hipError_t launch_down_skinny(const GemmProblem &g, hipStream_t st)
     SkinnyParams s = make_params(g);
     constexpr int rows = 16 * MOE_SKINNY_DOWN_BLOCKS;
     dim3 grid((unsigned)((g.N + rows - 1) / rows), g.dense_rows > 0 ? 1u : (unsigned)g.E);
-    hipLaunchKernelGGL(skinny_gemm_kernel<false>, grid, dim3(SW * 64), 0, st, s);
+    if (g.w_scale) hipLaunchKernelGGL((skinny_gemm_kernel<false, true>), grid, dim3(SW_W8 * 64), 0, st, s);
+    else hipLaunchKernelGGL((skinny_gemm_kernel<false, false>), grid, dim3(SW_BF * 64), 0, st, s);
     return hipGetLastError();
 }
 

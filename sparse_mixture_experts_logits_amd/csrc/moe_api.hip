@@ -76,6 +76,16 @@ int check_shape(int64_t T, int64_t H, int64_t I, int64_t E, int32_t k, const moe
             return fail(MOE_ERR_INVALID_ARG, "unknown flag bits 0x%x", opts->flags);
         if ((opts->flags & MOE_FLAG_FORCE_TILED) && (opts->flags & MOE_FLAG_FORCE_SKINNY))
             return fail(MOE_ERR_INVALID_ARG, "MOE_FLAG_FORCE_TILED and MOE_FLAG_FORCE_SKINNY both set");
+        if (opts->weight_format != MOE_WEIGHTS_NATIVE && opts->weight_format != MOE_WEIGHTS_FP8_E4M3)
+            return fail(MOE_ERR_INVALID_ARG, "unknown weight_format %d", opts->weight_format);
+        if (opts->weight_format == MOE_WEIGHTS_FP8_E4M3) {
+            if (dtype != MOE_BF16)
+                return fail(MOE_ERR_UNSUPPORTED, "FP8 expert weights need bf16 activations (dtype MOE_BF16)");
+            if (H % 16 || I % 16)
+                return fail(MOE_ERR_UNSUPPORTED, "FP8 expert weights need H and I multiples of 16");
+            if (opts->flags & MOE_FLAG_FORCE_TILED)
+                return fail(MOE_ERR_UNSUPPORTED, "FP8 expert weights run on the weight-streaming kernels only");
+        }
     }
     return MOE_OK;
 }
@@ -183,15 +193,23 @@ int moe_forward(const void *hidden, const void *router_w, const void *gate_up, c
     for (const void *p : small)
         if (p && !aligned(p, 4)) return fail(MOE_ERR_ALIGNMENT, "output pointer %p is not 4-byte aligned", p);
 
+    const bool w8 = opts->weight_format == MOE_WEIGHTS_FP8_E4M3;
+    if (w8 && (!opts->gate_up_scale || !opts->down_scale))
+        return fail(MOE_ERR_INVALID_ARG, "FP8 expert weights need gate_up_scale and down_scale");
+    if (w8 && (!aligned(opts->gate_up_scale, 4) || !aligned(opts->down_scale, 4)))
+        return fail(MOE_ERR_ALIGNMENT, "gate_up_scale / down_scale not 4-byte aligned");
     const uint64_t es = opts->dtype == MOE_BF16 ? 2 : 4;
+    const uint64_t wes = w8 ? 1 : es;  // bytes per routed expert weight
     const uint64_t out_bytes = (uint64_t)T * H * es;
     struct Range {
         const void *p;
         uint64_t n;
     } ins[] = {{hidden, (uint64_t)T * H * es},
                {router_w, (uint64_t)E * H * es},
-               {gate_up, (uint64_t)E * 2 * I * H * es},
-               {down, (uint64_t)E * H * I * es},
+               {gate_up, (uint64_t)E * 2 * I * H * wes},
+               {down, (uint64_t)E * H * I * wes},
+               {opts->gate_up_scale, w8 ? (uint64_t)E * 2 * I * 4 : 0},
+               {opts->down_scale, w8 ? (uint64_t)E * H * 4 : 0},
                {opts->shared_gate_up, shared ? (uint64_t)2 * opts->shared_I * H * es : 0},
                {opts->shared_down, shared ? (uint64_t)H * opts->shared_I * es : 0},
                {opts->router_bias, (uint64_t)E * 4},
@@ -215,6 +233,7 @@ int moe_forward(const void *hidden, const void *router_w, const void *gate_up, c
     if (opts->flags & MOE_FLAG_FORCE_SKINNY) skinny = true;
     else if (opts->flags & MOE_FLAG_FORCE_TILED) skinny = false;
     else skinny = T * k <= 32 * E;  // about 32 rows per expert or fewer: stream the weights
+    if (w8) skinny = true;          // FP8 weights: weight-streaming kernels only
 
     int step = 0;
     auto check = [&](hipError_t err, const char *what) -> int {
@@ -248,6 +267,7 @@ int moe_forward(const void *hidden, const void *router_w, const void *gate_up, c
     gu.A = hidden;
     gu.a_rows = ws.row_token;
     gu.W = gate_up;
+    gu.w_scale = w8 ? opts->gate_up_scale : nullptr;
     gu.w_expert_stride = 2 * I * H;
     gu.K = H;
     gu.N = I;
@@ -267,6 +287,7 @@ int moe_forward(const void *hidden, const void *router_w, const void *gate_up, c
     dn.A = ws.h;
     dn.a_rows = nullptr;
     dn.W = down;
+    dn.w_scale = w8 ? opts->down_scale : nullptr;
     dn.w_expert_stride = H * I;
     dn.K = I;
     dn.N = H;
@@ -288,6 +309,7 @@ int moe_forward(const void *hidden, const void *router_w, const void *gate_up, c
         moe::GemmProblem sg = gu;
         sg.a_rows = nullptr;
         sg.W = opts->shared_gate_up;
+        sg.w_scale = nullptr;  // the shared expert keeps opts->dtype
         sg.w_expert_stride = 0;
         sg.N = opts->shared_I;
         sg.C = ws.sh_h;
@@ -317,6 +339,26 @@ int moe_forward(const void *hidden, const void *router_w, const void *gate_up, c
     if ((rc = check(moe::launch_combine(s, ws.slot, shared ? ws.sh_y : nullptr, out, st), "combine")) ||
         (rc = mark(1 + MOE_STAGE_COMBINE)))
         return rc;
+    return MOE_OK;
+}
+
+int moe_quantize_fp8_rows(const void *w, int64_t rows, int64_t cols, void *q, float *scale, void *stream)
+{
+    g_err[0] = 0;
+    if (rows < 0) return fail(MOE_ERR_INVALID_ARG, "rows = %lld is negative", (long long)rows);
+    if (cols < 16 || cols % 16) return fail(MOE_ERR_INVALID_ARG, "cols = %lld must be a positive multiple of 16", (long long)cols);
+    if (rows >= ((int64_t)1 << 31) || cols >= ((int64_t)1 << 31))
+        return fail(MOE_ERR_UNSUPPORTED, "rows or cols at or above 2^31");
+    if (rows == 0) return MOE_OK;
+    if (!w || !q || !scale) return fail(MOE_ERR_INVALID_ARG, "w, q and scale must be non-NULL");
+    if (!aligned(w, 16) || !aligned(q, 16) || !aligned(scale, 4))
+        return fail(MOE_ERR_ALIGNMENT, "w and q must be 16-byte aligned, scale 4-byte aligned");
+    const uint64_t n = (uint64_t)rows * cols;
+    if (overlaps(q, n, w, 2 * n) || overlaps(scale, (uint64_t)rows * 4, w, 2 * n) || overlaps(scale, (uint64_t)rows * 4, q, n))
+        return fail(MOE_ERR_INVALID_ARG, "q, scale and w must not overlap");
+    hipError_t err = moe::launch_quantize_fp8_rows(w, rows, cols, q, scale, (hipStream_t)stream);
+    if (err == hipSuccess && debug_sync()) err = hipStreamSynchronize((hipStream_t)stream);
+    if (err != hipSuccess) return fail(MOE_ERR_HIP, "quantize_fp8_rows failed: %s", hipGetErrorString(err));
     return MOE_OK;
 }
 

@@ -108,7 +108,8 @@ hipError_t launch_route_permute(const Shape &s, int32_t *perm_out, int32_t *inv_
 struct GemmProblem {
     const void *A;           // gate_up: hidden [T, K]; down: h [rows, K]
     const int32_t *a_rows;   // gate_up: sorted position -> token (null = identity)
-    const void *W;           // packed weights
+    const void *W;           // packed weights (bf16 / fp32, or E4M3 bytes when w_scale is set)
+    const float *w_scale;    // E4M3 storage: per-row scales [E, rows per expert]; else null
     int64_t w_expert_stride; // elements between experts (0 for dense)
     int64_t K;               // reduction length
     int64_t N;               // gate_up: I (h columns); down: H
@@ -133,6 +134,9 @@ hipError_t launch_gate_up_f32(const GemmProblem &p, hipStream_t st);
 hipError_t launch_down_f32(const GemmProblem &p, hipStream_t st);
 
 int tiled_block_m();
+
+hipError_t launch_quantize_fp8_rows(const void *w, int64_t rows, int64_t cols, void *q, float *scale,
+                                    hipStream_t st);
 
 hipError_t launch_combine(const Shape &s, const float *slot, const float *sh_y, void *out,
                           hipStream_t st);

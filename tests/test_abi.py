@@ -154,3 +154,50 @@ def test_missing_library_raises(tmp_path, monkeypatch):
     monkeypatch.setattr(moe, "LIB_PATH", str(tmp_path / "absent.so"))
     with pytest.raises(FileNotFoundError):
         moe.load_library()
+
+
+def fp8_opts():
+    o = good_opts(nbytes=100)  # too small: a valid call stops at the workspace check, before any HIP call
+    o.weight_format = moe.WEIGHTS_FP8_E4M3
+    o.gate_up_scale = (1 << 40) + (5 << 30)
+    o.down_scale = (1 << 40) + (6 << 30)
+    return o
+
+
+def test_fp8_weight_options_are_checked():
+    rc, msg = call(opts=fp8_opts())  # valid apart from the fake addresses: reaches the workspace check
+    assert rc == -3, msg
+    o = fp8_opts()
+    o.gate_up_scale = None
+    rc, msg = call(opts=o)
+    assert rc == -1 and "scale" in msg
+    o = fp8_opts()
+    o.dtype = 1
+    rc, msg = call(opts=o)
+    assert rc == -2 and "bf16" in msg
+    o = fp8_opts()
+    o.flags = moe.FLAG_FORCE_TILED
+    assert call(opts=o)[0] == -2
+    rc, msg = call(H=72, opts=fp8_opts())  # H a multiple of 8 but not of 16
+    assert rc == -2 and "16" in msg
+    o = fp8_opts()
+    o.weight_format = 9
+    assert call(opts=o)[0] == -1
+    o = fp8_opts()
+    o.down_scale = (1 << 40) + (6 << 30) + 2
+    assert call(opts=o)[0] == -4
+    rc, msg = call(opts=fp8_opts(), out=(1 << 40) + (6 << 30))  # out on top of down_scale
+    assert rc == -1 and "overlaps" in msg
+
+
+def test_quantize_entry_point_checks_arguments():
+    lib = moe.load_library()
+    vp = ctypes.c_void_p
+    base = 1 << 40
+    w, q, s = vp(base), vp(base + (1 << 30)), vp(base + (2 << 30))
+    assert lib.moe_quantize_fp8_rows(w, 0, 64, q, s, None) == 0  # no rows: nothing to do
+    assert lib.moe_quantize_fp8_rows(w, 4, 40, q, s, None) == -1  # cols not a multiple of 16
+    assert lib.moe_quantize_fp8_rows(w, -1, 64, q, s, None) == -1
+    assert lib.moe_quantize_fp8_rows(None, 4, 64, q, s, None) == -1
+    assert lib.moe_quantize_fp8_rows(vp(base + 8), 4, 64, q, s, None) == -4
+    assert lib.moe_quantize_fp8_rows(w, 4, 64, vp(base + 64), s, None) == -1  # q overlaps w
