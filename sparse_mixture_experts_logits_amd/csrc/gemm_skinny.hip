@@ -69,30 +69,30 @@ struct SkinnyParams {
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8_t, v); }
 
-// Two fp32 values that are exact bf16 values -> packed bf16 pair.
-__device__ __forceinline__ uint32_t pack_hi16(float lo, float hi)
-{
-    return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
-}
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
 
-// Eight E4M3 weights (two 32-bit words, byte 0 first) -> eight bf16.
+// Eight E4M3 weights (two 32-bit words, byte 0 first) -> eight bf16, two per
+// instruction (gfx950's scaled FP8 conversion with scale 1: exact, since
+// every E4M3 value is a bf16 value).
 __device__ __forceinline__ u32x4 e4m3x8_to_bf16(uint32_t w0, uint32_t w1)
 {
-    const auto a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w0, false);
-    const auto b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w0, true);
-    const auto c = __builtin_amdgcn_cvt_pk_f32_fp8((int)w1, false);
-    const auto d = __builtin_amdgcn_cvt_pk_f32_fp8((int)w1, true);
-    return u32x4{pack_hi16(a[0], a[1]), pack_hi16(b[0], b[1]), pack_hi16(c[0], c[1]), pack_hi16(d[0], d[1])};
+    return u32x4{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false)),
+                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true)),
+                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false)),
+                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true))};
 }
 
 // 16-byte chunk c (0..15) of row r (0..31) in a wave's LDS tile of 256-byte rows
 __device__ __forceinline__ int tswz(int r, int c) { return r * 16 + (c ^ (r & 15)); }
 
 #ifndef MOE_SKINNY_W8_OCC
-#define MOE_SKINNY_W8_OCC 1
+#define MOE_SKINNY_W8_OCC 3
+#endif
+#ifndef MOE_SKINNY_BF_OCC
+#define MOE_SKINNY_BF_OCC 1
 #endif
 template <bool GATEUP, bool W8>
-__global__ __launch_bounds__((W8 ? SW_W8 : SW_BF) * 64, W8 ? MOE_SKINNY_W8_OCC : 1) void skinny_gemm_kernel(SkinnyParams p)
+__global__ __launch_bounds__((W8 ? SW_W8 : SW_BF) * 64, W8 ? MOE_SKINNY_W8_OCC : MOE_SKINNY_BF_OCC) void skinny_gemm_kernel(SkinnyParams p)
 {
     constexpr int SW = W8 ? SW_W8 : SW_BF;
     constexpr int PD = W8 ? MOE_SKINNY_PD_W8 : GATEUP ? MOE_SKINNY_PD_GU : MOE_SKINNY_PD_DN;  // steps in flight
@@ -160,12 +160,15 @@ __global__ __launch_bounds__((W8 ? SW_W8 : SW_BF) * 64, W8 ? MOE_SKINNY_W8_OCC :
         // weights of step kb and the token fragments it needs: MFMA j takes
         // chunk 4j + lgrp (bf16: 8 elements; E4M3: 16 elements, as two MFMAs
         // over its halves, fragment 2j + half)
-        auto gload = [&](int kb, int b) {
+        auto gload_w = [&](int kb, int b) {
             const int k = kb * KS;
             const bool ok = k + l16 * EPC < p.K;
             const uint32_t kbytes = (uint32_t)k * (W8 ? 1u : 2u);
 #pragma unroll
             for (int i = 0; i < NL; i++) st[b][i] = ok ? load_nt16(wbase + woff[i] + kbytes) : zero;
+        };
+        auto gload_x = [&](int kb, int b) {
+            const int k = kb * KS;
 #pragma unroll
             for (int f = 0; f < XF; f++) {
                 const int j = W8 ? f / 2 : f;
@@ -174,14 +177,17 @@ __global__ __launch_bounds__((W8 ? SW_W8 : SW_BF) * 64, W8 ? MOE_SKINNY_W8_OCC :
                 xs[b][f] = okx ? *reinterpret_cast<const u32x4 *>(xp + k + off) : zero;
             }
         };
-        // one reduction step from staging buffer b (a compile-time index after unrolling)
+        // One reduction step from staging buffer b (a compile-time index after
+        // unrolling). The next weights (from HBM, the long wait) are requested
+        // as soon as this step's are in LDS; the next token fragments (L2
+        // hits) only after this step's MFMAs have consumed the current ones, so
+        // they need no second register copy and more waves fit on a SIMD.
         auto step = [&](int kb, int b) {
 #pragma unroll
             for (int i = 0; i < NL; i++) tile[tswz(4 * i + lgrp, l16)] = st[b][i];
-            u32x4 xb[XF];
-#pragma unroll
-            for (int f = 0; f < XF; f++) xb[f] = xs[b][f];
-            if (kb + PD < kb_hi) gload(kb + PD, b);
+            const bool more = kb + PD < kb_hi;
+            if (more) gload_w(kb + PD, b);
+            const u32x4(&xb)[XF] = xs[b];
 #pragma unroll
             for (int j = 0; j < 4; j++) {
 #pragma unroll
@@ -197,10 +203,14 @@ __global__ __launch_bounds__((W8 ? SW_W8 : SW_BF) * 64, W8 ? MOE_SKINNY_W8_OCC :
                     }
                 }
             }
+            if (more) gload_x(kb + PD, b);
         };
 #pragma unroll
         for (int b = 0; b < PD; b++)
-            if (kb_lo + b < kb_hi) gload(kb_lo + b, b);
+            if (kb_lo + b < kb_hi) {
+                gload_w(kb_lo + b, b);
+                gload_x(kb_lo + b, b);
+            }
         int kb = kb_lo;
         for (; kb + PD <= kb_hi; kb += PD) {
 #pragma unroll
