@@ -113,6 +113,22 @@ typedef struct moe_opts {
     int32_t weight_format;
     const float *gate_up_scale;
     const float *down_scale;
+    /* Router statistics for the load-balancing auxiliary loss ("深入解析
+     * Transformers 中的 PhiMoE" page, section 6: the Switch Transformer
+     * load-balancing loss over the router logits, times router_aux_loss_coef
+     * = 0.001, padding tokens excluded). Computed when any output below is
+     * non-NULL, over the tokens with stats_mask[t] != 0 (all tokens when
+     * stats_mask is NULL); n = number of such tokens:
+     *   router_prob_mean[e] = (1/n) sum_t softmax(logits[t, :])[e]
+     *                         (softmax over all E experts, bias included),
+     *   expert_load[e]      = (1/n) #{(t, j): topk_ids[t, j] = e},
+     *   aux_loss[0]         = E * sum_e expert_load[e] * router_prob_mean[e]
+     *                         (the caller multiplies by its coefficient);
+     * all zero when n = 0. Routing itself ignores stats_mask. */
+    const int32_t *stats_mask; /* [T] or NULL                                   */
+    float *router_prob_mean;   /* [E] or NULL                                   */
+    float *expert_load;        /* [E] or NULL                                   */
+    float *aux_loss;           /* [1] or NULL                                   */
 } moe_opts;
 
 /* Stages of moe_forward, in launch order. */

@@ -48,13 +48,14 @@ def _load():
         lib.oracle_moe_tokens.argtypes = [vp, vp, vp, i32, i64, i64, vp, vp, i32, i32,
                                           vp, vp, vp, vp, i64, vp]
         lib.oracle_num_threads.argtypes = []
+        lib.oracle_router_stats.argtypes = [vp, vp, vp, i64, i64, i32, vp, vp, vp]
         lib.oracle_e4m3_values.argtypes = [vp]
         lib.oracle_quantize_e4m3_rows.argtypes = [vp, i64, i64, vp, vp]
         lib.oracle_moe_tokens_e4m3.argtypes = [vp, vp, vp, vp, vp, i64, i64, vp, vp, i32, i32,
                                                vp, vp, vp, vp, i64, vp]
         for f in (lib.oracle_router_logits, lib.oracle_select_topk, lib.oracle_route,
                   lib.oracle_moe_tokens, lib.oracle_num_threads, lib.oracle_e4m3_values,
-                  lib.oracle_quantize_e4m3_rows, lib.oracle_moe_tokens_e4m3):
+                  lib.oracle_quantize_e4m3_rows, lib.oracle_moe_tokens_e4m3, lib.oracle_router_stats):
             f.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -161,6 +162,24 @@ def moe_tokens(hidden, gate_up, down, ids, weights, tokens=None, shared=()):
                                      ctypes.cast(sdn, ctypes.c_void_p), _p(sI), _p(tokens),
                                      len(tokens), _p(out)), "moe_tokens")
     return out
+
+
+def router_stats(logits: np.ndarray, ids: np.ndarray, mask: np.ndarray | None = None):
+    """Load-balancing statistics (fp64): per-expert mean router probability,
+    per-expert load (assignments per counted token) and the auxiliary loss
+    E * sum(load * prob_mean), over the tokens with mask != 0 (all if None)."""
+    logits = np.ascontiguousarray(logits, dtype=np.float32)
+    ids = np.ascontiguousarray(ids, dtype=np.int32)
+    T, E = logits.shape
+    k = ids.shape[1]
+    if mask is not None:
+        mask = np.ascontiguousarray(mask, dtype=np.int32)
+    pm = np.empty(E, dtype=np.float64)
+    ld = np.empty(E, dtype=np.float64)
+    aux = np.empty(1, dtype=np.float64)
+    _check(_load().oracle_router_stats(_p(logits), _p(ids), _p(mask), T, E, int(k), _p(pm), _p(ld), _p(aux)),
+           "router_stats")
+    return dict(prob_mean=pm, load=ld, aux=float(aux[0]))
 
 
 def e4m3_values() -> np.ndarray:

@@ -270,6 +270,52 @@ int oracle_moe_tokens(const void *X, const void *gate_up, const void *down, int 
 }
 
 /*
+ * Router statistics for the load-balancing auxiliary loss (PhiMoE page,
+ * section 6: the Switch Transformer loss over the router logits, scaled by
+ * router_aux_loss_coef = 0.001, padding tokens excluded). The pages cite the
+ * Switch paper's equations without printing them; its form is used: with n
+ * counted tokens (mask[t] != 0, or all tokens when mask is NULL),
+ *   P[e] = (1/n) sum_t softmax(logits[t, :])[e]   (all E experts),
+ *   f[e] = (1/n) #{(t, j) : ids[t, j] = e}        (the top-k assignments),
+ *   aux  = E * sum_e f[e] * P[e];
+ * everything zero when n = 0. Evaluated in fp64.
+ */
+int oracle_router_stats(const float *logits, const int32_t *ids, const int32_t *mask, int64_t T, int64_t E,
+                        int k, double *prob_mean, double *load, double *aux)
+{
+    if (!logits || !ids || !prob_mean || !load || !aux || T < 0 || E < 1 || k < 1)
+        return OR_BAD;
+    for (int64_t e = 0; e < E; e++)
+        prob_mean[e] = load[e] = 0.0;
+    int64_t n = 0;
+    for (int64_t t = 0; t < T; t++) {
+        if (mask && mask[t] == 0)
+            continue;
+        n++;
+        const float *l = logits + t * E;
+        double m = l[0];
+        for (int64_t e = 1; e < E; e++)
+            if (l[e] > m)
+                m = l[e];
+        double z = 0.0;
+        for (int64_t e = 0; e < E; e++)
+            z += exp((double)l[e] - m);
+        for (int64_t e = 0; e < E; e++)
+            prob_mean[e] += exp((double)l[e] - m) / z;
+        for (int j = 0; j < k; j++)
+            load[ids[t * k + j]] += 1.0;
+    }
+    double a = 0.0;
+    for (int64_t e = 0; e < E; e++) {
+        prob_mean[e] = n ? prob_mean[e] / (double)n : 0.0;
+        load[e] = n ? load[e] / (double)n : 0.0;
+        a += load[e] * prob_mean[e];
+    }
+    *aux = (double)E * a;
+    return OR_OK;
+}
+
+/*
  * FP8 expert weights (the low-precision decode storage: the MoEs in
  * Transformers page, section on why MoEs are fast, prices decode at memory
  * bandwidth over the bytes of the active weights and notes that a native

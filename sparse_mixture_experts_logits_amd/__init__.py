@@ -59,6 +59,10 @@ class MoeOpts(ctypes.Structure):
         ("weight_format", ctypes.c_int32),
         ("gate_up_scale", ctypes.c_void_p),
         ("down_scale", ctypes.c_void_p),
+        ("stats_mask", ctypes.c_void_p),
+        ("router_prob_mean", ctypes.c_void_p),
+        ("expert_load", ctypes.c_void_p),
+        ("aux_loss", ctypes.c_void_p),
     ]
 
 
@@ -154,16 +158,20 @@ def quantize_fp8_rows(w, stream=None):
 
 def moe_forward(hidden, router_w, gate_up, down, k: int, *, routed_scale: float = 1.0, router_bias=None,
                 shared_gate_up=None, shared_down=None, flags: int = 0, return_routing: bool = False,
-                out=None, workspace=None, stream=None, stage_events=None, gate_up_scale=None, down_scale=None):
+                out=None, workspace=None, stream=None, stage_events=None, gate_up_scale=None, down_scale=None,
+                router_stats: bool = False, stats_mask=None):
     """Run the MoE layer on torch tensors already on the GPU.
 
     hidden [T, H], router_w [E, H], gate_up [E, 2I, H], down [E, H, I] (all
     bf16 or all fp32, contiguous); router_bias [E] fp32; shared_gate_up
     [2Is, H], shared_down [H, Is]. FP8 expert weights: gate_up and down as
     uint8 E4M3 codes with gate_up_scale [E, 2I] and down_scale [E, H] (fp32,
-    from quantize_fp8_rows); activations bf16. Returns out [T, H] (and a dict
-    of routing tensors when ``return_routing``). Work is enqueued on
-    ``stream`` (default: torch's current stream)."""
+    from quantize_fp8_rows); activations bf16. ``router_stats`` adds the
+    load-balancing statistics (prob_mean [E], load [E], aux_loss [1]) to the
+    routing dict, over the tokens with ``stats_mask`` != 0 (int32 [T]; all
+    tokens if None). Returns out [T, H] (and a dict of routing tensors when
+    ``return_routing`` or ``router_stats``). Work is enqueued on ``stream``
+    (default: torch's current stream)."""
     import torch
     lib = load_library()
     T, H = hidden.shape
@@ -213,6 +221,7 @@ def moe_forward(hidden, router_w, gate_up, down, k: int, *, routed_scale: float 
     if out is None:
         out = torch.empty((T, H), dtype=hidden.dtype, device=dev)
     routing = None
+    return_routing = return_routing or router_stats
     if return_routing:
         routing = dict(
             logits=torch.empty((T, E), dtype=torch.float32, device=dev),
@@ -230,6 +239,18 @@ def moe_forward(hidden, router_w, gate_up, down, k: int, *, routed_scale: float 
         o.expert_offsets = routing["offsets"].data_ptr()
         o.perm = routing["perm"].data_ptr()
         o.inv_perm = routing["inv"].data_ptr()
+    if router_stats:
+        routing["prob_mean"] = torch.empty((E,), dtype=torch.float32, device=dev)
+        routing["load"] = torch.empty((E,), dtype=torch.float32, device=dev)
+        routing["aux_loss"] = torch.empty((1,), dtype=torch.float32, device=dev)
+        o.router_prob_mean = routing["prob_mean"].data_ptr()
+        o.expert_load = routing["load"].data_ptr()
+        o.aux_loss = routing["aux_loss"].data_ptr()
+        if stats_mask is not None:
+            stats_mask = stats_mask.to(device=dev, dtype=torch.int32).contiguous()
+            if stats_mask.shape != (T,):
+                raise ValueError("stats_mask must be [T]")
+            o.stats_mask = stats_mask.data_ptr()
     need = lib.moe_workspace_bytes(T, H, I, E, k, ctypes.byref(o))
     if need < 0:
         raise MoeError(int(need), last_error())
@@ -242,7 +263,8 @@ def moe_forward(hidden, router_w, gate_up, down, k: int, *, routed_scale: float 
         stream = current
     if stream != current:
         # buffers allocated here belong to the current stream's pool
-        for t in (router_bias, workspace, out, gate_up_scale, down_scale, *(routing.values() if routing else ())):
+        for t in (router_bias, workspace, out, gate_up_scale, down_scale, stats_mask,
+                  *(routing.values() if routing else ())):
             if t is not None:
                 t.record_stream(stream)
     o.stream = stream.cuda_stream

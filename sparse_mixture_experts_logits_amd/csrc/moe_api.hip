@@ -129,6 +129,9 @@ int64_t workspace_layout(const Shape &s, void *base, Workspace *ws)
     w.wts = (float *)take(TK * 4);
     w.blk_counts = (int32_t *)take((int64_t)s.nblk * s.E * 4);
     w.blk_base = (int32_t *)take((int64_t)s.nblk * s.E * 4);
+    w.blk_prob = (float *)take((int64_t)s.nblk * s.E * 4);
+    w.blk_mcnt = (int32_t *)take((int64_t)s.nblk * s.E * 4);
+    w.blk_ntok = (int32_t *)take((int64_t)s.nblk * 4);
     w.counts = (int32_t *)take(s.E * 4);
     w.offsets = (int32_t *)take((s.E + 1) * 4);
     w.tile_start = (int32_t *)take((s.E + 1) * 4);
@@ -189,7 +192,8 @@ int moe_forward(const void *hidden, const void *router_w, const void *gate_up, c
     for (const void *p : tens)
         if (p && !aligned(p, 16)) return fail(MOE_ERR_ALIGNMENT, "tensor pointer %p is not 16-byte aligned", p);
     const void *small[] = {opts->router_bias, opts->router_logits, opts->topk_ids, opts->topk_weights,
-                           opts->expert_counts, opts->expert_offsets, opts->perm, opts->inv_perm};
+                           opts->expert_counts, opts->expert_offsets, opts->perm, opts->inv_perm,
+                           opts->stats_mask, opts->router_prob_mean, opts->expert_load, opts->aux_loss};
     for (const void *p : small)
         if (p && !aligned(p, 4)) return fail(MOE_ERR_ALIGNMENT, "output pointer %p is not 4-byte aligned", p);
 
@@ -213,6 +217,7 @@ int moe_forward(const void *hidden, const void *router_w, const void *gate_up, c
                {opts->shared_gate_up, shared ? (uint64_t)2 * opts->shared_I * H * es : 0},
                {opts->shared_down, shared ? (uint64_t)H * opts->shared_I * es : 0},
                {opts->router_bias, (uint64_t)E * 4},
+               {opts->stats_mask, (uint64_t)T * 4},
                {opts->workspace, opts->workspace_bytes}};
     for (const Range &r : ins)
         if (overlaps(out, out_bytes, r.p, r.n)) return fail(MOE_ERR_INVALID_ARG, "out overlaps an input or the workspace");
@@ -252,11 +257,16 @@ int moe_forward(const void *hidden, const void *router_w, const void *gate_up, c
     };
     if ((rc = mark(0))) return rc;
 
+    moe::RouterStats rs;
+    rs.mask = opts->stats_mask;
+    rs.prob_mean = opts->router_prob_mean;
+    rs.load = opts->expert_load;
+    rs.aux = opts->aux_loss;
     if ((rc = check(moe::launch_router_topk(s, hidden, router_w, opts->router_bias, opts->routed_scale,
-                                            opts->router_logits, opts->topk_ids, opts->topk_weights, ws, st),
+                                            opts->router_logits, opts->topk_ids, opts->topk_weights, rs, ws, st),
                     "router_topk")) || (rc = mark(1 + MOE_STAGE_ROUTER)))
         return rc;
-    if ((rc = check(moe::launch_route_scan(s, opts->expert_counts, opts->expert_offsets, ws, st), "route_scan")) ||
+    if ((rc = check(moe::launch_route_scan(s, opts->expert_counts, opts->expert_offsets, rs, ws, st), "route_scan")) ||
         (rc = mark(1 + MOE_STAGE_SCAN)))
         return rc;
     if ((rc = check(moe::launch_route_permute(s, opts->perm, opts->inv_perm, ws, st), "route_permute")) ||

@@ -64,6 +64,9 @@ struct Workspace {
     float *wts;            // [TK] routed weights (x routed_scale)
     int32_t *blk_counts;   // [nblk][E] per-router-block histogram
     int32_t *blk_base;     // [nblk][E] first sorted position of each block's run
+    float *blk_prob;       // [nblk][E] router-probability sums of the block's counted tokens
+    int32_t *blk_mcnt;     // [nblk][E] assignments of the block's counted tokens
+    int32_t *blk_ntok;     // [nblk] counted tokens of the block
     int32_t *counts;       // [E]
     int32_t *offsets;      // [E+1]
     int32_t *tile_start;   // [E+1] first M-tile of each expert (large-M schedule)
@@ -95,11 +98,20 @@ int64_t workspace_layout(const Shape &s, void *base, Workspace *ws);
 
 // ------------------------------------------------------------------ launchers (return hipError_t)
 
+// Optional router statistics (load-balancing loss inputs).
+struct RouterStats {
+    const int32_t *mask;  // [T] nonzero = counted; null = every token
+    float *prob_mean;     // [E]
+    float *load;          // [E]
+    float *aux;           // [1]
+    bool on() const { return prob_mean || load || aux; }
+};
+
 hipError_t launch_router_topk(const Shape &s, const void *X, const void *Wr, const float *bias,
                               float routed_scale, float *logits_out, int32_t *ids_out, float *wts_out,
-                              const Workspace &ws, hipStream_t st);
+                              const RouterStats &rs, const Workspace &ws, hipStream_t st);
 hipError_t launch_route_scan(const Shape &s, int32_t *counts_out, int32_t *offsets_out,
-                             const Workspace &ws, hipStream_t st);
+                             const RouterStats &rs, const Workspace &ws, hipStream_t st);
 hipError_t launch_route_permute(const Shape &s, int32_t *perm_out, int32_t *inv_out,
                                 const Workspace &ws, hipStream_t st);
 

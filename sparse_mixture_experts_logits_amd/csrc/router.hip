@@ -69,19 +69,30 @@ __global__ __launch_bounds__(256) void router_topk_kernel(
     const Tin *__restrict__ X, const Tin *__restrict__ Wr, const float *__restrict__ bias, int T,
     int H, int E, int k, float routed_scale, int32_t *__restrict__ ids, float *__restrict__ wts,
     int32_t *__restrict__ ids_out, float *__restrict__ wts_out, float *__restrict__ logits_out,
-    int32_t *__restrict__ blk_counts)
+    int32_t *__restrict__ blk_counts, const int32_t *__restrict__ stats_mask, float *__restrict__ blk_prob,
+    int32_t *__restrict__ blk_mcnt, int32_t *__restrict__ blk_ntok)
 {
     constexpr int TG = RT < 8 ? RT : 8;  // tokens per pass
     constexpr int EG = 4;                // experts per pass
     __shared__ float s_logit[RT][kMaxExperts];
     __shared__ float s_sel[4][kMaxExperts];
     __shared__ int s_hist[kMaxExperts];
+    // router statistics (when blk_prob is set): softmax over all experts of
+    // each counted token, and the assignments and number of counted tokens
+    __shared__ float s_prob[RT][kMaxExperts];
+    __shared__ int s_mhist[kMaxExperts];
+    __shared__ int s_ntok;
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
     const int tblk = blockIdx.x * RT;
+    const bool stats = blk_prob != nullptr;
 
-    for (int e = threadIdx.x; e < E; e += 256) s_hist[e] = 0;
+    for (int e = threadIdx.x; e < E; e += 256) {
+        s_hist[e] = 0;
+        s_mhist[e] = 0;
+    }
+    if (threadIdx.x == 0) s_ntok = 0;
 
     // ---- logits
     const int epw = (E + 3) / 4;
@@ -186,6 +197,29 @@ __global__ __launch_bounds__(256) void router_topk_kernel(
             v[q] = e < E ? lrow[e] : -FLT_MAX;
             taken[q] = e >= E;
         }
+        const bool counted = stats && (!stats_mask || stats_mask[t] != 0);  // wave-uniform
+        if (stats) {
+            // probabilities over all E experts (zero rows for tokens not counted)
+            float m = -FLT_MAX;
+#pragma unroll
+            for (int q = 0; q < 4; q++) m = fmaxf(m, v[q]);
+#pragma unroll
+            for (int d = 32; d >= 1; d >>= 1) m = fmaxf(m, __shfl_xor(m, d, 64));
+            float ex[4], sum = 0.0f;
+#pragma unroll
+            for (int q = 0; q < 4; q++) {
+                ex[q] = taken[q] ? 0.0f : __expf(v[q] - m);  // taken[] marks e >= E here
+                sum += ex[q];
+            }
+#pragma unroll
+            for (int d = 32; d >= 1; d >>= 1) sum += __shfl_xor(sum, d, 64);
+#pragma unroll
+            for (int q = 0; q < 4; q++) {
+                const int e = lane + 64 * q;
+                if (e < E) s_prob[j][e] = counted ? ex[q] / sum : 0.0f;
+            }
+            if (counted && lane == 0) atomicAdd(&s_ntok, 1);
+        }
         for (int s = 0; s < k; s++) {
             float bv = -FLT_MAX;
             int bi = INT_MAX;
@@ -215,6 +249,7 @@ __global__ __launch_bounds__(256) void router_topk_kernel(
                 if (ids_out) ids_out[(int64_t)t * k + s] = bi;
                 s_sel[wave][s] = bv;
                 atomicAdd(&s_hist[bi], 1);
+                if (counted) atomicAdd(&s_mhist[bi], 1);
             }
         }
         __builtin_amdgcn_wave_barrier();
@@ -234,6 +269,16 @@ __global__ __launch_bounds__(256) void router_topk_kernel(
     }
     __syncthreads();
     for (int e = threadIdx.x; e < E; e += 256) blk_counts[(int64_t)blockIdx.x * E + e] = s_hist[e];
+    if (stats) {
+        const int nt = min(RT, T - tblk);
+        for (int e = threadIdx.x; e < E; e += 256) {
+            float ps = 0.0f;
+            for (int j = 0; j < nt; j++) ps += s_prob[j][e];  // token order
+            blk_prob[(int64_t)blockIdx.x * E + e] = ps;
+            blk_mcnt[(int64_t)blockIdx.x * E + e] = s_mhist[e];
+        }
+        if (threadIdx.x == 0) blk_ntok[blockIdx.x] = s_ntok;
+    }
 }
 
 // One workgroup: expert totals, exclusive offsets, per-block bases and the
@@ -241,7 +286,9 @@ __global__ __launch_bounds__(256) void router_topk_kernel(
 __global__ __launch_bounds__(1024) void route_scan_kernel(
     const int32_t *__restrict__ blk_counts, int nblk, int E, int BM, int32_t *__restrict__ counts,
     int32_t *__restrict__ offsets, int32_t *__restrict__ blk_base, int32_t *__restrict__ tile_start,
-    MTile *__restrict__ tiles, int32_t *__restrict__ counts_out, int32_t *__restrict__ offsets_out)
+    MTile *__restrict__ tiles, int32_t *__restrict__ counts_out, int32_t *__restrict__ offsets_out,
+    const float *__restrict__ blk_prob, const int32_t *__restrict__ blk_mcnt, const int32_t *__restrict__ blk_ntok,
+    float *__restrict__ prob_mean, float *__restrict__ load, float *__restrict__ aux)
 {
     __shared__ int s_part[1024];
     __shared__ int s_cnt[kMaxExperts];
@@ -323,6 +370,53 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(
         tile_start[tid] = s_ts[tid];
         if (offsets_out) offsets_out[tid] = s_off[tid];
     }
+    if (!blk_prob) return;
+
+    // ---- router statistics: the same fixed group order for the fp32 sums
+    __shared__ float s_pp[1024];
+    __shared__ int s_mp[1024];
+    __shared__ int s_nt[1024];
+    __shared__ float s_load[kMaxExperts];
+    __shared__ float s_prob[kMaxExperts];
+    if (g < G) {
+        float ps = 0.0f;
+        int ms = 0;
+        for (int b = b0; b < b1; b++) {
+            ps += blk_prob[(int64_t)b * E + e];
+            ms += blk_mcnt[(int64_t)b * E + e];
+        }
+        s_pp[g * E + e] = ps;
+        s_mp[g * E + e] = ms;
+    }
+    int nt = 0;
+    for (int b = tid; b < nblk; b += 1024) nt += blk_ntok[b];
+    s_nt[tid] = nt;
+    __syncthreads();
+    for (int w = 512; w >= 1; w >>= 1) {  // integer tree sum (exact in any order)
+        if (tid < w) s_nt[tid] += s_nt[tid + w];
+        __syncthreads();
+    }
+    const int n = s_nt[0];
+    if (tid < E) {
+        float ps = 0.0f;
+        int ms = 0;
+        for (int gg = 0; gg < G; gg++) {
+            ps += s_pp[gg * E + tid];
+            ms += s_mp[gg * E + tid];
+        }
+        const float pm = n > 0 ? ps / (float)n : 0.0f;
+        const float ld = n > 0 ? (float)ms / (float)n : 0.0f;
+        s_prob[tid] = pm;
+        s_load[tid] = ld;
+        if (prob_mean) prob_mean[tid] = pm;
+        if (load) load[tid] = ld;
+    }
+    __syncthreads();
+    if (tid == 0 && aux) {
+        float a = 0.0f;
+        for (int x = 0; x < E; x++) a += s_load[x] * s_prob[x];
+        aux[0] = (float)E * a;
+    }
 }
 
 // Scatter: assignment a of router block b goes to sorted position
@@ -360,13 +454,14 @@ __global__ __launch_bounds__(256) void route_permute_kernel(
 
 hipError_t launch_router_topk(const Shape &s, const void *X, const void *Wr, const float *bias,
                               float routed_scale, float *logits_out, int32_t *ids_out, float *wts_out,
-                              const Workspace &ws, hipStream_t st)
+                              const RouterStats &rs, const Workspace &ws, hipStream_t st)
 {
     dim3 grid(s.nblk), block(256);
+    float *bp = rs.on() ? ws.blk_prob : nullptr;
 #define MOE_ROUTER_LAUNCH(TIN, RT)                                                                      \
     hipLaunchKernelGGL((router_topk_kernel<TIN, RT>), grid, block, 0, st, (const TIN *)X, (const TIN *)Wr, \
                        bias, (int)s.T, (int)s.H, (int)s.E, s.k, routed_scale, ws.ids, ws.wts, ids_out,  \
-                       wts_out, logits_out, ws.blk_counts)
+                       wts_out, logits_out, ws.blk_counts, rs.mask, bp, ws.blk_mcnt, ws.blk_ntok)
     static_assert(kRouterMaxTokensPerBlock == 4, "router blocks of 1 or 4 tokens");
     if (s.dtype == 0) {
         if (s.rtok == 1) MOE_ROUTER_LAUNCH(__bf16, 1);
@@ -380,11 +475,12 @@ hipError_t launch_router_topk(const Shape &s, const void *X, const void *Wr, con
 }
 
 hipError_t launch_route_scan(const Shape &s, int32_t *counts_out, int32_t *offsets_out,
-                             const Workspace &ws, hipStream_t st)
+                             const RouterStats &rs, const Workspace &ws, hipStream_t st)
 {
     hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(1024), 0, st, ws.blk_counts, s.nblk,
                        (int)s.E, s.tileBM, ws.counts, ws.offsets, ws.blk_base, ws.tile_start,
-                       ws.tiles, counts_out, offsets_out);
+                       ws.tiles, counts_out, offsets_out, rs.on() ? ws.blk_prob : nullptr, ws.blk_mcnt,
+                       ws.blk_ntok, rs.prob_mean, rs.load, rs.aux);
     return hipGetLastError();
 }
 

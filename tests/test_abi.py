@@ -201,3 +201,13 @@ def test_quantize_entry_point_checks_arguments():
     assert lib.moe_quantize_fp8_rows(None, 4, 64, q, s, None) == -1
     assert lib.moe_quantize_fp8_rows(vp(base + 8), 4, 64, q, s, None) == -4
     assert lib.moe_quantize_fp8_rows(w, 4, 64, vp(base + 64), s, None) == -1  # q overlaps w
+
+
+def test_router_stats_outputs_must_be_aligned():
+    o = good_opts(nbytes=100)
+    o.aux_loss = (1 << 40) + (7 << 30) + 2
+    assert call(opts=o)[0] == -4
+    o = good_opts(nbytes=100)
+    o.router_prob_mean = (1 << 40) + (7 << 30)
+    o.stats_mask = (1 << 40) + (7 << 30) + 4096
+    assert call(opts=o)[0] == -3  # valid: stops at the (too small) workspace, before any HIP call
