@@ -19,6 +19,8 @@
 //     share an expert's weight block run together on one XCD's L2.
 #include "moe_internal.h"
 
+#include <type_traits>
+
 namespace moe {
 
 namespace {
@@ -244,7 +246,12 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void tiled_gemm_kernel(TiledParam
         // Consume stage buffer b. When nkt >= 0, the copies of stage nkt into
         // buffer nb are spread between the MFMAs, one copy per MFMA_PER_COPY
         // MFMAs, so the copy engine never holds up the fragment reads.
-        auto compute_with = [&](int b, int nkt, int nb) {
+        // NB (compile time): how many of this wave's RM 32-row blocks hold
+        // rows of the tile; the rest skip their fragment reads and MFMAs, so
+        // the short last tile of an expert costs less than a full one. The
+        // copies keep their slots either way.
+        auto compute_with = [&](auto nbc, int b, int nkt, int nb) {
+            constexpr int NB = decltype(nbc)::value;
             constexpr int NMMA = (BK / 16) * RM * RN;
             constexpr int PER = NMMA / LOADS > 0 ? NMMA / LOADS : 1;
             static_assert(PER * LOADS <= NMMA, "every copy finds an MFMA slot");
@@ -253,12 +260,13 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void tiled_gemm_kernel(TiledParam
                 bf16x8_t af[RM], bf[RN];
                 const int c = kk * 2 + (lane >> 5);
 #pragma unroll
-                for (int i = 0; i < RM; i++) {
+                for (int i = 0; i < NB; i++) {
                     const int row = wm * (BM / WM) + i * 32 + (lane & 31);
                     af[i] = as_bf16x8(sA[b][lds_slot(row, c)]);
                 }
 #pragma unroll
                 for (int j = 0; j < RN; j++) {
+                    if (NB == 0) break;
                     int row;
                     if (GATEUP) {
                         constexpr int HW = BN / 2 / WN;
@@ -273,13 +281,17 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void tiled_gemm_kernel(TiledParam
                 for (int i = 0; i < RM; i++)
 #pragma unroll
                     for (int j = 0; j < RN; j++) {
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
+                        if (i < NB)
+                            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
                         const int mi = (kk * RM + i) * RN + j;  // compile-time after unrolling
                         if ((mi + 1) % PER == 0 && (mi + 1) / PER - 1 < LOADS) issue_one(nkt, nb, (mi + 1) / PER - 1);
                     }
             }
         };
+        // 32-row blocks of this wave that hold rows of the tile (wave-uniform)
+        const int nvb = max(0, min(RM, (rows - wm * (BM / WM) + 31) / 32));
         auto compute = [&](int b) {
+            if (nvb == 0) return;
 #pragma unroll
             for (int kk = 0; kk < BK / 16; kk++) {
                 bf16x8_t af[RM], bf[RN];
@@ -287,7 +299,7 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void tiled_gemm_kernel(TiledParam
 #pragma unroll
                 for (int i = 0; i < RM; i++) {
                     const int row = wm * (BM / WM) + i * 32 + (lane & 31);
-                    af[i] = as_bf16x8(sA[b][lds_slot(row, c)]);
+                    if (i < nvb) af[i] = as_bf16x8(sA[b][lds_slot(row, c)]);
                 }
 #pragma unroll
                 for (int j = 0; j < RN; j++) {
@@ -305,7 +317,7 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void tiled_gemm_kernel(TiledParam
                 for (int i = 0; i < RM; i++)
 #pragma unroll
                     for (int j = 0; j < RN; j++)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
+                        if (i < nvb) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
             }
         };
 
@@ -321,19 +333,26 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void tiled_gemm_kernel(TiledParam
         // (a ragged last stage is always left to the drain)
         int kt = 0;
         const int steady_last = nk - (ragged ? 1 : 0);
-        for (; kt + 2 * STAGES - 1 <= steady_last; kt += STAGES) {
+        auto steady = [&](auto nbc) {
+            for (; kt + 2 * STAGES - 1 <= steady_last; kt += STAGES) {
 #pragma unroll
-            for (int b = 0; b < STAGES; b++) {
-                wait_vm_barrier<(STAGES - 2) * LOADS>();
-                const int nkt = kt + b + STAGES - 1, nb = (b + STAGES - 1) % STAGES;
+                for (int b = 0; b < STAGES; b++) {
+                    wait_vm_barrier<(STAGES - 2) * LOADS>();
+                    const int nkt = kt + b + STAGES - 1, nb = (b + STAGES - 1) % STAGES;
 #if MOE_TILED_INTERLEAVE
-                compute_with(b, nkt, nb);
+                    compute_with(nbc, b, nkt, nb);
 #else
-                issue(nkt, nb);
-                compute(b);
+                    issue(nkt, nb);
+                    compute(b);
 #endif
+                }
             }
-        }
+        };
+        // one copy of the loop per number of live 32-row blocks (RM is 1 or 2)
+        static_assert(RM <= 2, "steady-state variants for up to two 32-row blocks per wave");
+        if (nvb >= RM) steady(std::integral_constant<int, RM>{});
+        else if (nvb == 1) steady(std::integral_constant<int, 1>{});
+        else steady(std::integral_constant<int, 0>{});
         // Drain: fewer than 2*STAGES-1 stages remain (kt is a multiple of STAGES,
         // so stage kt + b lives in buffer b).
 #pragma unroll
