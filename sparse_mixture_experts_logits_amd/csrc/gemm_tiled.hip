@@ -798,6 +798,7 @@ hipError_t launch_cfg(const GemmProblem &g, hipStream_t st)
 #define MOE_TILED_PP 0
 #endif
 
+#if MOE_TILED_PP
 template <bool GATEUP>
 hipError_t launch_pp(const GemmProblem &g, hipStream_t st)
 {
@@ -806,6 +807,7 @@ hipError_t launch_pp(const GemmProblem &g, hipStream_t st)
     hipLaunchKernelGGL((tiled_pp_kernel<256, 256, GATEUP>), dim3(persistent_grid(1)), dim3(256), 0, st, t);
     return hipGetLastError();
 }
+#endif
 
 }  // namespace
 
@@ -818,15 +820,21 @@ int tiled_block_m() { return 256; }
 hipError_t launch_gate_up_tiled(const GemmProblem &g, hipStream_t st)
 {
     if (g.dense_rows > 0) return launch_cfg<128, 256, 2, 2, 1, true>(g, st);
-    if (MOE_TILED_PP) return launch_pp<true>(g, st);
+#if MOE_TILED_PP
+    return launch_pp<true>(g, st);
+#else
     return launch_cfg<256, 256, 4, 2, 1, true>(g, st);
+#endif
 }
 
 hipError_t launch_down_tiled(const GemmProblem &g, hipStream_t st)
 {
     if (g.dense_rows > 0) return launch_cfg<128, 128, 2, 2, 2, false>(g, st);
-    if (MOE_TILED_PP) return launch_pp<false>(g, st);
+#if MOE_TILED_PP
+    return launch_pp<false>(g, st);
+#else
     return launch_cfg<256, 256, 4, 2, 1, false>(g, st);
+#endif
 }
 
 }  // namespace moe
