@@ -82,6 +82,13 @@ __device__ __forceinline__ u32x4 e4m3x8_to_bf16(uint32_t w0, uint32_t w1)
                  __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true))};
 }
 
+// v, or zeros when c is false (a per-component select: selecting between two
+// lvalues would take their addresses and keep the staging arrays in memory)
+__device__ __forceinline__ u32x4 keep_if(bool c, const u32x4 v)
+{
+    return u32x4{c ? v.x : 0u, c ? v.y : 0u, c ? v.z : 0u, c ? v.w : 0u};
+}
+
 // 16-byte chunk c (0..15) of row r (0..31) in a wave's LDS tile of 256-byte rows
 __device__ __forceinline__ int tswz(int r, int c) { return r * 16 + (c ^ (r & 15)); }
 
@@ -124,8 +131,8 @@ __global__ __launch_bounds__((W8 ? SW_W8 : SW_BF) * 64, W8 ? MOE_SKINNY_W8_OCC :
 
     // load instruction i covers tile rows 4i..4i+3; this lane: row 4i + lgrp, chunk l16
     // element offsets inside one expert fit in 32 bits (2*I*H < 2^31 is checked on the host)
-    const uint8_t *wbase =
-        reinterpret_cast<const uint8_t *>(p.W) + ((int64_t)e * p.w_expert_stride + l16 * EPC) * (W8 ? 1 : 2);
+    // the expert's weights; a lane's chunk adds l16 * EPC elements to its row
+    const uint8_t *wbase = reinterpret_cast<const uint8_t *>(p.W) + (int64_t)e * p.w_expert_stride * (W8 ? 1 : 2);
     uint32_t woff[NL];
 #pragma unroll
     for (int i = 0; i < NL; i++) {
@@ -149,7 +156,7 @@ __global__ __launch_bounds__((W8 ? SW_W8 : SW_BF) * 64, W8 ? MOE_SKINNY_W8_OCC :
         const bool xv = q < M;
         const int qc = xv ? q : M - 1;
         const int64_t src = p.a_rows ? (int64_t)p.a_rows[row0 + qc] : (int64_t)(row0 + qc);
-        const __bf16 *xp = p.A + src * p.K + lgrp * EPC;
+        const __bf16 *xp = p.A + src * p.K;  // the token's row; lanes add their chunk offsets
 
         f32x4_t acc[NW];
 #pragma unroll
@@ -160,21 +167,27 @@ __global__ __launch_bounds__((W8 ? SW_W8 : SW_BF) * 64, W8 ? MOE_SKINNY_W8_OCC :
         // weights of step kb and the token fragments it needs: MFMA j takes
         // chunk 4j + lgrp (bf16: 8 elements; E4M3: 16 elements, as two MFMAs
         // over its halves, fragment 2j + half)
+        // Loads are unconditional and whole 16-byte loads: a chunk past K (or
+        // a token past the expert's rows) reads the row's first chunk instead,
+        // and the consumer zeroes it. With no branches or selects between a
+        // load and its use, the compiler's wait counts stay exact and every
+        // load of a step is in flight together.
+        // (plain '&' and masks below, not '&&' or '?:', so that no branch is formed)
+        auto w_ok = [&](int kb) { return kb * KS + l16 * EPC < p.K; };
+        auto x_ok = [&](int kb, int f) { return xv & (kb * KS + (4 * (W8 ? f / 2 : f) + lgrp) * EPC < p.K); };
+        // (a chunk that is not read falls back to the row's first chunk, so
+        // every address stays inside a row that exists)
         auto gload_w = [&](int kb, int b) {
-            const int k = kb * KS;
-            const bool ok = k + l16 * EPC < p.K;
-            const uint32_t kbytes = (uint32_t)k * (W8 ? 1u : 2u);
+            const uint32_t kbytes = (uint32_t)(kb * KS + l16 * EPC) * (W8 ? 1u : 2u) & (0u - (uint32_t)w_ok(kb));
 #pragma unroll
-            for (int i = 0; i < NL; i++) st[b][i] = ok ? load_nt16(wbase + woff[i] + kbytes) : zero;
+            for (int i = 0; i < NL; i++) st[b][i] = load_nt16(wbase + woff[i] + kbytes);
         };
         auto gload_x = [&](int kb, int b) {
-            const int k = kb * KS;
 #pragma unroll
             for (int f = 0; f < XF; f++) {
                 const int j = W8 ? f / 2 : f;
                 const int off = W8 ? j * 64 + (f % 2) * 8 : j * 32;
-                const bool okx = xv && (k + (4 * j + lgrp) * EPC < p.K);
-                xs[b][f] = okx ? *reinterpret_cast<const u32x4 *>(xp + k + off) : zero;
+                xs[b][f] = load16(xp + ((kb * KS + lgrp * EPC + off) & (0 - (int)x_ok(kb, f))));
             }
         };
         // One reduction step from staging buffer b (a compile-time index after
@@ -183,11 +196,14 @@ __global__ __launch_bounds__((W8 ? SW_W8 : SW_BF) * 64, W8 ? MOE_SKINNY_W8_OCC :
         // hits) only after this step's MFMAs have consumed the current ones, so
         // they need no second register copy and more waves fit on a SIMD.
         auto step = [&](int kb, int b) {
+            const bool okw = w_ok(kb);
 #pragma unroll
-            for (int i = 0; i < NL; i++) tile[tswz(4 * i + lgrp, l16)] = st[b][i];
+            for (int i = 0; i < NL; i++) tile[tswz(4 * i + lgrp, l16)] = keep_if(okw, st[b][i]);
             const bool more = kb + PD < kb_hi;
             if (more) gload_w(kb + PD, b);
-            const u32x4(&xb)[XF] = xs[b];
+            u32x4 xb[XF];
+#pragma unroll
+            for (int f = 0; f < XF; f++) xb[f] = keep_if(x_ok(kb, f), xs[b][f]);
 #pragma unroll
             for (int j = 0; j < 4; j++) {
 #pragma unroll

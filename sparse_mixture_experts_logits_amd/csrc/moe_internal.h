@@ -26,6 +26,13 @@ __device__ __forceinline__ u32x4 load_nt16(const void *p)
     return u32x4{v.x, v.y, v.z, v.w};
 }
 
+// Plain 16-byte load (one dwordx4 instruction).
+__device__ __forceinline__ u32x4 load16(const void *p)
+{
+    const u32x4v_t v = *reinterpret_cast<const u32x4v_t *>(p);
+    return u32x4{v.x, v.y, v.z, v.w};
+}
+
 __device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xffff0000u); }
 
