@@ -126,13 +126,15 @@ __global__ __launch_bounds__(256) void router_topk_kernel(
                 Slice<Tin> xv[CU][TG], wv[CU][EG];
 #pragma unroll
                 for (int u = 0; u < CU; u++) {
+                    // H is a multiple of 8: a slice is all valid or all absent. An
+                    // absent slice loads the row's first slice (and is not used), so
+                    // the loads need no branch and all of them are in flight at once.
                     const int64_t i0 = (int64_t)(c0 + u) * 512 + lane * 8;
-                    if (i0 < H) {  // H is a multiple of 8: a slice is all valid or all absent
+                    const int64_t ia = i0 & -(int64_t)(i0 < H);
 #pragma unroll
-                        for (int j = 0; j < TG; j++) xv[u][j].load(xrow[j], i0);
+                    for (int j = 0; j < TG; j++) xv[u][j].load(xrow[j], ia);
 #pragma unroll
-                        for (int q = 0; q < EG; q++) wv[u][q].load(wrow[q], i0);
-                    }
+                    for (int q = 0; q < EG; q++) wv[u][q].load(wrow[q], ia);
                 }
 #pragma unroll
                 for (int u = 0; u < CU; u++) {
