@@ -61,6 +61,13 @@ typedef enum moe_dtype {
     MOE_F32 = 1   /* fp32 everywhere                                                */
 } moe_dtype;
 
+/* How router logits become expert scores (opts->score_func). */
+typedef enum moe_score_func {
+    MOE_SCORE_SOFTMAX = 0, /* weights: softmax over the selected logits          */
+    MOE_SCORE_SIGMOID = 1  /* scores sigmoid(logit); weights: the selected       */
+                           /* scores divided by their sum                         */
+} moe_score_func;
+
 /* Storage of the routed experts' weights (gate_up, down). */
 typedef enum moe_weight_format {
     MOE_WEIGHTS_NATIVE = 0,  /* same dtype as the activations (opts->dtype)          */
@@ -129,6 +136,37 @@ typedef struct moe_opts {
     float *router_prob_mean;   /* [E] or NULL                                   */
     float *expert_load;        /* [E] or NULL                                   */
     float *aux_loss;           /* [1] or NULL                                   */
+    /* Scoring variants. The Instella page names its top-k method "noaux_tc"
+     * on a DeepSeek-V3 base: sigmoid expert scores, a load-balancing bias
+     * that steers selection only, and group-limited selection. The pages do
+     * not spell these out; this follows DeepSeek-V3's published router.
+     * Defaults (all zero) give the PhiMoE softmax router above.
+     *
+     * score_func = MOE_SCORE_SIGMOID: the score of expert e is
+     * s = 1 / (1 + exp(-c)), c = the logit clamped to [-80, 80], in fp32 with
+     * exp built from correctly rounded IEEE operations only, so it is the
+     * same bit for bit on any conforming machine:
+     *   n = rint(x * fl(1/ln2)); r = fma(-n, A, x); r = fma(-n, B, r) with
+     *   A = 0.693145751953125 and B = fl(ln2 - A); p = Horner evaluation in
+     *   fma of the Taylor polynomial sum_{j=0..8} fl(1/j!) r^j;
+     *   exp(x) = ldexp(p, n)
+     * (fl = round to nearest fp32). Selection ranks experts by
+     * key = score + selection_bias[e] (score = the logit for softmax; the
+     * ranking rule as above), while the weights use the unbiased scores of
+     * the selected experts: softmax over the selected logits, or the
+     * selected sigmoid scores divided by their sum, times routed_scale.
+     *
+     * n_group > 1: the E experts form n_group equal groups of consecutive
+     * experts; a group's score is the fp32 sum, best first, of its best two
+     * keys (its one key when E == n_group); the topk_group best groups (ties
+     * to the lower group) are kept and the k experts are chosen among them.
+     * Requires E % n_group == 0, 1 <= topk_group <= n_group and
+     * k <= topk_group * E / n_group; otherwise MOE_ERR_INVALID_ARG.
+     * selection_bias values must be finite. */
+    int32_t score_func;           /* moe_score_func                            */
+    const float *selection_bias;  /* [E] fp32 added to selection keys, or NULL */
+    int32_t n_group;              /* 0 or 1: no grouping                        */
+    int32_t topk_group;
 } moe_opts;
 
 /* Stages of moe_forward, in launch order. */

@@ -53,7 +53,11 @@ def _load():
         lib.oracle_quantize_e4m3_rows.argtypes = [vp, i64, i64, vp, vp]
         lib.oracle_moe_tokens_e4m3.argtypes = [vp, vp, vp, vp, vp, i64, i64, vp, vp, i32, i32,
                                                vp, vp, vp, vp, i64, vp]
-        for f in (lib.oracle_router_logits, lib.oracle_select_topk, lib.oracle_route,
+        lib.oracle_exp_f32.argtypes = [vp, i64, vp]
+        lib.oracle_sigmoid_scores.argtypes = [vp, i64, vp]
+        lib.oracle_select_scored.argtypes = [vp, i64, i64, i32, f32, i32, vp, i32, i32, vp, vp]
+        for f in (lib.oracle_exp_f32, lib.oracle_sigmoid_scores, lib.oracle_select_scored,
+                  lib.oracle_router_logits, lib.oracle_select_topk, lib.oracle_route,
                   lib.oracle_moe_tokens, lib.oracle_num_threads, lib.oracle_e4m3_values,
                   lib.oracle_quantize_e4m3_rows, lib.oracle_moe_tokens_e4m3, lib.oracle_router_stats):
             f.restype = ctypes.c_int
@@ -107,6 +111,40 @@ def select_topk(logits: np.ndarray, k: int, routed_scale: float = 1.0):
     w = np.empty((T, k), dtype=np.float32)
     _check(_load().oracle_select_topk(_p(logits), T, E, int(k), float(routed_scale), _p(ids), _p(w)),
            "select_topk")
+    return ids, w
+
+
+def exp_f32(x: np.ndarray) -> np.ndarray:
+    """fp32 exp by argument reduction and a degree-8 Taylor polynomial (the
+    contract's reproducible exp), elementwise."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    y = np.empty_like(x)
+    _check(_load().oracle_exp_f32(_p(x), x.size, _p(y)), "exp_f32")
+    return y
+
+
+def sigmoid_scores(x: np.ndarray) -> np.ndarray:
+    """fp32 sigmoid scores 1 / (1 + exp_f32(-clamp(x, -80, 80))), elementwise."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    y = np.empty_like(x)
+    _check(_load().oracle_sigmoid_scores(_p(x), x.size, _p(y)), "sigmoid_scores")
+    return y
+
+
+def select_scored(logits: np.ndarray, k: int, routed_scale: float = 1.0, score_func: str = "softmax",
+                  selection_bias: np.ndarray | None = None, n_group: int = 0, topk_group: int = 0):
+    """Top-k under the scoring variants (sigmoid scores, selection-only bias,
+    group-limited selection): ids [T, k] int32 and weights [T, k] float32."""
+    logits = np.ascontiguousarray(logits, dtype=np.float32)
+    T, E = logits.shape
+    if selection_bias is not None:
+        selection_bias = np.ascontiguousarray(selection_bias, dtype=np.float32)
+        assert selection_bias.shape == (E,)
+    sf = {"softmax": 0, "sigmoid": 1}[score_func]
+    ids = np.empty((T, k), dtype=np.int32)
+    w = np.empty((T, k), dtype=np.float32)
+    _check(_load().oracle_select_scored(_p(logits), T, E, int(k), float(routed_scale), sf, _p(selection_bias),
+                                        int(n_group), int(topk_group), _p(ids), _p(w)), "select_scored")
     return ids, w
 
 
@@ -259,10 +297,13 @@ def moe_forward_e4m3(hidden, router_w, gate_up, down, k, routed_scale=1.0, bias=
 
 
 def moe_forward(hidden, router_w, gate_up, down, k, routed_scale=1.0, bias=None, shared=(),
-                tokens=None):
+                tokens=None, score_func="softmax", selection_bias=None, n_group=0, topk_group=0):
     """Whole layer: routing for every token, outputs for ``tokens`` (all if None)."""
     logits = router_logits(hidden, router_w, bias)
-    ids, w = select_topk(logits, k, routed_scale)
+    if score_func == "softmax" and selection_bias is None and n_group <= 1:
+        ids, w = select_topk(logits, k, routed_scale)
+    else:
+        ids, w = select_scored(logits, k, routed_scale, score_func, selection_bias, n_group, topk_group)
     counts, offsets, perm, inv = route(ids, router_w.shape[0])
     out = moe_tokens(hidden, gate_up, down, ids, w, tokens=tokens, shared=shared)
     return dict(logits=logits, ids=ids, weights=w, counts=counts, offsets=offsets,

@@ -502,3 +502,154 @@ int oracle_num_threads(void)
     }
     return n;
 }
+
+/*
+ * Scoring variants of the router. The Instella page gives its top-k method as
+ * "noaux_tc" on a DeepSeek-V3 base (64 routed experts, 6 per token, routed
+ * scale 2.5) without defining it; the definition taken is DeepSeek-V3's
+ * published router:
+ *   score   s[e] = sigmoid(l[e])           (the logit itself for softmax),
+ *   key     c[e] = s[e] + bias[e]          (the bias steers selection only),
+ *   groups  (n_group = G > 1) G groups of E/G consecutive experts; a group's
+ *           score is the sum of its two largest keys (its only key when
+ *           E/G = 1); the topk_group best groups are kept (ties to the lower
+ *           group) and only their experts may be selected,
+ *   top-k   greedy by key, ties to the lower expert index,
+ *   weights the selected scores over their sum (sigmoid) or the softmax of
+ *           the selected logits (softmax), times the routed scale.
+ * Keys decide integers (the ids), so they are computed in fp32 with the
+ * operation sequence the library's contract states: clamp to [-80, 80],
+ * exp(x) = 2^n e^r with n = rint(x / ln2) and ln2 split into a short high
+ * part and a rounded low part, e^r by its degree-8 Taylor polynomial in
+ * Horner form with fused multiply-adds, then 1 / (1 + exp(-c)); the key and
+ * the group sums (best key first, from 0) are fp32 additions. Weights are
+ * evaluated in fp64 from the fp32 scores.
+ */
+static float exp_by_reduction(float x)
+{
+    const double ln2 = log(2.0);
+    const float inv_ln2 = (float)(1.0 / ln2);
+    const float ln2_hi = 0.693145751953125f; /* 15 significant bits: n * ln2_hi is exact */
+    const float ln2_lo = (float)(ln2 - (double)ln2_hi);
+    const float n = rintf(x * inv_ln2);
+    float r = fmaf(-n, ln2_hi, x);
+    r = fmaf(-n, ln2_lo, r);
+    double fact[9];
+    fact[0] = 1.0;
+    for (int j = 1; j <= 8; j++)
+        fact[j] = fact[j - 1] * j;
+    float p = (float)(1.0 / fact[8]);
+    for (int j = 7; j >= 0; j--)
+        p = fmaf(p, r, (float)(1.0 / fact[j]));
+    return ldexpf(p, (int)n);
+}
+
+static float sigmoid_score(float l)
+{
+    float c = l < -80.0f ? -80.0f : l;
+    c = c > 80.0f ? 80.0f : c;
+    return 1.0f / (1.0f + exp_by_reduction(-c));
+}
+
+int oracle_exp_f32(const float *x, int64_t n, float *y)
+{
+    if (!x || !y || n < 0)
+        return OR_BAD;
+    for (int64_t i = 0; i < n; i++)
+        y[i] = exp_by_reduction(x[i]);
+    return OR_OK;
+}
+
+int oracle_sigmoid_scores(const float *x, int64_t n, float *y)
+{
+    if (!x || !y || n < 0)
+        return OR_BAD;
+    for (int64_t i = 0; i < n; i++)
+        y[i] = sigmoid_score(x[i]);
+    return OR_OK;
+}
+
+/* a ranks before b: larger value, then lower index */
+static int before(float va, int64_t a, float vb, int64_t b)
+{
+    return va > vb || (va == vb && a < b);
+}
+
+int oracle_select_scored(const float *logits, int64_t T, int64_t E, int k, float routed_scale,
+                         int score_func, const float *bias, int n_group, int topk_group,
+                         int32_t *ids, float *weights)
+{
+    if (!logits || !ids || !weights || T < 0 || E <= 0 || E > 4096 || k < 1 || k > E || k > 256 ||
+        (score_func != 0 && score_func != 1))
+        return OR_BAD;
+    const int grouped = n_group > 1;
+    if (grouped && (E % n_group || topk_group < 1 || topk_group > n_group ||
+                    (int64_t)k > (int64_t)topk_group * (E / n_group)))
+        return OR_BAD;
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; t++) {
+        const float *l = logits + t * E;
+        float s[4096], key[4096];
+        unsigned char allowed[4096];
+        for (int64_t e = 0; e < E; e++) {
+            s[e] = score_func == 1 ? sigmoid_score(l[e]) : l[e];
+            key[e] = bias ? s[e] + bias[e] : s[e];
+            allowed[e] = 1;
+        }
+        if (grouped) {
+            const int64_t gsz = E / n_group;
+            float gscore[4096];
+            for (int g = 0; g < n_group; g++) {
+                /* the group's best key, then its best other key */
+                int64_t b1 = -1, b2 = -1;
+                for (int64_t e = g * gsz; e < (g + 1) * gsz; e++)
+                    if (b1 < 0 || before(key[e], e, key[b1], b1))
+                        b1 = e;
+                for (int64_t e = g * gsz; e < (g + 1) * gsz; e++)
+                    if (e != b1 && (b2 < 0 || before(key[e], e, key[b2], b2)))
+                        b2 = e;
+                float sum = 0.0f + key[b1];
+                if (b2 >= 0)
+                    sum = sum + key[b2];
+                gscore[g] = sum;
+            }
+            unsigned char kept[4096];
+            for (int g = 0; g < n_group; g++)
+                kept[g] = 0;
+            for (int r = 0; r < topk_group; r++) {
+                int best = -1;
+                for (int g = 0; g < n_group; g++)
+                    if (!kept[g] && (best < 0 || before(gscore[g], g, gscore[best], best)))
+                        best = g;
+                kept[best] = 1;
+            }
+            for (int64_t e = 0; e < E; e++)
+                allowed[e] = kept[e / gsz];
+        }
+        for (int j = 0; j < k; j++) {
+            int64_t best = -1;
+            for (int64_t e = 0; e < E; e++)
+                if (allowed[e] && (best < 0 || before(key[e], e, key[best], best)))
+                    best = e;
+            ids[t * k + j] = (int32_t)best;
+            allowed[best] = 0;
+        }
+        double num[256], den = 0.0;
+        if (score_func == 1) {
+            for (int j = 0; j < k; j++)
+                num[j] = (double)s[ids[t * k + j]];
+        } else {
+            double m = -INFINITY;
+            for (int j = 0; j < k; j++)
+                if ((double)l[ids[t * k + j]] > m)
+                    m = (double)l[ids[t * k + j]];
+            for (int j = 0; j < k; j++)
+                num[j] = exp((double)l[ids[t * k + j]] - m);
+        }
+        for (int j = 0; j < k; j++)
+            den += num[j];
+        for (int j = 0; j < k; j++)
+            weights[t * k + j] = (float)((double)routed_scale * num[j] / den);
+    }
+    return OR_OK;
+}

@@ -14,6 +14,7 @@ import numpy as np
 
 __all__ = ["moe_forward", "workspace_bytes", "quantize_fp8_rows", "MoeError", "load_library", "LIB_PATH",
            "FLAG_FORCE_TILED", "FLAG_FORCE_SKINNY", "WEIGHTS_NATIVE", "WEIGHTS_FP8_E4M3",
+           "SCORE_SOFTMAX", "SCORE_SIGMOID",
            "bf16_bits_to_tensor", "EXPORTS"]
 
 # MOE_MI355X_LIB may point at another build of the same library (tuning builds)
@@ -26,6 +27,8 @@ FLAG_FORCE_TILED = 0x1
 FLAG_FORCE_SKINNY = 0x2
 WEIGHTS_NATIVE = 0
 WEIGHTS_FP8_E4M3 = 1
+SCORE_SOFTMAX = 0
+SCORE_SIGMOID = 1
 EXPORTS = ("moe_opts_init", "moe_workspace_bytes", "moe_forward", "moe_quantize_fp8_rows", "moe_last_error")
 STAGES = ("router", "scan", "permute", "gate_up", "down", "shared_gate_up", "shared_down", "combine")
 STAGE_EVENTS = len(STAGES) + 1
@@ -63,6 +66,10 @@ class MoeOpts(ctypes.Structure):
         ("router_prob_mean", ctypes.c_void_p),
         ("expert_load", ctypes.c_void_p),
         ("aux_loss", ctypes.c_void_p),
+        ("score_func", ctypes.c_int32),
+        ("selection_bias", ctypes.c_void_p),
+        ("n_group", ctypes.c_int32),
+        ("topk_group", ctypes.c_int32),
     ]
 
 
@@ -159,7 +166,8 @@ def quantize_fp8_rows(w, stream=None):
 def moe_forward(hidden, router_w, gate_up, down, k: int, *, routed_scale: float = 1.0, router_bias=None,
                 shared_gate_up=None, shared_down=None, flags: int = 0, return_routing: bool = False,
                 out=None, workspace=None, stream=None, stage_events=None, gate_up_scale=None, down_scale=None,
-                router_stats: bool = False, stats_mask=None):
+                router_stats: bool = False, stats_mask=None, score_func: str = "softmax",
+                selection_bias=None, n_group: int = 0, topk_group: int = 0):
     """Run the MoE layer on torch tensors already on the GPU.
 
     hidden [T, H], router_w [E, H], gate_up [E, 2I, H], down [E, H, I] (all
@@ -169,7 +177,11 @@ def moe_forward(hidden, router_w, gate_up, down, k: int, *, routed_scale: float 
     from quantize_fp8_rows); activations bf16. ``router_stats`` adds the
     load-balancing statistics (prob_mean [E], load [E], aux_loss [1]) to the
     routing dict, over the tokens with ``stats_mask`` != 0 (int32 [T]; all
-    tokens if None). Returns out [T, H] (and a dict of routing tensors when
+    tokens if None). ``score_func`` "sigmoid" scores experts by the sigmoid of
+    their logits and weights them by the selected scores over their sum;
+    ``selection_bias`` [E] fp32 is added to the scores for selection only;
+    ``n_group`` > 1 with ``topk_group`` limits selection to the best
+    topk_group of n_group equal expert groups. Returns out [T, H] (and a dict of routing tensors when
     ``return_routing`` or ``router_stats``). Work is enqueued on ``stream``
     (default: torch's current stream)."""
     import torch
@@ -207,6 +219,17 @@ def moe_forward(hidden, router_w, gate_up, down, k: int, *, routed_scale: float 
         raise ValueError("shape mismatch among hidden, router_w, gate_up, down")
     o.routed_scale = float(routed_scale)
     o.flags = int(flags)
+    funcs = {"softmax": SCORE_SOFTMAX, "sigmoid": SCORE_SIGMOID}
+    if score_func not in funcs:
+        raise ValueError(f"score_func must be one of {sorted(funcs)}")
+    o.score_func = funcs[score_func]
+    if selection_bias is not None:
+        selection_bias = selection_bias.to(device=hidden.device, dtype=torch.float32).contiguous()
+        if selection_bias.shape != (E,):
+            raise ValueError("selection_bias must be [E]")
+        o.selection_bias = selection_bias.data_ptr()
+    o.n_group = int(n_group)
+    o.topk_group = int(topk_group)
     if router_bias is not None:
         router_bias = router_bias.to(dtype=torch.float32).contiguous()
         o.router_bias = router_bias.data_ptr()
@@ -263,7 +286,7 @@ def moe_forward(hidden, router_w, gate_up, down, k: int, *, routed_scale: float 
         stream = current
     if stream != current:
         # buffers allocated here belong to the current stream's pool
-        for t in (router_bias, workspace, out, gate_up_scale, down_scale, stats_mask,
+        for t in (router_bias, workspace, out, gate_up_scale, down_scale, stats_mask, selection_bias,
                   *(routing.values() if routing else ())):
             if t is not None:
                 t.record_stream(stream)

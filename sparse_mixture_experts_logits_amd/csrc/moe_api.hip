@@ -76,6 +76,21 @@ int check_shape(int64_t T, int64_t H, int64_t I, int64_t E, int32_t k, const moe
             return fail(MOE_ERR_INVALID_ARG, "unknown flag bits 0x%x", opts->flags);
         if ((opts->flags & MOE_FLAG_FORCE_TILED) && (opts->flags & MOE_FLAG_FORCE_SKINNY))
             return fail(MOE_ERR_INVALID_ARG, "MOE_FLAG_FORCE_TILED and MOE_FLAG_FORCE_SKINNY both set");
+        if (opts->score_func != MOE_SCORE_SOFTMAX && opts->score_func != MOE_SCORE_SIGMOID)
+            return fail(MOE_ERR_INVALID_ARG, "unknown score_func %d", opts->score_func);
+        if (opts->n_group < 0) return fail(MOE_ERR_INVALID_ARG, "n_group = %d is negative", opts->n_group);
+        if (opts->n_group > 1) {
+            if (opts->n_group > moe::kMaxGroups)
+                return fail(MOE_ERR_UNSUPPORTED, "n_group = %d above %d", opts->n_group, moe::kMaxGroups);
+            if (E % opts->n_group)
+                return fail(MOE_ERR_INVALID_ARG, "E = %lld is not a multiple of n_group = %d", (long long)E,
+                            opts->n_group);
+            if (opts->topk_group < 1 || opts->topk_group > opts->n_group)
+                return fail(MOE_ERR_INVALID_ARG, "topk_group = %d outside [1, n_group = %d]", opts->topk_group,
+                            opts->n_group);
+            if ((int64_t)k > (int64_t)opts->topk_group * (E / opts->n_group))
+                return fail(MOE_ERR_INVALID_ARG, "k = %d exceeds the experts of topk_group groups", k);
+        }
         if (opts->weight_format != MOE_WEIGHTS_NATIVE && opts->weight_format != MOE_WEIGHTS_FP8_E4M3)
             return fail(MOE_ERR_INVALID_ARG, "unknown weight_format %d", opts->weight_format);
         if (opts->weight_format == MOE_WEIGHTS_FP8_E4M3) {
@@ -193,7 +208,8 @@ int moe_forward(const void *hidden, const void *router_w, const void *gate_up, c
         if (p && !aligned(p, 16)) return fail(MOE_ERR_ALIGNMENT, "tensor pointer %p is not 16-byte aligned", p);
     const void *small[] = {opts->router_bias, opts->router_logits, opts->topk_ids, opts->topk_weights,
                            opts->expert_counts, opts->expert_offsets, opts->perm, opts->inv_perm,
-                           opts->stats_mask, opts->router_prob_mean, opts->expert_load, opts->aux_loss};
+                           opts->stats_mask, opts->router_prob_mean, opts->expert_load, opts->aux_loss,
+                           opts->selection_bias};
     for (const void *p : small)
         if (p && !aligned(p, 4)) return fail(MOE_ERR_ALIGNMENT, "output pointer %p is not 4-byte aligned", p);
 
@@ -218,6 +234,7 @@ int moe_forward(const void *hidden, const void *router_w, const void *gate_up, c
                {opts->shared_down, shared ? (uint64_t)H * opts->shared_I * es : 0},
                {opts->router_bias, (uint64_t)E * 4},
                {opts->stats_mask, (uint64_t)T * 4},
+               {opts->selection_bias, (uint64_t)E * 4},
                {opts->workspace, opts->workspace_bytes}};
     for (const Range &r : ins)
         if (overlaps(out, out_bytes, r.p, r.n)) return fail(MOE_ERR_INVALID_ARG, "out overlaps an input or the workspace");
@@ -262,8 +279,14 @@ int moe_forward(const void *hidden, const void *router_w, const void *gate_up, c
     rs.prob_mean = opts->router_prob_mean;
     rs.load = opts->expert_load;
     rs.aux = opts->aux_loss;
+    moe::RouterCfg rcfg;
+    rcfg.score_func = opts->score_func;
+    rcfg.sel_bias = opts->selection_bias;
+    rcfg.n_group = opts->n_group > 1 ? opts->n_group : 0;
+    rcfg.topk_group = opts->topk_group;
     if ((rc = check(moe::launch_router_topk(s, hidden, router_w, opts->router_bias, opts->routed_scale,
-                                            opts->router_logits, opts->topk_ids, opts->topk_weights, rs, ws, st),
+                                            opts->router_logits, opts->topk_ids, opts->topk_weights, rs, rcfg, ws,
+                                            st),
                     "router_topk")) || (rc = mark(1 + MOE_STAGE_ROUTER)))
         return rc;
     if ((rc = check(moe::launch_route_scan(s, opts->expert_counts, opts->expert_offsets, rs, ws, st), "route_scan")) ||

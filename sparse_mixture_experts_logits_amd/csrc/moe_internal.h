@@ -114,9 +114,18 @@ struct RouterStats {
     bool on() const { return prob_mean || load || aux; }
 };
 
+// Scoring variant of the router (softmax by default).
+constexpr int kMaxGroups = 64;
+struct RouterCfg {
+    int score_func = 0;               // 0 softmax, 1 sigmoid
+    const float *sel_bias = nullptr;  // [E] added to selection keys only
+    int n_group = 0;                  // > 1: group-limited selection
+    int topk_group = 0;
+};
+
 hipError_t launch_router_topk(const Shape &s, const void *X, const void *Wr, const float *bias,
                               float routed_scale, float *logits_out, int32_t *ids_out, float *wts_out,
-                              const RouterStats &rs, const Workspace &ws, hipStream_t st);
+                              const RouterStats &rs, const RouterCfg &rc, const Workspace &ws, hipStream_t st);
 hipError_t launch_route_scan(const Shape &s, int32_t *counts_out, int32_t *offsets_out,
                              const RouterStats &rs, const Workspace &ws, hipStream_t st);
 hipError_t launch_route_permute(const Shape &s, int32_t *perm_out, int32_t *inv_out,

@@ -54,6 +54,35 @@ struct Slice<float> {
     }
 };
 
+// e^x for x in [-80, 80] from IEEE operations only (so it is the same bit for
+// bit wherever fma, rint, ldexp and the basic operations are correctly
+// rounded): x = n ln2 + r with ln2 split in two for an exact-enough r,
+// |r| <= ln2/2, e^r by its Taylor series to degree 8 (Horner, fused
+// multiply-adds), then scaled by 2^n.
+__device__ __forceinline__ float exp_ieee(float x)
+{
+    const float n = __builtin_rintf(x * 1.44269502f);
+    float r = __builtin_fmaf(-n, 0.693145751953125f, x);  // ln2 high part (exact product)
+    r = __builtin_fmaf(-n, 1.42860682e-06f, r);           // ln2 low part
+    float p = 2.48015873e-05f;                             // 1/8!
+    p = __builtin_fmaf(p, r, 1.98412698e-04f);             // 1/7!
+    p = __builtin_fmaf(p, r, 1.38888889e-03f);             // 1/6!
+    p = __builtin_fmaf(p, r, 8.33333333e-03f);             // 1/5!
+    p = __builtin_fmaf(p, r, 4.16666667e-02f);             // 1/4!
+    p = __builtin_fmaf(p, r, 1.66666667e-01f);             // 1/3!
+    p = __builtin_fmaf(p, r, 0.5f);
+    p = __builtin_fmaf(p, r, 1.0f);
+    p = __builtin_fmaf(p, r, 1.0f);
+    return __builtin_ldexpf(p, (int)n);
+}
+
+// sigmoid with the logit clamped to [-80, 80] (no subnormal results)
+__device__ __forceinline__ float sigmoid_ieee(float l)
+{
+    const float c = fminf(fmaxf(l, -80.0f), 80.0f);
+    return 1.0f / (1.0f + exp_ieee(-c));
+}
+
 // (va, ia) ranks before (vb, ib): larger logit first, then lower expert index.
 __device__ __forceinline__ bool ranks_before(float va, int ia, float vb, int ib)
 {
@@ -70,7 +99,8 @@ __global__ __launch_bounds__(256) void router_topk_kernel(
     int H, int E, int k, float routed_scale, int32_t *__restrict__ ids, float *__restrict__ wts,
     int32_t *__restrict__ ids_out, float *__restrict__ wts_out, float *__restrict__ logits_out,
     int32_t *__restrict__ blk_counts, const int32_t *__restrict__ stats_mask, float *__restrict__ blk_prob,
-    int32_t *__restrict__ blk_mcnt, int32_t *__restrict__ blk_ntok)
+    int32_t *__restrict__ blk_mcnt, int32_t *__restrict__ blk_ntok, int score_func,
+    const float *__restrict__ sel_bias, int n_group, int topk_group)
 {
     constexpr int TG = RT < 8 ? RT : 8;  // tokens per pass
     constexpr int EG = 4;                // experts per pass
@@ -82,6 +112,10 @@ __global__ __launch_bounds__(256) void router_topk_kernel(
     __shared__ float s_prob[RT][kMaxExperts];
     __shared__ int s_mhist[kMaxExperts];
     __shared__ int s_ntok;
+    // group-limited selection: selection keys and kept groups of each wave's token
+    __shared__ float s_key[4][kMaxExperts];
+    __shared__ int s_gkeep[4][kMaxGroups];
+    const bool sigm = score_func == 1;
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
@@ -199,6 +233,15 @@ __global__ __launch_bounds__(256) void router_topk_kernel(
             v[q] = e < E ? lrow[e] : -FLT_MAX;
             taken[q] = e >= E;
         }
+        // scores (weights) and selection keys
+        float sc[4], key[4];
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+            const int e = lane + 64 * q;
+            sc[q] = (e < E && sigm) ? sigmoid_ieee(v[q]) : v[q];
+            key[q] = sc[q];
+            if (e < E && sel_bias) key[q] = key[q] + sel_bias[e];
+        }
         const bool counted = stats && (!stats_mask || stats_mask[t] != 0);  // wave-uniform
         if (stats) {
             // probabilities over all E experts (zero rows for tokens not counted)
@@ -222,14 +265,73 @@ __global__ __launch_bounds__(256) void router_topk_kernel(
             }
             if (counted && lane == 0) atomicAdd(&s_ntok, 1);
         }
+        if (n_group > 1) {
+            // group score: fp32 sum of the group's best two keys (one if the
+            // group has one expert), best first
+            float *kr = s_key[wave];
+#pragma unroll
+            for (int q = 0; q < 4; q++)
+                if (lane + 64 * q < E) kr[lane + 64 * q] = key[q];
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+            const int gsz = E / n_group;
+            const int gtop = min(2, gsz);
+            float gsc = -INFINITY;
+            if (lane < n_group) {
+                float sum = 0.0f, pv = INFINITY;
+                int pi = -1;
+                for (int r = 0; r < gtop; r++) {
+                    float bv = -INFINITY;
+                    int bi = INT_MAX;
+                    for (int x = 0; x < gsz; x++) {
+                        const int e = lane * gsz + x;
+                        const float kv = kr[e];
+                        if (ranks_before(pv, pi, kv, e) && ranks_before(kv, e, bv, bi)) {
+                            bv = kv;
+                            bi = e;
+                        }
+                    }
+                    sum += bv;
+                    pv = bv;
+                    pi = bi;
+                }
+                gsc = sum;
+            }
+            // keep the topk_group best groups (ties to the lower group)
+            bool kept = false;
+            for (int r = 0; r < topk_group; r++) {
+                float bv = (lane < n_group && !kept) ? gsc : -INFINITY;
+                int bi = (lane < n_group && !kept) ? lane : INT_MAX;
+#pragma unroll
+                for (int d = 32; d >= 1; d >>= 1) {
+                    const float ov = __shfl_xor(bv, d, 64);
+                    const int oi = __shfl_xor(bi, d, 64);
+                    if (ranks_before(ov, oi, bv, bi)) {
+                        bv = ov;
+                        bi = oi;
+                    }
+                }
+                if (lane == bi) kept = true;
+            }
+            if (lane < n_group) s_gkeep[wave][lane] = kept ? 1 : 0;
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+#pragma unroll
+            for (int q = 0; q < 4; q++) {
+                const int e = lane + 64 * q;
+                if (e < E && !s_gkeep[wave][e / gsz]) taken[q] = true;
+            }
+        }
         for (int s = 0; s < k; s++) {
             float bv = -FLT_MAX;
             int bi = INT_MAX;
 #pragma unroll
             for (int q = 0; q < 4; q++) {
                 const int e = lane + 64 * q;
-                if (!taken[q] && ranks_before(v[q], e, bv, bi)) {
-                    bv = v[q];
+                if (!taken[q] && ranks_before(key[q], e, bv, bi)) {
+                    bv = key[q];
                     bi = e;
                 }
             }
@@ -242,28 +344,38 @@ __global__ __launch_bounds__(256) void router_topk_kernel(
                     bi = oi;
                 }
             }
-            // every lane now holds the winner (bv, bi)
+            // every lane now holds the winner (bv, bi); its owner records the
+            // winner's unbiased score (the logit for softmax)
 #pragma unroll
             for (int q = 0; q < 4; q++)
-                if (lane + 64 * q == bi) taken[q] = true;
+                if (lane + 64 * q == bi) {
+                    taken[q] = true;
+                    s_sel[wave][s] = sc[q];
+                }
             if (lane == 0) {
                 ids[(int64_t)t * k + s] = bi;
                 if (ids_out) ids_out[(int64_t)t * k + s] = bi;
-                s_sel[wave][s] = bv;
                 atomicAdd(&s_hist[bi], 1);
                 if (counted) atomicAdd(&s_mhist[bi], 1);
             }
         }
-        __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-        // weights: exp(l_s - l_0) / sum, times the routed scale
-        const float m = s_sel[wave][0];
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+        // weights, times the routed scale: softmax over the selected logits
+        // (relative to their largest), or the selected sigmoid scores over
+        // their sum
+        float m = -FLT_MAX;
+        for (int s = lane; s < k; s += 64) m = fmaxf(m, s_sel[wave][s]);
+#pragma unroll
+        for (int d = 32; d >= 1; d >>= 1) m = fmaxf(m, __shfl_xor(m, d, 64));
         float psum = 0.0f;
-        for (int s = lane; s < k; s += 64) psum += __expf(s_sel[wave][s] - m);
+        for (int s = lane; s < k; s += 64) psum += sigm ? s_sel[wave][s] : __expf(s_sel[wave][s] - m);
 #pragma unroll
         for (int d = 32; d >= 1; d >>= 1) psum += __shfl_xor(psum, d, 64);
         for (int s = lane; s < k; s += 64) {
-            const float w = routed_scale * (__expf(s_sel[wave][s] - m) / psum);
+            const float num = sigm ? s_sel[wave][s] : __expf(s_sel[wave][s] - m);
+            const float w = routed_scale * (num / psum);
             wts[(int64_t)t * k + s] = w;
             if (wts_out) wts_out[(int64_t)t * k + s] = w;
         }
@@ -456,14 +568,15 @@ __global__ __launch_bounds__(256) void route_permute_kernel(
 
 hipError_t launch_router_topk(const Shape &s, const void *X, const void *Wr, const float *bias,
                               float routed_scale, float *logits_out, int32_t *ids_out, float *wts_out,
-                              const RouterStats &rs, const Workspace &ws, hipStream_t st)
+                              const RouterStats &rs, const RouterCfg &rc, const Workspace &ws, hipStream_t st)
 {
     dim3 grid(s.nblk), block(256);
     float *bp = rs.on() ? ws.blk_prob : nullptr;
 #define MOE_ROUTER_LAUNCH(TIN, RT)                                                                      \
     hipLaunchKernelGGL((router_topk_kernel<TIN, RT>), grid, block, 0, st, (const TIN *)X, (const TIN *)Wr, \
                        bias, (int)s.T, (int)s.H, (int)s.E, s.k, routed_scale, ws.ids, ws.wts, ids_out,  \
-                       wts_out, logits_out, ws.blk_counts, rs.mask, bp, ws.blk_mcnt, ws.blk_ntok)
+                       wts_out, logits_out, ws.blk_counts, rs.mask, bp, ws.blk_mcnt, ws.blk_ntok,     \
+                       rc.score_func, rc.sel_bias, rc.n_group, rc.topk_group)
     static_assert(kRouterMaxTokensPerBlock == 4, "router blocks of 1 or 4 tokens");
     if (s.dtype == 0) {
         if (s.rtok == 1) MOE_ROUTER_LAUNCH(__bf16, 1);

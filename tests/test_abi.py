@@ -211,3 +211,36 @@ def test_router_stats_outputs_must_be_aligned():
     o.router_prob_mean = (1 << 40) + (7 << 30)
     o.stats_mask = (1 << 40) + (7 << 30) + 4096
     assert call(opts=o)[0] == -3  # valid: stops at the (too small) workspace, before any HIP call
+
+
+def scoring_opts(score_func=moe.SCORE_SIGMOID, n_group=0, topk_group=0):
+    o = good_opts(nbytes=100)  # valid calls stop at the workspace check, before any HIP call
+    o.score_func = score_func
+    o.selection_bias = (1 << 40) + (7 << 30)
+    o.n_group = n_group
+    o.topk_group = topk_group
+    return o
+
+
+def test_scoring_options_are_checked():
+    E, k = 16, 4
+    assert call(E=E, k=k, opts=scoring_opts())[0] == -3
+    assert call(E=E, k=k, opts=scoring_opts(n_group=4, topk_group=2))[0] == -3
+    assert call(E=E, k=k, opts=scoring_opts(n_group=1, topk_group=0))[0] == -3  # one group: no grouping
+    rc, msg = call(E=E, k=k, opts=scoring_opts(score_func=2))
+    assert rc == -1 and "score_func" in msg
+    rc, msg = call(E=E, k=k, opts=scoring_opts(n_group=3, topk_group=1))
+    assert rc == -1 and "multiple of n_group" in msg
+    for tg in (0, 5):
+        rc, msg = call(E=E, k=k, opts=scoring_opts(n_group=4, topk_group=tg))
+        assert rc == -1 and "topk_group" in msg
+    rc, msg = call(E=E, k=k, opts=scoring_opts(n_group=8, topk_group=1))  # 2 experts < k
+    assert rc == -1 and "k = 4" in msg
+    rc, msg = call(E=256, k=k, opts=scoring_opts(n_group=128, topk_group=4))
+    assert rc == -2 and "n_group" in msg
+    assert call(E=E, k=k, opts=scoring_opts(n_group=-2))[0] == -1
+    o = scoring_opts()
+    o.selection_bias = (1 << 40) + (7 << 30) + 2
+    assert call(E=E, k=k, opts=o)[0] == -4
+    rc, msg = call(E=E, k=k, opts=scoring_opts(), out=(1 << 40) + (7 << 30))  # out on top of the bias
+    assert rc == -1 and "overlaps" in msg
