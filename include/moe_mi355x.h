@@ -64,8 +64,9 @@ typedef enum moe_dtype {
 /* How router logits become expert scores (opts->score_func). */
 typedef enum moe_score_func {
     MOE_SCORE_SOFTMAX = 0, /* weights: softmax over the selected logits          */
-    MOE_SCORE_SIGMOID = 1  /* scores sigmoid(logit); weights: the selected       */
+    MOE_SCORE_SIGMOID = 1, /* scores sigmoid(logit); weights: the selected       */
                            /* scores divided by their sum                         */
+    MOE_SCORE_SPARSEMIXER = 2 /* PhiMoE's sparsemixer at inference (see below)   */
 } moe_score_func;
 
 /* Storage of the routed experts' weights (gate_up, down). */
@@ -162,11 +163,24 @@ typedef struct moe_opts {
      * to the lower group) are kept and the k experts are chosen among them.
      * Requires E % n_group == 0, 1 <= topk_group <= n_group and
      * k <= topk_group * E / n_group; otherwise MOE_ERR_INVALID_ARG.
-     * selection_bias values must be finite. */
+     * selection_bias values must be finite.
+     *
+     * score_func = MOE_SCORE_SPARSEMIXER (PhiMoE page, section 6, the
+     * sparsemixer router at inference; the threshold is the config's
+     * router_jitter_noise): experts are chosen greedily by logit as for
+     * softmax, and round j's weight is a softmax of its own. With m the
+     * logit of the expert chosen in round j and R the experts not chosen in
+     * earlier rounds, the round keeps the experts e of R with
+     * NOT ((m - l[e]) / max(|l[e]|, m) > 2 * jitter_eps) (fp32 subtraction,
+     * correctly rounded fp32 division, so a 0/0 keeps the expert), and
+     * w_j = routed_scale / sum over the kept e of exp(l[e] - m). The weights
+     * need not sum to routed_scale. No selection_bias or groups with it. */
     int32_t score_func;           /* moe_score_func                            */
     const float *selection_bias;  /* [E] fp32 added to selection keys, or NULL */
     int32_t n_group;              /* 0 or 1: no grouping                        */
     int32_t topk_group;
+    float jitter_eps;             /* sparsemixer threshold; moe_opts_init sets */
+                                  /* 0.01 (PhiMoE's router_jitter_noise)       */
 } moe_opts;
 
 /* Stages of moe_forward, in launch order. */

@@ -56,7 +56,8 @@ def _load():
         lib.oracle_exp_f32.argtypes = [vp, i64, vp]
         lib.oracle_sigmoid_scores.argtypes = [vp, i64, vp]
         lib.oracle_select_scored.argtypes = [vp, i64, i64, i32, f32, i32, vp, i32, i32, vp, vp]
-        for f in (lib.oracle_exp_f32, lib.oracle_sigmoid_scores, lib.oracle_select_scored,
+        lib.oracle_select_sparsemixer.argtypes = [vp, i64, i64, i32, f32, f32, vp, vp]
+        for f in (lib.oracle_select_sparsemixer, lib.oracle_exp_f32, lib.oracle_sigmoid_scores, lib.oracle_select_scored,
                   lib.oracle_router_logits, lib.oracle_select_topk, lib.oracle_route,
                   lib.oracle_moe_tokens, lib.oracle_num_threads, lib.oracle_e4m3_values,
                   lib.oracle_quantize_e4m3_rows, lib.oracle_moe_tokens_e4m3, lib.oracle_router_stats):
@@ -145,6 +146,18 @@ def select_scored(logits: np.ndarray, k: int, routed_scale: float = 1.0, score_f
     w = np.empty((T, k), dtype=np.float32)
     _check(_load().oracle_select_scored(_p(logits), T, E, int(k), float(routed_scale), sf, _p(selection_bias),
                                         int(n_group), int(topk_group), _p(ids), _p(w)), "select_scored")
+    return ids, w
+
+
+def select_sparsemixer(logits: np.ndarray, k: int, routed_scale: float = 1.0, jitter_eps: float = 0.01):
+    """PhiMoE's sparsemixer router at inference: ids [T, k] int32 (greedy by
+    logit) and weights [T, k] float32 (each round's own softmax value)."""
+    logits = np.ascontiguousarray(logits, dtype=np.float32)
+    T, E = logits.shape
+    ids = np.empty((T, k), dtype=np.int32)
+    w = np.empty((T, k), dtype=np.float32)
+    _check(_load().oracle_select_sparsemixer(_p(logits), T, E, int(k), float(routed_scale), float(jitter_eps),
+                                             _p(ids), _p(w)), "select_sparsemixer")
     return ids, w
 
 

@@ -653,3 +653,51 @@ int oracle_select_scored(const float *logits, int64_t T, int64_t E, int k, float
     }
     return OR_OK;
 }
+
+/*
+ * PhiMoE's sparsemixer router at inference (PhiMoE page, section 6: greedy
+ * top-1, mask the chosen expert, take the next; each chosen expert's weight
+ * comes out of a softmax; config table, section 3: router_jitter_noise 0.01
+ * is the epsilon handed to sparsemixer). The page does not print which
+ * experts enter each softmax; the published sparsemixer takes, in round j
+ * with winner logit m over the experts not chosen before, the experts whose
+ * relative gap (m - l[e]) / max(|l[e]|, m) is NOT above 2 * jitter_eps, and
+ * the weight is that softmax's value at the winner. k rounds generalise the
+ * page's two. The gap test decides membership, so it is taken in fp32 (a
+ * 0/0 gap is NaN, which is not above the threshold: the expert stays); the
+ * softmax is evaluated in fp64.
+ */
+int oracle_select_sparsemixer(const float *logits, int64_t T, int64_t E, int k, float routed_scale,
+                              float jitter_eps, int32_t *ids, float *weights)
+{
+    if (!logits || !ids || !weights || T < 0 || E <= 0 || E > 4096 || k < 1 || k > E || !(jitter_eps >= 0.0f))
+        return OR_BAD;
+    const float thr = 2.0f * jitter_eps;
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; t++) {
+        const float *l = logits + t * E;
+        unsigned char chosen[4096];
+        for (int64_t e = 0; e < E; e++)
+            chosen[e] = 0;
+        for (int j = 0; j < k; j++) {
+            int64_t w = -1;
+            for (int64_t e = 0; e < E; e++)
+                if (!chosen[e] && (w < 0 || before(l[e], e, l[w], w)))
+                    w = e;
+            const float m = l[w];
+            double z = 0.0;
+            for (int64_t e = 0; e < E; e++) {
+                if (chosen[e])
+                    continue;
+                const float a = fabsf(l[e]);
+                const float gap = (m - l[e]) / (a > m ? a : m);
+                if (!(gap > thr))
+                    z += exp((double)l[e] - (double)m);
+            }
+            ids[t * k + j] = (int32_t)w;
+            weights[t * k + j] = (float)((double)routed_scale / z);
+            chosen[w] = 1;
+        }
+    }
+    return OR_OK;
+}

@@ -14,7 +14,7 @@ import numpy as np
 
 __all__ = ["moe_forward", "workspace_bytes", "quantize_fp8_rows", "MoeError", "load_library", "LIB_PATH",
            "FLAG_FORCE_TILED", "FLAG_FORCE_SKINNY", "WEIGHTS_NATIVE", "WEIGHTS_FP8_E4M3",
-           "SCORE_SOFTMAX", "SCORE_SIGMOID",
+           "SCORE_SOFTMAX", "SCORE_SIGMOID", "SCORE_SPARSEMIXER",
            "bf16_bits_to_tensor", "EXPORTS"]
 
 # MOE_MI355X_LIB may point at another build of the same library (tuning builds)
@@ -29,6 +29,7 @@ WEIGHTS_NATIVE = 0
 WEIGHTS_FP8_E4M3 = 1
 SCORE_SOFTMAX = 0
 SCORE_SIGMOID = 1
+SCORE_SPARSEMIXER = 2
 EXPORTS = ("moe_opts_init", "moe_workspace_bytes", "moe_forward", "moe_quantize_fp8_rows", "moe_last_error")
 STAGES = ("router", "scan", "permute", "gate_up", "down", "shared_gate_up", "shared_down", "combine")
 STAGE_EVENTS = len(STAGES) + 1
@@ -70,6 +71,7 @@ class MoeOpts(ctypes.Structure):
         ("selection_bias", ctypes.c_void_p),
         ("n_group", ctypes.c_int32),
         ("topk_group", ctypes.c_int32),
+        ("jitter_eps", ctypes.c_float),
     ]
 
 
@@ -167,7 +169,7 @@ def moe_forward(hidden, router_w, gate_up, down, k: int, *, routed_scale: float 
                 shared_gate_up=None, shared_down=None, flags: int = 0, return_routing: bool = False,
                 out=None, workspace=None, stream=None, stage_events=None, gate_up_scale=None, down_scale=None,
                 router_stats: bool = False, stats_mask=None, score_func: str = "softmax",
-                selection_bias=None, n_group: int = 0, topk_group: int = 0):
+                selection_bias=None, n_group: int = 0, topk_group: int = 0, jitter_eps: float | None = None):
     """Run the MoE layer on torch tensors already on the GPU.
 
     hidden [T, H], router_w [E, H], gate_up [E, 2I, H], down [E, H, I] (all
@@ -181,7 +183,10 @@ def moe_forward(hidden, router_w, gate_up, down, k: int, *, routed_scale: float 
     their logits and weights them by the selected scores over their sum;
     ``selection_bias`` [E] fp32 is added to the scores for selection only;
     ``n_group`` > 1 with ``topk_group`` limits selection to the best
-    topk_group of n_group equal expert groups. Returns out [T, H] (and a dict of routing tensors when
+    topk_group of n_group equal expert groups. ``score_func`` "sparsemixer"
+    is PhiMoE's router at inference: greedy by logit, each round's weight a
+    softmax over the unchosen experts within the relative threshold
+    2 * ``jitter_eps`` (default 0.01) of that round's winner. Returns out [T, H] (and a dict of routing tensors when
     ``return_routing`` or ``router_stats``). Work is enqueued on ``stream``
     (default: torch's current stream)."""
     import torch
@@ -219,7 +224,7 @@ def moe_forward(hidden, router_w, gate_up, down, k: int, *, routed_scale: float 
         raise ValueError("shape mismatch among hidden, router_w, gate_up, down")
     o.routed_scale = float(routed_scale)
     o.flags = int(flags)
-    funcs = {"softmax": SCORE_SOFTMAX, "sigmoid": SCORE_SIGMOID}
+    funcs = {"softmax": SCORE_SOFTMAX, "sigmoid": SCORE_SIGMOID, "sparsemixer": SCORE_SPARSEMIXER}
     if score_func not in funcs:
         raise ValueError(f"score_func must be one of {sorted(funcs)}")
     o.score_func = funcs[score_func]
@@ -230,6 +235,8 @@ def moe_forward(hidden, router_w, gate_up, down, k: int, *, routed_scale: float 
         o.selection_bias = selection_bias.data_ptr()
     o.n_group = int(n_group)
     o.topk_group = int(topk_group)
+    if jitter_eps is not None:
+        o.jitter_eps = float(jitter_eps)
     if router_bias is not None:
         router_bias = router_bias.to(dtype=torch.float32).contiguous()
         o.router_bias = router_bias.data_ptr()

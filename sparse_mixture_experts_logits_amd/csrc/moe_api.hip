@@ -76,8 +76,15 @@ int check_shape(int64_t T, int64_t H, int64_t I, int64_t E, int32_t k, const moe
             return fail(MOE_ERR_INVALID_ARG, "unknown flag bits 0x%x", opts->flags);
         if ((opts->flags & MOE_FLAG_FORCE_TILED) && (opts->flags & MOE_FLAG_FORCE_SKINNY))
             return fail(MOE_ERR_INVALID_ARG, "MOE_FLAG_FORCE_TILED and MOE_FLAG_FORCE_SKINNY both set");
-        if (opts->score_func != MOE_SCORE_SOFTMAX && opts->score_func != MOE_SCORE_SIGMOID)
+        if (opts->score_func != MOE_SCORE_SOFTMAX && opts->score_func != MOE_SCORE_SIGMOID &&
+            opts->score_func != MOE_SCORE_SPARSEMIXER)
             return fail(MOE_ERR_INVALID_ARG, "unknown score_func %d", opts->score_func);
+        if (opts->score_func == MOE_SCORE_SPARSEMIXER) {
+            if (!isfinite(opts->jitter_eps) || opts->jitter_eps < 0.0f)
+                return fail(MOE_ERR_INVALID_ARG, "jitter_eps must be finite and >= 0");
+            if (opts->selection_bias || opts->n_group > 1)
+                return fail(MOE_ERR_INVALID_ARG, "sparsemixer scoring takes no selection_bias or groups");
+        }
         if (opts->n_group < 0) return fail(MOE_ERR_INVALID_ARG, "n_group = %d is negative", opts->n_group);
         if (opts->n_group > 1) {
             if (opts->n_group > moe::kMaxGroups)
@@ -175,6 +182,7 @@ void moe_opts_init(moe_opts *opts)
     opts->struct_size = sizeof(moe_opts);
     opts->dtype = MOE_BF16;
     opts->routed_scale = 1.0f;
+    opts->jitter_eps = 0.01f;
 }
 
 const char *moe_last_error(void) { return g_err; }
@@ -284,6 +292,7 @@ int moe_forward(const void *hidden, const void *router_w, const void *gate_up, c
     rcfg.sel_bias = opts->selection_bias;
     rcfg.n_group = opts->n_group > 1 ? opts->n_group : 0;
     rcfg.topk_group = opts->topk_group;
+    rcfg.jitter_eps = opts->jitter_eps;
     if ((rc = check(moe::launch_router_topk(s, hidden, router_w, opts->router_bias, opts->routed_scale,
                                             opts->router_logits, opts->topk_ids, opts->topk_weights, rs, rcfg, ws,
                                             st),

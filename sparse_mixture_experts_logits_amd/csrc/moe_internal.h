@@ -117,10 +117,11 @@ struct RouterStats {
 // Scoring variant of the router (softmax by default).
 constexpr int kMaxGroups = 64;
 struct RouterCfg {
-    int score_func = 0;               // 0 softmax, 1 sigmoid
+    int score_func = 0;               // 0 softmax, 1 sigmoid, 2 sparsemixer
     const float *sel_bias = nullptr;  // [E] added to selection keys only
     int n_group = 0;                  // > 1: group-limited selection
     int topk_group = 0;
+    float jitter_eps = 0.0f;          // sparsemixer threshold
 };
 
 hipError_t launch_router_topk(const Shape &s, const void *X, const void *Wr, const float *bias,

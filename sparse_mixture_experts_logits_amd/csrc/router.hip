@@ -100,7 +100,7 @@ __global__ __launch_bounds__(256) void router_topk_kernel(
     int32_t *__restrict__ ids_out, float *__restrict__ wts_out, float *__restrict__ logits_out,
     int32_t *__restrict__ blk_counts, const int32_t *__restrict__ stats_mask, float *__restrict__ blk_prob,
     int32_t *__restrict__ blk_mcnt, int32_t *__restrict__ blk_ntok, int score_func,
-    const float *__restrict__ sel_bias, int n_group, int topk_group)
+    const float *__restrict__ sel_bias, int n_group, int topk_group, float jitter_eps)
 {
     constexpr int TG = RT < 8 ? RT : 8;  // tokens per pass
     constexpr int EG = 4;                // experts per pass
@@ -116,6 +116,8 @@ __global__ __launch_bounds__(256) void router_topk_kernel(
     __shared__ float s_key[4][kMaxExperts];
     __shared__ int s_gkeep[4][kMaxGroups];
     const bool sigm = score_func == 1;
+    const bool smix = score_func == 2;
+    const float thr = 2.0f * jitter_eps;
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
@@ -344,13 +346,29 @@ __global__ __launch_bounds__(256) void router_topk_kernel(
                     bi = oi;
                 }
             }
-            // every lane now holds the winner (bv, bi); its owner records the
-            // winner's unbiased score (the logit for softmax)
+            // every lane now holds the winner (bv, bi)
+            if (smix) {
+                // sparsemixer round: a softmax, taken at the winner, over the
+                // experts not chosen yet whose logit is within the relative
+                // threshold of the winner's (bv is the winner's logit here)
+                float z = 0.0f;
+#pragma unroll
+                for (int q = 0; q < 4; q++)
+                    if (!taken[q]) {
+                        const float f = fmaxf(fabsf(v[q]), bv);
+                        if (!((bv - v[q]) / f > thr)) z += __expf(v[q] - bv);
+                    }
+#pragma unroll
+                for (int d = 32; d >= 1; d >>= 1) z += __shfl_xor(z, d, 64);
+                if (lane == 0) s_sel[wave][s] = 1.0f / z;
+            }
+            // the winner's owner marks it and records its unbiased score (the
+            // logit for softmax)
 #pragma unroll
             for (int q = 0; q < 4; q++)
                 if (lane + 64 * q == bi) {
                     taken[q] = true;
-                    s_sel[wave][s] = sc[q];
+                    if (!smix) s_sel[wave][s] = sc[q];
                 }
             if (lane == 0) {
                 ids[(int64_t)t * k + s] = bi;
@@ -363,8 +381,17 @@ __global__ __launch_bounds__(256) void router_topk_kernel(
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
         // weights, times the routed scale: softmax over the selected logits
-        // (relative to their largest), or the selected sigmoid scores over
-        // their sum
+        // (relative to their largest), the selected sigmoid scores over
+        // their sum, or each sparsemixer round's own softmax value
+        if (smix) {
+            for (int s = lane; s < k; s += 64) {
+                const float w = routed_scale * s_sel[wave][s];
+                wts[(int64_t)t * k + s] = w;
+                if (wts_out) wts_out[(int64_t)t * k + s] = w;
+            }
+            __builtin_amdgcn_wave_barrier();
+            continue;
+        }
         float m = -FLT_MAX;
         for (int s = lane; s < k; s += 64) m = fmaxf(m, s_sel[wave][s]);
 #pragma unroll
@@ -576,7 +603,7 @@ hipError_t launch_router_topk(const Shape &s, const void *X, const void *Wr, con
     hipLaunchKernelGGL((router_topk_kernel<TIN, RT>), grid, block, 0, st, (const TIN *)X, (const TIN *)Wr, \
                        bias, (int)s.T, (int)s.H, (int)s.E, s.k, routed_scale, ws.ids, ws.wts, ids_out,  \
                        wts_out, logits_out, ws.blk_counts, rs.mask, bp, ws.blk_mcnt, ws.blk_ntok,     \
-                       rc.score_func, rc.sel_bias, rc.n_group, rc.topk_group)
+                       rc.score_func, rc.sel_bias, rc.n_group, rc.topk_group, rc.jitter_eps)
     static_assert(kRouterMaxTokensPerBlock == 4, "router blocks of 1 or 4 tokens");
     if (s.dtype == 0) {
         if (s.rtok == 1) MOE_ROUTER_LAUNCH(__bf16, 1);

@@ -227,7 +227,7 @@ def test_scoring_options_are_checked():
     assert call(E=E, k=k, opts=scoring_opts())[0] == -3
     assert call(E=E, k=k, opts=scoring_opts(n_group=4, topk_group=2))[0] == -3
     assert call(E=E, k=k, opts=scoring_opts(n_group=1, topk_group=0))[0] == -3  # one group: no grouping
-    rc, msg = call(E=E, k=k, opts=scoring_opts(score_func=2))
+    rc, msg = call(E=E, k=k, opts=scoring_opts(score_func=3))
     assert rc == -1 and "score_func" in msg
     rc, msg = call(E=E, k=k, opts=scoring_opts(n_group=3, topk_group=1))
     assert rc == -1 and "multiple of n_group" in msg
@@ -244,3 +244,21 @@ def test_scoring_options_are_checked():
     assert call(E=E, k=k, opts=o)[0] == -4
     rc, msg = call(E=E, k=k, opts=scoring_opts(), out=(1 << 40) + (7 << 30))  # out on top of the bias
     assert rc == -1 and "overlaps" in msg
+
+
+def test_sparsemixer_options_are_checked():
+    o = moe.new_opts()
+    assert abs(o.jitter_eps - 0.01) < 1e-9  # PhiMoE's router_jitter_noise
+    assert call(E=16, k=2, opts=scoring_opts(score_func=moe.SCORE_SPARSEMIXER))[0] == -1  # no selection bias
+    o = scoring_opts(score_func=moe.SCORE_SPARSEMIXER)
+    o.selection_bias = None
+    assert call(E=16, k=2, opts=o)[0] == -3
+    o.n_group, o.topk_group = 4, 2
+    rc, msg = call(E=16, k=2, opts=o)
+    assert rc == -1 and "sparsemixer" in msg
+    for eps in (-0.5, float("nan"), float("inf")):
+        o = scoring_opts(score_func=moe.SCORE_SPARSEMIXER)
+        o.selection_bias = None
+        o.jitter_eps = eps
+        rc, msg = call(E=16, k=2, opts=o)
+        assert rc == -1 and "jitter_eps" in msg

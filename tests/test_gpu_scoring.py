@@ -1,5 +1,6 @@
 """GPU parity of the router scoring variants (sigmoid scores, a bias that
-steers selection only, group-limited selection) against the oracle.
+steers selection only, group-limited selection, PhiMoE's sparsemixer at
+inference) against the oracle.
 
 Bar: expert ids, counts, offsets and the permutation bit-exact (both sides
 compute the selection keys with the same IEEE fp32 operation sequence);
@@ -43,7 +44,8 @@ def run(inp, sc, flags=0):
     out, r = moe.moe_forward(d(inp.hidden), d(inp.router_w), d(inp.gate_up), d(inp.down), wl.k,
                              routed_scale=wl.routed_scale, router_bias=bias, shared_gate_up=sgu,
                              shared_down=sdn, flags=flags, return_routing=True, score_func=sc["score_func"],
-                             selection_bias=sb, n_group=sc.get("n_group", 0), topk_group=sc.get("topk_group", 0))
+                             selection_bias=sb, n_group=sc.get("n_group", 0), topk_group=sc.get("topk_group", 0),
+                             jitter_eps=sc.get("jitter_eps"))
     torch.cuda.synchronize()
     return out.float().cpu().numpy(), {k: v.cpu().numpy() for k, v in r.items()}
 
@@ -51,8 +53,11 @@ def run(inp, sc, flags=0):
 def check(inp, sc, tokens, what, flags=0):
     wl = inp.wl
     logits = oracle.router_logits(inp.hidden, inp.router_w, inp.bias)
-    ids, w = oracle.select_scored(logits, wl.k, wl.routed_scale, sc["score_func"], sc.get("selection_bias"),
-                                  sc.get("n_group", 0), sc.get("topk_group", 0))
+    if sc["score_func"] == "sparsemixer":
+        ids, w = oracle.select_sparsemixer(logits, wl.k, wl.routed_scale, sc.get("jitter_eps", 0.01))
+    else:
+        ids, w = oracle.select_scored(logits, wl.k, wl.routed_scale, sc["score_func"], sc.get("selection_bias"),
+                                      sc.get("n_group", 0), sc.get("topk_group", 0))
     counts, offsets, perm, inv = oracle.route(ids, wl.E)
     out, got = run(inp, sc, flags)
     assert np.array_equal(got["logits"].view(np.uint32), logits.view(np.uint32)), f"{what}: logits differ"
@@ -91,6 +96,11 @@ SMALL = [
      dict(score_func="sigmoid", selection_bias=sel_bias(32, 6), n_group=4, topk_group=1)),
     ("shared_sigmoid", dict(T=130, H=136, I=72, E=8, k=2, n_shared=2, shared_I=40),
      dict(score_func="sigmoid", selection_bias=sel_bias(8, 7))),
+    # sparsemixer: small router weights put many logits within the threshold
+    ("sparsemixer_decode", dict(T=32, H=512, I=64, E=16, k=2), dict(score_func="sparsemixer")),
+    ("sparsemixer_wide", dict(T=300, H=128, I=32, E=64, k=4), dict(score_func="sparsemixer", jitter_eps=0.2)),
+    ("sparsemixer_ties", dict(T=70, H=64, I=32, E=16, k=2),
+     dict(score_func="sparsemixer", jitter_eps=0.0)),
 ]
 
 
@@ -98,6 +108,9 @@ SMALL = [
 def test_scoring_small(name, kw, sc):
     _say(f"case scoring {name}")
     inp = W.custom_inputs(**kw, std_weight=0.05)
+    if name == "sparsemixer_ties":
+        # a zero router: every logit 0, so every gap is 0/0 and all experts tie
+        inp.router_w[:] = 0
     check(inp, sc, np.arange(kw["T"], dtype=np.int32), name)
 
 
@@ -107,6 +120,14 @@ def test_scoring_tiled_path():
     inp = W.custom_inputs(**kw, std_weight=0.05)
     sc = dict(score_func="sigmoid", selection_bias=sel_bias(16, 8), n_group=4, topk_group=2)
     check(inp, sc, np.arange(kw["T"], dtype=np.int32), "tiled", flags=moe.FLAG_FORCE_TILED)
+
+
+@pytest.mark.parametrize("T", [32, 4096])
+def test_sparsemixer_phimoe_full_size(T):
+    _say(f"case sparsemixer phimoe T={T}")
+    inp = W.make_inputs(W.BY_NAME["phimoe_decode"], T=T)
+    tokens = np.arange(T, dtype=np.int32) if T <= 32 else np.linspace(0, T - 1, 16).astype(np.int32)
+    check(inp, dict(score_func="sparsemixer"), tokens, f"sparsemixer phimoe T={T}")
 
 
 @pytest.mark.parametrize("T", [32, 4096])

@@ -163,3 +163,65 @@ def test_rejects_bad_group_arguments():
     for n_group, topk_group, k in [(3, 1, 1), (4, 0, 1), (4, 5, 1), (4, 1, 3)]:
         with pytest.raises(ValueError):
             oracle.select_scored(l, k, 1.0, "sigmoid", None, n_group, topk_group)
+
+
+# ---------------------------------------------------------------- sparsemixer at inference
+
+
+def test_sparsemixer_page_default_threshold():
+    import json
+    import os
+    facts = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "page_facts.json")))
+    assert facts["phimoe_config"]["router_jitter_noise"] == 0.01
+
+
+def test_sparsemixer_ids_are_greedy_topk():
+    rng = np.random.default_rng(11)
+    logits = (rng.standard_normal((60, 16)) * 1.28).astype(np.float32)
+    logits[5, :3] = logits[5, 7]  # ties: lower index first
+    for k in (1, 2, 4):
+        ids, _ = oracle.select_sparsemixer(logits, k)
+        assert np.array_equal(ids, oracle.select_topk(logits, k)[0])
+
+
+def test_sparsemixer_separated_logits_weigh_one():
+    # gaps far above 2 * eps relative: every round's softmax holds its winner alone
+    l = np.array([[4.0, 2.0, 1.0, -3.0], [-1.0, -2.0, -4.0, -8.0]], np.float32)
+    for eps in (0.0, 0.01, 0.1):
+        ids, w = oracle.select_sparsemixer(l, 2, 1.5, eps)
+        assert np.array_equal(w, np.full((2, 2), 1.5, np.float32))
+
+
+def test_sparsemixer_hand_worked_rounds():
+    l = np.array([[1.0, 0.99, 0.5],      # gap 0.01 <= 0.02: expert 1 joins round 1
+                  [-1.0, -1.01, -3.0],   # gap 0.01/1.01 (|l| is the larger divisor)
+                  [0.0, 0.0, -1.0],      # 0/0 gaps keep the tied zero; then it wins round 2 alone
+                  [2.0, 2.0, 2.0]],      # three-way tie: 1/3, then 1/2, then 1
+                 np.float32)
+    ids, w = oracle.select_sparsemixer(l, 3, 1.0, 0.01)
+    assert ids.tolist() == [[0, 1, 2]] * 4
+    a = 1 / (1 + math.exp(-0.01))
+    expect = [[a, 1.0, 1.0],
+              [1 / (1 + math.exp(-0.010000000000000009)), 1.0, 1.0],
+              [0.5, 1.0, 1.0],
+              [1 / 3, 0.5, 1.0]]
+    assert np.allclose(w, expect, rtol=1e-6, atol=0)
+    # a threshold just under the gap drops expert 1 from round 1
+    ids, w = oracle.select_sparsemixer(l[:1], 2, 1.0, 0.004)
+    assert np.allclose(w, [[1.0, 1.0]])
+
+
+def test_sparsemixer_unbounded_threshold_is_full_softmax():
+    # every unchosen expert passes: round j is the softmax over the experts
+    # left after j removals, evaluated at its winner
+    rng = np.random.default_rng(12)
+    logits = (rng.standard_normal((30, 12)) * 1.5).astype(np.float32)
+    ids, w = oracle.select_sparsemixer(logits, 3, 2.0, 1e30)
+    l = logits.astype(np.float64)
+    for t in range(30):
+        left = list(range(12))
+        for j in range(3):
+            e = ids[t, j]
+            p = np.exp(l[t, e] - np.max(l[t, left])) / np.exp(l[t, left] - np.max(l[t, left])).sum()
+            assert abs(w[t, j] - 2.0 * p) <= 1e-6 * 2.0 * p
+            left.remove(e)
