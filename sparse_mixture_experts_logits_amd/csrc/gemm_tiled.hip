@@ -93,7 +93,17 @@ __device__ __forceinline__ void dma16(const void *gptr, uint32_t lds)
 
 __device__ __forceinline__ uint32_t lds_addr(const void *p) { return (uint32_t)(uintptr_t)p; }
 
-template <int BM, int BN, int WM, int WN, int OCC, bool GATEUP>
+// XT: token rows a tile may carry past BM (0, or 32 for the routed
+// schedule). The routing kernels fold an expert's last rows, when at most XT
+// of them lie past a multiple of BM, into its previous tile instead of
+// opening a tile for them: the expert's weight block is then streamed once
+// for BM + tail rows instead of a second time for a handful of rows. The
+// extra 32-row block costs each wave one more 32x32 MFMA block per step:
+// down: wave (wm, wn) takes output column block wm of its own columns;
+// gate_up: the four waves of a column half take the gate and the up block of
+// its two output column blocks, and the gate blocks reach the matching up
+// waves through LDS in the epilogue.
+template <int BM, int BN, int WM, int WN, int OCC, bool GATEUP, int XT = 0>
 __global__ __launch_bounds__(WM *WN * 64, OCC) void tiled_gemm_kernel(TiledParams p)
 {
     constexpr int NT = WM * WN * 64;
@@ -103,17 +113,30 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void tiled_gemm_kernel(TiledParam
     constexpr int A_INS = BM / RPI / NWAVE;  // copy instructions per wave per stage
     constexpr int B_INS = BN / RPI / NWAVE;
     constexpr int LOADS = A_INS + B_INS;    // vector-memory ops per wave per stage
+    // extra rows: every wave copies XT / NWAVE of them with one instruction
+    // of CH * XT / NWAVE lanes, so all waves issue the same number of copies
+    constexpr int XR = XT / NWAVE;
     static_assert(A_INS >= 1 && B_INS >= 1 && RM >= 1 && RN >= 1, "tile shape");
     static_assert(!GATEUP || (RN % 2 == 0), "gate/up pairing needs an even RN");
+    static_assert(XT == 0 || (XT == 32 && WM == 4 && RN == 4 && XR * CH <= 64), "extra-block layout");
+    (void)NT;
 
-    __shared__ u32x4 sA[STAGES][BM * CH];
+    __shared__ u32x4 sA[STAGES][(BM + XT) * CH];
     __shared__ u32x4 sB[STAGES][BN * CH];
+    constexpr bool XG = XT > 0 && GATEUP;
+    __shared__ float s_xg[XG ? 2 * WN : 1][XG ? 16 * 64 : 1];  // gate halves of the extra block
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
     const int wm = wave / WN;
     const int wn = wave - wm * WN;
+    // this wave's B block for the extra rows (see above) and its LDS row
+    const int jx = GATEUP ? (wm >> 1) + (RN / 2) * (wm & 1) : wm;
+    const int xrow = (GATEUP ? ((jx < RN / 2) ? wn * (BN / 2 / WN) + jx * 32
+                                              : BN / 2 + wn * (BN / 2 / WN) + (jx - RN / 2) * 32)
+                             : wn * (BN / WN) + jx * 32) +
+                     (lane & 31);
 
     // first M-tile of each expert (read through the scalar cache, so the
     // whole LDS is left to the stage ring)
@@ -161,21 +184,31 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void tiled_gemm_kernel(TiledParam
             row0 = mt * BM;
             rows = min(BM, p.dense_rows - row0);
         }
+        const bool xtra = XT > 0 && rows > BM;  // tile-uniform
 
         // ---- per-lane DMA source rows (rows past the tile repeat row 0; dropped later)
+        // logical chunk (of 8 elements) a lane copies for LDS row rr
+        auto chunk_of = [&](int rr) { return (lane % CH) ^ lds_swz(rr); };
         const __bf16 *asrc[A_INS];
-        int alc[A_INS];
 #pragma unroll
         for (int i = 0; i < A_INS; i++) {
             const int rr = RPI * (wave * A_INS + i) + drow;
             const int rc = rr < rows ? rr : 0;
             const int64_t src = p.a_rows ? (int64_t)p.a_rows[row0 + rc] : (int64_t)(row0 + rc);
-            alc[i] = (lane % CH) ^ lds_swz(rr);
-            asrc[i] = p.A + src * p.K + alc[i] * 8;
+            asrc[i] = p.A + src * p.K + chunk_of(rr) * 8;
+        }
+        // extra rows BM + XR*wave + lane/CH, lanes below XR*CH (rows past the
+        // tile repeat row BM)
+        const __bf16 *xsrc = p.A;
+        const bool xlane = lane < XR * CH;
+        const int xrr = BM + XR * wave + (xlane ? drow : 0);
+        if (XT > 0 && xtra) {
+            const int rc = xrr < rows ? xrr : BM;
+            const int64_t src = p.a_rows ? (int64_t)p.a_rows[row0 + rc] : (int64_t)(row0 + rc);
+            xsrc = p.A + src * p.K + chunk_of(xrr) * 8;
         }
         const __bf16 *wbase = p.W + (int64_t)e * p.w_expert_stride;
         const __bf16 *bsrc[B_INS];
-        int blc[B_INS];
 #pragma unroll
         for (int i = 0; i < B_INS; i++) {
             const int rr = RPI * (wave * B_INS + i) + drow;
@@ -189,8 +222,7 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void tiled_gemm_kernel(TiledParam
                 const int n = nb * BN + rr;
                 wrow = n < p.N ? n : 0;
             }
-            blc[i] = (lane % CH) ^ lds_swz(rr);
-            bsrc[i] = wbase + (int64_t)wrow * p.K + blc[i] * 8;
+            bsrc[i] = wbase + (int64_t)wrow * p.K + chunk_of(rr) * 8;
         }
 
         // stage kt -> LDS buffer b: every lane copies 16 bytes. Only a final
@@ -203,13 +235,14 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void tiled_gemm_kernel(TiledParam
 #pragma unroll
             for (int i = 0; i < B_INS; i++)
                 dma16(bsrc[i] + k0, lds_addr(&sB[b][(wave * B_INS + i) * 64]));
+            if (XT > 0 && xtra && xlane) dma16(xsrc + k0, lds_addr(&sA[b][(BM + XR * wave) * CH]));
         };
         auto issue_tail = [&](int kt, int b) {
             const int k0 = kt * BK;
 #pragma unroll
             for (int i = 0; i < A_INS; i++) {
                 u32x4 *dst = &sA[b][(wave * A_INS + i) * 64];
-                if (k0 + alc[i] * 8 < p.K)
+                if (k0 + chunk_of(RPI * (wave * A_INS + i) + drow) * 8 < p.K)
                     dma16(asrc[i] + k0, lds_addr(dst));
                 else
                     dst[lane] = u32x4{0u, 0u, 0u, 0u};
@@ -217,8 +250,15 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void tiled_gemm_kernel(TiledParam
 #pragma unroll
             for (int i = 0; i < B_INS; i++) {
                 u32x4 *dst = &sB[b][(wave * B_INS + i) * 64];
-                if (k0 + blc[i] * 8 < p.K)
+                if (k0 + chunk_of(RPI * (wave * B_INS + i) + drow) * 8 < p.K)
                     dma16(bsrc[i] + k0, lds_addr(dst));
+                else
+                    dst[lane] = u32x4{0u, 0u, 0u, 0u};
+            }
+            if (XT > 0 && xtra && xlane) {
+                u32x4 *dst = &sA[b][(BM + XR * wave) * CH];
+                if (k0 + chunk_of(xrr) * 8 < p.K)
+                    dma16(xsrc + k0, lds_addr(dst));
                 else
                     dst[lane] = u32x4{0u, 0u, 0u, 0u};
             }
@@ -236,33 +276,46 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void tiled_gemm_kernel(TiledParam
             for (int j = 0; j < RN; j++)
 #pragma unroll
                 for (int q = 0; q < 16; q++) acc[i][j][q] = 0.0f;
+        f32x16_t accx;
+#pragma unroll
+        for (int q = 0; q < 16; q++) accx[q] = 0.0f;
 
-        // copy instruction q (A rows first, then B rows) of stage kt into buffer b
+        // copy instruction q (A rows, then B rows, then the extra rows) of stage kt into buffer b
         auto issue_one = [&](int kt, int b, int q) {
             const int k0 = kt * BK;
             if (q < A_INS) dma16(asrc[q] + k0, lds_addr(&sA[b][(wave * A_INS + q) * 64]));
-            else dma16(bsrc[q - A_INS] + k0, lds_addr(&sB[b][(wave * B_INS + q - A_INS) * 64]));
+            else if (q < LOADS) dma16(bsrc[q - A_INS] + k0, lds_addr(&sB[b][(wave * B_INS + q - A_INS) * 64]));
+            else if (xlane) dma16(xsrc + k0, lds_addr(&sA[b][(BM + XR * wave) * CH]));
         };
-        // Consume stage buffer b. When nkt >= 0, the copies of stage nkt into
-        // buffer nb are spread between the MFMAs, one copy per MFMA_PER_COPY
-        // MFMAs, so the copy engine never holds up the fragment reads.
+        // Consume stage buffer b. When nkt >= 0, the LX copies of stage nkt
+        // into buffer nbuf are spread between the MFMAs, one copy per PER
+        // MFMA slots, so the copy engine never holds up the fragment reads.
         // NB (compile time): how many of this wave's RM 32-row blocks hold
         // rows of the tile; the rest skip their fragment reads and MFMAs, so
         // the short last tile of an expert costs less than a full one. The
-        // copies keep their slots either way.
-        auto compute_with = [&](auto nbc, int b, int nkt, int nb) {
+        // copies keep their slots either way. EX: the tile has extra rows.
+        auto compute_stage = [&](auto nbc, auto exc, auto cpc, int b, int nkt, int nbuf) {
             constexpr int NB = decltype(nbc)::value;
-            constexpr int NMMA = (BK / 16) * RM * RN;
-            constexpr int PER = NMMA / LOADS > 0 ? NMMA / LOADS : 1;
-            static_assert(PER * LOADS <= NMMA, "every copy finds an MFMA slot");
+            constexpr bool EX = decltype(exc)::value;
+            constexpr bool CP = decltype(cpc)::value;  // issue the copies of stage nkt
+            constexpr int LX = LOADS + (EX ? 1 : 0);
+            constexpr int NMMA = (BK / 16) * (RM * RN + (EX ? 1 : 0));
+            constexpr int PER = NMMA / LX > 0 ? NMMA / LX : 1;
+            static_assert(PER * LX <= NMMA, "every copy finds an MFMA slot");
 #pragma unroll
             for (int kk = 0; kk < BK / 16; kk++) {
-                bf16x8_t af[RM], bf[RN];
+                bf16x8_t af[RM], bf[RN], ax, bx;
                 const int c = kk * 2 + (lane >> 5);
 #pragma unroll
                 for (int i = 0; i < NB; i++) {
                     const int row = wm * (BM / WM) + i * 32 + (lane & 31);
                     af[i] = as_bf16x8(sA[b][lds_slot(row, c)]);
+                }
+                if (EX) {
+                    // the extra rows and this wave's B block jx for them (read
+                    // again rather than picked from bf[] with a runtime index)
+                    ax = as_bf16x8(sA[b][lds_slot(BM + (lane & 31), c)]);
+                    bx = as_bf16x8(sB[b][lds_slot(xrow, c)]);
                 }
 #pragma unroll
                 for (int j = 0; j < RN; j++) {
@@ -277,47 +330,22 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void tiled_gemm_kernel(TiledParam
                     row += lane & 31;
                     bf[j] = as_bf16x8(sB[b][lds_slot(row, c)]);
                 }
+                auto slot = [&](int mi) {  // compile-time after unrolling
+                    if (CP && (mi + 1) % PER == 0 && (mi + 1) / PER - 1 < LX)
+                        issue_one(nkt, nbuf, (mi + 1) / PER - 1);
+                };
 #pragma unroll
                 for (int i = 0; i < RM; i++)
 #pragma unroll
                     for (int j = 0; j < RN; j++) {
                         if (i < NB)
                             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
-                        const int mi = (kk * RM + i) * RN + j;  // compile-time after unrolling
-                        if ((mi + 1) % PER == 0 && (mi + 1) / PER - 1 < LOADS) issue_one(nkt, nb, (mi + 1) / PER - 1);
+                        slot((kk * (RM * RN + (EX ? 1 : 0)) + i * RN + j));
                     }
-            }
-        };
-        // 32-row blocks of this wave that hold rows of the tile (wave-uniform)
-        const int nvb = max(0, min(RM, (rows - wm * (BM / WM) + 31) / 32));
-        auto compute = [&](int b) {
-            if (nvb == 0) return;
-#pragma unroll
-            for (int kk = 0; kk < BK / 16; kk++) {
-                bf16x8_t af[RM], bf[RN];
-                const int c = kk * 2 + (lane >> 5);
-#pragma unroll
-                for (int i = 0; i < RM; i++) {
-                    const int row = wm * (BM / WM) + i * 32 + (lane & 31);
-                    if (i < nvb) af[i] = as_bf16x8(sA[b][lds_slot(row, c)]);
+                if (EX) {
+                    accx = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ax, bx, accx, 0, 0, 0);
+                    slot(kk * (RM * RN + 1) + RM * RN);
                 }
-#pragma unroll
-                for (int j = 0; j < RN; j++) {
-                    int row;
-                    if (GATEUP) {
-                        constexpr int HW = BN / 2 / WN;  // gate (or up) rows per wave
-                        row = (j < RN / 2) ? wn * HW + j * 32 : BN / 2 + wn * HW + (j - RN / 2) * 32;
-                    } else {
-                        row = wn * (BN / WN) + j * 32;
-                    }
-                    row += lane & 31;
-                    bf[j] = as_bf16x8(sB[b][lds_slot(row, c)]);
-                }
-#pragma unroll
-                for (int i = 0; i < RM; i++)
-#pragma unroll
-                    for (int j = 0; j < RN; j++)
-                        if (i < nvb) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
             }
         };
 
@@ -330,41 +358,47 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void tiled_gemm_kernel(TiledParam
         // Steady state: stage kt is consumed while stages kt+1, kt+2 are in
         // flight and stage kt+3 is issued into the buffer stage kt-1 used.
         // Unrolled by STAGES so every buffer index is a compile-time constant.
-        // (a ragged last stage is always left to the drain)
-        int kt = 0;
+        // (a ragged last stage is always left to the drain). Then the drain:
+        // fewer than 2*STAGES-1 stages remain (kt is a multiple of STAGES, so
+        // stage kt + b lives in buffer b). LX: this wave's copies per stage.
         const int steady_last = nk - (ragged ? 1 : 0);
-        auto steady = [&](auto nbc) {
+        auto kloop = [&](auto nbc, auto exc) {
+            constexpr int LX = LOADS + (decltype(exc)::value ? 1 : 0);
+            using CP = std::integral_constant<bool, true>;
+            using NOCP = std::integral_constant<bool, false>;
+            int kt = 0;
             for (; kt + 2 * STAGES - 1 <= steady_last; kt += STAGES) {
 #pragma unroll
                 for (int b = 0; b < STAGES; b++) {
-                    wait_vm_barrier<(STAGES - 2) * LOADS>();
-                    const int nkt = kt + b + STAGES - 1, nb = (b + STAGES - 1) % STAGES;
-#if MOE_TILED_INTERLEAVE
-                    compute_with(nbc, b, nkt, nb);
-#else
-                    issue(nkt, nb);
-                    compute(b);
-#endif
+                    wait_vm_barrier<(STAGES - 2) * LX>();
+                    compute_stage(nbc, exc, CP{}, b, kt + b + STAGES - 1, (b + STAGES - 1) % STAGES);
                 }
             }
-        };
-        // one copy of the loop per number of live 32-row blocks (RM is 1 or 2)
-        static_assert(RM <= 2, "steady-state variants for up to two 32-row blocks per wave");
-        if (nvb >= RM) steady(std::integral_constant<int, RM>{});
-        else if (nvb == 1) steady(std::integral_constant<int, 1>{});
-        else steady(std::integral_constant<int, 0>{});
-        // Drain: fewer than 2*STAGES-1 stages remain (kt is a multiple of STAGES,
-        // so stage kt + b lives in buffer b).
 #pragma unroll
-        for (int b = 0; b < 2 * STAGES - 1; b++) {
-            if (kt + b >= nk) break;
-            const int ahead = min(STAGES - 2, nk - 1 - (kt + b));
-            if (ahead >= 2 && STAGES >= 4) wait_vm_barrier<(STAGES >= 4 ? 2 : 0) * LOADS>();
-            else if (ahead == 1) wait_vm_barrier<LOADS>();
-            else wait_vm_barrier<0>();
-            if (kt + b + STAGES - 1 < nk) issue_any(kt + b + STAGES - 1, (b + STAGES - 1) % STAGES);
-            compute(b % STAGES);
-        }
+            for (int b = 0; b < 2 * STAGES - 1; b++) {
+                if (kt + b >= nk) break;
+                const int ahead = min(STAGES - 2, nk - 1 - (kt + b));
+                if (ahead >= 2 && STAGES >= 4) wait_vm_barrier<(STAGES >= 4 ? 2 : 0) * LX>();
+                else if (ahead == 1) wait_vm_barrier<LX>();
+                else wait_vm_barrier<0>();
+                if (kt + b + STAGES - 1 < nk) issue_any(kt + b + STAGES - 1, (b + STAGES - 1) % STAGES);
+                compute_stage(nbc, exc, NOCP{}, b % STAGES, 0, 0);
+            }
+        };
+        // 32-row blocks of this wave that hold rows of the tile (wave-uniform);
+        // one copy of the loop per case
+        const int nvb = max(0, min(RM, (rows - wm * (BM / WM) + 31) / 32));
+        static_assert(RM <= 2, "loop variants for up to two 32-row blocks per wave");
+        using I0 = std::integral_constant<int, 0>;
+        using I1 = std::integral_constant<int, 1>;
+        using IRM = std::integral_constant<int, RM>;
+        using F = std::integral_constant<bool, false>;
+        using T = std::integral_constant<bool, true>;
+        if (XT > 0 && xtra) kloop(IRM{}, std::integral_constant<bool, XT != 0>{});
+        else if (nvb >= RM) kloop(IRM{}, F{});
+        else if (nvb == 1) kloop(I1{}, F{});
+        else kloop(I0{}, F{});
+        (void)T{};
 
         // ---- epilogue
         if (GATEUP) {
@@ -386,6 +420,26 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void tiled_gemm_kernel(TiledParam
                         }
                     }
                 }
+            if (XG && xtra) {
+                // gate blocks (even wm) to LDS; the up waves (odd wm) combine
+                float *xg = s_xg[XG ? wn * 2 + (wm >> 1) : 0];
+                if ((wm & 1) == 0) {
+#pragma unroll
+                    for (int q = 0; q < 16; q++) xg[q * 64 + lane] = accx[q];
+                }
+                __syncthreads();
+                if (wm & 1) {
+                    const int c = nb * (BN / 2) + wn * HW + (wm >> 1) * 32 + (lane & 31);
+#pragma unroll
+                    for (int q = 0; q < 16; q++) {
+                        const int rr = BM + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
+                        if (rr < rows && c < p.N) {
+                            const uint32_t hb = f32_to_bf16_bits(silu_f32(xg[q * 64 + lane]) * accx[q]);
+                            reinterpret_cast<uint16_t *>(H)[(int64_t)(row0 + rr) * p.N + c] = (uint16_t)hb;
+                        }
+                    }
+                }
+            }
         } else {
             float *Y = reinterpret_cast<float *>(p.C);
 #pragma unroll
@@ -404,347 +458,17 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void tiled_gemm_kernel(TiledParam
                         }
                     }
                 }
-        }
-    }
-}
-
-// Software-pipelined variant: 4 waves (one per SIMD), 128 tokens x 128
-// weight rows per wave (accumulators live in AGPRs), fragments
-// double-buffered across the two 16-wide halves of a stage, with the barrier
-// between the halves and each stage's copies split over both halves (the
-// schedule is spelled out above the steady-state loop). Per stage it reads
-// 64 KB of fragments from LDS against 96 KB for the 8-wave kernel; it is
-// faster on the balanced prefill shapes and slower on the down GEMM of
-// skewed routing, so it is off by default. The MFMA takes weight rows as its A operand and tokens as B, so a lane of
-// the 32x32 result holds one token and 4 consecutive output columns per
-// group of 4 registers: the epilogue writes packed 8-byte (h) or 16-byte
-// (weighted fp32 slot) chunks and looks up each token's row once.
-template <int BM, int BN, bool GATEUP>
-__global__ __launch_bounds__(256) void tiled_pp_kernel(TiledParams p)
-{
-    constexpr int WM = 2, WN = 2, NT = 256, NWAVE = 4;
-    constexpr int RT = BM / WM / 32;  // 32-token blocks per wave
-    constexpr int RW = BN / WN / 32;  // 32-weight-row blocks per wave
-    constexpr int A_INS = BM / RPI / NWAVE;
-    constexpr int B_INS = BN / RPI / NWAVE;
-    constexpr int LOADS = A_INS + B_INS;
-    static_assert(!GATEUP || (RW % 2 == 0), "gate/up pairing needs an even RW");
-
-    static_assert(BK == 32 && STAGES >= 3, "the pipelined schedule reads two 16-wide halves per stage");
-    __shared__ u32x4 sA[STAGES][BM * CH];  // token rows
-    __shared__ u32x4 sB[STAGES][BN * CH];  // weight rows
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
-    const int wm = wave / WN;
-    const int wn = wave - wm * WN;
-
-    // first M-tile of each expert (read through the scalar cache, so the
-    // whole LDS is left to the stage ring)
-    const int32_t *s_ts = p.tile_start;
-    int n_mtiles;
-    if (p.tiles) {
-        n_mtiles = s_ts[p.E];
-    } else {
-        n_mtiles = (p.dense_rows + BM - 1) / BM;
-    }
-    const int total = n_mtiles * p.NB;
-    const int G = gridDim.x;
-    const int nx = G >> 3;
-    const int xcd = blockIdx.x & 7;
-    const int li = blockIdx.x >> 3;
-    const int nk = (p.K + BK - 1) / BK;
-    const bool ragged = (p.K % BK) != 0;
-    const int drow = lane / CH;
-
-    // Fragment addressing. Every fragment row is (multiple of 32) + lane%32, so
-    // the swizzle term depends on the lane only and a fragment's LDS index is
-    // (block row + lane row) * CH + (chunk ^ swizzle): the block part is a
-    // compile-time constant per block.
-    const int sw = lds_swz(lane & 31);
-    const int lrow = (lane & 31) * CH;
-    int xo[BK / 16];
+            if (XT > 0 && xtra) {
+                const int m = nb * BN + wn * (BN / WN) + jx * 32 + (lane & 31);
 #pragma unroll
-    for (int h = 0; h < BK / 16; h++) xo[h] = lrow + ((2 * h + (lane >> 5)) ^ sw);
-    auto t_blk = [&](int i) { return (wm * (BM / WM) + i * 32) * CH; };
-    auto w_blk = [&](int j) {
-        int row;
-        if (GATEUP) {
-            constexpr int HW = BN / 2 / WN;
-            row = (j < RW / 2) ? wn * HW + j * 32 : BN / 2 + wn * HW + (j - RW / 2) * 32;
-        } else {
-            row = wn * (BN / WN) + j * 32;
-        }
-        return row * CH;
-    };
-
-    for (int r = 0;; r++) {
-        const int id = r * G + xcd * nx + li;
-        if (id >= total) break;
-
-        int e, nb, row0, rows;
-        if (p.tiles) {
-            int lo = 0, hi = p.E;
-            while (hi - lo > 1) {
-                const int mid = (lo + hi) >> 1;
-                if (s_ts[mid] * p.NB <= id) lo = mid; else hi = mid;
-            }
-            e = lo;
-            const int nte = s_ts[e + 1] - s_ts[e];
-            const int local = id - s_ts[e] * p.NB;
-            nb = local / nte;
-            const MTile t = p.tiles[s_ts[e] + (local - nb * nte)];
-            row0 = t.row0;
-            rows = t.rows;
-        } else {
-            e = 0;
-            nb = id / n_mtiles;
-            const int mt = id - nb * n_mtiles;
-            row0 = mt * BM;
-            rows = min(BM, p.dense_rows - row0);
-        }
-
-        // element offsets of the lane's DMA rows: activations are < 2^31
-        // elements and one expert's weights are < 2^31 elements (host checks)
-        uint32_t aoff[A_INS];
-        int alc[A_INS];
-#pragma unroll
-        for (int i = 0; i < A_INS; i++) {
-            const int rr = RPI * (wave * A_INS + i) + drow;
-            const int rc = rr < rows ? rr : 0;
-            const uint32_t src = p.a_rows ? (uint32_t)p.a_rows[row0 + rc] : (uint32_t)(row0 + rc);
-            alc[i] = (lane % CH) ^ lds_swz(rr);
-            aoff[i] = src * (uint32_t)p.K + alc[i] * 8;
-        }
-        const __bf16 *wbase = p.W + (int64_t)e * p.w_expert_stride;
-        uint32_t boff[B_INS];
-        int blc[B_INS];
-#pragma unroll
-        for (int i = 0; i < B_INS; i++) {
-            const int rr = RPI * (wave * B_INS + i) + drow;
-            int wrow;
-            if (GATEUP) {
-                const int half = BN / 2;
-                const int n = nb * half + (rr < half ? rr : rr - half);
-                const int nc = n < p.N ? n : 0;
-                wrow = rr < half ? nc : p.N + nc;
-            } else {
-                const int n = nb * BN + rr;
-                wrow = n < p.N ? n : 0;
-            }
-            blc[i] = (lane % CH) ^ lds_swz(rr);
-            boff[i] = (uint32_t)wrow * (uint32_t)p.K + blc[i] * 8;
-        }
-
-        // copy q (A rows first, then B rows; 64 chunks of 16 bytes each) of
-        // stage kt into buffer b. Only a final partial stage masks lanes (they
-        // zero-fill); every copy instruction still issues, since chunk 0 of
-        // each of its rows is always in range, so each stage is exactly
-        // LOADS vector-memory operations for the vmcnt waits below.
-        auto copy_full = [&](int kt, int b, int q) {
-            const int k0 = kt * BK;
-            if (q < A_INS) dma16(p.A + aoff[q] + k0, lds_addr(&sA[b][(wave * A_INS + q) * 64]));
-            else dma16(wbase + boff[q - A_INS] + k0, lds_addr(&sB[b][(wave * B_INS + q - A_INS) * 64]));
-        };
-        auto copy_any = [&](int kt, int b, int q) {
-            if (ragged && kt == nk - 1) {
-                const int k0 = kt * BK;
-                u32x4 *dst = q < A_INS ? &sA[b][(wave * A_INS + q) * 64] : &sB[b][(wave * B_INS + q - A_INS) * 64];
-                const int lc = q < A_INS ? alc[q] : blc[q - A_INS];
-                if (k0 + lc * 8 < p.K)
-                    dma16(q < A_INS ? (const void *)(p.A + aoff[q] + k0) : (const void *)(wbase + boff[q - A_INS] + k0),
-                          lds_addr(dst));
-                else
-                    dst[lane] = u32x4{0u, 0u, 0u, 0u};
-            } else {
-                copy_full(kt, b, q);
-            }
-        };
-
-        f32x16_t acc[RW][RT];
-#pragma unroll
-        for (int j = 0; j < RW; j++)
-#pragma unroll
-            for (int i = 0; i < RT; i++)
-#pragma unroll
-                for (int q = 0; q < 16; q++) acc[j][i][q] = 0.0f;
-
-        bf16x8_t ft[2][RT], fw[2][RW];
-        // fragments of half h (k16 step) of the stage in buffer b into set f
-        auto frag = [&](int b, int h, int f) {
-            const u32x4 *pa = &sA[b][xo[h]];
-            const u32x4 *pb = &sB[b][xo[h]];
-#pragma unroll
-            for (int i = 0; i < RT; i++) ft[f][i] = as_bf16x8(pa[t_blk(i)]);
-#pragma unroll
-            for (int j = 0; j < RW; j++) fw[f][j] = as_bf16x8(pb[w_blk(j)]);
-        };
-        // MFMAs of fragment set f. With copies, copies q0 .. q0+HALF-1 of
-        // stage nkt into buffer nbuf go out between them, one every PER MFMAs
-        // (compile-time slots), so the vector-memory path is fed evenly.
-        constexpr int HALF = LOADS / 2;
-        static_assert(LOADS % 2 == 0, "copies split evenly over the two halves of a stage");
-        auto mma = [&](int f, bool copies, int nkt, int nbuf, int q0) {
-            constexpr int NM = RW * RT;
-            constexpr int PER = NM / HALF > 0 ? NM / HALF : 1;
-            constexpr int INL = NM / PER < HALF ? NM / PER : HALF;
-#pragma unroll
-            for (int j = 0; j < RW; j++)
-#pragma unroll
-                for (int i = 0; i < RT; i++) {
-                    const int mi = j * RT + i;  // compile-time after unrolling
-                    if (copies && mi % PER == 0 && mi / PER < INL) copy_full(nkt, nbuf, q0 + mi / PER);
-                    acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[f][j], ft[f][i], acc[j][i], 0, 0, 0);
-                }
-#pragma unroll
-            for (int q = INL; q < HALF; q++)
-                if (copies) copy_full(nkt, nbuf, q0 + q);
-        };
-
-        // One 16-wide half in steady state, in a fixed instruction order: the
-        // MFMAs of fragment set f, one fragment read (half rh of buffer rb into
-        // set g) after each of the first RT+RW MFMAs, and the copies q0 ..
-        // q0+HALF-1 of stage nkt into buffer nbuf after every second MFMA of
-        // the rest. Scheduling fences pin the order: left to itself the
-        // compiler bunches the reads and the copies, and a wave that queues
-        // many LDS or memory instructions at once stops issuing MFMAs.
-        auto half_step = [&](int f, int rb, int rh, int g, int nkt, int nbuf, int q0) {
-            constexpr int NM = RW * RT;
-            constexpr int NR = RT + RW;
-            static_assert(NR + 2 * HALF <= NM + 1, "reads and copies fit between the MFMAs");
-            const u32x4 *pa = &sA[rb][xo[rh]];
-            const u32x4 *pb = &sB[rb][xo[rh]];
-            // read r after MFMA r; copy c after MFMA NR + 2c (compile-time slots)
-            auto read_at = [&](int mi) { return mi < NR ? mi : -1; };
-            auto copy_at = [&](int mi) {
-                return ((mi - NR) >= 0 && (mi - NR) % 2 == 0 && (mi - NR) / 2 < HALF) ? (mi - NR) / 2 : -1;
-            };
-#pragma unroll
-            for (int mi = 0; mi < NM; mi++) {
-                const int j = mi / RT, i = mi % RT;
-                acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[f][j], ft[f][i], acc[j][i], 0, 0, 0);
-                __builtin_amdgcn_sched_barrier(0);
-                const int r = read_at(mi);
-                if (r >= 0 && r < RT) {
-                    ft[g][r] = as_bf16x8(pa[t_blk(r)]);
-                    __builtin_amdgcn_sched_barrier(0);
-                } else if (r >= RT) {
-                    fw[g][r - RT] = as_bf16x8(pb[w_blk(r - RT)]);
-                    __builtin_amdgcn_sched_barrier(0);
-                }
-                const int c = copy_at(mi);
-                if (c >= 0) {
-                    copy_full(nkt, nbuf, q0 + c);
-                    __builtin_amdgcn_sched_barrier(0);
-                }
-            }
-        };
-
-        // Schedule of stage s (buffer s % STAGES). The barrier sits between
-        // the two 16-wide halves: before it, the second half of s is read and
-        // the first half's MFMAs run; after it (stage s+1 has landed and
-        // every wave is done with buffer s), the first half of s+1 is read
-        // while the second half's MFMAs run. Copies of stage s+STAGES go
-        // into buffer s in two parts: the first during the second half of s,
-        // the rest during the first half of s+1, so copy traffic is spread
-        // over the whole stage.
-        wait_vm_barrier<0>();  // previous tile fully consumed
-#pragma unroll
-        for (int st = 0; st < STAGES - 1; st++)
-            if (st < nk)
-#pragma unroll
-                for (int q = 0; q < LOADS; q++) copy_any(st, st, q);
-        if (STAGES - 1 < nk)
-#pragma unroll
-            for (int q = 0; q < HALF; q++) copy_any(STAGES - 1, STAGES - 1, q);
-        // stage 0 landed: what may stay in flight is everything issued for later stages
-        if (nk >= STAGES) wait_vm_barrier<(STAGES - 2) * LOADS + HALF>();
-        else if (nk == 3 && STAGES >= 4) wait_vm_barrier<2 * LOADS>();
-        else if (nk == 2) wait_vm_barrier<LOADS>();
-        else wait_vm_barrier<0>();
-        frag(0, 0, 0);
-
-        // Steady state, unrolled by STAGES so buffer indices are constants;
-        // every stage it copies is a full one. Scheduling fences keep each
-        // fragment read ahead of the MFMAs it overlaps (the compiler would
-        // otherwise sink the reads below them).
-        int kt = 0;
-        const int steady_last = nk - (ragged ? 1 : 0);
-        for (; kt + 2 * STAGES <= steady_last; kt += STAGES) {
-#pragma unroll
-            for (int b = 0; b < STAGES; b++) {
-                __builtin_amdgcn_sched_barrier(0);
-                half_step(0, b, 1, 1, kt + b + STAGES - 1, (b + STAGES - 1) % STAGES, HALF);
-                __builtin_amdgcn_sched_barrier(0);
-                wait_vm_barrier<(STAGES - 2) * LOADS>();
-                __builtin_amdgcn_sched_barrier(0);
-                half_step(1, (b + 1) % STAGES, 0, 0, kt + b + STAGES, b, 0);
-                __builtin_amdgcn_sched_barrier(0);
-            }
-        }
-        // Drain: same schedule with run-time buffers and exact waits.
-#pragma unroll 1
-        for (; kt < nk; kt++) {
-            const int b = kt % STAGES;
-            frag(b, 1, 1);
-            if (kt + STAGES - 1 < nk)
-#pragma unroll
-                for (int q = HALF; q < LOADS; q++) copy_any(kt + STAGES - 1, (kt + STAGES - 1) % STAGES, q);
-            mma(0, false, 0, 0, 0);
-            if (kt + 1 < nk) {
-                const int beyond = min(nk - 1, kt + STAGES - 1) - (kt + 1);  // later stages, all issued
-                if (beyond >= 2 && STAGES >= 4) wait_vm_barrier<(STAGES >= 4 ? 2 : 0) * LOADS>();
-                else if (beyond >= 1) wait_vm_barrier<LOADS>();
-                else wait_vm_barrier<0>();
-                frag((b + 1) % STAGES, 0, 0);
-                if (kt + STAGES < nk)
-#pragma unroll
-                    for (int q = 0; q < HALF; q++) copy_any(kt + STAGES, b, q);
-            }
-            mma(1, false, 0, 0, 0);
-        }
-
-        // ---- epilogue: lane = one token of each 32-token block, 4 columns per group
-#pragma unroll
-        for (int i = 0; i < RT; i++) {
-            const int t = wm * (BM / WM) + i * 32 + (lane & 31);
-            if (t < rows) {
-                const int pos = row0 + t;
-                if (GATEUP) {
-                    constexpr int HW = BN / 2 / WN;
-                    uint16_t *Hh = reinterpret_cast<uint16_t *>(p.C) + (int64_t)pos * p.N;
-#pragma unroll
-                    for (int j = 0; j < RW / 2; j++)
-#pragma unroll
-                        for (int g4 = 0; g4 < 4; g4++) {
-                            const int c = nb * (BN / 2) + wn * HW + j * 32 + 8 * g4 + 4 * (lane >> 5);
-                            if (c < p.N) {
-                                float hv[4];
-#pragma unroll
-                                for (int u = 0; u < 4; u++)
-                                    hv[u] = silu_f32(acc[j][i][4 * g4 + u]) * acc[j + RW / 2][i][4 * g4 + u];
-                                uint2 pk;
-                                pk.x = pack_bf16x2(hv[0], hv[1]);
-                                pk.y = pack_bf16x2(hv[2], hv[3]);
-                                *reinterpret_cast<uint2 *>(Hh + c) = pk;
-                            }
-                        }
-                } else {
-                    const int64_t orow = p.c_rows ? (int64_t)p.c_rows[pos] : (int64_t)pos;
-                    const float sc = p.c_scale ? p.c_scale[pos] : 1.0f;
-                    float *Y = reinterpret_cast<float *>(p.C) + orow * p.N;
-#pragma unroll
-                    for (int j = 0; j < RW; j++)
-#pragma unroll
-                        for (int g4 = 0; g4 < 4; g4++) {
-                            const int m = nb * BN + wn * (BN / WN) + j * 32 + 8 * g4 + 4 * (lane >> 5);
-                            if (m < p.N) {
-                                float4 y = make_float4(acc[j][i][4 * g4] * sc, acc[j][i][4 * g4 + 1] * sc,
-                                                       acc[j][i][4 * g4 + 2] * sc, acc[j][i][4 * g4 + 3] * sc);
-                                *reinterpret_cast<float4 *>(Y + m) = y;
-                            }
-                        }
+                for (int q = 0; q < 16; q++) {
+                    const int rr = BM + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
+                    if (rr < rows && m < p.N) {
+                        const int pos = row0 + rr;
+                        const int64_t orow = p.c_rows ? (int64_t)p.c_rows[pos] : (int64_t)pos;
+                        const float sc = p.c_scale ? p.c_scale[pos] : 1.0f;
+                        Y[orow * p.N + m] = accx[q] * sc;
+                    }
                 }
             }
         }
@@ -784,57 +508,40 @@ TiledParams make_params(const GemmProblem &g, int NB)
     return t;
 }
 
-template <int BM, int BN, int WM, int WN, int OCC, bool GATEUP>
+template <int BM, int BN, int WM, int WN, int OCC, bool GATEUP, int XT = 0>
 hipError_t launch_cfg(const GemmProblem &g, hipStream_t st)
 {
     const int cols = GATEUP ? BN / 2 : BN;  // output columns per N-block
     TiledParams t = make_params(g, (int)((g.N + cols - 1) / cols));
-    hipLaunchKernelGGL((tiled_gemm_kernel<BM, BN, WM, WN, OCC, GATEUP>), dim3(persistent_grid(OCC)),
+    hipLaunchKernelGGL((tiled_gemm_kernel<BM, BN, WM, WN, OCC, GATEUP, XT>), dim3(persistent_grid(OCC)),
                        dim3(WM * WN * 64), 0, st, t);
     return hipGetLastError();
 }
 
-#ifndef MOE_TILED_PP
-#define MOE_TILED_PP 0
-#endif
-
-#if MOE_TILED_PP
-template <bool GATEUP>
-hipError_t launch_pp(const GemmProblem &g, hipStream_t st)
-{
-    const int cols = GATEUP ? 128 : 256;
-    TiledParams t = make_params(g, (int)((g.N + cols - 1) / cols));
-    hipLaunchKernelGGL((tiled_pp_kernel<256, 256, GATEUP>), dim3(persistent_grid(1)), dim3(256), 0, st, t);
-    return hipGetLastError();
-}
+#ifndef MOE_TILED_TAIL
+#define MOE_TILED_TAIL 32
 #endif
 
 }  // namespace
 
-// Routed experts: 256x256 tiles, 8 waves, one workgroup per CU; the M-tile
-// list is built for this height. Dense problems (the shared expert, all T
-// rows) use smaller tiles so that a few thousand rows still fill the CUs:
-// 128x256 (gate_up) and 128x128 with two workgroups per CU (down).
+// Routed experts: 256x256 tiles (up to 32 more token rows in an expert's
+// last tile), 8 waves, one workgroup per CU; the M-tile list is built for
+// these sizes. Dense problems (the shared expert, all T rows) use smaller
+// tiles so that a few thousand rows still fill the CUs: 128x256 (gate_up)
+// and 128x128 with two workgroups per CU (down).
 int tiled_block_m() { return 256; }
+int tiled_tail_m() { return MOE_TILED_TAIL; }
 
 hipError_t launch_gate_up_tiled(const GemmProblem &g, hipStream_t st)
 {
     if (g.dense_rows > 0) return launch_cfg<128, 256, 2, 2, 1, true>(g, st);
-#if MOE_TILED_PP
-    return launch_pp<true>(g, st);
-#else
-    return launch_cfg<256, 256, 4, 2, 1, true>(g, st);
-#endif
+    return launch_cfg<256, 256, 4, 2, 1, true, MOE_TILED_TAIL>(g, st);
 }
 
 hipError_t launch_down_tiled(const GemmProblem &g, hipStream_t st)
 {
     if (g.dense_rows > 0) return launch_cfg<128, 128, 2, 2, 2, false>(g, st);
-#if MOE_TILED_PP
-    return launch_pp<false>(g, st);
-#else
-    return launch_cfg<256, 256, 4, 2, 1, false>(g, st);
-#endif
+    return launch_cfg<256, 256, 4, 2, 1, false, MOE_TILED_TAIL>(g, st);
 }
 
 }  // namespace moe

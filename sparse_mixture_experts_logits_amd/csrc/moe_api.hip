@@ -127,6 +127,7 @@ moe::Shape make_shape(int64_t T, int64_t H, int64_t I, int64_t E, int32_t k, con
     s.rtok = T <= 256 ? 1 : 4;
     s.nblk = (int)((T + s.rtok - 1) / s.rtok);
     s.tileBM = moe::tiled_block_m();
+    s.tileXT = moe::tiled_tail_m();
     s.maxTiles = (T * k) / s.tileBM + E + 1;
     return s;
 }

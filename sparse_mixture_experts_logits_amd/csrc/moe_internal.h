@@ -97,6 +97,7 @@ struct Shape {
     int rtok;        // tokens per router block (1 or 4)
     int nblk;        // router blocks
     int tileBM;      // rows per M-tile of the large-M schedule
+    int tileXT;      // extra rows an expert's last M-tile may take (0: none)
     int64_t maxTiles;
 };
 
@@ -163,6 +164,7 @@ hipError_t launch_gate_up_f32(const GemmProblem &p, hipStream_t st);
 hipError_t launch_down_f32(const GemmProblem &p, hipStream_t st);
 
 int tiled_block_m();
+int tiled_tail_m();  // rows an expert's last M-tile may carry past tiled_block_m()
 
 hipError_t launch_quantize_fp8_rows(const void *w, int64_t rows, int64_t cols, void *q, float *scale,
                                     hipStream_t st);

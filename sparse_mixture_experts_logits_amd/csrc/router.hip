@@ -425,7 +425,7 @@ __global__ __launch_bounds__(256) void router_topk_kernel(
 // One workgroup: expert totals, exclusive offsets, per-block bases and the
 // M-tile list of the large-M schedule.
 __global__ __launch_bounds__(1024) void route_scan_kernel(
-    const int32_t *__restrict__ blk_counts, int nblk, int E, int BM, int32_t *__restrict__ counts,
+    const int32_t *__restrict__ blk_counts, int nblk, int E, int BM, int XT, int32_t *__restrict__ counts,
     int32_t *__restrict__ offsets, int32_t *__restrict__ blk_base, int32_t *__restrict__ tile_start,
     MTile *__restrict__ tiles, int32_t *__restrict__ counts_out, int32_t *__restrict__ offsets_out,
     const float *__restrict__ blk_prob, const int32_t *__restrict__ blk_mcnt, const int32_t *__restrict__ blk_ntok,
@@ -435,6 +435,12 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(
     __shared__ int s_cnt[kMaxExperts];
     __shared__ int s_off[kMaxExperts + 1];
     __shared__ int s_ts[kMaxExperts + 1];
+    // M-tiles of an expert with c rows: ceil(c / BM), less one when the last
+    // would hold at most XT rows (they go to the tile before it)
+    auto n_tiles = [&](int c) {
+        const int n = (c + BM - 1) / BM;
+        return (n > 1 && c - (n - 1) * BM <= XT) ? n - 1 : n;
+    };
 
     const int tid = threadIdx.x;
     const int G = 1024 / E;  // E <= 256 so G >= 4
@@ -471,7 +477,7 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(
         s_ts[0] = 0;
         for (int x = 0; x < E; x++) {
             s_off[x + 1] = s_off[x] + s_cnt[x];
-            s_ts[x + 1] = s_ts[x] + (s_cnt[x] + BM - 1) / BM;
+            s_ts[x + 1] = s_ts[x] + n_tiles(s_cnt[x]);
         }
     }
     __syncthreads();
@@ -496,12 +502,12 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(
     if (tid < E) {
         counts[tid] = s_cnt[tid];
         if (counts_out) counts_out[tid] = s_cnt[tid];
-        const int nt = (s_cnt[tid] + BM - 1) / BM;
+        const int nt = n_tiles(s_cnt[tid]);
         for (int i = 0; i < nt; i++) {
             MTile m;
             m.expert = tid;
             m.row0 = s_off[tid] + i * BM;
-            m.rows = min(BM, s_cnt[tid] - i * BM);
+            m.rows = i == nt - 1 ? s_cnt[tid] - i * BM : BM;
             m.pad = 0;
             tiles[s_ts[tid] + i] = m;
         }
@@ -620,7 +626,7 @@ hipError_t launch_route_scan(const Shape &s, int32_t *counts_out, int32_t *offse
                              const RouterStats &rs, const Workspace &ws, hipStream_t st)
 {
     hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(1024), 0, st, ws.blk_counts, s.nblk,
-                       (int)s.E, s.tileBM, ws.counts, ws.offsets, ws.blk_base, ws.tile_start,
+                       (int)s.E, s.tileBM, s.tileXT, ws.counts, ws.offsets, ws.blk_base, ws.tile_start,
                        ws.tiles, counts_out, offsets_out, rs.on() ? ws.blk_prob : nullptr, ws.blk_mcnt,
                        ws.blk_ntok, rs.prob_mean, rs.load, rs.aux);
     return hipGetLastError();

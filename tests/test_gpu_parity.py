@@ -182,6 +182,47 @@ def test_run_to_run_bitwise_identical():
         assert np.array_equal(ra[key], rb[key])
 
 
+def routed_by_construction(counts, H, I, seed=0):
+    """Inputs whose top-2 routing gives each expert exactly counts[e] rows:
+    router row e is the unit vector of hidden dimension e, and token t
+    carries 2 and 1 in the dimensions of its two experts (its other
+    dimensions are random, unseen by the router)."""
+    E = len(counts)
+    T = sum(counts) // 2
+    assert sum(counts) == 2 * T and max(counts) <= T
+    inp = W.custom_inputs(T=T, H=H, I=I, E=E, k=2, seed=seed, std_weight=0.05)
+    slots = np.repeat(np.arange(E), counts)  # expert of each of the 2T slots, grouped
+    first, second = slots[:T], slots[T:]     # distinct: no expert holds more than T slots
+    x = W.bf16_bits_to_f32(inp.hidden).copy()
+    x[:, :E] = 0.0
+    x[np.arange(T), first] = 2.0
+    x[np.arange(T), second] = 1.0
+    inp.hidden = W.f32_to_bf16_bits(x)
+    wr = np.zeros((E, H), np.float32)
+    wr[np.arange(E), np.arange(E)] = 1.0
+    inp.router_w = W.f32_to_bf16_bits(wr)
+    return inp
+
+
+@pytest.mark.parametrize("counts,H,I", [
+    # 257 / 272 / 288 rows: one 256-row tile plus a short tail folded into it;
+    # 289: the tail is too long and gets a tile of its own; 532 = 2*256 + 20
+    ((257, 288, 289, 532), 256, 256),
+    ((272, 530, 300, 256), 328, 200),  # ragged K (328) and N (200 outputs per half)
+    ((288, 33, 290, 545), 512, 320),  # 545 = 2*256 + 33: its tail is one row too long
+])
+def test_tail_rows_folded_into_tiles(counts, H, I):
+    _say(f"case tail tiles counts={counts} H={H} I={I}")
+    inp = routed_by_construction(list(counts), H, I)
+    ref = oracle_routing(inp)
+    assert ref["counts"].tolist() == list(counts)
+    for flags in (moe.FLAG_FORCE_TILED, 0):
+        out, got = run_gpu(inp, flags=flags)
+        check_routing(got, ref, f"tail tiles flags={flags}")
+        r_out = oracle_out(inp, ref, np.arange(inp.wl.T, dtype=np.int32))
+        check_out(out, r_out, f"tail tiles flags={flags}")
+
+
 # ------------------------------------------------------------------ full-size workloads
 
 FULL = ["phimoe_decode", "phimoe_prefill", "instella_fine", "phimoe_skewed"]
