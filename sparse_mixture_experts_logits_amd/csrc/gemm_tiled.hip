@@ -54,8 +54,156 @@ struct TiledParams {
     const int32_t *tile_start;
     int E;
     int dense_rows;
-    int NB;  // N-blocks
+    int NB;     // N-blocks
+    float *part;  // partial sums of split tiles (null: no splitting)
+    int G;      // workgroups of the persistent launch
 };
+
+// The last, partial round of a persistent launch leaves most CUs idle when
+// only a few tiles remain (total % G of them). Such tiles are split along K
+// into up to kMaxSplit pieces, one workgroup each; every piece writes its
+// fp32 partial sums (in accumulator layout) and a second kernel adds the
+// pieces in piece order and runs the tile's epilogue, so the result does not
+// depend on timing.
+constexpr int kSplitPieces = 256;  // capacity of the partial-sum buffer, in pieces
+constexpr int kMaxSplit = 8;
+
+struct SplitPlan {
+    int full;   // tiles [0, full) run whole
+    int split;  // pieces per remaining tile (1: none)
+    int nks;    // k-stages per piece
+    int nwork;  // work items of the persistent loop
+};
+
+__device__ __forceinline__ SplitPlan split_plan(int total, int G, int nk, bool enabled)
+{
+    SplitPlan sp{total, 1, nk, total};
+    const int cap = min(G, kSplitPieces);
+    const int rem = total % G;
+    if (!enabled || rem == 0 || 2 * rem > cap || nk < 2) return sp;
+    int split = min(min(cap / rem, kMaxSplit), nk);
+    const int nks = (nk + split - 1) / split;
+    split = (nk + nks - 1) / nks;  // every piece holds at least one stage
+    if (split < 2) return sp;
+    sp.full = total - rem;
+    sp.split = split;
+    sp.nks = nks;
+    sp.nwork = sp.full + rem * split;
+    return sp;
+}
+
+// tile id -> (expert, N-block, first row, rows); M-tiles of one expert are
+// consecutive within each N-block
+template <int BM>
+__device__ __forceinline__ void decode_tile(const TiledParams &p, int id, int n_mtiles, int &e, int &nb, int &row0,
+                                            int &rows)
+{
+    if (p.tiles) {
+        const int32_t *s_ts = p.tile_start;
+        int lo = 0, hi = p.E;  // find e: s_ts[e]*NB <= id < s_ts[e+1]*NB
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (s_ts[mid] * p.NB <= id) lo = mid; else hi = mid;
+        }
+        e = lo;
+        const int nte = s_ts[e + 1] - s_ts[e];
+        const int local = id - s_ts[e] * p.NB;
+        nb = local / nte;
+        const MTile t = p.tiles[s_ts[e] + (local - nb * nte)];
+        row0 = t.row0;
+        rows = t.rows;
+    } else {
+        e = 0;
+        nb = id / n_mtiles;
+        const int mt = id - nb * n_mtiles;
+        row0 = mt * BM;
+        rows = min(BM, p.dense_rows - row0);
+    }
+}
+
+// Epilogue of one tile from the accumulators of wave (wm, wn): h = silu(gate)
+// * up as bf16 (gate_up) or the weighted fp32 slot rows (down). xg: LDS for
+// the gate halves of the extra rows (gate_up with XT > 0).
+template <int BM, int BN, int WM, int WN, bool GATEUP, int XT>
+__device__ __forceinline__ void tile_epilogue(const TiledParams &p, const f32x16_t (&acc)[BM / WM / 32][BN / WN / 32],
+                                              const f32x16_t &accx, int wm, int wn, int lane, int row0, int rows,
+                                              int nb, bool xtra, float *xgs)
+{
+    constexpr int RM = BM / WM / 32;
+    constexpr int RN = BN / WN / 32;
+    const int jx = GATEUP ? (wm >> 1) + (RN / 2) * (wm & 1) : wm;
+    if (GATEUP) {
+        constexpr int HW = BN / 2 / WN;
+        __bf16 *H = reinterpret_cast<__bf16 *>(p.C);
+#pragma unroll
+        for (int i = 0; i < RM; i++)
+#pragma unroll
+            for (int j = 0; j < RN / 2; j++) {
+                const int c = nb * (BN / 2) + wn * HW + j * 32 + (lane & 31);
+#pragma unroll
+                for (int q = 0; q < 16; q++) {
+                    const int rr = wm * (BM / WM) + i * 32 + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
+                    if (rr < rows && c < p.N) {
+                        const float g = acc[i][j][q];
+                        const float u = acc[i][j + RN / 2][q];
+                        const uint32_t hb = f32_to_bf16_bits(silu_f32(g) * u);
+                        reinterpret_cast<uint16_t *>(H)[(int64_t)(row0 + rr) * p.N + c] = (uint16_t)hb;
+                    }
+                }
+            }
+        if (XT > 0 && xtra) {
+            // gate blocks (even wm) to LDS; the up waves (odd wm) combine
+            float *xg = xgs + (wn * 2 + (wm >> 1)) * (16 * 64);
+            if ((wm & 1) == 0) {
+#pragma unroll
+                for (int q = 0; q < 16; q++) xg[q * 64 + lane] = accx[q];
+            }
+            __syncthreads();
+            if (wm & 1) {
+                const int c = nb * (BN / 2) + wn * HW + (wm >> 1) * 32 + (lane & 31);
+#pragma unroll
+                for (int q = 0; q < 16; q++) {
+                    const int rr = BM + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
+                    if (rr < rows && c < p.N) {
+                        const uint32_t hb = f32_to_bf16_bits(silu_f32(xg[q * 64 + lane]) * accx[q]);
+                        reinterpret_cast<uint16_t *>(H)[(int64_t)(row0 + rr) * p.N + c] = (uint16_t)hb;
+                    }
+                }
+            }
+        }
+    } else {
+        float *Y = reinterpret_cast<float *>(p.C);
+#pragma unroll
+        for (int i = 0; i < RM; i++)
+#pragma unroll
+            for (int q = 0; q < 16; q++) {
+                const int rr = wm * (BM / WM) + i * 32 + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
+                if (rr < rows) {
+                    const int pos = row0 + rr;
+                    const int64_t orow = p.c_rows ? (int64_t)p.c_rows[pos] : (int64_t)pos;
+                    const float sc = p.c_scale ? p.c_scale[pos] : 1.0f;
+#pragma unroll
+                    for (int j = 0; j < RN; j++) {
+                        const int m = nb * BN + wn * (BN / WN) + j * 32 + (lane & 31);
+                        if (m < p.N) Y[orow * p.N + m] = acc[i][j][q] * sc;
+                    }
+                }
+            }
+        if (XT > 0 && xtra) {
+            const int m = nb * BN + wn * (BN / WN) + jx * 32 + (lane & 31);
+#pragma unroll
+            for (int q = 0; q < 16; q++) {
+                const int rr = BM + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
+                if (rr < rows && m < p.N) {
+                    const int pos = row0 + rr;
+                    const int64_t orow = p.c_rows ? (int64_t)p.c_rows[pos] : (int64_t)pos;
+                    const float sc = p.c_scale ? p.c_scale[pos] : 1.0f;
+                    Y[orow * p.N + m] = accx[q] * sc;
+                }
+            }
+        }
+    }
+}
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) void global_void_t;
@@ -138,12 +286,11 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void tiled_gemm_kernel(TiledParam
                              : wn * (BN / WN) + jx * 32) +
                      (lane & 31);
 
-    // first M-tile of each expert (read through the scalar cache, so the
-    // whole LDS is left to the stage ring)
-    const int32_t *s_ts = p.tile_start;
+    // number of M-tiles (read through the scalar cache, so the whole LDS is
+    // left to the stage ring)
     int n_mtiles;
     if (p.tiles) {
-        n_mtiles = s_ts[p.E];
+        n_mtiles = p.tile_start[p.E];
     } else {
         n_mtiles = (p.dense_rows + BM - 1) / BM;
     }
@@ -152,38 +299,34 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void tiled_gemm_kernel(TiledParam
     const int nx = G >> 3;
     const int xcd = blockIdx.x & 7;
     const int li = blockIdx.x >> 3;
-    const int nk = (p.K + BK - 1) / BK;
+    const int nk_all = (p.K + BK - 1) / BK;
 
     // copy geometry: instruction i of this wave fills LDS rows
     // RPI*(wave*INS + i) + lane/CH, chunk slot lane%CH (logical chunk lc below)
     const int drow = lane / CH;
 
+    const SplitPlan sp = split_plan(total, G, nk_all, p.part != nullptr);
+
     for (int r = 0;; r++) {
-        const int id = r * G + xcd * nx + li;
-        if (id >= total) break;
+        const int wid = r * G + xcd * nx + li;
+        if (wid >= sp.nwork) break;
+        // work item -> tile and its k-stages [ks, ke): whole tiles first, then
+        // the pieces of the split ones (piece = wid - full)
+        int id = wid, ks = 0, ke = nk_all;
+        if (wid >= sp.full) {
+            const int q = wid - sp.full;
+            id = sp.full + q / sp.split;
+            ks = (q % sp.split) * sp.nks;
+            ke = min(nk_all, ks + sp.nks);
+        }
+        const int nk = ke - ks;                               // k-stages of this work item
+        const int64_t kbase = (int64_t)ks * BK;               // its first k
+        const int Kl = p.K - (int)kbase;                      // k bound relative to kbase
+        const bool ragged = ke == nk_all && (p.K % BK) != 0;  // a partial last stage
 
         // ---- decode tile id -> (expert, M-tile, N-block)
         int e, nb, row0, rows;
-        if (p.tiles) {
-            int lo = 0, hi = p.E;  // find e: s_ts[e]*NB <= id < s_ts[e+1]*NB
-            while (hi - lo > 1) {
-                const int mid = (lo + hi) >> 1;
-                if (s_ts[mid] * p.NB <= id) lo = mid; else hi = mid;
-            }
-            e = lo;
-            const int nte = s_ts[e + 1] - s_ts[e];
-            const int local = id - s_ts[e] * p.NB;
-            nb = local / nte;
-            const MTile t = p.tiles[s_ts[e] + (local - nb * nte)];
-            row0 = t.row0;
-            rows = t.rows;
-        } else {
-            e = 0;
-            nb = id / n_mtiles;
-            const int mt = id - nb * n_mtiles;
-            row0 = mt * BM;
-            rows = min(BM, p.dense_rows - row0);
-        }
+        decode_tile<BM>(p, id, n_mtiles, e, nb, row0, rows);
         const bool xtra = XT > 0 && rows > BM;  // tile-uniform
 
         // ---- per-lane DMA source rows (rows past the tile repeat row 0; dropped later)
@@ -195,7 +338,7 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void tiled_gemm_kernel(TiledParam
             const int rr = RPI * (wave * A_INS + i) + drow;
             const int rc = rr < rows ? rr : 0;
             const int64_t src = p.a_rows ? (int64_t)p.a_rows[row0 + rc] : (int64_t)(row0 + rc);
-            asrc[i] = p.A + src * p.K + chunk_of(rr) * 8;
+            asrc[i] = p.A + src * p.K + kbase + chunk_of(rr) * 8;
         }
         // extra rows BM + XR*wave + lane/CH, lanes below XR*CH (rows past the
         // tile repeat row BM)
@@ -205,7 +348,7 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void tiled_gemm_kernel(TiledParam
         if (XT > 0 && xtra) {
             const int rc = xrr < rows ? xrr : BM;
             const int64_t src = p.a_rows ? (int64_t)p.a_rows[row0 + rc] : (int64_t)(row0 + rc);
-            xsrc = p.A + src * p.K + chunk_of(xrr) * 8;
+            xsrc = p.A + src * p.K + kbase + chunk_of(xrr) * 8;
         }
         const __bf16 *wbase = p.W + (int64_t)e * p.w_expert_stride;
         const __bf16 *bsrc[B_INS];
@@ -222,7 +365,7 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void tiled_gemm_kernel(TiledParam
                 const int n = nb * BN + rr;
                 wrow = n < p.N ? n : 0;
             }
-            bsrc[i] = wbase + (int64_t)wrow * p.K + chunk_of(rr) * 8;
+            bsrc[i] = wbase + (int64_t)wrow * p.K + kbase + chunk_of(rr) * 8;
         }
 
         // stage kt -> LDS buffer b: every lane copies 16 bytes. Only a final
@@ -242,7 +385,7 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void tiled_gemm_kernel(TiledParam
 #pragma unroll
             for (int i = 0; i < A_INS; i++) {
                 u32x4 *dst = &sA[b][(wave * A_INS + i) * 64];
-                if (k0 + chunk_of(RPI * (wave * A_INS + i) + drow) * 8 < p.K)
+                if (k0 + chunk_of(RPI * (wave * A_INS + i) + drow) * 8 < Kl)
                     dma16(asrc[i] + k0, lds_addr(dst));
                 else
                     dst[lane] = u32x4{0u, 0u, 0u, 0u};
@@ -250,20 +393,19 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void tiled_gemm_kernel(TiledParam
 #pragma unroll
             for (int i = 0; i < B_INS; i++) {
                 u32x4 *dst = &sB[b][(wave * B_INS + i) * 64];
-                if (k0 + chunk_of(RPI * (wave * B_INS + i) + drow) * 8 < p.K)
+                if (k0 + chunk_of(RPI * (wave * B_INS + i) + drow) * 8 < Kl)
                     dma16(bsrc[i] + k0, lds_addr(dst));
                 else
                     dst[lane] = u32x4{0u, 0u, 0u, 0u};
             }
             if (XT > 0 && xtra && xlane) {
                 u32x4 *dst = &sA[b][(BM + XR * wave) * CH];
-                if (k0 + chunk_of(xrr) * 8 < p.K)
+                if (k0 + chunk_of(xrr) * 8 < Kl)
                     dma16(xsrc + k0, lds_addr(dst));
                 else
                     dst[lane] = u32x4{0u, 0u, 0u, 0u};
             }
         };
-        const bool ragged = (p.K % BK) != 0;
         auto issue_any = [&](int kt, int b) {
             if (ragged && kt == nk - 1) issue_tail(kt, b);
             else issue(kt, b);
@@ -400,75 +542,137 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void tiled_gemm_kernel(TiledParam
         else kloop(I0{}, F{});
         (void)T{};
 
-        // ---- epilogue
-        if (GATEUP) {
-            constexpr int HW = BN / 2 / WN;
-            __bf16 *H = reinterpret_cast<__bf16 *>(p.C);
+        // ---- epilogue, or the partial sums of a piece of a split tile
+        if (wid >= sp.full) {
+            constexpr int NBLK = RM * RN + (XT > 0 ? 1 : 0);
+            float *pp = p.part + ((int64_t)(wid - sp.full) * NWAVE + wave) * NBLK * 1024 + lane;
 #pragma unroll
             for (int i = 0; i < RM; i++)
 #pragma unroll
-                for (int j = 0; j < RN / 2; j++) {
-                    const int c = nb * (BN / 2) + wn * HW + j * 32 + (lane & 31);
+                for (int j = 0; j < RN; j++)
 #pragma unroll
-                    for (int q = 0; q < 16; q++) {
-                        const int rr = wm * (BM / WM) + i * 32 + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
-                        if (rr < rows && c < p.N) {
-                            const float g = acc[i][j][q];
-                            const float u = acc[i][j + RN / 2][q];
-                            const uint32_t hb = f32_to_bf16_bits(silu_f32(g) * u);
-                            reinterpret_cast<uint16_t *>(H)[(int64_t)(row0 + rr) * p.N + c] = (uint16_t)hb;
-                        }
-                    }
-                }
-            if (XG && xtra) {
-                // gate blocks (even wm) to LDS; the up waves (odd wm) combine
-                float *xg = s_xg[XG ? wn * 2 + (wm >> 1) : 0];
-                if ((wm & 1) == 0) {
+                    for (int q = 0; q < 16; q++) pp[(i * RN + j) * 1024 + q * 64] = acc[i][j][q];
+            if (XT > 0) {
 #pragma unroll
-                    for (int q = 0; q < 16; q++) xg[q * 64 + lane] = accx[q];
-                }
-                __syncthreads();
-                if (wm & 1) {
-                    const int c = nb * (BN / 2) + wn * HW + (wm >> 1) * 32 + (lane & 31);
-#pragma unroll
-                    for (int q = 0; q < 16; q++) {
-                        const int rr = BM + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
-                        if (rr < rows && c < p.N) {
-                            const uint32_t hb = f32_to_bf16_bits(silu_f32(xg[q * 64 + lane]) * accx[q]);
-                            reinterpret_cast<uint16_t *>(H)[(int64_t)(row0 + rr) * p.N + c] = (uint16_t)hb;
-                        }
-                    }
-                }
+                for (int q = 0; q < 16; q++) pp[(RM * RN) * 1024 + q * 64] = accx[q];
             }
         } else {
-            float *Y = reinterpret_cast<float *>(p.C);
+            tile_epilogue<BM, BN, WM, WN, GATEUP, XT>(p, acc, accx, wm, wn, lane, row0, rows, nb, xtra, &s_xg[0][0]);
+        }
+    }
+}
+
+// Second half of a split launch: one single-wave workgroup per (split tile,
+// wave of the main kernel, 32-row block of that wave) adds the block's
+// partial sums over the tile's pieces, in piece order, and writes its part of
+// the tile as the main kernel's epilogue would (the extra rows go with row
+// block 0; for gate_up an up wave sums its gate partner's partials as well). The split plan is recomputed from the
+// same inputs as the main kernel's.
+template <int BM, int BN, int WM, int WN, bool GATEUP, int XT>
+__global__ __launch_bounds__(64) void tiled_split_finish_kernel(TiledParams p)
+{
+    constexpr int NWAVE = WM * WN;
+    constexpr int RM = BM / WM / 32;
+    constexpr int RN = BN / WN / 32;
+    constexpr int NBLK = RM * RN + (XT > 0 ? 1 : 0);
+
+    const int n_mtiles = p.tiles ? p.tile_start[p.E] : (p.dense_rows + BM - 1) / BM;
+    const int total = n_mtiles * p.NB;
+    const int nk_all = (p.K + BK - 1) / BK;
+    const SplitPlan sp = split_plan(total, p.G, nk_all, p.part != nullptr);
+    const int t = blockIdx.x / (NWAVE * RM);
+    const int wave = (blockIdx.x / RM) % NWAVE;
+    const int i = blockIdx.x % RM;  // this workgroup's 32-row block
+    if (sp.split < 2 || sp.full + t >= total) return;  // workgroup-uniform
+
+    const int lane = threadIdx.x;
+    const int wm = wave / WN;
+    const int wn = wave - wm * WN;
+    int e, nb, row0, rows;
+    decode_tile<BM>(p, sp.full + t, n_mtiles, e, nb, row0, rows);
+    (void)e;
+    const bool xtra = XT > 0 && rows > BM;
+
+    const int64_t pstride = (int64_t)NWAVE * NBLK * 1024;  // between pieces
+    // block b of wave w summed over the pieces in piece order; all kMaxSplit
+    // loads are issued unconditionally (pieces past the last re-read it and
+    // count 0)
+    auto sum_block = [&](int w, int b, f32x16_t &v) {
+        const float *pp = p.part + ((int64_t)t * sp.split * NWAVE + w) * NBLK * 1024 + b * 1024 + lane;
+        float x[kMaxSplit][16];
 #pragma unroll
-            for (int i = 0; i < RM; i++)
+        for (int c = 0; c < kMaxSplit; c++)
+#pragma unroll
+            for (int q = 0; q < 16; q++) x[c][q] = pp[min(c, sp.split - 1) * pstride + q * 64];
+#pragma unroll
+        for (int q = 0; q < 16; q++) {
+            float a = x[0][q];
+#pragma unroll
+            for (int c = 1; c < kMaxSplit; c++) a += c < sp.split ? x[c][q] : 0.0f;
+            v[q] = a;
+        }
+    };
+
+    if (GATEUP) {
+        constexpr int HW = BN / 2 / WN;
+        uint16_t *H = reinterpret_cast<uint16_t *>(p.C);
+#pragma unroll
+            for (int j = 0; j < RN / 2; j++) {
+                f32x16_t g, u;
+                sum_block(wave, i * RN + j, g);
+                sum_block(wave, i * RN + j + RN / 2, u);
+                const int c = nb * (BN / 2) + wn * HW + j * 32 + (lane & 31);
 #pragma unroll
                 for (int q = 0; q < 16; q++) {
                     const int rr = wm * (BM / WM) + i * 32 + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
-                    if (rr < rows) {
-                        const int pos = row0 + rr;
-                        const int64_t orow = p.c_rows ? (int64_t)p.c_rows[pos] : (int64_t)pos;
-                        const float sc = p.c_scale ? p.c_scale[pos] : 1.0f;
-#pragma unroll
-                        for (int j = 0; j < RN; j++) {
-                            const int m = nb * BN + wn * (BN / WN) + j * 32 + (lane & 31);
-                            if (m < p.N) Y[orow * p.N + m] = acc[i][j][q] * sc;
-                        }
-                    }
+                    if (rr < rows && c < p.N)
+                        H[(int64_t)(row0 + rr) * p.N + c] = (uint16_t)f32_to_bf16_bits(silu_f32(g[q]) * u[q]);
                 }
-            if (XT > 0 && xtra) {
-                const int m = nb * BN + wn * (BN / WN) + jx * 32 + (lane & 31);
+            }
+        if (XT > 0 && xtra && (wm & 1) && i == 0) {
+            // up block of the extra rows; its gate block is in wave (wm - 1, wn)
+            f32x16_t g, u;
+            sum_block(wave - WN, RM * RN, g);
+            sum_block(wave, RM * RN, u);
+            const int c = nb * (BN / 2) + wn * HW + (wm >> 1) * 32 + (lane & 31);
+#pragma unroll
+            for (int q = 0; q < 16; q++) {
+                const int rr = BM + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
+                if (rr < rows && c < p.N)
+                    H[(int64_t)(row0 + rr) * p.N + c] = (uint16_t)f32_to_bf16_bits(silu_f32(g[q]) * u[q]);
+            }
+        }
+    } else {
+        float *Y = reinterpret_cast<float *>(p.C);
+#pragma unroll
+            for (int j = 0; j < RN; j++) {
+                f32x16_t y;
+                sum_block(wave, i * RN + j, y);
+                const int m = nb * BN + wn * (BN / WN) + j * 32 + (lane & 31);
 #pragma unroll
                 for (int q = 0; q < 16; q++) {
-                    const int rr = BM + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
+                    const int rr = wm * (BM / WM) + i * 32 + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
                     if (rr < rows && m < p.N) {
                         const int pos = row0 + rr;
                         const int64_t orow = p.c_rows ? (int64_t)p.c_rows[pos] : (int64_t)pos;
                         const float sc = p.c_scale ? p.c_scale[pos] : 1.0f;
-                        Y[orow * p.N + m] = accx[q] * sc;
+                        Y[orow * p.N + m] = y[q] * sc;
                     }
+                }
+            }
+        if (XT > 0 && xtra && i == 0) {
+            f32x16_t y;
+            sum_block(wave, RM * RN, y);
+            const int jx = wm;
+            const int m = nb * BN + wn * (BN / WN) + jx * 32 + (lane & 31);
+#pragma unroll
+            for (int q = 0; q < 16; q++) {
+                const int rr = BM + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
+                if (rr < rows && m < p.N) {
+                    const int pos = row0 + rr;
+                    const int64_t orow = p.c_rows ? (int64_t)p.c_rows[pos] : (int64_t)pos;
+                    const float sc = p.c_scale ? p.c_scale[pos] : 1.0f;
+                    Y[orow * p.N + m] = y[q] * sc;
                 }
             }
         }
@@ -505,6 +709,8 @@ TiledParams make_params(const GemmProblem &g, int NB)
     t.E = (int)g.E;
     t.dense_rows = (int)g.dense_rows;
     t.NB = NB;
+    t.part = nullptr;
+    t.G = 0;
     return t;
 }
 
@@ -513,8 +719,14 @@ hipError_t launch_cfg(const GemmProblem &g, hipStream_t st)
 {
     const int cols = GATEUP ? BN / 2 : BN;  // output columns per N-block
     TiledParams t = make_params(g, (int)((g.N + cols - 1) / cols));
-    hipLaunchKernelGGL((tiled_gemm_kernel<BM, BN, WM, WN, OCC, GATEUP, XT>), dim3(persistent_grid(OCC)),
-                       dim3(WM * WN * 64), 0, st, t);
+    t.G = persistent_grid(OCC);
+    t.part = (OCC == 1 && g.part) ? g.part : nullptr;
+    hipLaunchKernelGGL((tiled_gemm_kernel<BM, BN, WM, WN, OCC, GATEUP, XT>), dim3(t.G), dim3(WM * WN * 64), 0, st, t);
+    if (t.part) {
+        // at most kSplitPieces / 2 tiles are split (two pieces or more each)
+        hipLaunchKernelGGL((tiled_split_finish_kernel<BM, BN, WM, WN, GATEUP, XT>),
+                           dim3(kSplitPieces / 2 * WM * WN * (BM / WM / 32)), dim3(64), 0, st, t);
+    }
     return hipGetLastError();
 }
 
@@ -530,6 +742,9 @@ hipError_t launch_cfg(const GemmProblem &g, hipStream_t st)
 // tiles so that a few thousand rows still fill the CUs: 128x256 (gate_up)
 // and 128x128 with two workgroups per CU (down).
 int tiled_block_m() { return 256; }
+// partial-sum buffer of split tiles for the routed launches (256x256 tiles,
+// 8 waves, 9 accumulator blocks of 32x32 per wave)
+int64_t tiled_split_bytes() { return (int64_t)kSplitPieces * 8 * (2 * 4 + 1) * 1024 * sizeof(float); }
 int tiled_tail_m() { return MOE_TILED_TAIL; }
 
 hipError_t launch_gate_up_tiled(const GemmProblem &g, hipStream_t st)

@@ -112,6 +112,17 @@ int check_shape(int64_t T, int64_t H, int64_t I, int64_t E, int32_t k, const moe
     return MOE_OK;
 }
 
+// Routed experts on the weight-streaming kernels (few rows per expert, FP8
+// weights, or forced) rather than the large-M tiled schedule.
+bool use_skinny(int64_t T, int32_t k, int64_t E, const moe_opts *opts)
+{
+    const uint32_t flags = opts ? opts->flags : 0;
+    if (opts && opts->weight_format == MOE_WEIGHTS_FP8_E4M3) return true;
+    if (flags & MOE_FLAG_FORCE_SKINNY) return true;
+    if (flags & MOE_FLAG_FORCE_TILED) return false;
+    return T * k <= 32 * E;  // about 32 rows per expert or fewer: stream the weights
+}
+
 moe::Shape make_shape(int64_t T, int64_t H, int64_t I, int64_t E, int32_t k, const moe_opts *opts)
 {
     moe::Shape s;
@@ -129,6 +140,7 @@ moe::Shape make_shape(int64_t T, int64_t H, int64_t I, int64_t E, int32_t k, con
     s.tileBM = moe::tiled_block_m();
     s.tileXT = moe::tiled_tail_m();
     s.maxTiles = (T * k) / s.tileBM + E + 1;
+    s.partBytes = (s.dtype == MOE_BF16 && !use_skinny(T, k, E, opts)) ? moe::tiled_split_bytes() : 0;
     return s;
 }
 
@@ -168,6 +180,7 @@ int64_t workspace_layout(const Shape &s, void *base, Workspace *ws)
     w.slot = (float *)take(TK * s.H * 4);
     w.sh_h = s.sharedI > 0 ? take(s.T * s.sharedI * es) : nullptr;
     w.sh_y = s.sharedI > 0 ? (float *)take(s.T * s.H * 4) : nullptr;
+    w.part = s.partBytes > 0 ? (float *)take(s.partBytes) : nullptr;
     if (ws) *ws = w;
     return align_up(off);
 }
@@ -260,11 +273,7 @@ int moe_forward(const void *hidden, const void *router_w, const void *gate_up, c
     hipStream_t st = (hipStream_t)opts->stream;
 
     const bool f32 = opts->dtype == MOE_F32;
-    bool skinny;
-    if (opts->flags & MOE_FLAG_FORCE_SKINNY) skinny = true;
-    else if (opts->flags & MOE_FLAG_FORCE_TILED) skinny = false;
-    else skinny = T * k <= 32 * E;  // about 32 rows per expert or fewer: stream the weights
-    if (w8) skinny = true;          // FP8 weights: weight-streaming kernels only
+    const bool skinny = use_skinny(T, k, E, opts);
 
     int step = 0;
     auto check = [&](hipError_t err, const char *what) -> int {
@@ -325,6 +334,7 @@ int moe_forward(const void *hidden, const void *router_w, const void *gate_up, c
     gu.E = E;
     gu.dense_rows = 0;
     gu.total_rows = T * k;
+    gu.part = ws.part;
 
     moe::GemmProblem dn = gu;
     dn.A = ws.h;
@@ -360,6 +370,7 @@ int moe_forward(const void *hidden, const void *router_w, const void *gate_up, c
         sg.c_scale = nullptr;
         sg.dense_rows = T;
         sg.total_rows = T;
+        sg.part = nullptr;  // dense problems are not split
         moe::GemmProblem sd = sg;
         sd.A = ws.sh_h;
         sd.W = opts->shared_down;

@@ -87,6 +87,7 @@ struct Workspace {
     float *slot;           // [TK, H] weighted routed outputs, flat-assignment order
     void *sh_h;            // [T, shared_I] shared-expert activation
     float *sh_y;           // [T, H] shared-expert output
+    float *part;           // large-M schedule: partial sums of split tiles (or null)
 };
 
 struct Shape {
@@ -99,6 +100,7 @@ struct Shape {
     int tileBM;      // rows per M-tile of the large-M schedule
     int tileXT;      // extra rows an expert's last M-tile may take (0: none)
     int64_t maxTiles;
+    int64_t partBytes;  // partial-sum buffer (0 unless the large-M schedule may run)
 };
 
 // Byte layout of the workspace; returns total bytes, fills ws when base != null.
@@ -154,6 +156,7 @@ struct GemmProblem {
     int64_t E;
     int64_t dense_rows;
     int64_t total_rows;      // host-known number of rows (TK or T)
+    float *part = nullptr;   // large-M schedule: partial sums of split tiles (null: no splitting)
 };
 
 hipError_t launch_gate_up_tiled(const GemmProblem &p, hipStream_t st);
@@ -164,6 +167,7 @@ hipError_t launch_gate_up_f32(const GemmProblem &p, hipStream_t st);
 hipError_t launch_down_f32(const GemmProblem &p, hipStream_t st);
 
 int tiled_block_m();
+int64_t tiled_split_bytes();  // partial-sum buffer of the large-M schedule
 int tiled_tail_m();  // rows an expert's last M-tile may carry past tiled_block_m()
 
 hipError_t launch_quantize_fp8_rows(const void *w, int64_t rows, int64_t cols, void *q, float *scale,
