@@ -25,6 +25,8 @@
 //     accumulated sum in the epilogue, so a decode step reads half the bytes.
 #include "moe_internal.h"
 
+#include <limits.h>
+
 namespace moe {
 
 namespace {
@@ -65,6 +67,15 @@ struct SkinnyParams {
     const int32_t *counts;
     const int32_t *offsets;
     int dense_rows;
+    // direct routing (ids != null): the expert's rows, their order and its
+    // first sorted position come straight from the top-k ids, with no sorted
+    // tables: row q of expert e is the q-th assignment a (ascending) with
+    // ids[a] == e, its first position is the number of assignments to lower
+    // experts, token a / k and routing weight wts[a]; down writes slot a.
+    const int32_t *ids;
+    const float *wts;
+    int k;
+    int TK;
 };
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8_t, v); }
@@ -98,7 +109,8 @@ __device__ __forceinline__ int tswz(int r, int c) { return r * 16 + (c ^ (r & 15
 #ifndef MOE_SKINNY_BF_OCC
 #define MOE_SKINNY_BF_OCC 1
 #endif
-template <bool GATEUP, bool W8>
+// DIRECT: route straight from the top-k ids (see SkinnyParams).
+template <bool GATEUP, bool W8, bool DIRECT>
 __global__ __launch_bounds__((W8 ? SW_W8 : SW_BF) * 64, W8 ? MOE_SKINNY_W8_OCC : MOE_SKINNY_BF_OCC) void skinny_gemm_kernel(SkinnyParams p)
 {
     constexpr int SW = W8 ? SW_W8 : SW_BF;
@@ -113,14 +125,44 @@ __global__ __launch_bounds__((W8 ? SW_W8 : SW_BF) * 64, W8 ? MOE_SKINNY_W8_OCC :
     constexpr int NL = NR / 4;          // load instructions per step
     __shared__ u32x4 s_w[SW][NR * 16];
     __shared__ f32x4_t s_red[SW][NW][64];
-
-    const int e = p.counts ? (int)blockIdx.y : 0;
-    const int M = p.counts ? p.counts[e] : p.dense_rows;
-    if (M <= 0) return;
-    const int row0 = p.counts ? p.offsets[e] : 0;
+    // direct routing: per row of the expert, its token (gate_up) or its
+    // assignment (down)
+    __shared__ int s_rows[DIRECT ? kSkinnyDirectMax : 1];
+    __shared__ int s_cnt[2];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+    const int e = (DIRECT || p.counts) ? (int)blockIdx.y : 0;
+    int M, row0;
+    if (DIRECT) {
+        // one wave scans the ids 64 at a time: a ballot of "== e" gives each
+        // match its rank, a ballot of "< e" counts the lower experts' rows
+        if (wave == 0) {
+            int cnt = 0, lower = 0;
+            for (int a0 = 0; a0 < p.TK; a0 += 64) {
+                const int a = a0 + lane;
+                const int id = a < p.TK ? p.ids[a] : INT_MAX;
+                const uint64_t eq = __ballot(id == e);
+                const uint64_t lt = __ballot(id < e);
+                const int rank = __builtin_amdgcn_mbcnt_hi((uint32_t)(eq >> 32),
+                                                           __builtin_amdgcn_mbcnt_lo((uint32_t)eq, 0u));
+                if (id == e) s_rows[cnt + rank] = GATEUP ? a / p.k : a;
+                cnt += __popcll(eq);
+                lower += __popcll(lt);
+            }
+            if (lane == 0) {
+                s_cnt[0] = cnt;
+                s_cnt[1] = lower;
+            }
+        }
+        __syncthreads();
+        M = s_cnt[0];
+        row0 = s_cnt[1];
+    } else {
+        M = p.counts ? p.counts[e] : p.dense_rows;
+        row0 = p.counts ? p.offsets[e] : 0;
+    }
+    if (M <= 0) return;  // workgroup-uniform
     const int n0 = blockIdx.x * (GATEUP ? 16 : 16 * NW);
     const int lgrp = lane >> 4;
     const int l16 = lane & 15;
@@ -155,7 +197,8 @@ __global__ __launch_bounds__((W8 ? SW_W8 : SW_BF) * 64, W8 ? MOE_SKINNY_W8_OCC :
         const int q = pass + l16;
         const bool xv = q < M;
         const int qc = xv ? q : M - 1;
-        const int64_t src = p.a_rows ? (int64_t)p.a_rows[row0 + qc] : (int64_t)(row0 + qc);
+        const int64_t src = (GATEUP && DIRECT) ? (int64_t)s_rows[qc]
+                            : p.a_rows ? (int64_t)p.a_rows[row0 + qc] : (int64_t)(row0 + qc);
         const __bf16 *xp = p.A + src * p.K;  // the token's row; lanes add their chunk offsets
 
         f32x4_t acc[NW];
@@ -277,8 +320,8 @@ __global__ __launch_bounds__((W8 ? SW_W8 : SW_BF) * 64, W8 ? MOE_SKINNY_W8_OCC :
                         *reinterpret_cast<uint2 *>(reinterpret_cast<__bf16 *>(p.C) + (int64_t)pos * p.N + c) = packed;
                     }
                 } else {
-                    const int64_t orow = p.c_rows ? (int64_t)p.c_rows[pos] : (int64_t)pos;
-                    const float sc = p.c_scale ? p.c_scale[pos] : 1.0f;
+                    const int64_t orow = DIRECT ? (int64_t)s_rows[q] : p.c_rows ? (int64_t)p.c_rows[pos] : (int64_t)pos;
+                    const float sc = DIRECT ? p.wts[s_rows[q]] : p.c_scale ? p.c_scale[pos] : 1.0f;
 #pragma unroll
                     for (int w = 0; w < NW; w++) {
                         const int c = n0 + 16 * w + 4 * lgrp;
@@ -310,6 +353,11 @@ SkinnyParams make_params(const GemmProblem &g)
     s.counts = g.dense_rows > 0 ? nullptr : g.counts;
     s.offsets = g.dense_rows > 0 ? nullptr : g.offsets;
     s.dense_rows = (int)g.dense_rows;
+    const bool direct = g.ids && g.dense_rows <= 0;
+    s.ids = direct ? g.ids : nullptr;
+    s.wts = direct ? g.wts : nullptr;
+    s.k = g.k;
+    s.TK = (int)g.total_rows;
     return s;
 }
 
@@ -319,8 +367,13 @@ hipError_t launch_gate_up_skinny(const GemmProblem &g, hipStream_t st)
 {
     SkinnyParams s = make_params(g);
     dim3 grid((unsigned)((g.N + 15) / 16), g.dense_rows > 0 ? 1u : (unsigned)g.E);
-    if (g.w_scale) hipLaunchKernelGGL((skinny_gemm_kernel<true, true>), grid, dim3(SW_W8 * 64), 0, st, s);
-    else hipLaunchKernelGGL((skinny_gemm_kernel<true, false>), grid, dim3(SW_BF * 64), 0, st, s);
+    if (g.w_scale) {
+        s.ids = nullptr;  // E4M3 weights always take the sorted tables
+        hipLaunchKernelGGL((skinny_gemm_kernel<true, true, false>), grid, dim3(SW_W8 * 64), 0, st, s);
+    } else {
+        if (s.ids) hipLaunchKernelGGL((skinny_gemm_kernel<true, false, true>), grid, dim3(SW_BF * 64), 0, st, s);
+        else hipLaunchKernelGGL((skinny_gemm_kernel<true, false, false>), grid, dim3(SW_BF * 64), 0, st, s);
+    }
     return hipGetLastError();
 }
 
@@ -329,8 +382,13 @@ hipError_t launch_down_skinny(const GemmProblem &g, hipStream_t st)
     SkinnyParams s = make_params(g);
     constexpr int rows = 16 * MOE_SKINNY_DOWN_BLOCKS;
     dim3 grid((unsigned)((g.N + rows - 1) / rows), g.dense_rows > 0 ? 1u : (unsigned)g.E);
-    if (g.w_scale) hipLaunchKernelGGL((skinny_gemm_kernel<false, true>), grid, dim3(SW_W8 * 64), 0, st, s);
-    else hipLaunchKernelGGL((skinny_gemm_kernel<false, false>), grid, dim3(SW_BF * 64), 0, st, s);
+    if (g.w_scale) {
+        s.ids = nullptr;
+        hipLaunchKernelGGL((skinny_gemm_kernel<false, true, false>), grid, dim3(SW_W8 * 64), 0, st, s);
+    } else {
+        if (s.ids) hipLaunchKernelGGL((skinny_gemm_kernel<false, false, true>), grid, dim3(SW_BF * 64), 0, st, s);
+        else hipLaunchKernelGGL((skinny_gemm_kernel<false, false, false>), grid, dim3(SW_BF * 64), 0, st, s);
+    }
     return hipGetLastError();
 }
 

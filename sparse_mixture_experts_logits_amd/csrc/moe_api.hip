@@ -308,12 +308,23 @@ int moe_forward(const void *hidden, const void *router_w, const void *gate_up, c
                                             st),
                     "router_topk")) || (rc = mark(1 + MOE_STAGE_ROUTER)))
         return rc;
-    if ((rc = check(moe::launch_route_scan(s, opts->expert_counts, opts->expert_offsets, rs, ws, st), "route_scan")) ||
-        (rc = mark(1 + MOE_STAGE_SCAN)))
-        return rc;
-    if ((rc = check(moe::launch_route_permute(s, opts->perm, opts->inv_perm, ws, st), "route_permute")) ||
-        (rc = mark(1 + MOE_STAGE_PERMUTE)))
-        return rc;
+    // Few assignments on the weight-streaming kernels, with no sorted routing
+    // tables or statistics asked for: those kernels route straight from the
+    // top-k ids, and the scan and permute launches are skipped (bf16 weights
+    // only: the E4M3 kernels lose more to the extra registers than the two
+    // launches cost).
+    const bool direct = skinny && !f32 && !w8 && T * k <= moe::kSkinnyDirectMax && !opts->expert_counts &&
+                        !opts->expert_offsets && !opts->perm && !opts->inv_perm && !rs.on();
+    if (!direct) {
+        if ((rc = check(moe::launch_route_scan(s, opts->expert_counts, opts->expert_offsets, rs, ws, st),
+                        "route_scan")))
+            return rc;
+    }
+    if ((rc = mark(1 + MOE_STAGE_SCAN))) return rc;
+    if (!direct) {
+        if ((rc = check(moe::launch_route_permute(s, opts->perm, opts->inv_perm, ws, st), "route_permute"))) return rc;
+    }
+    if ((rc = mark(1 + MOE_STAGE_PERMUTE))) return rc;
 
     moe::GemmProblem gu;
     gu.A = hidden;
@@ -335,6 +346,9 @@ int moe_forward(const void *hidden, const void *router_w, const void *gate_up, c
     gu.dense_rows = 0;
     gu.total_rows = T * k;
     gu.part = ws.part;
+    gu.ids = direct ? ws.ids : nullptr;
+    gu.wts = direct ? ws.wts : nullptr;
+    gu.k = k;
 
     moe::GemmProblem dn = gu;
     dn.A = ws.h;
@@ -371,6 +385,8 @@ int moe_forward(const void *hidden, const void *router_w, const void *gate_up, c
         sg.dense_rows = T;
         sg.total_rows = T;
         sg.part = nullptr;  // dense problems are not split
+        sg.ids = nullptr;
+        sg.wts = nullptr;
         moe::GemmProblem sd = sg;
         sd.A = ws.sh_h;
         sd.W = opts->shared_down;

@@ -157,7 +157,15 @@ struct GemmProblem {
     int64_t dense_rows;
     int64_t total_rows;      // host-known number of rows (TK or T)
     float *part = nullptr;   // large-M schedule: partial sums of split tiles (null: no splitting)
+    // weight-streaming schedule, direct routing: rows taken straight from the
+    // top-k ids (no sorted tables; see the skinny kernel)
+    const int32_t *ids = nullptr;
+    const float *wts = nullptr;
+    int k = 0;
 };
+
+// Largest T*k for which the weight-streaming kernels route directly from the ids.
+constexpr int kSkinnyDirectMax = 1024;
 
 hipError_t launch_gate_up_tiled(const GemmProblem &p, hipStream_t st);
 hipError_t launch_down_tiled(const GemmProblem &p, hipStream_t st);

@@ -72,6 +72,23 @@ def run_gpu(inp, flags=0, T=None, shared=True):
     return out, r
 
 
+def run_gpu_plain(inp, flags=0):
+    """The layer with no routing outputs requested (the launch configuration
+    the benchmark times: at few assignments the weight-streaming kernels
+    route straight from the top-k ids)."""
+    wl = inp.wl
+    sgu = sdn = None
+    if inp.shared_gate_up:
+        gu, dn = inp.shared_concat()
+        sgu, sdn = dev(gu), dev(dn)
+    bias = None if inp.bias is None else torch.from_numpy(inp.bias).cuda()
+    out = moe.moe_forward(dev(inp.hidden), dev(inp.router_w), dev(inp.gate_up), dev(inp.down), wl.k,
+                          routed_scale=wl.routed_scale, router_bias=bias, shared_gate_up=sgu,
+                          shared_down=sdn, flags=flags)
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy()
+
+
 def oracle_routing(inp):
     wl = inp.wl
     logits = oracle.router_logits(inp.hidden, inp.router_w, inp.bias)
@@ -223,6 +240,23 @@ def test_tail_rows_folded_into_tiles(counts, H, I):
         check_out(out, r_out, f"tail tiles flags={flags}")
 
 
+@pytest.mark.parametrize("kw", [
+    dict(T=32, H=512, I=256, E=16, k=2),                     # 64 assignments: one ballot round
+    dict(T=5, H=256, I=128, E=64, k=6, routed_scale=2.5),    # most experts without rows
+    dict(T=200, H=264, I=136, E=8, k=4),                     # 800 assignments, ragged K and N
+    dict(T=40, H=128, I=64, E=4, k=2, n_shared=1, shared_I=32),
+    dict(T=300, H=128, I=64, E=8, k=4),                      # 1200 > 1024: sorted tables again
+], ids=["decode", "sparse_experts", "many_rows", "shared", "over_limit"])
+def test_direct_routing_matches_sorted_tables(kw):
+    _say(f"case direct routing {kw}")
+    inp = W.custom_inputs(**kw, std_weight=0.05)
+    out_sorted, _ = run_gpu(inp, flags=moe.FLAG_FORCE_SKINNY)
+    out_direct = run_gpu_plain(inp, flags=moe.FLAG_FORCE_SKINNY)
+    assert np.array_equal(out_direct.view(np.uint32), out_sorted.view(np.uint32))
+    ref = oracle_routing(inp)
+    check_out(out_direct, oracle_out(inp, ref, np.arange(inp.wl.T, dtype=np.int32)), "direct routing")
+
+
 # ------------------------------------------------------------------ full-size workloads
 
 FULL = ["phimoe_decode", "phimoe_prefill", "instella_fine", "phimoe_skewed"]
@@ -242,6 +276,18 @@ def test_full_size_workload(name):
     toks = sample_tokens(inp.wl.T)
     r_out = oracle_out(inp, ref, toks)
     check_out(out[toks], r_out, name)
+
+
+def test_full_size_decode_as_benchmarked():
+    # the default launch (no routing outputs): direct routing on the decode workload
+    _say("case phimoe_decode, benchmark launch")
+    inp = host_inputs("phimoe_decode")
+    ref = oracle_routing(inp)
+    out = run_gpu_plain(inp)
+    out_sorted, got = run_gpu(inp)
+    check_routing(got, ref, "phimoe_decode")
+    assert np.array_equal(out.view(np.uint32), out_sorted.view(np.uint32))
+    check_out(out, oracle_out(inp, ref, np.arange(inp.wl.T, dtype=np.int32)), "phimoe_decode direct")
 
 
 @pytest.mark.parametrize("name,flags", [("phimoe_decode", moe.FLAG_FORCE_TILED),
