@@ -144,7 +144,8 @@ typedef struct moe_opts {
      * Defaults (all zero) give the PhiMoE softmax router above.
      *
      * score_func = MOE_SCORE_SIGMOID: the score of expert e is
-     * s = 1 / (1 + exp(-c)), c = the logit clamped to [-80, 80], in fp32 with
+     * s = 1 / (1 + exp(-c)), c = the logit clamped to [-80, 80] (fmin/fmax:
+     * a NaN logit becomes -80), in fp32 with
      * exp built from correctly rounded IEEE operations only, so it is the
      * same bit for bit on any conforming machine:
      *   n = rint(x * fl(1/ln2)); r = fma(-n, A, x); r = fma(-n, B, r) with
@@ -228,8 +229,10 @@ int64_t moe_workspace_bytes(int64_t T, int64_t H, int64_t I, int64_t E, int32_t 
  * P[0..63], element i = 512c + 8L + v (v = 0..7) fused-multiply-added into
  * P[L] with c ascending, then v ascending; then for d = 32, 16, 8, 4, 2, 1
  * every P[L] becomes P[L] + P[L xor d]; the logit is P[0] + router_bias[e].
- * Experts rank by logit, ties to the lower index; slot j of a token holds
- * its j-th ranked expert. Weights are exp(l_j - l_0) / sum_i exp(l_i - l_0)
+ * Experts rank by logit, ties to the lower index, a NaN key below every
+ * number (so every token gets k valid experts whatever its inputs; its
+ * weights and outputs are then NaN); slot j of a token holds its j-th
+ * ranked expert. Weights are exp(l_j - l_0) / sum_i exp(l_i - l_0)
  * over the selected experts, times routed_scale. Assignments are grouped by
  * expert, ascending t*k+j inside each group.
  *

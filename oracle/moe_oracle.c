@@ -110,10 +110,18 @@ int oracle_router_logits(const void *X, const void *Wr, const float *bias, int d
     return OR_OK;
 }
 
-/* Expert a ranks before expert b iff l[a] > l[b], or l[a] == l[b] and a < b. */
+/* Ranking value of a key: a NaN ranks below every number (as -inf). */
+static float rank_value(float x)
+{
+    return x != x ? -INFINITY : x;
+}
+
+/* Expert a ranks before expert b iff l[a] > l[b], or l[a] == l[b] and a < b
+ * (NaN taken as -inf). */
 static int ranks_before(const float *l, int64_t a, int64_t b)
 {
-    return l[a] > l[b] || (l[a] == l[b] && a < b);
+    const float va = rank_value(l[a]), vb = rank_value(l[b]);
+    return va > vb || (va == vb && a < b);
 }
 
 int oracle_select_topk(const float *logits, int64_t T, int64_t E, int k, float routed_scale,
@@ -546,8 +554,9 @@ static float exp_by_reduction(float x)
 
 static float sigmoid_score(float l)
 {
-    float c = l < -80.0f ? -80.0f : l;
-    c = c > 80.0f ? 80.0f : c;
+    /* fmaxf / fminf return the number when the other operand is NaN: a NaN
+       logit scores as -80 */
+    const float c = fminf(fmaxf(l, -80.0f), 80.0f);
     return 1.0f / (1.0f + exp_by_reduction(-c));
 }
 
@@ -569,9 +578,11 @@ int oracle_sigmoid_scores(const float *x, int64_t n, float *y)
     return OR_OK;
 }
 
-/* a ranks before b: larger value, then lower index */
+/* a ranks before b: larger value, then lower index (NaN taken as -inf) */
 static int before(float va, int64_t a, float vb, int64_t b)
 {
+    va = rank_value(va);
+    vb = rank_value(vb);
     return va > vb || (va == vb && a < b);
 }
 

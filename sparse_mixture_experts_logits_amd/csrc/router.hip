@@ -243,6 +243,7 @@ __global__ __launch_bounds__(256) void router_topk_kernel(
             sc[q] = (e < E && sigm) ? sigmoid_ieee(v[q]) : v[q];
             key[q] = sc[q];
             if (e < E && sel_bias) key[q] = key[q] + sel_bias[e];
+            if (key[q] != key[q]) key[q] = -INFINITY;  // a NaN key ranks below every number
         }
         const bool counted = stats && (!stats_mask || stats_mask[t] != 0);  // wave-uniform
         if (stats) {
@@ -298,7 +299,7 @@ __global__ __launch_bounds__(256) void router_topk_kernel(
                     pv = bv;
                     pi = bi;
                 }
-                gsc = sum;
+                gsc = sum != sum ? -INFINITY : sum;  // (+inf) + (-inf)
             }
             // keep the topk_group best groups (ties to the lower group)
             bool kept = false;
@@ -327,7 +328,9 @@ __global__ __launch_bounds__(256) void router_topk_kernel(
             }
         }
         for (int s = 0; s < k; s++) {
-            float bv = -FLT_MAX;
+            // -inf, so that an expert whose key is -inf can still be chosen:
+            // every token gets k valid experts whatever its logits
+            float bv = -INFINITY;
             int bi = INT_MAX;
 #pragma unroll
             for (int q = 0; q < 4; q++) {

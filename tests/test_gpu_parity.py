@@ -182,6 +182,34 @@ def test_router_ties_and_zero_router():
     assert np.all(got["ids"] == np.arange(3))
 
 
+@pytest.mark.parametrize("flags", [0, moe.FLAG_FORCE_TILED], ids=["auto", "tiled"])
+def test_nan_and_inf_inputs_route_to_valid_experts(flags):
+    # NaN keys rank below every number on both sides, so routing stays
+    # bit-exact and in range; outputs are compared where the inputs are clean
+    _say(f"case NaN/inf inputs flags={flags}")
+    inp = W.custom_inputs(T=64, H=256, I=64, E=8, k=2, std_weight=0.05)
+    nan16, inf16 = np.uint16(0x7FC0), np.uint16(0x7F80)
+    wr = inp.router_w.copy()
+    wr[3, :] = nan16          # expert 3: NaN logits for every token
+    wr[5, 17] = inf16         # expert 5: +-inf (or NaN) logits
+    inp.router_w = wr
+    hid = inp.hidden.copy()
+    hid[7, :] = nan16         # token 7: every logit NaN -> experts 0, 1
+    hid[9, 100] = inf16
+    inp.hidden = hid
+    ref = oracle_routing(inp)
+    out, got = run_gpu(inp, flags=flags)
+    for key in ("ids", "counts", "offsets", "perm", "inv"):
+        assert np.array_equal(got[key], ref[key]), f"{key} differs"
+    assert got["ids"].min() >= 0 and got["ids"].max() < 8
+    assert got["ids"][7].tolist() == [0, 1]
+    sel = np.take_along_axis(ref["logits"], ref["ids"], 1)
+    clean = np.isfinite(sel).all(1) & np.isfinite(W.bf16_bits_to_f32(hid)).all(1)
+    toks = np.nonzero(clean)[0].astype(np.int32)
+    assert len(toks) > 20
+    check_out(out[toks], oracle_out(inp, ref, toks), "clean tokens")
+
+
 def test_zero_tokens_is_a_no_op():
     inp = W.custom_inputs(T=4, H=64, I=32, E=4, k=2)
     h = dev(inp.hidden)[:0]

@@ -354,3 +354,22 @@ def test_decode_bandwidth_model_matches_page_estimate():
                                           d["active_params_billion"] * 1e9 * d["bytes_per_param"])
     assert round(tps) == d["estimate_tok_per_s"]
     assert abs(d["measured_tok_per_s"] - tps) / tps < 0.05
+
+
+def test_nan_keys_rank_below_every_number():
+    # NaN logits rank as -inf (ties among them to the lower index), so every
+    # token still gets k distinct valid experts
+    nan, inf = np.float32("nan"), np.float32("inf")
+    l = np.array([[nan, 1.0, nan, -inf, 0.5],
+                  [nan, nan, nan, nan, nan],
+                  [-inf, -inf, 2.0, nan, -inf],
+                  [inf, nan, -1.0, inf, 0.0]], np.float32)
+    ids, _ = oracle.select_topk(l, 3)
+    assert ids.tolist() == [[1, 4, 0], [0, 1, 2], [2, 0, 1], [0, 3, 4]]
+    sids, _ = oracle.select_scored(l, 3, 1.0, "softmax")
+    assert np.array_equal(sids, ids)
+    # sigmoid scoring: the clamp maps NaN and -inf alike to -80 (equal
+    # scores, lower index first)
+    g, _ = oracle.select_scored(l, 2, 1.0, "sigmoid")
+    assert g.tolist()[1] == [0, 1]
+    assert g.tolist()[2] == [2, 0]
