@@ -19,6 +19,7 @@
 //     share an expert's weight block run together on one XCD's L2.
 #include "moe_internal.h"
 
+#include <algorithm>
 #include <type_traits>
 
 namespace moe {
@@ -57,6 +58,7 @@ struct TiledParams {
     int NB;     // N-blocks
     float *part;  // partial sums of split tiles (null: no splitting)
     int G;      // workgroups of the persistent launch
+    int cap;    // pieces the partial-sum buffer holds for this tile shape
 };
 
 // The last, partial round of a persistent launch leaves most CUs idle when
@@ -65,7 +67,7 @@ struct TiledParams {
 // fp32 partial sums (in accumulator layout) and a second kernel adds the
 // pieces in piece order and runs the tile's epilogue, so the result does not
 // depend on timing.
-constexpr int kSplitPieces = 256;  // capacity of the partial-sum buffer, in pieces
+constexpr int kSplitPieces = 256;  // routed 256x256 tiles: pieces the buffer is sized for
 constexpr int kMaxSplit = 8;
 
 struct SplitPlan {
@@ -75,10 +77,10 @@ struct SplitPlan {
     int nwork;  // work items of the persistent loop
 };
 
-__device__ __forceinline__ SplitPlan split_plan(int total, int G, int nk, bool enabled)
+__device__ __forceinline__ SplitPlan split_plan(int total, int G, int cap, int nk, bool enabled)
 {
     SplitPlan sp{total, 1, nk, total};
-    const int cap = min(G, kSplitPieces);
+    cap = min(G, cap);
     const int rem = total % G;
     if (!enabled || rem == 0 || 2 * rem > cap || nk < 2) return sp;
     int split = min(min(cap / rem, kMaxSplit), nk);
@@ -305,7 +307,7 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void tiled_gemm_kernel(TiledParam
     // RPI*(wave*INS + i) + lane/CH, chunk slot lane%CH (logical chunk lc below)
     const int drow = lane / CH;
 
-    const SplitPlan sp = split_plan(total, G, nk_all, p.part != nullptr);
+    const SplitPlan sp = split_plan(total, G, p.cap, nk_all, p.part != nullptr);
 
     for (int r = 0;; r++) {
         const int wid = r * G + xcd * nx + li;
@@ -579,7 +581,7 @@ __global__ __launch_bounds__(64) void tiled_split_finish_kernel(TiledParams p)
     const int n_mtiles = p.tiles ? p.tile_start[p.E] : (p.dense_rows + BM - 1) / BM;
     const int total = n_mtiles * p.NB;
     const int nk_all = (p.K + BK - 1) / BK;
-    const SplitPlan sp = split_plan(total, p.G, nk_all, p.part != nullptr);
+    const SplitPlan sp = split_plan(total, p.G, p.cap, nk_all, p.part != nullptr);
     const int t = blockIdx.x / (NWAVE * RM);
     const int wave = (blockIdx.x / RM) % NWAVE;
     const int i = blockIdx.x % RM;  // this workgroup's 32-row block
@@ -711,6 +713,7 @@ TiledParams make_params(const GemmProblem &g, int NB)
     t.NB = NB;
     t.part = nullptr;
     t.G = 0;
+    t.cap = 0;
     return t;
 }
 
@@ -720,12 +723,16 @@ hipError_t launch_cfg(const GemmProblem &g, hipStream_t st)
     const int cols = GATEUP ? BN / 2 : BN;  // output columns per N-block
     TiledParams t = make_params(g, (int)((g.N + cols - 1) / cols));
     t.G = persistent_grid(OCC);
-    t.part = (OCC == 1 && g.part) ? g.part : nullptr;
+    // pieces of this tile shape that fit the buffer (sized for kSplitPieces
+    // routed 256x256 pieces), at most one round of the launch
+    constexpr int64_t piece_bytes = (int64_t)WM * WN * ((BM / WM / 32) * (BN / WN / 32) + (XT > 0 ? 1 : 0)) * 1024 * 4;
+    t.cap = (int)std::min<int64_t>(t.G, tiled_split_bytes() / piece_bytes);
+    t.part = g.part;
     hipLaunchKernelGGL((tiled_gemm_kernel<BM, BN, WM, WN, OCC, GATEUP, XT>), dim3(t.G), dim3(WM * WN * 64), 0, st, t);
     if (t.part) {
-        // at most kSplitPieces / 2 tiles are split (two pieces or more each)
+        // at most cap / 2 tiles are split (two pieces or more each)
         hipLaunchKernelGGL((tiled_split_finish_kernel<BM, BN, WM, WN, GATEUP, XT>),
-                           dim3(kSplitPieces / 2 * WM * WN * (BM / WM / 32)), dim3(64), 0, st, t);
+                           dim3(t.cap / 2 * WM * WN * (BM / WM / 32)), dim3(64), 0, st, t);
     }
     return hipGetLastError();
 }

@@ -384,7 +384,7 @@ int moe_forward(const void *hidden, const void *router_w, const void *gate_up, c
         sg.c_scale = nullptr;
         sg.dense_rows = T;
         sg.total_rows = T;
-        sg.part = nullptr;  // dense problems are not split
+        sg.part = ws.part;  // free again: the routed launches have finished with it
         sg.ids = nullptr;
         sg.wts = nullptr;
         moe::GemmProblem sd = sg;
