@@ -16,7 +16,10 @@
 //     un-permute); a later pass sums the k slots of each token in order.
 //   * tiles are visited expert-major, then N-block, then M-tile, and each
 //     XCD takes a contiguous run of tile ids per round, so the M-tiles that
-//     share an expert's weight block run together on one XCD's L2.
+//     share an expert's weight block run together on one XCD's L2;
+//   * an expert's last few rows ride in its previous tile (XT below) and the
+//     tiles of a short last round are split along K (SplitPlan below), so
+//     neither a handful of rows nor a handful of tiles holds the launch.
 #include "moe_internal.h"
 
 #include <algorithm>
@@ -28,9 +31,6 @@ namespace {
 
 #ifndef MOE_TILED_BK
 #define MOE_TILED_BK 32
-#endif
-#ifndef MOE_TILED_INTERLEAVE
-#define MOE_TILED_INTERLEAVE 1
 #endif
 #ifndef MOE_TILED_STAGES
 #define MOE_TILED_STAGES 4
