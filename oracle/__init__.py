@@ -57,7 +57,11 @@ def _load():
         lib.oracle_sigmoid_scores.argtypes = [vp, i64, vp]
         lib.oracle_select_scored.argtypes = [vp, i64, i64, i32, f32, i32, vp, i32, i32, vp, vp]
         lib.oracle_select_sparsemixer.argtypes = [vp, i64, i64, i32, f32, f32, vp, vp]
-        for f in (lib.oracle_select_sparsemixer, lib.oracle_exp_f32, lib.oracle_sigmoid_scores, lib.oracle_select_scored,
+        lib.oracle_e2m1_values.argtypes = [vp]
+        lib.oracle_quantize_mxfp4_rows.argtypes = [vp, i64, i64, vp, vp]
+        lib.oracle_dequantize_mxfp4_rows.argtypes = [vp, vp, i64, i64, vp]
+        for f in (lib.oracle_e2m1_values, lib.oracle_quantize_mxfp4_rows, lib.oracle_dequantize_mxfp4_rows,
+                  lib.oracle_select_sparsemixer, lib.oracle_exp_f32, lib.oracle_sigmoid_scores, lib.oracle_select_scored,
                   lib.oracle_router_logits, lib.oracle_select_topk, lib.oracle_route,
                   lib.oracle_moe_tokens, lib.oracle_num_threads, lib.oracle_e4m3_values,
                   lib.oracle_quantize_e4m3_rows, lib.oracle_moe_tokens_e4m3, lib.oracle_router_stats):
@@ -250,6 +254,38 @@ def quantize_e4m3_rows(w: np.ndarray):
     scale = np.empty(w.shape[:-1], dtype=np.float32)
     _check(_load().oracle_quantize_e4m3_rows(_p(w), rows, cols, _p(q), _p(scale)), "quantize_e4m3_rows")
     return q, scale
+
+
+def e2m1_values() -> np.ndarray:
+    """Value of each of the 16 FP4 E2M1 codes (fp64)."""
+    out = np.empty(16, dtype=np.float64)
+    _check(_load().oracle_e2m1_values(_p(out)), "e2m1_values")
+    return out
+
+
+def quantize_mxfp4_rows(w: np.ndarray):
+    """MXFP4 quantisation of bf16 bits w [..., cols] (cols % 32 == 0) ->
+    (q uint8 [..., cols/2] two codes per byte, scale uint8 [..., cols/32] E8M0)."""
+    w = np.ascontiguousarray(w)
+    assert w.dtype == np.uint16
+    cols = w.shape[-1]
+    rows = w.size // cols
+    q = np.empty(w.shape[:-1] + (cols // 2,), dtype=np.uint8)
+    scale = np.empty(w.shape[:-1] + (cols // 32,), dtype=np.uint8)
+    _check(_load().oracle_quantize_mxfp4_rows(_p(w), rows, cols, _p(q), _p(scale)), "quantize_mxfp4_rows")
+    return q, scale
+
+
+def dequantize_mxfp4_rows(q: np.ndarray, scale: np.ndarray) -> np.ndarray:
+    """bf16 bits of e2m1(q) * 2^(scale - 127), the shape of q with cols doubled."""
+    q = np.ascontiguousarray(q, dtype=np.uint8)
+    scale = np.ascontiguousarray(scale, dtype=np.uint8)
+    cols = q.shape[-1] * 2
+    rows = q.size * 2 // cols
+    assert scale.shape == q.shape[:-1] + (cols // 32,)
+    w = np.empty(q.shape[:-1] + (cols,), dtype=np.uint16)
+    _check(_load().oracle_dequantize_mxfp4_rows(_p(q), _p(scale), rows, cols, _p(w)), "dequantize_mxfp4_rows")
+    return w
 
 
 def moe_tokens_e4m3(hidden, gate_up_q, gu_scale, down_q, dn_scale, ids, weights, tokens=None, shared=()):

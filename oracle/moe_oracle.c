@@ -712,3 +712,105 @@ int oracle_select_sparsemixer(const float *logits, int64_t T, int64_t E, int k, 
     }
     return OR_OK;
 }
+
+/*
+ * MXFP4 expert weights (OCP Microscaling Formats v1.0, MXFP4: the pages' "mxfp4
+ * with block scales", the MoEs in Transformers page, sections on why MoEs are
+ * fast and on weight loading). Each row of a weight matrix is cut into blocks
+ * of 32 consecutive elements sharing one power-of-two factor 2^x, x stored
+ * as the E8M0 byte x + 127; each element is an FP4 E2M1 code: bit 3 sign,
+ * bits 2..1 exponent field e (bias 1), bit 0 mantissa m; e = 0 gives m * 0.5,
+ * otherwise 2^(e-1) * (1 + m/2) -- magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6.
+ * Quantisation follows the specification's conversion: x = floor(log2 a) - 2
+ * for the block's largest magnitude a (2 = the largest E2M1 exponent),
+ * clamped to [-127, 127] (a = 0 or below 2^-126 gives -127); each element
+ * becomes the E2M1 value nearest to w / 2^x, ties to the even code (m = 0),
+ * magnitudes past 6 saturating to 6; the sign bit is w's. Packing: element 2i
+ * in the low nibble of byte i, element 2i+1 in the high nibble.
+ */
+static double e2m1_value(int code)
+{
+    const int e = (code >> 1) & 3, m = code & 1;
+    const double v = e == 0 ? 0.5 * m : ldexp(1.0 + 0.5 * m, e - 1);
+    return (code & 8) ? -v : v;
+}
+
+int oracle_e2m1_values(double *out)
+{
+    if (!out)
+        return OR_BAD;
+    for (int c = 0; c < 16; c++)
+        out[c] = e2m1_value(c);
+    return OR_OK;
+}
+
+static double bf16_value(uint16_t b)
+{
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+/* x of a block whose largest magnitude is a */
+static int mx_block_exponent(double a)
+{
+    if (!(a >= ldexp(1.0, -126)))
+        return -127;
+    int x;
+    frexp(a, &x); /* a = f * 2^x, f in [0.5, 1): floor(log2 a) = x - 1 */
+    int s = x - 1 - 2;
+    return s < -127 ? -127 : (s > 127 ? 127 : s);
+}
+
+int oracle_quantize_mxfp4_rows(const uint16_t *w, int64_t rows, int64_t cols, uint8_t *q, uint8_t *scale)
+{
+    if (!w || !q || !scale || rows < 0 || cols <= 0 || cols % 32)
+        return OR_BAD;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; r++)
+        for (int64_t b = 0; b < cols / 32; b++) {
+            const uint16_t *blk = w + r * cols + b * 32;
+            double a = 0.0;
+            for (int i = 0; i < 32; i++)
+                a = fmax(a, fabs(bf16_value(blk[i])));
+            const int x = mx_block_exponent(a);
+            scale[r * (cols / 32) + b] = (uint8_t)(x + 127);
+            for (int i = 0; i < 32; i++) {
+                const double y = fabs(bf16_value(blk[i])) / ldexp(1.0, x); /* exact in fp64 */
+                /* brute force: the nearest of the 8 magnitudes, ties to the even code */
+                int best = 0;
+                for (int c = 1; c < 8; c++) {
+                    const double dc = fabs(y - e2m1_value(c)), db = fabs(y - e2m1_value(best));
+                    if (dc < db || (dc == db && (c & 1) == 0))
+                        best = c;
+                }
+                const int code = best | ((blk[i] >> 15) ? 8 : 0);
+                uint8_t *dst = q + r * (cols / 2) + b * 16 + i / 2;
+                if (i % 2 == 0)
+                    *dst = (uint8_t)code;
+                else
+                    *dst = (uint8_t)(*dst | (code << 4));
+            }
+        }
+    return OR_OK;
+}
+
+/* w = e2m1(q) * 2^(scale - 127) as bf16 bits (exact: three significant bits) */
+int oracle_dequantize_mxfp4_rows(const uint8_t *q, const uint8_t *scale, int64_t rows, int64_t cols, uint16_t *w)
+{
+    if (!q || !scale || !w || rows < 0 || cols <= 0 || cols % 32)
+        return OR_BAD;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; r++)
+        for (int64_t i = 0; i < cols; i++) {
+            const uint8_t byte = q[r * (cols / 2) + i / 2];
+            const int code = (i % 2 == 0) ? (byte & 15) : (byte >> 4);
+            const int x = (int)scale[r * (cols / 32) + i / 32] - 127;
+            const float f = (float)(e2m1_value(code) * ldexp(1.0, x));
+            uint32_t u;
+            memcpy(&u, &f, sizeof u);
+            w[r * cols + i] = (uint16_t)(u >> 16);
+        }
+    return OR_OK;
+}
