@@ -72,9 +72,12 @@ typedef enum moe_score_func {
 /* Storage of the routed experts' weights (gate_up, down). */
 typedef enum moe_weight_format {
     MOE_WEIGHTS_NATIVE = 0,  /* same dtype as the activations (opts->dtype)          */
-    MOE_WEIGHTS_FP8_E4M3 = 1 /* one byte per weight, OCP FP8 E4M3, plus one fp32    */
+    MOE_WEIGHTS_FP8_E4M3 = 1, /* one byte per weight, OCP FP8 E4M3, plus one fp32   */
                              /* scale per weight row: w = e4m3(q) * scale (see      */
                              /* moe_quantize_fp8_rows); bf16 activations only        */
+    MOE_WEIGHTS_MXFP4 = 2    /* OCP MX FP4: two E2M1 weights per byte and one E8M0 */
+                             /* scale byte per 32 weights of a row (see            */
+                             /* moe_quantize_mxfp4_rows); bf16 activations only     */
 } moe_weight_format;
 
 /* opts->flags bits: choose the expert-GEMM schedule (default: by shape). */
@@ -182,6 +185,13 @@ typedef struct moe_opts {
     int32_t topk_group;
     float jitter_eps;             /* sparsemixer threshold; moe_opts_init sets */
                                   /* 0.01 (PhiMoE's router_jitter_noise)       */
+    /* MOE_WEIGHTS_MXFP4: gate_up holds [E, 2I, H/2] bytes and down [E, H, I/2]
+     * (codes of elements 2i and 2i+1 in the low and high nibble of byte i),
+     * with E8M0 block scales gate_up_block_scale [E, 2I, H/32] and
+     * down_block_scale [E, H, I/32]; H and I multiples of 32; weight-streaming
+     * kernels only (MOE_FLAG_FORCE_TILED is rejected). */
+    const uint8_t *gate_up_block_scale;
+    const uint8_t *down_block_scale;
 } moe_opts;
 
 /* Stages of moe_forward, in launch order. */
@@ -261,6 +271,25 @@ int moe_forward(const void *hidden, const void *router_w, const void *gate_up, c
 int moe_quantize_fp8_rows(const void *w, int64_t rows, int64_t cols, void *q, float *scale, void *stream);
 
 /* Message describing the last failing call on this thread ("" if none). */
+/*
+ * MXFP4 quantisation (OCP Microscaling Formats v1.0, MXFP4) of a bf16 matrix
+ * w [rows, cols], in blocks of 32 consecutive elements of a row:
+ *   a = the block's largest magnitude; x = floor(log2 a) - 2 (2 = the largest
+ *   E2M1 exponent), clamped to [-127, 127], -127 when a < 2^-126;
+ *   scale byte = x + 127 (E8M0: the block's factor is 2^x);
+ *   each code = the E2M1 value nearest to w / 2^x, ties to the even code,
+ *   magnitudes past 6 saturating to 6, sign bit = w's sign bit.
+ * E2M1 code: bit 3 sign, bits 2..1 exponent e (bias 1), bit 0 mantissa m;
+ * e = 0 gives m * 0.5, otherwise 2^(e-1) * (1 + m/2): 0, 0.5, 1, 1.5, 2, 3,
+ * 4, 6. The weight is code value * 2^x (exactly a bf16 value).
+ * q [rows, cols/2] bytes (element 2i in the low nibble of byte i, 2i+1 in the
+ * high nibble) and scale [rows, cols/32] bytes are device outputs; cols a
+ * positive multiple of 32; w 16-byte aligned. Asynchronous on stream
+ * (hipStream_t, NULL = default). Returns MOE_OK or a negative moe_status
+ * (argument errors before any HIP call).
+ */
+int moe_quantize_mxfp4_rows(const void *w, int64_t rows, int64_t cols, void *q, void *scale, void *stream);
+
 const char *moe_last_error(void);
 
 #ifdef __cplusplus

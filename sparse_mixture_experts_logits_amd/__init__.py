@@ -13,7 +13,7 @@ import os
 import numpy as np
 
 __all__ = ["moe_forward", "workspace_bytes", "quantize_fp8_rows", "MoeError", "load_library", "LIB_PATH",
-           "FLAG_FORCE_TILED", "FLAG_FORCE_SKINNY", "WEIGHTS_NATIVE", "WEIGHTS_FP8_E4M3",
+           "FLAG_FORCE_TILED", "FLAG_FORCE_SKINNY", "WEIGHTS_NATIVE", "WEIGHTS_FP8_E4M3", "WEIGHTS_MXFP4", "quantize_mxfp4_rows",
            "SCORE_SOFTMAX", "SCORE_SIGMOID", "SCORE_SPARSEMIXER",
            "bf16_bits_to_tensor", "EXPORTS"]
 
@@ -27,10 +27,12 @@ FLAG_FORCE_TILED = 0x1
 FLAG_FORCE_SKINNY = 0x2
 WEIGHTS_NATIVE = 0
 WEIGHTS_FP8_E4M3 = 1
+WEIGHTS_MXFP4 = 2
 SCORE_SOFTMAX = 0
 SCORE_SIGMOID = 1
 SCORE_SPARSEMIXER = 2
-EXPORTS = ("moe_opts_init", "moe_workspace_bytes", "moe_forward", "moe_quantize_fp8_rows", "moe_last_error")
+EXPORTS = ("moe_opts_init", "moe_workspace_bytes", "moe_forward", "moe_quantize_fp8_rows",
+           "moe_quantize_mxfp4_rows", "moe_last_error")
 STAGES = ("router", "scan", "permute", "gate_up", "down", "shared_gate_up", "shared_down", "combine")
 STAGE_EVENTS = len(STAGES) + 1
 
@@ -72,6 +74,8 @@ class MoeOpts(ctypes.Structure):
         ("n_group", ctypes.c_int32),
         ("topk_group", ctypes.c_int32),
         ("jitter_eps", ctypes.c_float),
+        ("gate_up_block_scale", ctypes.c_void_p),
+        ("down_block_scale", ctypes.c_void_p),
     ]
 
 
@@ -105,6 +109,8 @@ def load_library():
         lib.moe_forward.restype = ctypes.c_int
         lib.moe_quantize_fp8_rows.argtypes = [vp, i64, i64, vp, vp, vp]
         lib.moe_quantize_fp8_rows.restype = ctypes.c_int
+        lib.moe_quantize_mxfp4_rows.argtypes = [vp, i64, i64, vp, vp, vp]
+        lib.moe_quantize_mxfp4_rows.restype = ctypes.c_int
         lib.moe_last_error.argtypes = []
         lib.moe_last_error.restype = ctypes.c_char_p
         _lib = lib
@@ -165,18 +171,43 @@ def quantize_fp8_rows(w, stream=None):
     return q, scale
 
 
+def quantize_mxfp4_rows(w, stream=None):
+    """MXFP4 quantisation (OCP MX: E2M1 codes, one E8M0 scale per 32
+    consecutive elements of a row) of a contiguous bf16 CUDA tensor viewed as
+    [rows, cols], cols a multiple of 32: returns (q uint8 [..., cols/2], two
+    codes per byte, low nibble first; scale uint8 [..., cols/32])."""
+    import torch
+    if w.dtype != torch.bfloat16 or not w.is_contiguous() or not w.is_cuda:
+        raise ValueError("w must be a contiguous bf16 CUDA tensor")
+    cols = w.shape[-1]
+    rows = w.numel() // cols if cols else 0
+    q = torch.empty(w.shape[:-1] + (cols // 2,), dtype=torch.uint8, device=w.device)
+    scale = torch.empty(w.shape[:-1] + (cols // 32,), dtype=torch.uint8, device=w.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(w.device)
+    rc = load_library().moe_quantize_mxfp4_rows(_ptr(w), rows, cols, _ptr(q), _ptr(scale),
+                                                ctypes.c_void_p(stream.cuda_stream))
+    if rc != 0:
+        raise MoeError(rc, last_error())
+    return q, scale
+
+
 def moe_forward(hidden, router_w, gate_up, down, k: int, *, routed_scale: float = 1.0, router_bias=None,
                 shared_gate_up=None, shared_down=None, flags: int = 0, return_routing: bool = False,
                 out=None, workspace=None, stream=None, stage_events=None, gate_up_scale=None, down_scale=None,
                 router_stats: bool = False, stats_mask=None, score_func: str = "softmax",
-                selection_bias=None, n_group: int = 0, topk_group: int = 0, jitter_eps: float | None = None):
+                selection_bias=None, n_group: int = 0, topk_group: int = 0, jitter_eps: float | None = None,
+                gate_up_block_scale=None, down_block_scale=None):
     """Run the MoE layer on torch tensors already on the GPU.
 
     hidden [T, H], router_w [E, H], gate_up [E, 2I, H], down [E, H, I] (all
     bf16 or all fp32, contiguous); router_bias [E] fp32; shared_gate_up
     [2Is, H], shared_down [H, Is]. FP8 expert weights: gate_up and down as
     uint8 E4M3 codes with gate_up_scale [E, 2I] and down_scale [E, H] (fp32,
-    from quantize_fp8_rows); activations bf16. ``router_stats`` adds the
+    from quantize_fp8_rows); activations bf16. MXFP4 expert weights: gate_up
+    [E, 2I, H/2] and down [E, H, I/2] uint8 (two E2M1 codes per byte) with
+    gate_up_block_scale [E, 2I, H/32] and down_block_scale [E, H, I/32] uint8
+    (from quantize_mxfp4_rows). ``router_stats`` adds the
     load-balancing statistics (prob_mean [E], load [E], aux_loss [1]) to the
     routing dict, over the tokens with ``stats_mask`` != 0 (int32 [T]; all
     tokens if None). ``score_func`` "sigmoid" scores experts by the sigmoid of
@@ -201,8 +232,9 @@ def moe_forward(hidden, router_w, gate_up, down, k: int, *, routed_scale: float 
         o.dtype = MOE_F32
     else:
         raise TypeError(f"unsupported dtype {hidden.dtype}")
-    w8 = gate_up.dtype == torch.uint8
-    if w8:
+    lowp = gate_up.dtype == torch.uint8  # FP8 or MXFP4 expert weights
+    w4 = lowp and gate_up_block_scale is not None
+    if lowp and not w4:
         if down.dtype != torch.uint8 or gate_up_scale is None or down_scale is None:
             raise ValueError("FP8 weights need uint8 gate_up and down plus gate_up_scale and down_scale")
         gate_up_scale = gate_up_scale.to(dtype=torch.float32).contiguous()
@@ -212,15 +244,27 @@ def moe_forward(hidden, router_w, gate_up, down, k: int, *, routed_scale: float 
         o.weight_format = WEIGHTS_FP8_E4M3
         o.gate_up_scale = gate_up_scale.data_ptr()
         o.down_scale = down_scale.data_ptr()
+    if w4:
+        if down.dtype != torch.uint8 or down_block_scale is None:
+            raise ValueError("MXFP4 weights need uint8 gate_up and down plus both block scales")
+        gate_up_block_scale = gate_up_block_scale.to(dtype=torch.uint8).contiguous()
+        down_block_scale = down_block_scale.to(dtype=torch.uint8).contiguous()
+        if gate_up_block_scale.shape != (E, 2 * I, H // 32) or down_block_scale.shape != (E, H, I // 32):
+            raise ValueError("block scales must be [E, 2I, H/32] and [E, H, I/32]")
+        o.weight_format = WEIGHTS_MXFP4
+        o.gate_up_block_scale = gate_up_block_scale.data_ptr()
+        o.down_block_scale = down_block_scale.data_ptr()
     acts = [hidden, router_w] + [t for t in (shared_gate_up, shared_down) if t is not None]
-    acts += [] if w8 else [gate_up, down]
-    for t in acts + ([gate_up, down] if w8 else []):
+    acts += [] if lowp else [gate_up, down]
+    for t in acts + ([gate_up, down] if lowp else []):
         if not t.is_contiguous() or not t.is_cuda:
             raise ValueError("all tensors must be contiguous CUDA tensors")
     for t in acts:
         if t.dtype != hidden.dtype:
             raise ValueError("activations, router and native-format weights must share one dtype")
-    if router_w.shape != (E, H) or gate_up.shape != (E, 2 * I, H) or down.shape != (E, H, I):
+    wcols = 2 if w4 else 1  # MXFP4: two codes per byte
+    if router_w.shape != (E, H) or gate_up.shape != (E, 2 * I, H // wcols) or \
+            down.shape != (E, H, I // wcols) or (w4 and (H % 32 or I % 32)):
         raise ValueError("shape mismatch among hidden, router_w, gate_up, down")
     o.routed_scale = float(routed_scale)
     o.flags = int(flags)
@@ -294,6 +338,7 @@ def moe_forward(hidden, router_w, gate_up, down, k: int, *, routed_scale: float 
     if stream != current:
         # buffers allocated here belong to the current stream's pool
         for t in (router_bias, workspace, out, gate_up_scale, down_scale, stats_mask, selection_bias,
+                  gate_up_block_scale, down_block_scale,
                   *(routing.values() if routing else ())):
             if t is not None:
                 t.record_stream(stream)

@@ -23,6 +23,12 @@
 //     chunk is widened to two bf16 MFMA fragments in registers (exact: every
 //     E4M3 value is a bf16 value) and the row scale multiplies the
 //     accumulated sum in the epilogue, so a decode step reads half the bytes.
+//   * MXFP4 weights (OCP MX: FP4 E2M1, two per byte, one E8M0 scale per 32
+//     weights of a row): a 16-byte chunk is one block of 32 weights; its
+//     scale byte travels with it through LDS, and each 32-bit word becomes
+//     one bf16 MFMA fragment through four gfx950 scaled conversions (exact:
+//     an E2M1 value times a power of two is a bf16 value), a quarter of the
+//     bf16 bytes per decode step.
 #include "moe_internal.h"
 
 #include <limits.h>
@@ -56,8 +62,9 @@ constexpr int SW_W8 = MOE_SKINNY_WAVES_W8;  // the same for E4M3 weights
 struct SkinnyParams {
     const __bf16 *A;
     const int32_t *a_rows;
-    const void *W;             // bf16 or E4M3 bytes
+    const void *W;             // bf16, E4M3 bytes or packed E2M1 nibbles
     const float *w_scale;      // E4M3: [E, rows per expert] scales, else null
+    const uint8_t *w_bscale;   // MXFP4: [E, rows per expert, K / 32] E8M0 bytes, else null
     int64_t w_expert_stride;
     int K;
     int N;
@@ -93,6 +100,19 @@ __device__ __forceinline__ u32x4 e4m3x8_to_bf16(uint32_t w0, uint32_t w1)
                  __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true))};
 }
 
+// Eight E2M1 weights (one 32-bit word, element 2i in the low nibble of byte
+// i) times the block factor s -> eight bf16 (exact for these products).
+__device__ __forceinline__ u32x4 e2m1x8_to_bf16(uint32_t w, float s)
+{
+    return u32x4{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 0)),
+                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 1)),
+                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 2)),
+                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 3))};
+}
+
+// the factor 2^(b - 127) of an E8M0 byte b as fp32 (b = 0: the subnormal 2^-127)
+__device__ __forceinline__ float e8m0_factor(uint32_t b) { return __uint_as_float(b ? b << 23 : 0x00400000u); }
+
 // v, or zeros when c is false (a per-component select: selecting between two
 // lvalues would take their addresses and keep the staging arrays in memory)
 __device__ __forceinline__ u32x4 keep_if(bool c, const u32x4 v)
@@ -106,18 +126,28 @@ __device__ __forceinline__ int tswz(int r, int c) { return r * 16 + (c ^ (r & 15
 #ifndef MOE_SKINNY_W8_OCC
 #define MOE_SKINNY_W8_OCC 3
 #endif
+#ifndef MOE_SKINNY_W4_OCC
+#define MOE_SKINNY_W4_OCC 2
+#endif
 #ifndef MOE_SKINNY_BF_OCC
 #define MOE_SKINNY_BF_OCC 1
 #endif
+// FMT: weight storage, 0 bf16, 1 E4M3 (row scales), 2 MXFP4 (block scales).
 // DIRECT: route straight from the top-k ids (see SkinnyParams).
-template <bool GATEUP, bool W8, bool DIRECT>
-__global__ __launch_bounds__((W8 ? SW_W8 : SW_BF) * 64, W8 ? MOE_SKINNY_W8_OCC : MOE_SKINNY_BF_OCC) void skinny_gemm_kernel(SkinnyParams p)
+template <bool GATEUP, int FMT, bool DIRECT>
+__global__ __launch_bounds__((FMT ? SW_W8 : SW_BF) * 64,
+                             FMT == 2 ? MOE_SKINNY_W4_OCC : FMT ? MOE_SKINNY_W8_OCC : MOE_SKINNY_BF_OCC) void skinny_gemm_kernel(SkinnyParams p)
 {
-    constexpr int SW = W8 ? SW_W8 : SW_BF;
-    constexpr int PD = W8 ? MOE_SKINNY_PD_W8 : GATEUP ? MOE_SKINNY_PD_GU : MOE_SKINNY_PD_DN;  // steps in flight
-    constexpr int KS = W8 ? 2 * KB : KB;  // reduction elements per step (256 bytes of each row)
-    constexpr int EPC = W8 ? 16 : 8;      // elements per 16-byte chunk
-    constexpr int XF = W8 ? 8 : 4;        // token fragments per step
+    constexpr bool W8 = FMT == 1;
+    constexpr bool W4 = FMT == 2;
+    constexpr int SW = FMT ? SW_W8 : SW_BF;
+    constexpr int PD = FMT ? MOE_SKINNY_PD_W8 : GATEUP ? MOE_SKINNY_PD_GU : MOE_SKINNY_PD_DN;  // steps in flight
+    constexpr int KS = W4 ? 4 * KB : W8 ? 2 * KB : KB;  // reduction elements per step (256 bytes of each row)
+    constexpr int EPC = W4 ? 32 : W8 ? 16 : 8;          // elements per 16-byte chunk
+    constexpr int FPC = EPC / 8;                        // MFMA fragments per chunk
+    constexpr int XF = 4 * FPC;                         // token fragments per step
+    // bytes of x weights (compile-time shifts, no multiply-then-divide)
+    auto wbytes = [](uint32_t x) -> uint32_t { return W4 ? x >> 1 : W8 ? x : x << 1; };
     // 16-row MFMA blocks per workgroup: gate_up takes 16 gate + the matching 16
     // up rows; down takes MOE_SKINNY_DOWN_BLOCKS consecutive blocks of 16 rows
     constexpr int NW = GATEUP ? 2 : MOE_SKINNY_DOWN_BLOCKS;
@@ -125,6 +155,7 @@ __global__ __launch_bounds__((W8 ? SW_W8 : SW_BF) * 64, W8 ? MOE_SKINNY_W8_OCC :
     constexpr int NL = NR / 4;          // load instructions per step
     __shared__ u32x4 s_w[SW][NR * 16];
     __shared__ f32x4_t s_red[SW][NW][64];
+    __shared__ uint8_t s_bs[W4 ? SW : 1][W4 ? NR * 16 : 1];  // MXFP4: the block scale of each chunk
     // direct routing: per row of the expert, its token (gate_up) or its
     // assignment (down)
     __shared__ int s_rows[DIRECT ? kSkinnyDirectMax : 1];
@@ -174,8 +205,11 @@ __global__ __launch_bounds__((W8 ? SW_W8 : SW_BF) * 64, W8 ? MOE_SKINNY_W8_OCC :
     // load instruction i covers tile rows 4i..4i+3; this lane: row 4i + lgrp, chunk l16
     // element offsets inside one expert fit in 32 bits (2*I*H < 2^31 is checked on the host)
     // the expert's weights; a lane's chunk adds l16 * EPC elements to its row
-    const uint8_t *wbase = reinterpret_cast<const uint8_t *>(p.W) + (int64_t)e * p.w_expert_stride * (W8 ? 1 : 2);
-    uint32_t woff[NL];
+    const uint8_t *wbase = reinterpret_cast<const uint8_t *>(p.W) +
+                           (W4 ? (int64_t)e * p.w_expert_stride / 2 : (int64_t)e * p.w_expert_stride * (W8 ? 1 : 2));
+    // MXFP4: the expert's block scales, K / 32 per row; chunk l16 of a step is block kb * 16 + l16
+    const uint8_t *sbase = W4 ? p.w_bscale + (int64_t)e * (GATEUP ? 2 * p.N : p.N) * (p.K / 32) : nullptr;
+    uint32_t woff[NL], soff[NL];
 #pragma unroll
     for (int i = 0; i < NL; i++) {
         const int tr = 4 * i + lgrp;  // tile row
@@ -188,7 +222,8 @@ __global__ __launch_bounds__((W8 ? SW_W8 : SW_BF) * 64, W8 ? MOE_SKINNY_W8_OCC :
             const int n = n0 + tr;
             mrow = n < p.N ? n : 0;
         }
-        woff[i] = (uint32_t)mrow * (uint32_t)p.K * (W8 ? 1u : 2u);  // bytes
+        woff[i] = wbytes((uint32_t)mrow * (uint32_t)p.K);
+        if (W4) soff[i] = (uint32_t)mrow * (uint32_t)(p.K / 32);
     }
     u32x4 *tile = s_w[wave];
     const u32x4 zero = {0u, 0u, 0u, 0u};
@@ -206,6 +241,7 @@ __global__ __launch_bounds__((W8 ? SW_W8 : SW_BF) * 64, W8 ? MOE_SKINNY_W8_OCC :
         for (int w = 0; w < NW; w++) acc[w] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
         u32x4 st[PD][NL];
+        uint32_t bs[PD][W4 ? NL : 1];  // MXFP4 block scale bytes of the staged chunks
         u32x4 xs[PD][XF];
         // weights of step kb and the token fragments it needs: MFMA j takes
         // chunk 4j + lgrp (bf16: 8 elements; E4M3: 16 elements, as two MFMAs
@@ -217,19 +253,25 @@ __global__ __launch_bounds__((W8 ? SW_W8 : SW_BF) * 64, W8 ? MOE_SKINNY_W8_OCC :
         // load of a step is in flight together.
         // (plain '&' and masks below, not '&&' or '?:', so that no branch is formed)
         auto w_ok = [&](int kb) { return kb * KS + l16 * EPC < p.K; };
-        auto x_ok = [&](int kb, int f) { return xv & (kb * KS + (4 * (W8 ? f / 2 : f) + lgrp) * EPC < p.K); };
+        auto x_ok = [&](int kb, int f) { return xv & (kb * KS + (4 * (f / FPC) + lgrp) * EPC < p.K); };
         // (a chunk that is not read falls back to the row's first chunk, so
         // every address stays inside a row that exists)
         auto gload_w = [&](int kb, int b) {
-            const uint32_t kbytes = (uint32_t)(kb * KS + l16 * EPC) * (W8 ? 1u : 2u) & (0u - (uint32_t)w_ok(kb));
+            const uint32_t okm = 0u - (uint32_t)w_ok(kb);
+            const uint32_t kbytes = wbytes((uint32_t)(kb * KS + l16 * EPC)) & okm;
 #pragma unroll
             for (int i = 0; i < NL; i++) st[b][i] = load_nt16(wbase + woff[i] + kbytes);
+            if (W4) {
+                const uint32_t kblk = (uint32_t)(kb * 16 + l16) & okm;
+#pragma unroll
+                for (int i = 0; i < NL; i++) bs[b][i] = sbase[soff[i] + kblk];
+            }
         };
         auto gload_x = [&](int kb, int b) {
 #pragma unroll
             for (int f = 0; f < XF; f++) {
-                const int j = W8 ? f / 2 : f;
-                const int off = W8 ? j * 64 + (f % 2) * 8 : j * 32;
+                // fragment f: chunk 4 * (f / FPC) + lgrp, its 8 elements (f % FPC)
+                const int off = (f / FPC) * 4 * EPC + (f % FPC) * 8;
                 xs[b][f] = load16(xp + ((kb * KS + lgrp * EPC + off) & (0 - (int)x_ok(kb, f))));
             }
         };
@@ -242,6 +284,10 @@ __global__ __launch_bounds__((W8 ? SW_W8 : SW_BF) * 64, W8 ? MOE_SKINNY_W8_OCC :
             const bool okw = w_ok(kb);
 #pragma unroll
             for (int i = 0; i < NL; i++) tile[tswz(4 * i + lgrp, l16)] = keep_if(okw, st[b][i]);
+            if (W4) {
+#pragma unroll
+                for (int i = 0; i < NL; i++) s_bs[W4 ? wave : 0][(4 * i + lgrp) * 16 + l16] = (uint8_t)bs[b][i];
+            }
             const bool more = kb + PD < kb_hi;
             if (more) gload_w(kb + PD, b);
             u32x4 xb[XF];
@@ -252,7 +298,17 @@ __global__ __launch_bounds__((W8 ? SW_W8 : SW_BF) * 64, W8 ? MOE_SKINNY_W8_OCC :
 #pragma unroll
                 for (int w = 0; w < NW; w++) {
                     const u32x4 a = tile[tswz(16 * w + l16, 4 * j + lgrp)];
-                    if (W8) {
+                    if (W4) {
+                        const float sf = e8m0_factor(s_bs[W4 ? wave : 0][(16 * w + l16) * 16 + 4 * j + lgrp]);
+                        acc[w] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(e2m1x8_to_bf16(a.x, sf)),
+                                                                         as_bf16x8(xb[4 * j]), acc[w], 0, 0, 0);
+                        acc[w] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(e2m1x8_to_bf16(a.y, sf)),
+                                                                         as_bf16x8(xb[4 * j + 1]), acc[w], 0, 0, 0);
+                        acc[w] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(e2m1x8_to_bf16(a.z, sf)),
+                                                                         as_bf16x8(xb[4 * j + 2]), acc[w], 0, 0, 0);
+                        acc[w] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(e2m1x8_to_bf16(a.w, sf)),
+                                                                         as_bf16x8(xb[4 * j + 3]), acc[w], 0, 0, 0);
+                    } else if (W8) {
                         acc[w] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(e4m3x8_to_bf16(a.x, a.y)),
                                                                          as_bf16x8(xb[2 * j]), acc[w], 0, 0, 0);
                         acc[w] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(e4m3x8_to_bf16(a.z, a.w)),
@@ -344,6 +400,7 @@ SkinnyParams make_params(const GemmProblem &g)
     s.a_rows = g.a_rows;
     s.W = g.W;
     s.w_scale = g.w_scale;
+    s.w_bscale = g.w_bscale;
     s.w_expert_stride = g.w_expert_stride;
     s.K = (int)g.K;
     s.N = (int)g.N;
@@ -367,12 +424,15 @@ hipError_t launch_gate_up_skinny(const GemmProblem &g, hipStream_t st)
 {
     SkinnyParams s = make_params(g);
     dim3 grid((unsigned)((g.N + 15) / 16), g.dense_rows > 0 ? 1u : (unsigned)g.E);
-    if (g.w_scale) {
-        s.ids = nullptr;  // E4M3 weights always take the sorted tables
-        hipLaunchKernelGGL((skinny_gemm_kernel<true, true, false>), grid, dim3(SW_W8 * 64), 0, st, s);
+    if (g.w_bscale) {
+        s.ids = nullptr;  // low-precision weights always take the sorted tables
+        hipLaunchKernelGGL((skinny_gemm_kernel<true, 2, false>), grid, dim3(SW_W8 * 64), 0, st, s);
+    } else if (g.w_scale) {
+        s.ids = nullptr;
+        hipLaunchKernelGGL((skinny_gemm_kernel<true, 1, false>), grid, dim3(SW_W8 * 64), 0, st, s);
     } else {
-        if (s.ids) hipLaunchKernelGGL((skinny_gemm_kernel<true, false, true>), grid, dim3(SW_BF * 64), 0, st, s);
-        else hipLaunchKernelGGL((skinny_gemm_kernel<true, false, false>), grid, dim3(SW_BF * 64), 0, st, s);
+        if (s.ids) hipLaunchKernelGGL((skinny_gemm_kernel<true, 0, true>), grid, dim3(SW_BF * 64), 0, st, s);
+        else hipLaunchKernelGGL((skinny_gemm_kernel<true, 0, false>), grid, dim3(SW_BF * 64), 0, st, s);
     }
     return hipGetLastError();
 }
@@ -382,12 +442,15 @@ hipError_t launch_down_skinny(const GemmProblem &g, hipStream_t st)
     SkinnyParams s = make_params(g);
     constexpr int rows = 16 * MOE_SKINNY_DOWN_BLOCKS;
     dim3 grid((unsigned)((g.N + rows - 1) / rows), g.dense_rows > 0 ? 1u : (unsigned)g.E);
-    if (g.w_scale) {
+    if (g.w_bscale) {
         s.ids = nullptr;
-        hipLaunchKernelGGL((skinny_gemm_kernel<false, true, false>), grid, dim3(SW_W8 * 64), 0, st, s);
+        hipLaunchKernelGGL((skinny_gemm_kernel<false, 2, false>), grid, dim3(SW_W8 * 64), 0, st, s);
+    } else if (g.w_scale) {
+        s.ids = nullptr;
+        hipLaunchKernelGGL((skinny_gemm_kernel<false, 1, false>), grid, dim3(SW_W8 * 64), 0, st, s);
     } else {
-        if (s.ids) hipLaunchKernelGGL((skinny_gemm_kernel<false, false, true>), grid, dim3(SW_BF * 64), 0, st, s);
-        else hipLaunchKernelGGL((skinny_gemm_kernel<false, false, false>), grid, dim3(SW_BF * 64), 0, st, s);
+        if (s.ids) hipLaunchKernelGGL((skinny_gemm_kernel<false, 0, true>), grid, dim3(SW_BF * 64), 0, st, s);
+        else hipLaunchKernelGGL((skinny_gemm_kernel<false, 0, false>), grid, dim3(SW_BF * 64), 0, st, s);
     }
     return hipGetLastError();
 }

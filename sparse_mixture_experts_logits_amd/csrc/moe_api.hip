@@ -98,8 +98,17 @@ int check_shape(int64_t T, int64_t H, int64_t I, int64_t E, int32_t k, const moe
             if ((int64_t)k > (int64_t)opts->topk_group * (E / opts->n_group))
                 return fail(MOE_ERR_INVALID_ARG, "k = %d exceeds the experts of topk_group groups", k);
         }
-        if (opts->weight_format != MOE_WEIGHTS_NATIVE && opts->weight_format != MOE_WEIGHTS_FP8_E4M3)
+        if (opts->weight_format != MOE_WEIGHTS_NATIVE && opts->weight_format != MOE_WEIGHTS_FP8_E4M3 &&
+            opts->weight_format != MOE_WEIGHTS_MXFP4)
             return fail(MOE_ERR_INVALID_ARG, "unknown weight_format %d", opts->weight_format);
+        if (opts->weight_format == MOE_WEIGHTS_MXFP4) {
+            if (dtype != MOE_BF16)
+                return fail(MOE_ERR_UNSUPPORTED, "MXFP4 expert weights need bf16 activations (dtype MOE_BF16)");
+            if (H % 32 || I % 32)
+                return fail(MOE_ERR_UNSUPPORTED, "MXFP4 expert weights need H and I multiples of 32");
+            if (opts->flags & MOE_FLAG_FORCE_TILED)
+                return fail(MOE_ERR_UNSUPPORTED, "MXFP4 expert weights run on the weight-streaming kernels only");
+        }
         if (opts->weight_format == MOE_WEIGHTS_FP8_E4M3) {
             if (dtype != MOE_BF16)
                 return fail(MOE_ERR_UNSUPPORTED, "FP8 expert weights need bf16 activations (dtype MOE_BF16)");
@@ -117,7 +126,7 @@ int check_shape(int64_t T, int64_t H, int64_t I, int64_t E, int32_t k, const moe
 bool use_skinny(int64_t T, int32_t k, int64_t E, const moe_opts *opts)
 {
     const uint32_t flags = opts ? opts->flags : 0;
-    if (opts && opts->weight_format == MOE_WEIGHTS_FP8_E4M3) return true;
+    if (opts && opts->weight_format != MOE_WEIGHTS_NATIVE) return true;  // low-precision weights
     if (flags & MOE_FLAG_FORCE_SKINNY) return true;
     if (flags & MOE_FLAG_FORCE_TILED) return false;
     return T * k <= 32 * E;  // about 32 rows per expert or fewer: stream the weights
@@ -236,22 +245,27 @@ int moe_forward(const void *hidden, const void *router_w, const void *gate_up, c
         if (p && !aligned(p, 4)) return fail(MOE_ERR_ALIGNMENT, "output pointer %p is not 4-byte aligned", p);
 
     const bool w8 = opts->weight_format == MOE_WEIGHTS_FP8_E4M3;
+    const bool w4 = opts->weight_format == MOE_WEIGHTS_MXFP4;
     if (w8 && (!opts->gate_up_scale || !opts->down_scale))
         return fail(MOE_ERR_INVALID_ARG, "FP8 expert weights need gate_up_scale and down_scale");
+    if (w4 && (!opts->gate_up_block_scale || !opts->down_block_scale))
+        return fail(MOE_ERR_INVALID_ARG, "MXFP4 expert weights need gate_up_block_scale and down_block_scale");
     if (w8 && (!aligned(opts->gate_up_scale, 4) || !aligned(opts->down_scale, 4)))
         return fail(MOE_ERR_ALIGNMENT, "gate_up_scale / down_scale not 4-byte aligned");
     const uint64_t es = opts->dtype == MOE_BF16 ? 2 : 4;
-    const uint64_t wes = w8 ? 1 : es;  // bytes per routed expert weight
+    const uint64_t wes2 = w4 ? 1 : w8 ? 2 : 2 * es;  // twice the bytes per routed expert weight
     const uint64_t out_bytes = (uint64_t)T * H * es;
     struct Range {
         const void *p;
         uint64_t n;
     } ins[] = {{hidden, (uint64_t)T * H * es},
                {router_w, (uint64_t)E * H * es},
-               {gate_up, (uint64_t)E * 2 * I * H * wes},
-               {down, (uint64_t)E * H * I * wes},
+               {gate_up, (uint64_t)E * 2 * I * H * wes2 / 2},
+               {down, (uint64_t)E * H * I * wes2 / 2},
                {opts->gate_up_scale, w8 ? (uint64_t)E * 2 * I * 4 : 0},
                {opts->down_scale, w8 ? (uint64_t)E * H * 4 : 0},
+               {opts->gate_up_block_scale, w4 ? (uint64_t)E * 2 * I * (H / 32) : 0},
+               {opts->down_block_scale, w4 ? (uint64_t)E * H * (I / 32) : 0},
                {opts->shared_gate_up, shared ? (uint64_t)2 * opts->shared_I * H * es : 0},
                {opts->shared_down, shared ? (uint64_t)H * opts->shared_I * es : 0},
                {opts->router_bias, (uint64_t)E * 4},
@@ -313,7 +327,7 @@ int moe_forward(const void *hidden, const void *router_w, const void *gate_up, c
     // top-k ids, and the scan and permute launches are skipped (bf16 weights
     // only: the E4M3 kernels lose more to the extra registers than the two
     // launches cost).
-    const bool direct = skinny && !f32 && !w8 && T * k <= moe::kSkinnyDirectMax && !opts->expert_counts &&
+    const bool direct = skinny && !f32 && !w8 && !w4 && T * k <= moe::kSkinnyDirectMax && !opts->expert_counts &&
                         !opts->expert_offsets && !opts->perm && !opts->inv_perm && !rs.on();
     if (!direct) {
         if ((rc = check(moe::launch_route_scan(s, opts->expert_counts, opts->expert_offsets, rs, ws, st),
@@ -331,6 +345,7 @@ int moe_forward(const void *hidden, const void *router_w, const void *gate_up, c
     gu.a_rows = ws.row_token;
     gu.W = gate_up;
     gu.w_scale = w8 ? opts->gate_up_scale : nullptr;
+    gu.w_bscale = w4 ? opts->gate_up_block_scale : nullptr;
     gu.w_expert_stride = 2 * I * H;
     gu.K = H;
     gu.N = I;
@@ -355,6 +370,7 @@ int moe_forward(const void *hidden, const void *router_w, const void *gate_up, c
     dn.a_rows = nullptr;
     dn.W = down;
     dn.w_scale = w8 ? opts->down_scale : nullptr;
+    dn.w_bscale = w4 ? opts->down_block_scale : nullptr;
     dn.w_expert_stride = H * I;
     dn.K = I;
     dn.N = H;
@@ -377,6 +393,7 @@ int moe_forward(const void *hidden, const void *router_w, const void *gate_up, c
         sg.a_rows = nullptr;
         sg.W = opts->shared_gate_up;
         sg.w_scale = nullptr;  // the shared expert keeps opts->dtype
+        sg.w_bscale = nullptr;
         sg.w_expert_stride = 0;
         sg.N = opts->shared_I;
         sg.C = ws.sh_h;
@@ -429,6 +446,25 @@ int moe_quantize_fp8_rows(const void *w, int64_t rows, int64_t cols, void *q, fl
     hipError_t err = moe::launch_quantize_fp8_rows(w, rows, cols, q, scale, (hipStream_t)stream);
     if (err == hipSuccess && debug_sync()) err = hipStreamSynchronize((hipStream_t)stream);
     if (err != hipSuccess) return fail(MOE_ERR_HIP, "quantize_fp8_rows failed: %s", hipGetErrorString(err));
+    return MOE_OK;
+}
+
+int moe_quantize_mxfp4_rows(const void *w, int64_t rows, int64_t cols, void *q, void *scale, void *stream)
+{
+    g_err[0] = 0;
+    if (rows < 0) return fail(MOE_ERR_INVALID_ARG, "rows = %lld is negative", (long long)rows);
+    if (cols < 32 || cols % 32) return fail(MOE_ERR_INVALID_ARG, "cols = %lld must be a positive multiple of 32", (long long)cols);
+    if (rows >= ((int64_t)1 << 31) || cols >= ((int64_t)1 << 31) || rows * (cols / 32) >= ((int64_t)1 << 36))
+        return fail(MOE_ERR_UNSUPPORTED, "rows or cols too large");
+    if (rows == 0) return MOE_OK;
+    if (!w || !q || !scale) return fail(MOE_ERR_INVALID_ARG, "w, q and scale must be non-NULL");
+    if (!aligned(w, 16) || !aligned(q, 16)) return fail(MOE_ERR_ALIGNMENT, "w and q must be 16-byte aligned");
+    const uint64_t n = (uint64_t)rows * cols;
+    if (overlaps(q, n / 2, w, 2 * n) || overlaps(scale, n / 32, w, 2 * n) || overlaps(scale, n / 32, q, n / 2))
+        return fail(MOE_ERR_INVALID_ARG, "q, scale and w must not overlap");
+    hipError_t err = moe::launch_quantize_mxfp4_rows(w, rows, cols, q, scale, (hipStream_t)stream);
+    if (err == hipSuccess && debug_sync()) err = hipStreamSynchronize((hipStream_t)stream);
+    if (err != hipSuccess) return fail(MOE_ERR_HIP, "quantize_mxfp4_rows failed: %s", hipGetErrorString(err));
     return MOE_OK;
 }
 

@@ -142,6 +142,7 @@ struct GemmProblem {
     const int32_t *a_rows;   // gate_up: sorted position -> token (null = identity)
     const void *W;           // packed weights (bf16 / fp32, or E4M3 bytes when w_scale is set)
     const float *w_scale;    // E4M3 storage: per-row scales [E, rows per expert]; else null
+    const uint8_t *w_bscale = nullptr;  // MXFP4 storage: E8M0 block scales [E, rows, K / 32]; else null
     int64_t w_expert_stride; // elements between experts (0 for dense)
     int64_t K;               // reduction length
     int64_t N;               // gate_up: I (h columns); down: H
@@ -180,6 +181,7 @@ int tiled_tail_m();  // rows an expert's last M-tile may carry past tiled_block_
 
 hipError_t launch_quantize_fp8_rows(const void *w, int64_t rows, int64_t cols, void *q, float *scale,
                                     hipStream_t st);
+hipError_t launch_quantize_mxfp4_rows(const void *w, int64_t rows, int64_t cols, void *q, void *scale, hipStream_t st);
 
 hipError_t launch_combine(const Shape &s, const float *slot, const float *sh_y, void *out,
                           hipStream_t st);

@@ -84,7 +84,64 @@ __global__ __launch_bounds__(256) void quantize_e4m3_rows_kernel(const __bf16 *_
     if (threadIdx.x == 0) scale[r] = s;
 }
 
+// MXFP4 (OCP Microscaling Formats v1.0): one thread per block of 32
+// consecutive elements of a row. The block factor 2^x has x = floor(log2 a)
+// - 2 for the block's largest magnitude a (read off a's fp32 exponent field;
+// x = -127 below 2^-126), clamped to [-127, 127]; y = |w| * 2^-x is exact;
+// its E2M1 code counts the rounding boundaries at or below it (ties go to
+// the even code: 0.25 -> 0, 0.75 -> 1.0, 1.25 -> 1.0, 1.75 -> 2, 2.5 -> 2,
+// 3.5 -> 4, 5 -> 4, past 5 -> 6), and the sign bit is w's.
+__device__ __forceinline__ uint32_t e2m1_code(float y)
+{
+    return (uint32_t)(y > 0.25f) + (uint32_t)(y >= 0.75f) + (uint32_t)(y > 1.25f) + (uint32_t)(y >= 1.75f) +
+           (uint32_t)(y > 2.5f) + (uint32_t)(y >= 3.5f) + (uint32_t)(y > 5.0f);
+}
+
+__global__ __launch_bounds__(256) void quantize_mxfp4_rows_kernel(const __bf16 *__restrict__ w, int64_t nblocks,
+                                                                  uint8_t *__restrict__ q, uint8_t *__restrict__ scale)
+{
+    const int64_t b = (int64_t)blockIdx.x * 256 + threadIdx.x;  // block of 32 elements
+    if (b >= nblocks) return;
+    const u32x4 *src = reinterpret_cast<const u32x4 *>(w + b * 32);
+    uint32_t wd[16];
+#pragma unroll
+    for (int c = 0; c < 4; c++) {
+        const u32x4 v = src[c];
+        wd[4 * c] = v.x;
+        wd[4 * c + 1] = v.y;
+        wd[4 * c + 2] = v.z;
+        wd[4 * c + 3] = v.w;
+    }
+    float a = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; i++) a = fmaxf(a, fmaxf(fabsf(bf16_lo(wd[i])), fabsf(bf16_hi(wd[i]))));
+    const int ef = (int)((__float_as_uint(a) >> 23) & 0xffu);
+    const int x = ef == 0 ? -127 : max(-127, min(127, ef - 129));
+    uint32_t out[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 16; i++) {  // word i holds elements 2i (low half) and 2i+1
+#pragma unroll
+        for (int h = 0; h < 2; h++) {
+            const float v = h ? bf16_hi(wd[i]) : bf16_lo(wd[i]);
+            const uint32_t sign = h ? (wd[i] >> 31) : ((wd[i] >> 15) & 1u);
+            const uint32_t code = e2m1_code(__builtin_ldexpf(fabsf(v), -x)) | (sign << 3);
+            const int el = 2 * i + h;  // element: byte el / 2, nibble el % 2
+            out[el / 8] |= code << (4 * (el % 8));
+        }
+    }
+    reinterpret_cast<u32x4 *>(q)[b] = u32x4{out[0], out[1], out[2], out[3]};
+    scale[b] = (uint8_t)(x + 127);
+}
+
 }  // namespace
+
+hipError_t launch_quantize_mxfp4_rows(const void *w, int64_t rows, int64_t cols, void *q, void *scale, hipStream_t st)
+{
+    const int64_t nblocks = rows * (cols / 32);
+    hipLaunchKernelGGL(quantize_mxfp4_rows_kernel, dim3((unsigned)((nblocks + 255) / 256)), dim3(256), 0, st,
+                       (const __bf16 *)w, nblocks, (uint8_t *)q, (uint8_t *)scale);
+    return hipGetLastError();
+}
 
 hipError_t launch_quantize_fp8_rows(const void *w, int64_t rows, int64_t cols, void *q, float *scale,
                                     hipStream_t st)

@@ -262,3 +262,43 @@ def test_sparsemixer_options_are_checked():
         o.jitter_eps = eps
         rc, msg = call(E=16, k=2, opts=o)
         assert rc == -1 and "jitter_eps" in msg
+
+
+def mxfp4_opts():
+    o = good_opts(nbytes=100)  # too small: a valid call stops at the workspace check
+    o.weight_format = moe.WEIGHTS_MXFP4
+    o.gate_up_block_scale = (1 << 40) + (5 << 30)
+    o.down_block_scale = (1 << 40) + (6 << 30) + 1  # byte arrays: any alignment
+    return o
+
+
+def test_mxfp4_weight_options_are_checked():
+    rc, msg = call(opts=mxfp4_opts())
+    assert rc == -3, msg
+    o = mxfp4_opts()
+    o.down_block_scale = None
+    rc, msg = call(opts=o)
+    assert rc == -1 and "block_scale" in msg
+    o = mxfp4_opts()
+    o.dtype = 1
+    assert call(opts=o)[0] == -2
+    o = mxfp4_opts()
+    o.flags = moe.FLAG_FORCE_TILED
+    assert call(opts=o)[0] == -2
+    rc, msg = call(H=80, opts=mxfp4_opts())  # a multiple of 16 but not of 32
+    assert rc == -2 and "32" in msg
+    rc, msg = call(opts=mxfp4_opts(), out=(1 << 40) + (5 << 30))  # out on top of a block scale
+    assert rc == -1 and "overlaps" in msg
+
+
+def test_mxfp4_quantize_entry_point_checks_arguments():
+    lib = moe.load_library()
+    vp = ctypes.c_void_p
+    base = 1 << 40
+    w, q, s = vp(base), vp(base + (1 << 30)), vp(base + (2 << 30))
+    assert lib.moe_quantize_mxfp4_rows(w, 0, 64, q, s, None) == 0
+    assert lib.moe_quantize_mxfp4_rows(w, 4, 48, q, s, None) == -1  # not a multiple of 32
+    assert lib.moe_quantize_mxfp4_rows(w, -1, 64, q, s, None) == -1
+    assert lib.moe_quantize_mxfp4_rows(None, 4, 64, q, s, None) == -1
+    assert lib.moe_quantize_mxfp4_rows(vp(base + 8), 4, 64, q, s, None) == -4
+    assert lib.moe_quantize_mxfp4_rows(w, 4, 64, vp(base + 64), s, None) == -1  # q overlaps w
