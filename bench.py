@@ -10,9 +10,10 @@ line on stdout.
 Default workload: the PhiMoE decode step (T=32, H=4096, I=6400, E=16, top-2),
 a weight-bandwidth-bound case. The PhiMoE prefill chunk (T=4096) is measured
 in the same run and reported under "prefill" (MFMA-bound), and the decode
-step with FP8 (E4M3, per-row scaled) expert weights under "decode_fp8" (a
-different weight storage, so never the headline value; --fp8 makes it the
-main line, marked in its config). A short untimed
+step with FP8 (E4M3, per-row scaled) and MXFP4 (E2M1, E8M0 scale per 32)
+expert weights under "decode_fp8" and "decode_mxfp4" (different weight
+storage, so never the headline value; --weights fp8|mxfp4 makes one of them
+the main line, marked in its config). A short untimed
 pilot with events at every stage boundary finds the dominant kernel; every
 timed call then records HIP events around that kernel on the library's
 stream, so the roofline figures come from the timed region itself.
@@ -53,14 +54,28 @@ def log(*a):
 
 # ------------------------------------------------------------------ algorithmic work
 
-def work(wl, counts, fp8=False):
+WEIGHT_FORMATS = {"bf16": "bf16 as given", "fp8": "OCP FP8 E4M3, one fp32 scale per row",
+                  "mxfp4": "OCP MXFP4: FP4 E2M1, one E8M0 scale per 32 weights of a row"}
+
+
+def weight_bytes(rows, cols, es, weights):
+    """Bytes of a [rows, cols] expert weight matrix in the given storage."""
+    if weights == "fp8":
+        return rows * cols + rows * 4
+    if weights == "mxfp4":
+        return rows * cols // 2 + rows * cols // 32
+    return rows * cols * es
+
+
+def work(wl, counts, weights="bf16"):
     """Algorithmic FLOPs and bytes of the layer and of its two expert GEMMs.
 
     Bytes count what the method itself must move once: weights of experts that
     received tokens, hidden, router weights and the output for the layer; for
     a GEMM kernel, its weights once plus its input and output activations once
     (gate_up: hidden in, h out; down: h in, fp32 weighted slots out). With
-    FP8 expert weights a weight is one byte plus its row's 4-byte scale."""
+    FP8 expert weights a weight is one byte plus its row's 4-byte scale; with
+    MXFP4 half a byte plus one scale byte per 32 weights."""
     es = 2 if wl.dtype == "bf16" else 4
     T, H, I, E, k = wl.T, wl.H, wl.I, wl.E, wl.k
     TK = T * k
@@ -70,8 +85,8 @@ def work(wl, counts, fp8=False):
     f_dn = 2.0 * TK * H * I
     f_router = 2.0 * T * H * E
     f_shared = 2.0 * T * 3 * Is * H
-    w_gu = hit * (2 * I * H + 2 * I * 4) if fp8 else hit * 2 * I * H * es
-    w_dn = hit * (H * I + H * 4) if fp8 else hit * H * I * es
+    w_gu = hit * weight_bytes(2 * I, H, es, weights)
+    w_dn = hit * weight_bytes(H, I, es, weights)
     b_gu = w_gu + T * H * es + TK * I * es
     b_dn = w_dn + TK * I * es + TK * H * 4
     b_layer = w_gu + w_dn + 2 * T * H * es + E * H * es + 3 * Is * H * es
@@ -164,7 +179,56 @@ def measured_traffic(kernel, workload):
 
 # ------------------------------------------------------------------ GPU timing
 
-def run_workload(name, steps, warmup, fp8=False):
+HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000
+
+
+class TimingEvent:
+    """A hipEvent_t made with hipEventDisableSystemFence, recorded by the
+    library on its own stream at a stage boundary. A default event record ends
+    with a system-scope release (L2 writeback and invalidate) that slows the
+    kernels after it; an event used only for its timestamp does not need it.
+    Created through the HIP runtime torch has loaded, so the handles belong to
+    the same runtime as torch's streams."""
+
+    _hip = None
+
+    @classmethod
+    def runtime(cls):
+        if cls._hip is None:
+            paths = sorted({ln.split()[-1] for ln in open("/proc/self/maps") if "libamdhip64.so" in ln})
+            if not paths:
+                raise RuntimeError("the HIP runtime is not loaded")
+            hip = ctypes.CDLL(paths[0])
+            hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+            hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+            hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+            hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+            cls._hip = hip
+        return cls._hip
+
+    def __init__(self):
+        h = ctypes.c_void_p()
+        rc = self.runtime().hipEventCreateWithFlags(ctypes.byref(h), HIP_EVENT_DISABLE_SYSTEM_FENCE)
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags failed ({rc})")
+        self.cuda_event = h.value
+
+    def record(self, stream):
+        if self.runtime().hipEventRecord(self.cuda_event, stream) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
+    def elapsed_time(self, end):
+        ms = ctypes.c_float()
+        rc = self.runtime().hipEventElapsedTime(ctypes.byref(ms), self.cuda_event, end.cuda_event)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return ms.value
+
+    def __del__(self):
+        if self.cuda_event and self._hip is not None:
+            self._hip.hipEventDestroy(self.cuda_event)
+
+def run_workload(name, steps, warmup, weights="bf16"):
     import torch
     import numpy as np
     import sparse_mixture_experts_logits_amd as moe
@@ -184,10 +248,15 @@ def run_workload(name, steps, warmup, fp8=False):
     router_w, gate_up, down = _DEV_CACHE[key]
     hidden = d(inp.hidden)
     scales = {}
-    if fp8:  # quantise the routed experts once, outside the timed region
+    # low-precision weights: the routed experts are quantised once, outside the timed region
+    if weights == "fp8":
         gate_up, gs = moe.quantize_fp8_rows(gate_up)
         down, ds = moe.quantize_fp8_rows(down)
         scales = dict(gate_up_scale=gs, down_scale=ds)
+    elif weights == "mxfp4":
+        gate_up, gs = moe.quantize_mxfp4_rows(gate_up)
+        down, ds = moe.quantize_mxfp4_rows(down)
+        scales = dict(gate_up_block_scale=gs, down_block_scale=ds)
     sgu = sdn = None
     if inp.shared_gate_up:
         gu, dn = inp.shared_concat()
@@ -206,11 +275,13 @@ def run_workload(name, steps, warmup, fp8=False):
 
     nev = moe.STAGE_EVENTS
 
+    stream = torch.cuda.current_stream(dev).cuda_stream
+
     def event_sets(n):
-        sets = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(n)]
+        sets = [[TimingEvent() for _ in range(nev)] for _ in range(n)]
         for evs in sets:
             for e in evs:
-                e.record()  # creates the underlying hipEvent_t
+                e.record(stream)
         torch.cuda.synchronize()
         return sets
 
@@ -252,7 +323,7 @@ def run_workload(name, steps, warmup, fp8=False):
     stages = dict(zip(moe.STAGES, stage_ms.tolist()))
     stages[moe.STAGES[dom]] = dom_ms  # live value from the timed region
     return dict(wl=wl, counts=counts, wall_s=wall, gpu_ms=gpu_ms, steps=steps, stages=stages,
-                dominant=moe.STAGES[dom], inp=inp, fp8=fp8)
+                dominant=moe.STAGES[dom], inp=inp, weights=weights)
 
 
 _INPUT_CACHE = {}
@@ -262,7 +333,7 @@ _DEV_CACHE = {}
 def roofline_of(res):
     """Roofline of the dominant expert GEMM (the stage with the largest time)."""
     wl = res["wl"]
-    w = work(wl, res["counts"], fp8=res["fp8"])
+    w = work(wl, res["counts"], weights=res["weights"])
     st = res["stages"]
     kernel = res["dominant"]
     if kernel not in ("gate_up", "down"):  # the expert GEMMs dominate every workload here
@@ -278,7 +349,7 @@ def roofline_of(res):
         achieved = w[f"flop_{kernel}"] / dur_s / 1e12
         r = dict(bound="mfma", achieved=round(achieved, 1), peak=peak, unit="TFLOP/s",
                  frac=round(achieved / peak, 4))
-    tr = measured_traffic(kernel, wl.name + ("_fp8" if res["fp8"] else ""))
+    tr = measured_traffic(kernel, wl.name + ("" if res["weights"] == "bf16" else "_" + res["weights"]))
     r["traffic"] = tr
     r["kernel"] = kernel
     r["avg_launch_ms"] = round(st[kernel], 4)
@@ -330,7 +401,10 @@ def main(argv=None):
     ap.add_argument("--no-prefill", action="store_true", help="skip the secondary prefill measurement")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-fp8", action="store_true", help="skip the secondary FP8-weight decode measurement")
-    ap.add_argument("--fp8", action="store_true", help="time the main workload with FP8 expert weights")
+    ap.add_argument("--no-mxfp4", action="store_true", help="skip the secondary MXFP4-weight decode measurement")
+    ap.add_argument("--weights", choices=sorted(WEIGHT_FORMATS), default="bf16",
+                    help="expert weight storage of the main workload (fp8 / mxfp4: decode-shaped work only)")
+    ap.add_argument("--fp8", action="store_true", help="same as --weights fp8")
     ap.add_argument("--cpu-tokens", type=int, default=32)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a 1 GiB device copy (counter calibration under rocprofv3)")
@@ -356,7 +430,9 @@ def main(argv=None):
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
 
-    res = run_workload(args.workload, args.steps, args.warmup, fp8=args.fp8)
+    if args.fp8:
+        args.weights = "fp8"
+    res = run_workload(args.workload, args.steps, args.warmup, weights=args.weights)
     roof, w = roofline_of(res)
     lay = layer_summary(res, w)
     wl = res["wl"]
@@ -376,17 +452,19 @@ def main(argv=None):
         "config": {"workload": wl.name, "T": wl.T, "H": wl.H, "I": wl.I, "E": wl.E, "k": wl.k,
                    "routed_scale": wl.routed_scale, "shared_I": wl.n_shared * wl.shared_I,
                    "parallelism": "single GPU",
-                   **({"expert_weights": "fp8_e4m3_row_scaled"} if args.fp8 else {})},
+                   **({"expert_weights": WEIGHT_FORMATS[args.weights]} if args.weights != "bf16" else {})},
         "roofline": roof,
         "layer": lay,
     }
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(res, args.cpu_tokens)
-    if not args.no_fp8 and not args.fp8 and args.workload == "phimoe_decode":
-        fres = run_workload("phimoe_decode", args.steps, args.warmup, fp8=True)
+    for fmt, skip in (("fp8", args.no_fp8), ("mxfp4", args.no_mxfp4)):
+        if skip or args.weights != "bf16" or args.workload != "phimoe_decode":
+            continue
+        fres = run_workload("phimoe_decode", args.steps, args.warmup, weights=fmt)
         froof, fw = roofline_of(fres)
-        line["decode_fp8"] = dict(workload="phimoe_decode", weights="OCP FP8 E4M3, one fp32 scale per row",
-                                  roofline=froof, layer=layer_summary(fres, fw))
+        line["decode_" + fmt] = dict(workload="phimoe_decode", weights=WEIGHT_FORMATS[fmt],
+                                     roofline=froof, layer=layer_summary(fres, fw))
     if not args.no_prefill and args.workload != "phimoe_prefill":
         pres = run_workload("phimoe_prefill", args.prefill_steps, 3)
         proof, pw = roofline_of(pres)

@@ -1,0 +1,36 @@
+"""Host-side checks of the benchmark's bookkeeping (no GPU): the algorithmic
+byte counts behind the roofline figures and the single-GPU guard."""
+import subprocess
+import sys
+import os
+
+import bench
+import workloads as W
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_weight_bytes_per_storage():
+    # bf16: 2 bytes a weight; FP8 E4M3: 1 byte plus a 4-byte scale per row;
+    # MXFP4: half a byte plus one E8M0 byte per 32 weights
+    assert bench.weight_bytes(12800, 4096, 2, "bf16") == 12800 * 4096 * 2
+    assert bench.weight_bytes(12800, 4096, 2, "fp8") == 12800 * 4096 + 12800 * 4
+    assert bench.weight_bytes(12800, 4096, 2, "mxfp4") == 12800 * 4096 // 2 + 12800 * 128
+
+
+def test_work_counts_only_experts_that_received_tokens():
+    wl = W.BY_NAME["phimoe_decode"]
+    counts = [0] * wl.E
+    counts[3], counts[9] = 40, 24
+    for fmt in ("bf16", "fp8", "mxfp4"):
+        w = bench.work(wl, counts, weights=fmt)
+        assert w["hit"] == 2
+        gu = 2 * bench.weight_bytes(2 * wl.I, wl.H, 2, fmt)
+        assert w["bytes_gate_up"] == gu + wl.T * wl.H * 2 + wl.T * wl.k * wl.I * 2
+        assert w["flop_gate_up"] == 2.0 * wl.T * wl.k * 2 * wl.I * wl.H
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, "bench.py", "--gpus", "2"], cwd=ROOT, capture_output=True, text=True,
+                       timeout=120)
+    assert r.returncode == 2 and "one GPU" in r.stderr
