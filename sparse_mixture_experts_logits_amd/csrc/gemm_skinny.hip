@@ -7,15 +7,18 @@
 // swap: weight rows are the MFMA M side (16 rows per v_mfma_f32_16x16x32_bf16)
 // and the expert's tokens are the N side (groups of 16).
 //   * Loads are shaped for HBM, not for the MFMA: one load instruction reads
-//     4 whole 256-byte row segments (16 lanes per row, non-temporal). Each
+//     4 whole 256-byte row segments (16 lanes per row, non-temporal) through
+//     a buffer resource, the row group's offset in a scalar register. Each
 //     wave writes them to its own LDS tile and reads MFMA fragments back with
 //     an xor swizzle that keeps both directions free of bank conflicts.
-//   * The next step's loads (weights and the token fragments) are issued as
-//     soon as the current step's data is in LDS and registers, so one step is
-//     always in flight per wave.
+//   * The weight loads of the next steps (two ahead for bf16, one for the
+//     low-precision formats) are issued as soon as the current step's data
+//     is in LDS, the token fragments after the MFMAs that use the current
+//     ones, so the bytes in flight per wave stay constant.
 //   * A workgroup owns 32 weight rows (gate_up: 16 gate + the matching 16 up
-//     rows; down: 32 consecutive rows) and splits K over its waves; partial sums meet in LDS in wave
-//     order, so the result does not depend on timing.
+//     rows; MXFP4 gate_up: 32 + 32; down: 32 consecutive rows) and splits K
+//     over its waves; partial sums meet in LDS in wave order, so the result
+//     does not depend on timing.
 //   * Experts with no tokens exit before reading anything, so only the
 //     weights of experts that received tokens are read.
 //   * FP8 weights (one byte each, OCP E4M3, one fp32 scale per weight row):
@@ -42,13 +45,16 @@ constexpr int KB = 128;  // reduction elements per step: 256 bytes of each row
 #define MOE_SKINNY_WAVES 4
 #endif
 #ifndef MOE_SKINNY_PD_GU
-#define MOE_SKINNY_PD_GU 1
+#define MOE_SKINNY_PD_GU 2
 #endif
 #ifndef MOE_SKINNY_PD_DN
-#define MOE_SKINNY_PD_DN 1
+#define MOE_SKINNY_PD_DN 2
 #endif
 #ifndef MOE_SKINNY_PD_W8
 #define MOE_SKINNY_PD_W8 1
+#endif
+#ifndef MOE_SKINNY_PD_W4
+#define MOE_SKINNY_PD_W4 1
 #endif
 #ifndef MOE_SKINNY_DOWN_BLOCKS
 #define MOE_SKINNY_DOWN_BLOCKS 2
@@ -56,8 +62,32 @@ constexpr int KB = 128;  // reduction elements per step: 256 bytes of each row
 #ifndef MOE_SKINNY_WAVES_W8
 #define MOE_SKINNY_WAVES_W8 4
 #endif
+#ifndef MOE_SKINNY_GU_BLOCKS_W8
+#define MOE_SKINNY_GU_BLOCKS_W8 2
+#endif
+#ifndef MOE_SKINNY_GU_BLOCKS_W4
+#define MOE_SKINNY_GU_BLOCKS_W4 4
+#endif
+#ifndef MOE_SKINNY_DN_BLOCKS_W8
+#define MOE_SKINNY_DN_BLOCKS_W8 MOE_SKINNY_DOWN_BLOCKS
+#endif
+#ifndef MOE_SKINNY_DN_BLOCKS_W4
+#define MOE_SKINNY_DN_BLOCKS_W4 MOE_SKINNY_DOWN_BLOCKS
+#endif
 constexpr int SW_BF = MOE_SKINNY_WAVES;     // waves per workgroup, splitting K (bf16 weights)
-constexpr int SW_W8 = MOE_SKINNY_WAVES_W8;  // the same for E4M3 weights
+constexpr int SW_W8 = MOE_SKINNY_WAVES_W8;  // the same for E4M3 and MXFP4 weights
+
+// 16-row MFMA blocks per workgroup. gate_up: half of them gate rows, half the
+// matching up rows; down: consecutive rows. A wave's token fragments serve
+// all of its blocks, so the formats with more weights per byte (and so more
+// token fragments per byte streamed) take more rows.
+constexpr int skinny_blocks(bool gateup, int fmt)
+{
+    return gateup ? (fmt == 2 ? MOE_SKINNY_GU_BLOCKS_W4 : fmt == 1 ? MOE_SKINNY_GU_BLOCKS_W8 : 2)
+                  : (fmt == 2 ? MOE_SKINNY_DN_BLOCKS_W4 : fmt == 1 ? MOE_SKINNY_DN_BLOCKS_W8 : MOE_SKINNY_DOWN_BLOCKS);
+}
+// output columns of h (gate_up) or output rows (down) per workgroup
+constexpr int skinny_cols(bool gateup, int fmt) { return (gateup ? 8 : 16) * skinny_blocks(gateup, fmt); }
 
 struct SkinnyParams {
     const __bf16 *A;
@@ -110,6 +140,21 @@ __device__ __forceinline__ u32x4 e2m1x8_to_bf16(uint32_t w, float s)
                  __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 3))};
 }
 
+// Buffer resource over n bytes at base (raw, untyped: word 3 as for gfx9
+// raw buffers); loads through it take a per-lane 32-bit offset and a
+// wave-uniform offset in a scalar register, so a row group's base address
+// never occupies vector registers.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t n)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)n, 0x00020000);
+}
+// 16 bytes at base + soff + voff, non-temporal (cache policy bit nt)
+__device__ __forceinline__ u32x4 buffer_load_nt16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff)
+{
+    const u32x4v_t v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 2);
+    return u32x4{v.x, v.y, v.z, v.w};
+}
+
 // the factor 2^(b - 127) of an E8M0 byte b as fp32 (b = 0: the subnormal 2^-127)
 __device__ __forceinline__ float e8m0_factor(uint32_t b) { return __uint_as_float(b ? b << 23 : 0x00400000u); }
 
@@ -141,20 +186,19 @@ __global__ __launch_bounds__((FMT ? SW_W8 : SW_BF) * 64,
     constexpr bool W8 = FMT == 1;
     constexpr bool W4 = FMT == 2;
     constexpr int SW = FMT ? SW_W8 : SW_BF;
-    constexpr int PD = FMT ? MOE_SKINNY_PD_W8 : GATEUP ? MOE_SKINNY_PD_GU : MOE_SKINNY_PD_DN;  // steps in flight
+    constexpr int PD = W4 ? MOE_SKINNY_PD_W4 : W8 ? MOE_SKINNY_PD_W8 : GATEUP ? MOE_SKINNY_PD_GU : MOE_SKINNY_PD_DN;  // steps in flight
     constexpr int KS = W4 ? 4 * KB : W8 ? 2 * KB : KB;  // reduction elements per step (256 bytes of each row)
     constexpr int EPC = W4 ? 32 : W8 ? 16 : 8;          // elements per 16-byte chunk
     constexpr int FPC = EPC / 8;                        // MFMA fragments per chunk
     constexpr int XF = 4 * FPC;                         // token fragments per step
     // bytes of x weights (compile-time shifts, no multiply-then-divide)
     auto wbytes = [](uint32_t x) -> uint32_t { return W4 ? x >> 1 : W8 ? x : x << 1; };
-    // 16-row MFMA blocks per workgroup: gate_up takes 16 gate + the matching 16
-    // up rows; down takes MOE_SKINNY_DOWN_BLOCKS consecutive blocks of 16 rows
-    constexpr int NW = GATEUP ? 2 : MOE_SKINNY_DOWN_BLOCKS;
-    constexpr int NR = 16 * NW;         // weight rows per step
+    constexpr int NW = skinny_blocks(GATEUP, FMT);
+    constexpr int NR = 16 * NW;         // weight rows per step (gate_up: NR / 2 gate, then NR / 2 up rows)
     constexpr int NL = NR / 4;          // load instructions per step
+    static_assert(!GATEUP || NW % 2 == 0, "gate_up pairs gate and up blocks");
+    // each wave's weight tile; after the K loop it holds the wave's partial sums
     __shared__ u32x4 s_w[SW][NR * 16];
-    __shared__ f32x4_t s_red[SW][NW][64];
     __shared__ uint8_t s_bs[W4 ? SW : 1][W4 ? NR * 16 : 1];  // MXFP4: the block scale of each chunk
     // direct routing: per row of the expert, its token (gate_up) or its
     // assignment (down)
@@ -194,7 +238,7 @@ __global__ __launch_bounds__((FMT ? SW_W8 : SW_BF) * 64,
         row0 = p.counts ? p.offsets[e] : 0;
     }
     if (M <= 0) return;  // workgroup-uniform
-    const int n0 = blockIdx.x * (GATEUP ? 16 : 16 * NW);
+    const int n0 = blockIdx.x * skinny_cols(GATEUP, FMT);
     const int lgrp = lane >> 4;
     const int l16 = lane & 15;
 
@@ -209,22 +253,20 @@ __global__ __launch_bounds__((FMT ? SW_W8 : SW_BF) * 64,
                            (W4 ? (int64_t)e * p.w_expert_stride / 2 : (int64_t)e * p.w_expert_stride * (W8 ? 1 : 2));
     // MXFP4: the expert's block scales, K / 32 per row; chunk l16 of a step is block kb * 16 + l16
     const uint8_t *sbase = W4 ? p.w_bscale + (int64_t)e * (GATEUP ? 2 * p.N : p.N) * (p.K / 32) : nullptr;
-    uint32_t woff[NL], soff[NL];
-#pragma unroll
-    for (int i = 0; i < NL; i++) {
-        const int tr = 4 * i + lgrp;  // tile row
-        int mrow;
-        if (GATEUP) {
-            const int n = n0 + (tr & 15);
-            const int nc = n < p.N ? n : 0;
-            mrow = (tr < 16) ? nc : p.N + nc;  // gate rows, then up rows
-        } else {
-            const int n = n0 + tr;
-            mrow = n < p.N ? n : 0;
-        }
-        woff[i] = wbytes((uint32_t)mrow * (uint32_t)p.K);
-        if (W4) soff[i] = (uint32_t)mrow * (uint32_t)(p.K / 32);
-    }
+    // Weights are read through buffer resources: load i's group of 4 rows
+    // starts at a wave-uniform row (a scalar offset) and a lane adds its row
+    // in the group (lgrp) and its chunk (a 32-bit vector offset), so no
+    // per-load address occupies vector registers. A group past N is moved
+    // back to rows N-4..N-1 (N % 4 == 0); columns past N are never written.
+    auto urow = [&](int i) -> uint32_t {
+        constexpr int half = GATEUP ? NR / 2 : NR;
+        const int tr = 4 * i;
+        const int n = min(n0 + tr % half, p.N - 4);
+        return (GATEUP && tr >= half) ? p.N + n : n;
+    };
+    const uint32_t wrows = GATEUP ? 2 * p.N : p.N;
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(wbase, wbytes(wrows * (uint32_t)p.K));
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(sbase, W4 ? wrows * (uint32_t)(p.K / 32) : 0u);
     u32x4 *tile = s_w[wave];
     const u32x4 zero = {0u, 0u, 0u, 0u};
 
@@ -259,12 +301,12 @@ __global__ __launch_bounds__((FMT ? SW_W8 : SW_BF) * 64,
         auto gload_w = [&](int kb, int b) {
             const uint32_t okm = 0u - (uint32_t)w_ok(kb);
             const uint32_t kbytes = wbytes((uint32_t)(kb * KS + l16 * EPC)) & okm;
+            const uint32_t lw = wbytes((uint32_t)lgrp * (uint32_t)p.K) + kbytes;
+            const uint32_t ls = (uint32_t)lgrp * (uint32_t)(p.K / 32) + ((uint32_t)(kb * 16 + l16) & okm);
 #pragma unroll
-            for (int i = 0; i < NL; i++) st[b][i] = load_nt16(wbase + woff[i] + kbytes);
-            if (W4) {
-                const uint32_t kblk = (uint32_t)(kb * 16 + l16) & okm;
-#pragma unroll
-                for (int i = 0; i < NL; i++) bs[b][i] = sbase[soff[i] + kblk];
+            for (int i = 0; i < NL; i++) {
+                st[b][i] = buffer_load_nt16(rw, lw, wbytes(urow(i) * (uint32_t)p.K));
+                if (W4) bs[b][i] = __builtin_amdgcn_raw_buffer_load_b8(rs, ls, urow(i) * (uint32_t)(p.K / 32), 0);
             }
         };
         auto gload_x = [&](int kb, int b) {
@@ -292,7 +334,7 @@ __global__ __launch_bounds__((FMT ? SW_W8 : SW_BF) * 64,
             if (more) gload_w(kb + PD, b);
             u32x4 xb[XF];
 #pragma unroll
-            for (int f = 0; f < XF; f++) xb[f] = keep_if(x_ok(kb, f), xs[b][f]);
+            for (int f = 0; f < XF; f++) xb[f] = W4 ? xs[b][f] : keep_if(x_ok(kb, f), xs[b][f]);
 #pragma unroll
             for (int j = 0; j < 4; j++) {
 #pragma unroll
@@ -317,6 +359,9 @@ __global__ __launch_bounds__((FMT ? SW_W8 : SW_BF) * 64,
                         acc[w] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(xb[j]), acc[w], 0, 0, 0);
                     }
                 }
+                // MXFP4: convert each chunk just before its MFMAs; hoisting
+                // every conversion of a step would need 256 more registers
+                if (W4) __builtin_amdgcn_sched_barrier(0);
             }
             if (more) gload_x(kb + PD, b);
         };
@@ -335,18 +380,21 @@ __global__ __launch_bounds__((FMT ? SW_W8 : SW_BF) * 64,
         for (int b = 0; b < PD - 1; b++)
             if (kb + b < kb_hi) step(kb + b, b);
 
-        // ---- split-K reduction across the waves, in wave order
+        // ---- split-K reduction across the waves, in wave order (each wave's
+        // partial sums go to its own tile, which it no longer reads)
+        static_assert(NW * 64 * sizeof(f32x4_t) <= NR * 16 * sizeof(u32x4), "partials fit the tile");
+        auto red = [&](int v) { return reinterpret_cast<f32x4_t *>(s_w[v]); };
 #pragma unroll
-        for (int w = 0; w < NW; w++) s_red[wave][w][lane] = acc[w];
+        for (int w = 0; w < NW; w++) red(wave)[w * 64 + lane] = acc[w];
         __syncthreads();
         if (wave == 0) {
             f32x4_t sm[NW];
 #pragma unroll
             for (int w = 0; w < NW; w++) {
-                sm[w] = s_red[0][w][lane];
+                sm[w] = red(0)[w * 64 + lane];
 #pragma unroll
                 for (int v = 1; v < SW; v++) {
-                    const f32x4_t o = s_red[v][w][lane];
+                    const f32x4_t o = red(v)[w * 64 + lane];
                     sm[w][0] += o[0]; sm[w][1] += o[1]; sm[w][2] += o[2]; sm[w][3] += o[3];
                 }
             }
@@ -357,23 +405,26 @@ __global__ __launch_bounds__((FMT ? SW_W8 : SW_BF) * 64,
                 for (int w = 0; w < NW; w++)
 #pragma unroll
                     for (int i = 0; i < 4; i++) {
-                        const int r = GATEUP ? n0 + 4 * lgrp + i + w * p.N : n0 + 16 * w + 4 * lgrp + i;
-                        const bool in = GATEUP ? n0 + 4 * lgrp + i < p.N : r < p.N;
-                        sm[w][i] *= in ? sc[r] : 0.0f;
+                        const int cn = n0 + 16 * (GATEUP ? w % (NW / 2) : w) + 4 * lgrp + i;
+                        const int r = GATEUP && w >= NW / 2 ? cn + p.N : cn;
+                        sm[w][i] *= cn < p.N ? sc[r] : 0.0f;
                     }
             }
             if (xv) {
                 const int pos = row0 + q;
                 if (GATEUP) {
-                    const int c = n0 + 4 * lgrp;
-                    if (c < p.N) {
-                        float hv[4];
 #pragma unroll
-                        for (int i = 0; i < 4; i++) hv[i] = silu_f32(sm[0][i]) * sm[1][i];
-                        uint2 packed;
-                        packed.x = pack_bf16x2(hv[0], hv[1]);
-                        packed.y = pack_bf16x2(hv[2], hv[3]);
-                        *reinterpret_cast<uint2 *>(reinterpret_cast<__bf16 *>(p.C) + (int64_t)pos * p.N + c) = packed;
+                    for (int w = 0; w < NW / 2; w++) {  // gate block w, up block w + NW / 2
+                        const int c = n0 + 16 * w + 4 * lgrp;
+                        if (c < p.N) {
+                            float hv[4];
+#pragma unroll
+                            for (int i = 0; i < 4; i++) hv[i] = silu_f32(sm[w][i]) * sm[w + NW / 2][i];
+                            uint2 packed;
+                            packed.x = pack_bf16x2(hv[0], hv[1]);
+                            packed.y = pack_bf16x2(hv[2], hv[3]);
+                            *reinterpret_cast<uint2 *>(reinterpret_cast<__bf16 *>(p.C) + (int64_t)pos * p.N + c) = packed;
+                        }
                     }
                 } else {
                     const int64_t orow = DIRECT ? (int64_t)s_rows[q] : p.c_rows ? (int64_t)p.c_rows[pos] : (int64_t)pos;
@@ -423,7 +474,8 @@ SkinnyParams make_params(const GemmProblem &g)
 hipError_t launch_gate_up_skinny(const GemmProblem &g, hipStream_t st)
 {
     SkinnyParams s = make_params(g);
-    dim3 grid((unsigned)((g.N + 15) / 16), g.dense_rows > 0 ? 1u : (unsigned)g.E);
+    const int cols = skinny_cols(true, g.w_bscale ? 2 : g.w_scale ? 1 : 0);
+    dim3 grid((unsigned)((g.N + cols - 1) / cols), g.dense_rows > 0 ? 1u : (unsigned)g.E);
     if (g.w_bscale) {
         s.ids = nullptr;  // low-precision weights always take the sorted tables
         hipLaunchKernelGGL((skinny_gemm_kernel<true, 2, false>), grid, dim3(SW_W8 * 64), 0, st, s);
@@ -440,7 +492,7 @@ hipError_t launch_gate_up_skinny(const GemmProblem &g, hipStream_t st)
 hipError_t launch_down_skinny(const GemmProblem &g, hipStream_t st)
 {
     SkinnyParams s = make_params(g);
-    constexpr int rows = 16 * MOE_SKINNY_DOWN_BLOCKS;
+    const int rows = skinny_cols(false, g.w_bscale ? 2 : g.w_scale ? 1 : 0);
     dim3 grid((unsigned)((g.N + rows - 1) / rows), g.dense_rows > 0 ? 1u : (unsigned)g.E);
     if (g.w_bscale) {
         s.ids = nullptr;

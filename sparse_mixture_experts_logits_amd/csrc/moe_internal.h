@@ -19,13 +19,6 @@ struct alignas(16) u32x4 {
 
 typedef uint32_t u32x4v_t __attribute__((ext_vector_type(4)));
 
-// 16-byte load marked non-temporal (streamed data that is read once).
-__device__ __forceinline__ u32x4 load_nt16(const void *p)
-{
-    const u32x4v_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4v_t *>(p));
-    return u32x4{v.x, v.y, v.z, v.w};
-}
-
 // Plain 16-byte load (one dwordx4 instruction).
 __device__ __forceinline__ u32x4 load16(const void *p)
 {
