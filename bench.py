@@ -143,8 +143,12 @@ def write_traffic(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, kernel, 
 
     f_k, nf = avg(_counter_rows(fetch_dir), "FETCH_SIZE", rx)
     w_k, nw = avg(_counter_rows(write_dir), "WRITE_SIZE", rx)
+    if not nf or not nw:
+        raise SystemExit(f"no dispatch of a kernel matching {regex!r} in {fetch_dir} / {write_dir}")
     f_c = copy_avg(_counter_rows(copy_fetch_dir), "FETCH_SIZE")
     w_c = copy_avg(_counter_rows(copy_write_dir), "WRITE_SIZE")
+    if f_c is None or w_c is None:
+        raise SystemExit(f"no copy dispatch in {copy_fetch_dir} / {copy_write_dir}")
     ff = copy_bytes / (f_c * 1024.0)
     fw = copy_bytes / (w_c * 1024.0)
     d = {

@@ -72,10 +72,20 @@ constexpr int KB = 128;  // reduction elements per step: 256 bytes of each row
 #define MOE_SKINNY_DN_BLOCKS_W8 MOE_SKINNY_DOWN_BLOCKS
 #endif
 #ifndef MOE_SKINNY_DN_BLOCKS_W4
-#define MOE_SKINNY_DN_BLOCKS_W4 MOE_SKINNY_DOWN_BLOCKS
+#define MOE_SKINNY_DN_BLOCKS_W4 4
 #endif
-constexpr int SW_BF = MOE_SKINNY_WAVES;     // waves per workgroup, splitting K (bf16 weights)
-constexpr int SW_W8 = MOE_SKINNY_WAVES_W8;  // the same for E4M3 and MXFP4 weights
+#ifndef MOE_SKINNY_WAVES_W4
+#define MOE_SKINNY_WAVES_W4 2
+#endif
+#ifndef MOE_SKINNY_WAVES_W4_DN
+#define MOE_SKINNY_WAVES_W4_DN MOE_SKINNY_WAVES_W4
+#endif
+// waves per workgroup, splitting K, per GEMM and weight storage (bf16, E4M3, MXFP4)
+constexpr int skinny_waves(bool gateup, int fmt)
+{
+    return fmt >= 2 ? (gateup ? MOE_SKINNY_WAVES_W4 : MOE_SKINNY_WAVES_W4_DN)
+                    : fmt == 1 ? MOE_SKINNY_WAVES_W8 : MOE_SKINNY_WAVES;
+}
 
 // 16-row MFMA blocks per workgroup. gate_up: half of them gate rows, half the
 // matching up rows; down: consecutive rows. A wave's token fragments serve
@@ -83,8 +93,8 @@ constexpr int SW_W8 = MOE_SKINNY_WAVES_W8;  // the same for E4M3 and MXFP4 weigh
 // token fragments per byte streamed) take more rows.
 constexpr int skinny_blocks(bool gateup, int fmt)
 {
-    return gateup ? (fmt == 2 ? MOE_SKINNY_GU_BLOCKS_W4 : fmt == 1 ? MOE_SKINNY_GU_BLOCKS_W8 : 2)
-                  : (fmt == 2 ? MOE_SKINNY_DN_BLOCKS_W4 : fmt == 1 ? MOE_SKINNY_DN_BLOCKS_W8 : MOE_SKINNY_DOWN_BLOCKS);
+    return gateup ? (fmt >= 2 ? MOE_SKINNY_GU_BLOCKS_W4 : fmt == 1 ? MOE_SKINNY_GU_BLOCKS_W8 : 2)
+                  : (fmt >= 2 ? MOE_SKINNY_DN_BLOCKS_W4 : fmt == 1 ? MOE_SKINNY_DN_BLOCKS_W8 : MOE_SKINNY_DOWN_BLOCKS);
 }
 // output columns of h (gate_up) or output rows (down) per workgroup
 constexpr int skinny_cols(bool gateup, int fmt) { return (gateup ? 8 : 16) * skinny_blocks(gateup, fmt); }
@@ -177,15 +187,18 @@ __device__ __forceinline__ int tswz(int r, int c) { return r * 16 + (c ^ (r & 15
 #ifndef MOE_SKINNY_BF_OCC
 #define MOE_SKINNY_BF_OCC 1
 #endif
-// FMT: weight storage, 0 bf16, 1 E4M3 (row scales), 2 MXFP4 (block scales).
+// FMT: weight storage, 0 bf16, 1 E4M3 (row scales), 2 MXFP4 (block scales),
+// 3 MXFP4 whose rows of block scales start 4-byte aligned (K % 128 == 0), so
+// a lane reads one row's 16 scales of a step with one 16-byte load.
 // DIRECT: route straight from the top-k ids (see SkinnyParams).
 template <bool GATEUP, int FMT, bool DIRECT>
-__global__ __launch_bounds__((FMT ? SW_W8 : SW_BF) * 64,
-                             FMT == 2 ? MOE_SKINNY_W4_OCC : FMT ? MOE_SKINNY_W8_OCC : MOE_SKINNY_BF_OCC) void skinny_gemm_kernel(SkinnyParams p)
+__global__ __launch_bounds__(skinny_waves(GATEUP, FMT) * 64,
+                             FMT >= 2 ? MOE_SKINNY_W4_OCC : FMT ? MOE_SKINNY_W8_OCC : MOE_SKINNY_BF_OCC) void skinny_gemm_kernel(SkinnyParams p)
 {
     constexpr bool W8 = FMT == 1;
-    constexpr bool W4 = FMT == 2;
-    constexpr int SW = FMT ? SW_W8 : SW_BF;
+    constexpr bool W4 = FMT >= 2;
+    constexpr bool SC4 = FMT == 3;
+    constexpr int SW = skinny_waves(GATEUP, FMT);
     constexpr int PD = W4 ? MOE_SKINNY_PD_W4 : W8 ? MOE_SKINNY_PD_W8 : GATEUP ? MOE_SKINNY_PD_GU : MOE_SKINNY_PD_DN;  // steps in flight
     constexpr int KS = W4 ? 4 * KB : W8 ? 2 * KB : KB;  // reduction elements per step (256 bytes of each row)
     constexpr int EPC = W4 ? 32 : W8 ? 16 : 8;          // elements per 16-byte chunk
@@ -199,7 +212,8 @@ __global__ __launch_bounds__((FMT ? SW_W8 : SW_BF) * 64,
     static_assert(!GATEUP || NW % 2 == 0, "gate_up pairs gate and up blocks");
     // each wave's weight tile; after the K loop it holds the wave's partial sums
     __shared__ u32x4 s_w[SW][NR * 16];
-    __shared__ uint8_t s_bs[W4 ? SW : 1][W4 ? NR * 16 : 1];  // MXFP4: the block scale of each chunk
+    // MXFP4: the block scale of each chunk, row r's 16 in bytes [16r, 16r + 16)
+    __shared__ __attribute__((aligned(16))) uint32_t s_bs[W4 ? SW : 1][W4 ? NR * 4 : 1];
     // direct routing: per row of the expert, its token (gate_up) or its
     // assignment (down)
     __shared__ int s_rows[DIRECT ? kSkinnyDirectMax : 1];
@@ -283,11 +297,13 @@ __global__ __launch_bounds__((FMT ? SW_W8 : SW_BF) * 64,
         for (int w = 0; w < NW; w++) acc[w] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
         u32x4 st[PD][NL];
-        uint32_t bs[PD][W4 ? NL : 1];  // MXFP4 block scale bytes of the staged chunks
+        uint32_t bs[PD][FMT == 2 ? NL : 1];  // MXFP4 block scale bytes of the staged chunks
+        u32x4 sc[PD];                        // MXFP4, aligned scale rows: this lane's row's 16 scales
         u32x4 xs[PD][XF];
         // weights of step kb and the token fragments it needs: MFMA j takes
         // chunk 4j + lgrp (bf16: 8 elements; E4M3: 16 elements, as two MFMAs
-        // over its halves, fragment 2j + half)
+        // over its halves, fragment 2j + half; MXFP4: 32 elements, as four
+        // MFMAs over its words, fragment 4j + word)
         // Loads are unconditional and whole 16-byte loads: a chunk past K (or
         // a token past the expert's rows) reads the row's first chunk instead,
         // and the consumer zeroes it. With no branches or selects between a
@@ -306,7 +322,17 @@ __global__ __launch_bounds__((FMT ? SW_W8 : SW_BF) * 64,
 #pragma unroll
             for (int i = 0; i < NL; i++) {
                 st[b][i] = buffer_load_nt16(rw, lw, wbytes(urow(i) * (uint32_t)p.K));
-                if (W4) bs[b][i] = __builtin_amdgcn_raw_buffer_load_b8(rs, ls, urow(i) * (uint32_t)(p.K / 32), 0);
+                if (FMT == 2) bs[b][i] = __builtin_amdgcn_raw_buffer_load_b8(rs, ls, urow(i) * (uint32_t)(p.K / 32), 0);
+            }
+            if (SC4) {
+                // lane r (mod NR) reads tile row r's 16 scales of the step (a
+                // row past N reads row N - 1; its columns are never written)
+                constexpr int half = GATEUP ? NR / 2 : NR;
+                const int r = lane % NR;
+                const int n = min(n0 + r % half, p.N - 1);
+                const uint32_t grow = (GATEUP && r >= half) ? p.N + n : n;
+                const u32x4v_t v = __builtin_amdgcn_raw_buffer_load_b128(rs, grow * (uint32_t)(p.K / 32) + kb * 16, 0, 0);
+                sc[b] = u32x4{v.x, v.y, v.z, v.w};
             }
         };
         auto gload_x = [&](int kb, int b) {
@@ -326,9 +352,24 @@ __global__ __launch_bounds__((FMT ? SW_W8 : SW_BF) * 64,
             const bool okw = w_ok(kb);
 #pragma unroll
             for (int i = 0; i < NL; i++) tile[tswz(4 * i + lgrp, l16)] = keep_if(okw, st[b][i]);
-            if (W4) {
+            if (FMT == 2) {
+                uint8_t *sb = reinterpret_cast<uint8_t *>(s_bs[W4 ? wave : 0]);
 #pragma unroll
-                for (int i = 0; i < NL; i++) s_bs[W4 ? wave : 0][(4 * i + lgrp) * 16 + l16] = (uint8_t)bs[b][i];
+                for (int i = 0; i < NL; i++) sb[(4 * i + lgrp) * 16 + l16] = (uint8_t)bs[b][i];
+            }
+            if (SC4) {
+                // scales of blocks past K (a ragged last step) read the next
+                // row's; they become 127 (factor 1) so that the zero weights
+                // there stay zero whatever those bytes hold
+                const int nb = p.K / 32 - kb * 16;  // blocks of this step inside K
+                auto keep = [&](uint32_t v, int d) {
+                    const int nv = nb - 4 * d;
+                    const uint32_t m = nv >= 4 ? 0xFFFFFFFFu : nv <= 0 ? 0u : (1u << (8 * nv)) - 1u;
+                    return (v & m) | (0x7F7F7F7Fu & ~m);
+                };
+                if (lane < NR)
+                    reinterpret_cast<u32x4 *>(s_bs[W4 ? wave : 0])[lane] =
+                        u32x4{keep(sc[b].x, 0), keep(sc[b].y, 1), keep(sc[b].z, 2), keep(sc[b].w, 3)};
             }
             const bool more = kb + PD < kb_hi;
             if (more) gload_w(kb + PD, b);
@@ -341,7 +382,8 @@ __global__ __launch_bounds__((FMT ? SW_W8 : SW_BF) * 64,
                 for (int w = 0; w < NW; w++) {
                     const u32x4 a = tile[tswz(16 * w + l16, 4 * j + lgrp)];
                     if (W4) {
-                        const float sf = e8m0_factor(s_bs[W4 ? wave : 0][(16 * w + l16) * 16 + 4 * j + lgrp]);
+                        const uint8_t *sb = reinterpret_cast<const uint8_t *>(s_bs[W4 ? wave : 0]);
+                        const float sf = e8m0_factor(sb[(16 * w + l16) * 16 + 4 * j + lgrp]);
                         acc[w] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(e2m1x8_to_bf16(a.x, sf)),
                                                                          as_bf16x8(xb[4 * j]), acc[w], 0, 0, 0);
                         acc[w] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(e2m1x8_to_bf16(a.y, sf)),
@@ -478,13 +520,16 @@ hipError_t launch_gate_up_skinny(const GemmProblem &g, hipStream_t st)
     dim3 grid((unsigned)((g.N + cols - 1) / cols), g.dense_rows > 0 ? 1u : (unsigned)g.E);
     if (g.w_bscale) {
         s.ids = nullptr;  // low-precision weights always take the sorted tables
-        hipLaunchKernelGGL((skinny_gemm_kernel<true, 2, false>), grid, dim3(SW_W8 * 64), 0, st, s);
+        if ((g.K / 32) % 4 == 0)
+            hipLaunchKernelGGL((skinny_gemm_kernel<true, 3, false>), grid, dim3(skinny_waves(true, 3) * 64), 0, st, s);
+        else
+            hipLaunchKernelGGL((skinny_gemm_kernel<true, 2, false>), grid, dim3(skinny_waves(true, 2) * 64), 0, st, s);
     } else if (g.w_scale) {
         s.ids = nullptr;
-        hipLaunchKernelGGL((skinny_gemm_kernel<true, 1, false>), grid, dim3(SW_W8 * 64), 0, st, s);
+        hipLaunchKernelGGL((skinny_gemm_kernel<true, 1, false>), grid, dim3(skinny_waves(true, 1) * 64), 0, st, s);
     } else {
-        if (s.ids) hipLaunchKernelGGL((skinny_gemm_kernel<true, 0, true>), grid, dim3(SW_BF * 64), 0, st, s);
-        else hipLaunchKernelGGL((skinny_gemm_kernel<true, 0, false>), grid, dim3(SW_BF * 64), 0, st, s);
+        if (s.ids) hipLaunchKernelGGL((skinny_gemm_kernel<true, 0, true>), grid, dim3(skinny_waves(true, 0) * 64), 0, st, s);
+        else hipLaunchKernelGGL((skinny_gemm_kernel<true, 0, false>), grid, dim3(skinny_waves(true, 0) * 64), 0, st, s);
     }
     return hipGetLastError();
 }
@@ -496,13 +541,16 @@ hipError_t launch_down_skinny(const GemmProblem &g, hipStream_t st)
     dim3 grid((unsigned)((g.N + rows - 1) / rows), g.dense_rows > 0 ? 1u : (unsigned)g.E);
     if (g.w_bscale) {
         s.ids = nullptr;
-        hipLaunchKernelGGL((skinny_gemm_kernel<false, 2, false>), grid, dim3(SW_W8 * 64), 0, st, s);
+        if ((g.K / 32) % 4 == 0)
+            hipLaunchKernelGGL((skinny_gemm_kernel<false, 3, false>), grid, dim3(skinny_waves(false, 3) * 64), 0, st, s);
+        else
+            hipLaunchKernelGGL((skinny_gemm_kernel<false, 2, false>), grid, dim3(skinny_waves(false, 2) * 64), 0, st, s);
     } else if (g.w_scale) {
         s.ids = nullptr;
-        hipLaunchKernelGGL((skinny_gemm_kernel<false, 1, false>), grid, dim3(SW_W8 * 64), 0, st, s);
+        hipLaunchKernelGGL((skinny_gemm_kernel<false, 1, false>), grid, dim3(skinny_waves(false, 1) * 64), 0, st, s);
     } else {
-        if (s.ids) hipLaunchKernelGGL((skinny_gemm_kernel<false, 0, true>), grid, dim3(SW_BF * 64), 0, st, s);
-        else hipLaunchKernelGGL((skinny_gemm_kernel<false, 0, false>), grid, dim3(SW_BF * 64), 0, st, s);
+        if (s.ids) hipLaunchKernelGGL((skinny_gemm_kernel<false, 0, true>), grid, dim3(skinny_waves(false, 0) * 64), 0, st, s);
+        else hipLaunchKernelGGL((skinny_gemm_kernel<false, 0, false>), grid, dim3(skinny_waves(false, 0) * 64), 0, st, s);
     }
     return hipGetLastError();
 }
