@@ -513,46 +513,36 @@ SkinnyParams make_params(const GemmProblem &g)
 
 }  // namespace
 
-hipError_t launch_gate_up_skinny(const GemmProblem &g, hipStream_t st)
+namespace {
+
+template <bool GATEUP, int FMT>
+void launch_fmt(dim3 grid, const SkinnyParams &s, hipStream_t st)
 {
-    SkinnyParams s = make_params(g);
-    const int cols = skinny_cols(true, g.w_bscale ? 2 : g.w_scale ? 1 : 0);
-    dim3 grid((unsigned)((g.N + cols - 1) / cols), g.dense_rows > 0 ? 1u : (unsigned)g.E);
-    if (g.w_bscale) {
-        s.ids = nullptr;  // low-precision weights always take the sorted tables
-        if ((g.K / 32) % 4 == 0)
-            hipLaunchKernelGGL((skinny_gemm_kernel<true, 3, false>), grid, dim3(skinny_waves(true, 3) * 64), 0, st, s);
-        else
-            hipLaunchKernelGGL((skinny_gemm_kernel<true, 2, false>), grid, dim3(skinny_waves(true, 2) * 64), 0, st, s);
-    } else if (g.w_scale) {
-        s.ids = nullptr;
-        hipLaunchKernelGGL((skinny_gemm_kernel<true, 1, false>), grid, dim3(skinny_waves(true, 1) * 64), 0, st, s);
-    } else {
-        if (s.ids) hipLaunchKernelGGL((skinny_gemm_kernel<true, 0, true>), grid, dim3(skinny_waves(true, 0) * 64), 0, st, s);
-        else hipLaunchKernelGGL((skinny_gemm_kernel<true, 0, false>), grid, dim3(skinny_waves(true, 0) * 64), 0, st, s);
+    const dim3 block(skinny_waves(GATEUP, FMT) * 64);
+    if (s.ids) hipLaunchKernelGGL((skinny_gemm_kernel<GATEUP, FMT, true>), grid, block, 0, st, s);
+    else hipLaunchKernelGGL((skinny_gemm_kernel<GATEUP, FMT, false>), grid, block, 0, st, s);
+}
+
+template <bool GATEUP>
+hipError_t launch_skinny(const GemmProblem &g, hipStream_t st)
+{
+    const SkinnyParams s = make_params(g);
+    const int fmt = g.w_bscale ? ((g.K / 32) % 4 == 0 ? 3 : 2) : g.w_scale ? 1 : 0;
+    const int cols = skinny_cols(GATEUP, fmt);
+    const dim3 grid((unsigned)((g.N + cols - 1) / cols), g.dense_rows > 0 ? 1u : (unsigned)g.E);
+    switch (fmt) {
+    case 3: launch_fmt<GATEUP, 3>(grid, s, st); break;
+    case 2: launch_fmt<GATEUP, 2>(grid, s, st); break;
+    case 1: launch_fmt<GATEUP, 1>(grid, s, st); break;
+    default: launch_fmt<GATEUP, 0>(grid, s, st); break;
     }
     return hipGetLastError();
 }
 
-hipError_t launch_down_skinny(const GemmProblem &g, hipStream_t st)
-{
-    SkinnyParams s = make_params(g);
-    const int rows = skinny_cols(false, g.w_bscale ? 2 : g.w_scale ? 1 : 0);
-    dim3 grid((unsigned)((g.N + rows - 1) / rows), g.dense_rows > 0 ? 1u : (unsigned)g.E);
-    if (g.w_bscale) {
-        s.ids = nullptr;
-        if ((g.K / 32) % 4 == 0)
-            hipLaunchKernelGGL((skinny_gemm_kernel<false, 3, false>), grid, dim3(skinny_waves(false, 3) * 64), 0, st, s);
-        else
-            hipLaunchKernelGGL((skinny_gemm_kernel<false, 2, false>), grid, dim3(skinny_waves(false, 2) * 64), 0, st, s);
-    } else if (g.w_scale) {
-        s.ids = nullptr;
-        hipLaunchKernelGGL((skinny_gemm_kernel<false, 1, false>), grid, dim3(skinny_waves(false, 1) * 64), 0, st, s);
-    } else {
-        if (s.ids) hipLaunchKernelGGL((skinny_gemm_kernel<false, 0, true>), grid, dim3(skinny_waves(false, 0) * 64), 0, st, s);
-        else hipLaunchKernelGGL((skinny_gemm_kernel<false, 0, false>), grid, dim3(skinny_waves(false, 0) * 64), 0, st, s);
-    }
-    return hipGetLastError();
-}
+}  // namespace
+
+hipError_t launch_gate_up_skinny(const GemmProblem &g, hipStream_t st) { return launch_skinny<true>(g, st); }
+
+hipError_t launch_down_skinny(const GemmProblem &g, hipStream_t st) { return launch_skinny<false>(g, st); }
 
 }  // namespace moe

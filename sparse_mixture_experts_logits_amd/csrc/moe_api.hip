@@ -324,10 +324,8 @@ int moe_forward(const void *hidden, const void *router_w, const void *gate_up, c
         return rc;
     // Few assignments on the weight-streaming kernels, with no sorted routing
     // tables or statistics asked for: those kernels route straight from the
-    // top-k ids, and the scan and permute launches are skipped (bf16 weights
-    // only: the E4M3 kernels lose more to the extra registers than the two
-    // launches cost).
-    const bool direct = skinny && !f32 && !w8 && !w4 && T * k <= moe::kSkinnyDirectMax && !opts->expert_counts &&
+    // top-k ids, and the scan and permute launches are skipped.
+    const bool direct = skinny && !f32 && T * k <= moe::kSkinnyDirectMax && !opts->expert_counts &&
                         !opts->expert_offsets && !opts->perm && !opts->inv_perm && !rs.on();
     if (!direct) {
         if ((rc = check(moe::launch_route_scan(s, opts->expert_counts, opts->expert_offsets, rs, ws, st),

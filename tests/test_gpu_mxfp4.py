@@ -86,17 +86,20 @@ def test_quantize_kernel_bit_exact_on_random_rows(rows, cols, std):
     check_quant(W.f32_to_bf16_bits(x), f"{rows}x{cols}")
 
 
-def run_mxfp4(inp, gq, gs, dq, ds, flags=0):
+def run_mxfp4(inp, gq, gs, dq, ds, flags=0, routing=True):
     wl = inp.wl
     sgu = sdn = None
     if inp.shared_gate_up:
         g, d = inp.shared_concat()
         sgu, sdn = dev(g), dev(d)
     bias = None if inp.bias is None else torch.from_numpy(inp.bias).cuda()
-    out, r = moe.moe_forward(dev(inp.hidden), dev(inp.router_w), gq, dq, wl.k, routed_scale=wl.routed_scale,
-                             router_bias=bias, shared_gate_up=sgu, shared_down=sdn, flags=flags,
-                             gate_up_block_scale=gs, down_block_scale=ds, return_routing=True)
+    res = moe.moe_forward(dev(inp.hidden), dev(inp.router_w), gq, dq, wl.k, routed_scale=wl.routed_scale,
+                          router_bias=bias, shared_gate_up=sgu, shared_down=sdn, flags=flags,
+                          gate_up_block_scale=gs, down_block_scale=ds, return_routing=routing)
     torch.cuda.synchronize()
+    if not routing:
+        return res.float().cpu().numpy(), None
+    out, r = res
     return out.float().cpu().numpy(), {k: v.cpu().numpy() for k, v in r.items()}
 
 
@@ -104,6 +107,10 @@ def check_against_oracle(inp, tokens, what, flags=0):
     gq, gs, rgq, rgs = check_quant(inp.gate_up, f"{what} gate_up")
     dq, ds, rdq, rds = check_quant(inp.down, f"{what} down")
     out, got = run_mxfp4(inp, gq, gs, dq, ds, flags)
+    # the launch without routing outputs (direct routing at few assignments)
+    # computes the same thing bit for bit
+    out_plain, _ = run_mxfp4(inp, gq, gs, dq, ds, flags, routing=False)
+    assert np.array_equal(out_plain.view(np.uint32), out.view(np.uint32)), f"{what}: direct routing differs"
     wl = inp.wl
     logits = oracle.router_logits(inp.hidden, inp.router_w, inp.bias)
     ids, w = oracle.select_topk(logits, wl.k, wl.routed_scale)
