@@ -34,3 +34,11 @@ def test_more_than_one_gpu_is_refused():
     r = subprocess.run([sys.executable, "bench.py", "--gpus", "2"], cwd=ROOT, capture_output=True, text=True,
                        timeout=120)
     assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+def test_cpu_baseline_repeats_whole_passes():
+    wl = W.BY_NAME["tiny_f32"]
+    res = {"inp": W.make_inputs(wl)}
+    b = bench.cpu_baseline(res, 64, min_seconds=0.3)
+    assert b["kind"] == "oracle" and b["unit"] == "tokens/s" and b["value"] > 0 and b["cores"] >= 1
+    assert "passes" in b["sample"] and b["sample"].startswith(f"all {wl.T} tokens of tiny_f32")
