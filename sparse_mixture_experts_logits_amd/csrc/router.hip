@@ -438,11 +438,17 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(
     __shared__ int s_cnt[kMaxExperts];
     __shared__ int s_off[kMaxExperts + 1];
     __shared__ int s_ts[kMaxExperts + 1];
-    // M-tiles of an expert with c rows: ceil(c / BM), less one when the last
-    // would hold at most XT rows (they go to the tile before it)
-    auto n_tiles = [&](int c) {
-        const int n = (c + BM - 1) / BM;
-        return (n > 1 && c - (n - 1) * BM <= XT) ? n - 1 : n;
+    // M-tiles of an expert with c rows: as few as hold them at up to BM + XT
+    // rows each. When c exceeds n * BM, the excess rides as extra rows in the
+    // first tiles (XT each, the rest in the next), so no tile is left with a
+    // handful of rows that would stream a whole weight block for them; else
+    // the tiles hold BM rows and the last one the remainder.
+    auto n_tiles = [&](int c) { return (c + BM + XT - 1) / (BM + XT); };
+    // first row (relative to the expert's offset) and rows of its tile i of n
+    auto tile_rows = [&](int c, int n, int i, int &r0, int &rows) {
+        const int extra = max(c - n * BM, 0);
+        r0 = i * BM + min(extra, i * XT);
+        rows = extra > 0 ? BM + min(max(extra - i * XT, 0), XT) : (i == n - 1 ? c - i * BM : BM);
     };
 
     const int tid = threadIdx.x;
@@ -508,9 +514,11 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(
         const int nt = n_tiles(s_cnt[tid]);
         for (int i = 0; i < nt; i++) {
             MTile m;
+            int r0, rows;
+            tile_rows(s_cnt[tid], nt, i, r0, rows);
             m.expert = tid;
-            m.row0 = s_off[tid] + i * BM;
-            m.rows = i == nt - 1 ? s_cnt[tid] - i * BM : BM;
+            m.row0 = s_off[tid] + r0;
+            m.rows = rows;
             m.pad = 0;
             tiles[s_ts[tid] + i] = m;
         }

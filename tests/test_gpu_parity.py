@@ -250,11 +250,14 @@ def routed_by_construction(counts, H, I, seed=0):
 
 
 @pytest.mark.parametrize("counts,H,I", [
-    # 257 / 272 / 288 rows: one 256-row tile plus a short tail folded into it;
-    # 289: the tail is too long and gets a tile of its own; 532 = 2*256 + 20
+    # a tile holds up to 256 + 32 rows. 257 / 272 / 288 rows: one tile with
+    # extra rows; 289: two tiles (256 + 33); 532: two (276 + 256)
     ((257, 288, 289, 532), 256, 256),
     ((272, 530, 300, 256), 328, 200),  # ragged K (328) and N (200 outputs per half)
-    ((288, 33, 290, 545), 512, 320),  # 545 = 2*256 + 33: its tail is one row too long
+    # 545 and 576: two tiles with extra rows each (288 + 257, 288 + 288);
+    # 577: three tiles (256 + 256 + 65)
+    ((288, 33, 290, 545), 512, 320),
+    ((576, 577, 300, 3), 256, 256),
 ])
 def test_tail_rows_folded_into_tiles(counts, H, I):
     _say(f"case tail tiles counts={counts} H={H} I={I}")
