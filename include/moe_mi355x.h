@@ -232,7 +232,9 @@ int64_t moe_workspace_bytes(int64_t T, int64_t H, int64_t I, int64_t E, int32_t 
  * out      [T, H]       written in full; must not overlap any input
  *
  * Sizes: T >= 0 (T = 0 is a successful no-op), 1 <= k <= E <= 256, H, I >= 8
- * and multiples of 8, T*k < 2^31.
+ * and multiples of 8, T*k < 2^31; one expert (2*I*H, 2*shared_I*H) and one
+ * activation tensor (T*H, T*k*I, T*shared_I) below 2^31 elements, H, I and
+ * shared_I at most 2^24 (else MOE_ERR_UNSUPPORTED).
  *
  * Routing is reproducible bit for bit. The logit of expert e is an fp32 sum
  * of products hidden[t,i]*router_w[e,i] taken in this order: 64 partial sums

@@ -72,6 +72,9 @@ int check_shape(int64_t T, int64_t H, int64_t I, int64_t E, int32_t k, const moe
             return fail(MOE_ERR_INVALID_ARG, "shared_I = %lld must be 0 or a positive multiple of 8",
                         (long long)opts->shared_I);
         if (opts->shared_I > (1 << 24)) return fail(MOE_ERR_UNSUPPORTED, "shared_I above 2^24");
+        // the shared expert runs on the same kernels: 32-bit element offsets
+        if (2 * opts->shared_I * H >= ((int64_t)1 << 31) || T * opts->shared_I >= ((int64_t)1 << 31))
+            return fail(MOE_ERR_UNSUPPORTED, "the shared expert or its activations exceed 2^31 elements");
         if (opts->flags & ~(MOE_FLAG_FORCE_TILED | MOE_FLAG_FORCE_SKINNY))
             return fail(MOE_ERR_INVALID_ARG, "unknown flag bits 0x%x", opts->flags);
         if ((opts->flags & MOE_FLAG_FORCE_TILED) && (opts->flags & MOE_FLAG_FORCE_SKINNY))

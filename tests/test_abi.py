@@ -302,3 +302,11 @@ def test_mxfp4_quantize_entry_point_checks_arguments():
     assert lib.moe_quantize_mxfp4_rows(None, 4, 64, q, s, None) == -1
     assert lib.moe_quantize_mxfp4_rows(vp(base + 8), 4, 64, q, s, None) == -4
     assert lib.moe_quantize_mxfp4_rows(w, 4, 64, vp(base + 64), s, None) == -1  # q overlaps w
+
+
+def test_rejects_shared_expert_past_32_bit_offsets():
+    # 2 * shared_I * H = 2^31 elements: the shared expert's offsets would overflow
+    with pytest.raises(moe.MoeError) as ei:
+        moe.workspace_bytes(4, 4096, 64, 4, 2, shared_I=1 << 18)
+    assert ei.value.status == -2 and "shared expert" in str(ei.value)
+    assert moe.workspace_bytes(4, 4096, 64, 4, 2, shared_I=(1 << 18) - 8) > 0
