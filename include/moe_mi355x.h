@@ -188,8 +188,10 @@ typedef struct moe_opts {
     /* MOE_WEIGHTS_MXFP4: gate_up holds [E, 2I, H/2] bytes and down [E, H, I/2]
      * (codes of elements 2i and 2i+1 in the low and high nibble of byte i),
      * with E8M0 block scales gate_up_block_scale [E, 2I, H/32] and
-     * down_block_scale [E, H, I/32]; H and I multiples of 32; weight-streaming
-     * kernels only (MOE_FLAG_FORCE_TILED is rejected). */
+     * down_block_scale [E, H, I/32] (byte arrays, any alignment; rows of
+     * scales that start 4-byte aligned, K % 128 == 0 and a 4-byte aligned
+     * array, are read 16 bytes at a time); H and I multiples of 32;
+     * weight-streaming kernels only (MOE_FLAG_FORCE_TILED is rejected). */
     const uint8_t *gate_up_block_scale;
     const uint8_t *down_block_scale;
 } moe_opts;

@@ -527,7 +527,10 @@ template <bool GATEUP>
 hipError_t launch_skinny(const GemmProblem &g, hipStream_t st)
 {
     const SkinnyParams s = make_params(g);
-    const int fmt = g.w_bscale ? ((g.K / 32) % 4 == 0 ? 3 : 2) : g.w_scale ? 1 : 0;
+    // MXFP4 with 16-byte scale loads when every row of scales starts 4-byte
+    // aligned: K / 32 a multiple of 4 and an aligned scale array
+    const bool sc4 = g.w_bscale && (g.K / 32) % 4 == 0 && (uintptr_t)g.w_bscale % 4 == 0;
+    const int fmt = g.w_bscale ? (sc4 ? 3 : 2) : g.w_scale ? 1 : 0;
     const int cols = skinny_cols(GATEUP, fmt);
     const dim3 grid((unsigned)((g.N + cols - 1) / cols), g.dense_rows > 0 ? 1u : (unsigned)g.E);
     switch (fmt) {

@@ -160,3 +160,22 @@ def test_mxfp4_layer_run_to_run_identical():
     a, _ = run_mxfp4(inp, gq, gs, dq, ds)
     b, _ = run_mxfp4(inp, gq, gs, dq, ds)
     assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+def test_mxfp4_unaligned_scale_arrays():
+    # block scales that start at an odd byte address take the byte-wise scale
+    # loads; the result is the same bit for bit
+    _say("case mxfp4 unaligned scale arrays")
+    inp = W.custom_inputs(T=24, H=512, I=256, E=4, k=2)
+    gq, gs = moe.quantize_mxfp4_rows(dev(inp.gate_up))
+    dq, ds = moe.quantize_mxfp4_rows(dev(inp.down))
+    a, _ = run_mxfp4(inp, gq, gs, dq, ds)
+    gs_buf = torch.empty(gs.numel() + 1, dtype=torch.uint8, device=gs.device)
+    ds_buf = torch.empty(ds.numel() + 1, dtype=torch.uint8, device=ds.device)
+    gs_odd = gs_buf[1:].view(gs.shape)
+    ds_odd = ds_buf[1:].view(ds.shape)
+    gs_odd.copy_(gs)
+    ds_odd.copy_(ds)
+    assert gs_odd.data_ptr() % 4 == 1 and ds_odd.data_ptr() % 4 == 1
+    b, _ = run_mxfp4(inp, gq, gs_odd, dq, ds_odd)
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
