@@ -418,6 +418,8 @@ def main(argv=None):
                     help="expert weight storage of the main workload (fp8 / mxfp4: decode-shaped work only)")
     ap.add_argument("--fp8", action="store_true", help="same as --weights fp8")
     ap.add_argument("--cpu-tokens", type=int, default=32)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="whole oracle passes over the CPU sample until this many seconds have passed")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a 1 GiB device copy (counter calibration under rocprofv3)")
     ap.add_argument("--write-traffic", nargs=7, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR",
@@ -469,7 +471,7 @@ def main(argv=None):
         "layer": lay,
     }
     if not args.no_cpu:
-        line["cpu_baseline"] = cpu_baseline(res, args.cpu_tokens)
+        line["cpu_baseline"] = cpu_baseline(res, args.cpu_tokens, args.cpu_seconds)
     for fmt, skip in (("fp8", args.no_fp8), ("mxfp4", args.no_mxfp4)):
         if skip or args.weights != "bf16" or args.workload != "phimoe_decode":
             continue

@@ -77,6 +77,9 @@ constexpr int KB = 128;  // reduction elements per step: 256 bytes of each row
 #ifndef MOE_SKINNY_WAVES_W4
 #define MOE_SKINNY_WAVES_W4 2
 #endif
+#ifndef MOE_SKINNY_WAVES_DN
+#define MOE_SKINNY_WAVES_DN MOE_SKINNY_WAVES
+#endif
 #ifndef MOE_SKINNY_WAVES_W4_DN
 #define MOE_SKINNY_WAVES_W4_DN MOE_SKINNY_WAVES_W4
 #endif
@@ -84,7 +87,7 @@ constexpr int KB = 128;  // reduction elements per step: 256 bytes of each row
 constexpr int skinny_waves(bool gateup, int fmt)
 {
     return fmt >= 2 ? (gateup ? MOE_SKINNY_WAVES_W4 : MOE_SKINNY_WAVES_W4_DN)
-                    : fmt == 1 ? MOE_SKINNY_WAVES_W8 : MOE_SKINNY_WAVES;
+                    : fmt == 1 ? MOE_SKINNY_WAVES_W8 : (gateup ? MOE_SKINNY_WAVES : MOE_SKINNY_WAVES_DN);
 }
 
 // 16-row MFMA blocks per workgroup. gate_up: half of them gate rows, half the
