@@ -139,6 +139,7 @@ SMALL = [
     ("single_expert_bf16", dict(T=40, H=64, I=48, E=1, k=1)),
     ("k_equals_E_bf16", dict(T=50, H=64, I=32, E=5, k=5)),
     ("one_token_bf16", dict(T=1, H=4096, I=256, E=16, k=2)),
+    ("max_experts_bf16", dict(T=300, H=128, I=64, E=256, k=8)),   # the largest E the ABI takes
     ("f32_small", dict(T=77, H=96, I=40, E=5, k=2, dtype="f32", n_shared=1, shared_I=24)),
 ]
 
@@ -155,6 +156,16 @@ def test_small_full_parity(name, kw, flags):
     rel = check_out(out, r_out, name)
     if inp.wl.dtype == "f32":
         assert rel < 1e-4
+
+
+def test_zero_tokens_is_a_no_op():
+    _say("case T = 0")
+    inp = W.custom_inputs(T=8, H=64, I=32, E=4, k=2)
+    d = lambda a: moe.bf16_bits_to_tensor(a)  # noqa: E731
+    hidden = d(inp.hidden)[:0]
+    out, r = moe.moe_forward(hidden, d(inp.router_w), d(inp.gate_up), d(inp.down), 2, return_routing=True)
+    torch.cuda.synchronize()
+    assert out.shape == (0, 64) and r["ids"].shape == (0, 2) and r["perm"].numel() == 0
 
 
 def test_tiny_workload_full_parity():
