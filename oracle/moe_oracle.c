@@ -286,7 +286,10 @@ int oracle_moe_tokens(const void *X, const void *gate_up, const void *down, int 
  *   P[e] = (1/n) sum_t softmax(logits[t, :])[e]   (all E experts),
  *   f[e] = (1/n) #{(t, j) : ids[t, j] = e}        (the top-k assignments),
  *   aux  = E * sum_e f[e] * P[e];
- * everything zero when n = 0. Evaluated in fp64.
+ * everything zero when n = 0. Evaluated in fp64. Against the pages this is
+ * partly unpinned (they print no equation); the tests pin it to the loss's
+ * closed forms (uniform logits, certain and balanced routing) and to a
+ * separate numpy evaluation.
  */
 int oracle_router_stats(const float *logits, const int32_t *ids, const int32_t *mask, int64_t T, int64_t E,
                         int k, double *prob_mean, double *load, double *aux)
@@ -532,6 +535,10 @@ int oracle_num_threads(void)
  * Horner form with fused multiply-adds, then 1 / (1 + exp(-c)); the key and
  * the group sums (best key first, from 0) are fp32 additions. Weights are
  * evaluated in fp64 from the fp32 scores.
+ * Parity unpinned against the pages, which name the rule without defining
+ * it; the tests pin these functions to the mathematics (exp and sigmoid
+ * against fp64, symmetry, the clamp) and to the published rule's
+ * consequences (bias that only moves selection, groups, ties).
  */
 static float exp_by_reduction(float x)
 {
@@ -677,6 +684,10 @@ int oracle_select_scored(const float *logits, int64_t T, int64_t E, int k, float
  * page's two. The gap test decides membership, so it is taken in fp32 (a
  * 0/0 gap is NaN, which is not above the threshold: the expert stays); the
  * softmax is evaluated in fp64.
+ * The membership rule is the published one, not the page's: parity of that
+ * detail is unpinned against the pages; the tests pin the page's threshold
+ * value, the greedy ids, and the limits (well separated logits, an unbounded
+ * threshold giving the textbook softmax).
  */
 int oracle_select_sparsemixer(const float *logits, int64_t T, int64_t E, int k, float routed_scale,
                               float jitter_eps, int32_t *ids, float *weights)
