@@ -41,6 +41,12 @@ namespace moe {
 namespace {
 
 constexpr int KB = 128;  // reduction elements per step: 256 bytes of each row
+// Compile-time shape knobs of the streaming kernels, per GEMM and weight
+// storage (bf16 / E4M3 "W8" / MXFP4 "W4"); the defaults are the fastest
+// measured on MI355X for the decode shapes:
+//   MOE_SKINNY_WAVES*     waves per workgroup, each taking a contiguous K range
+//   MOE_SKINNY_PD_*       weight steps in flight per wave (staging registers)
+//   MOE_SKINNY_*BLOCKS*   16-row blocks per workgroup (gate_up: half gate, half up)
 #ifndef MOE_SKINNY_WAVES
 #define MOE_SKINNY_WAVES 4
 #endif
