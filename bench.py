@@ -40,7 +40,7 @@ HBM_PEAK_GBPS = 8000.0         # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 FP32_PEAK_TFLOPS = 157.3       # MI355X fp32 vector
 METRIC = "MoE layer tokens/sec + % of bf16 MFMA peak (prefill) / % HBM BW (decode)"
-KERNEL_SOURCES = {"gate_up": ("gemm_skinny.hip", "gemm_tiled.hip"), "down": ("gemm_skinny.hip", "gemm_tiled.hip")}
+KERNEL_SOURCES = {k: ("gemm_skinny.hip", "gemm_tiled.hip", "moe_internal.h") for k in ("gate_up", "down")}
 
 
 def decode_tokens_per_s_bound(bandwidth_Bps: float, bytes_per_token: float) -> float:
@@ -95,10 +95,16 @@ def work(wl, counts, weights="bf16"):
 
 
 def source_hash(names):
+    """Hash of the kernels' code (comments and spacing removed), so that stored
+    counter figures are dropped when the code changes, not when a comment does."""
+    import re
     h = hashlib.sha256()
     for n in sorted(set(names)):
-        with open(os.path.join(ROOT, "sparse_mixture_experts_logits_amd", "csrc", n), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "sparse_mixture_experts_logits_amd", "csrc", n)) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

@@ -42,3 +42,15 @@ def test_cpu_baseline_repeats_whole_passes():
     b = bench.cpu_baseline(res, 64, min_seconds=0.3)
     assert b["kind"] == "oracle" and b["unit"] == "tokens/s" and b["value"] > 0 and b["cores"] >= 1
     assert "passes" in b["sample"] and b["sample"].startswith(f"all {wl.T} tokens of tiny_f32")
+
+
+def test_source_hash_ignores_comments_only(tmp_path, monkeypatch):
+    src = tmp_path / "sparse_mixture_experts_logits_amd" / "csrc"
+    src.mkdir(parents=True)
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    (src / "k.hip").write_text("int f() { return 1; }  // one\n/* block */\n")
+    a = bench.source_hash(["k.hip"])
+    (src / "k.hip").write_text("// another comment\nint f()  {\n  return 1;\n}\n")
+    assert bench.source_hash(["k.hip"]) == a
+    (src / "k.hip").write_text("int f() { return 2; }\n")
+    assert bench.source_hash(["k.hip"]) != a
