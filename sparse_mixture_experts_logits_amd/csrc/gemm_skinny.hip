@@ -16,7 +16,7 @@
 //     is in LDS, the token fragments after the MFMAs that use the current
 //     ones, so the bytes in flight per wave stay constant.
 //   * A workgroup owns 32 weight rows (gate_up: 16 gate + the matching 16 up
-//     rows; MXFP4 gate_up: 32 + 32; down: 32 consecutive rows) and splits K
+//     rows; down: 32 consecutive rows; MXFP4: 32 + 32 and 64) and splits K
 //     over its waves; partial sums meet in LDS in wave order, so the result
 //     does not depend on timing.
 //   * Experts with no tokens exit before reading anything, so only the
