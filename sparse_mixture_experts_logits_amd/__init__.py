@@ -328,10 +328,14 @@ def moe_forward(hidden, router_w, gate_up, down, k: int, *, routed_scale: float 
     need = lib.moe_workspace_bytes(T, H, I, E, k, ctypes.byref(o))
     if need < 0:
         raise MoeError(int(need), last_error())
-    if workspace is None or workspace.numel() < need:
+    if workspace is None:
         workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
+    elif workspace.numel() * workspace.element_size() < need or not workspace.is_cuda:
+        # a caller that passes a workspace relies on the call allocating nothing
+        raise ValueError(f"workspace holds {workspace.numel() * workspace.element_size()} bytes; "
+                         f"{need} are needed (workspace_bytes with the same flags and dtype)")
     o.workspace = workspace.data_ptr()
-    o.workspace_bytes = workspace.numel()
+    o.workspace_bytes = workspace.numel() * workspace.element_size()
     current = torch.cuda.current_stream(dev)
     if stream is None:
         stream = current

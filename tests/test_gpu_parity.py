@@ -168,6 +168,21 @@ def test_zero_tokens_is_a_no_op():
     assert out.shape == (0, 64) and r["ids"].shape == (0, 2) and r["perm"].numel() == 0
 
 
+def test_caller_workspace_too_small_is_an_error():
+    # a caller-provided workspace means "allocate nothing": too small is an error, not a fallback
+    _say("case workspace too small")
+    inp = W.custom_inputs(T=8, H=64, I=32, E=4, k=2)
+    d = lambda a: moe.bf16_bits_to_tensor(a)  # noqa: E731
+    need = moe.workspace_bytes(8, 64, 32, 4, 2)
+    ws = torch.empty((need - 256,), dtype=torch.uint8, device="cuda")
+    with pytest.raises(ValueError, match="workspace"):
+        moe.moe_forward(d(inp.hidden), d(inp.router_w), d(inp.gate_up), d(inp.down), 2, workspace=ws)
+    ws = torch.empty((need,), dtype=torch.uint8, device="cuda")
+    out = moe.moe_forward(d(inp.hidden), d(inp.router_w), d(inp.gate_up), d(inp.down), 2, workspace=ws)
+    torch.cuda.synchronize()
+    assert out.shape == (8, 64)
+
+
 def test_tiny_workload_full_parity():
     inp = host_inputs("tiny_f32")
     ref = oracle_routing(inp)
