@@ -237,8 +237,8 @@ def moe_forward(hidden, router_w, gate_up, down, k: int, *, routed_scale: float 
     if lowp and not w4:
         if down.dtype != torch.uint8 or gate_up_scale is None or down_scale is None:
             raise ValueError("FP8 weights need uint8 gate_up and down plus gate_up_scale and down_scale")
-        gate_up_scale = gate_up_scale.to(dtype=torch.float32).contiguous()
-        down_scale = down_scale.to(dtype=torch.float32).contiguous()
+        gate_up_scale = gate_up_scale.to(device=hidden.device, dtype=torch.float32).contiguous()
+        down_scale = down_scale.to(device=hidden.device, dtype=torch.float32).contiguous()
         if gate_up_scale.shape != (E, 2 * I) or down_scale.shape != (E, H):
             raise ValueError("gate_up_scale must be [E, 2I] and down_scale [E, H]")
         o.weight_format = WEIGHTS_FP8_E4M3
@@ -247,8 +247,8 @@ def moe_forward(hidden, router_w, gate_up, down, k: int, *, routed_scale: float 
     if w4:
         if down.dtype != torch.uint8 or down_block_scale is None:
             raise ValueError("MXFP4 weights need uint8 gate_up and down plus both block scales")
-        gate_up_block_scale = gate_up_block_scale.to(dtype=torch.uint8).contiguous()
-        down_block_scale = down_block_scale.to(dtype=torch.uint8).contiguous()
+        gate_up_block_scale = gate_up_block_scale.to(device=hidden.device, dtype=torch.uint8).contiguous()
+        down_block_scale = down_block_scale.to(device=hidden.device, dtype=torch.uint8).contiguous()
         if gate_up_block_scale.shape != (E, 2 * I, H // 32) or down_block_scale.shape != (E, H, I // 32):
             raise ValueError("block scales must be [E, 2I, H/32] and [E, H, I/32]")
         o.weight_format = WEIGHTS_MXFP4
@@ -282,7 +282,9 @@ def moe_forward(hidden, router_w, gate_up, down, k: int, *, routed_scale: float 
     if jitter_eps is not None:
         o.jitter_eps = float(jitter_eps)
     if router_bias is not None:
-        router_bias = router_bias.to(dtype=torch.float32).contiguous()
+        router_bias = router_bias.to(device=hidden.device, dtype=torch.float32).contiguous()
+        if router_bias.shape != (E,):
+            raise ValueError("router_bias must be [E]")
         o.router_bias = router_bias.data_ptr()
     if shared_gate_up is not None:
         Is = shared_gate_up.shape[0] // 2
@@ -294,6 +296,8 @@ def moe_forward(hidden, router_w, gate_up, down, k: int, *, routed_scale: float 
     dev = hidden.device
     if out is None:
         out = torch.empty((T, H), dtype=hidden.dtype, device=dev)
+    elif out.shape != (T, H) or out.dtype != hidden.dtype or not out.is_contiguous() or not out.is_cuda:
+        raise ValueError("out must be a contiguous CUDA tensor of hidden's dtype and shape [T, H]")
     routing = None
     return_routing = return_routing or router_stats
     if return_routing:

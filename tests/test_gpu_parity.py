@@ -183,6 +183,25 @@ def test_caller_workspace_too_small_is_an_error():
     assert out.shape == (8, 64)
 
 
+def test_binding_rejects_bad_out_and_bias():
+    _say("case binding argument checks")
+    inp = W.custom_inputs(T=8, H=64, I=32, E=4, k=2)
+    d = lambda a: moe.bf16_bits_to_tensor(a)  # noqa: E731
+    args = (d(inp.hidden), d(inp.router_w), d(inp.gate_up), d(inp.down), 2)
+    with pytest.raises(ValueError, match="out"):
+        moe.moe_forward(*args, out=torch.empty((8, 32), dtype=torch.bfloat16, device="cuda"))
+    with pytest.raises(ValueError, match="out"):
+        moe.moe_forward(*args, out=torch.empty((8, 64), dtype=torch.float32, device="cuda"))
+    with pytest.raises(ValueError, match="router_bias"):
+        moe.moe_forward(*args, router_bias=torch.zeros(3))
+    # a host bias is moved to the device and gives the same result as a device one
+    b = torch.tensor([0.5, -0.5, 0.0, 1.0])
+    a1 = moe.moe_forward(*args, router_bias=b)
+    a2 = moe.moe_forward(*args, router_bias=b.cuda())
+    torch.cuda.synchronize()
+    assert torch.equal(a1, a2)
+
+
 def test_tiny_workload_full_parity():
     inp = host_inputs("tiny_f32")
     ref = oracle_routing(inp)
