@@ -33,12 +33,12 @@ bool overlaps(const void *a, uint64_t na, const void *b, uint64_t nb)
 
 bool debug_sync()
 {
-    static int v = -1;
-    if (v < 0) {
+    // read once; a function-local static is initialised thread-safely
+    static const bool v = [] {
         const char *s = getenv("MOE_DEBUG_SYNC");
-        v = (s && s[0] == '1') ? 1 : 0;
-    }
-    return v == 1;
+        return s && s[0] == '1';
+    }();
+    return v;
 }
 
 constexpr int64_t kAlign = 256;
