@@ -179,3 +179,38 @@ def test_mxfp4_unaligned_scale_arrays():
     assert gs_odd.data_ptr() % 4 == 1 and ds_odd.data_ptr() % 4 == 1
     b, _ = run_mxfp4(inp, gq, gs_odd, dq, ds_odd)
     assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+@pytest.mark.parametrize("score", ["sigmoid_groups", "sparsemixer"])
+def test_mxfp4_with_scoring_variants_shared_expert_and_direct_routing(score):
+    # the options meet: MXFP4 routed weights, a router variant, a shared
+    # expert (bf16) and the launch without routing outputs (direct routing)
+    _say(f"case mxfp4 + {score} + shared expert")
+    inp = W.custom_inputs(T=24, H=256, I=128, E=32, k=4, routed_scale=2.5, n_shared=1, shared_I=64)
+    wl = inp.wl
+    gq, gs = moe.quantize_mxfp4_rows(dev(inp.gate_up))
+    dq, ds = moe.quantize_mxfp4_rows(dev(inp.down))
+    rgq, rgs = oracle.quantize_mxfp4_rows(inp.gate_up)
+    rdq, rds = oracle.quantize_mxfp4_rows(inp.down)
+    g, d = inp.shared_concat()
+    kw = dict(routed_scale=wl.routed_scale, shared_gate_up=dev(g), shared_down=dev(d),
+              gate_up_block_scale=gs, down_block_scale=ds)
+    logits = oracle.router_logits(inp.hidden, inp.router_w, inp.bias)
+    if score == "sparsemixer":
+        kw.update(score_func="sparsemixer", jitter_eps=0.05)
+        ids, w = oracle.select_sparsemixer(logits, wl.k, wl.routed_scale, 0.05)
+    else:
+        bias = (np.random.default_rng(9).standard_normal(wl.E) * 0.02).astype(np.float32)
+        kw.update(score_func="sigmoid", selection_bias=torch.from_numpy(bias).cuda(), n_group=8, topk_group=3)
+        ids, w = oracle.select_scored(logits, wl.k, wl.routed_scale, "sigmoid", bias, 8, 3)
+    out_r, r = moe.moe_forward(dev(inp.hidden), dev(inp.router_w), gq, dq, wl.k, return_routing=True, **kw)
+    out_d = moe.moe_forward(dev(inp.hidden), dev(inp.router_w), gq, dq, wl.k, **kw)
+    torch.cuda.synchronize()
+    assert np.array_equal(r["ids"].cpu().numpy(), ids)
+    a, b = out_r.float().cpu().numpy(), out_d.float().cpu().numpy()
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), "direct routing differs"
+    ref = oracle.moe_tokens(inp.hidden, oracle.dequantize_mxfp4_rows(rgq, rgs), oracle.dequantize_mxfp4_rows(rdq, rds),
+                            ids, w, tokens=np.arange(wl.T, dtype=np.int32), shared=[(g, d)])
+    err, scale = np.max(np.abs(b - ref)), np.max(np.abs(ref))
+    _say(f"  max|err|/max|ref| = {err / scale:.3e}")
+    assert np.all(np.isfinite(b)) and err <= OUT_TOL * scale
