@@ -162,3 +162,29 @@ def test_fp8_layer_run_to_run_identical():
     a, _ = run_fp8(inp, gq, gs, dq, ds)
     b, _ = run_fp8(inp, gq, gs, dq, ds)
     assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+def test_fp8_with_sigmoid_groups_shared_expert_and_direct_routing():
+    _say("case fp8 + sigmoid groups + shared expert")
+    inp = W.custom_inputs(T=24, H=256, I=128, E=32, k=4, routed_scale=2.5, n_shared=1, shared_I=64)
+    wl = inp.wl
+    gq, gs, rgq, rgs = check_quant(inp.gate_up, "gate_up")
+    dq, ds, rdq, rds = check_quant(inp.down, "down")
+    g, d = inp.shared_concat()
+    bias = (np.random.default_rng(11).standard_normal(wl.E) * 0.02).astype(np.float32)
+    kw = dict(routed_scale=wl.routed_scale, shared_gate_up=dev(g), shared_down=dev(d), gate_up_scale=gs,
+              down_scale=ds, score_func="sigmoid", selection_bias=torch.from_numpy(bias).cuda(), n_group=8,
+              topk_group=3)
+    out_r, r = moe.moe_forward(dev(inp.hidden), dev(inp.router_w), gq, dq, wl.k, return_routing=True, **kw)
+    out_d = moe.moe_forward(dev(inp.hidden), dev(inp.router_w), gq, dq, wl.k, **kw)
+    torch.cuda.synchronize()
+    logits = oracle.router_logits(inp.hidden, inp.router_w, inp.bias)
+    ids, w = oracle.select_scored(logits, wl.k, wl.routed_scale, "sigmoid", bias, 8, 3)
+    assert np.array_equal(r["ids"].cpu().numpy(), ids)
+    a, b = out_r.float().cpu().numpy(), out_d.float().cpu().numpy()
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), "direct routing differs"
+    ref = oracle.moe_tokens_e4m3(inp.hidden, rgq, rgs, rdq, rds, ids, w, tokens=np.arange(wl.T, dtype=np.int32),
+                                 shared=[(g, d)])
+    err, scale = np.max(np.abs(b - ref)), np.max(np.abs(ref))
+    _say(f"  max|err|/max|ref| = {err / scale:.3e}")
+    assert np.all(np.isfinite(b)) and err <= OUT_TOL * scale

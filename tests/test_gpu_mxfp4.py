@@ -136,6 +136,7 @@ SMALL = [
     ("shared_bias", dict(T=70, H=128, I=64, E=16, k=2, n_shared=2, shared_I=32,
                          bias=((0, 6.0), (13, -30.0), (14, -30.0), (15, -30.0)))),
     ("one_token", dict(T=1, H=4096, I=256, E=16, k=2)),
+    ("max_experts", dict(T=40, H=128, I=64, E=256, k=8)),          # the largest E the ABI takes
 ]
 
 
