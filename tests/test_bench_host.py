@@ -54,3 +54,40 @@ def test_source_hash_ignores_comments_only(tmp_path, monkeypatch):
     assert bench.source_hash(["k.hip"]) == a
     (src / "k.hip").write_text("int f() { return 2; }\n")
     assert bench.source_hash(["k.hip"]) != a
+
+
+def _pmc(dirpath, rows):
+    import csv
+    dirpath.mkdir(parents=True)
+    with open(dirpath / "pmc_counter_collection.csv", "w", newline="") as fh:
+        w = csv.DictWriter(fh, fieldnames=["Kernel_Name", "Counter_Name", "Counter_Value"])
+        w.writeheader()
+        for name, counter, value in rows:
+            w.writerow({"Kernel_Name": name, "Counter_Name": counter, "Counter_Value": value})
+
+
+def test_write_traffic_scales_counters_by_the_copy_calibration(tmp_path, monkeypatch):
+    # the kernel's FETCH_SIZE / WRITE_SIZE (KiB per dispatch) scaled by what the
+    # same counters read for a copy of known size; other kernels are ignored
+    (tmp_path / "profiles").mkdir()
+    src = tmp_path / "sparse_mixture_experts_logits_amd" / "csrc"
+    src.mkdir(parents=True)
+    for n in ("gemm_skinny.hip", "gemm_tiled.hip", "moe_internal.h"):
+        (src / n).write_text("int x;\n")
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    k = "void skinny_gemm_kernel<true, 0, true>(p)"
+    _pmc(tmp_path / "f", [(k, "FETCH_SIZE", 1000.0), (k, "FETCH_SIZE", 1200.0), ("other", "FETCH_SIZE", 9e9)])
+    _pmc(tmp_path / "w", [(k, "WRITE_SIZE", 10.0), (k, "WRITE_SIZE", 30.0)])
+    copy = 1 << 20
+    _pmc(tmp_path / "cf", [("copy", "FETCH_SIZE", copy / 1024 / 2), ("small", "FETCH_SIZE", 1.0)])
+    _pmc(tmp_path / "cw", [("copy", "WRITE_SIZE", copy / 1024)])
+    bench.write_traffic(str(tmp_path / "f"), str(tmp_path / "w"), str(tmp_path / "cf"), str(tmp_path / "cw"),
+                        "gate_up", "unit", r"skinny_gemm_kernel<true, 0, true>", copy, "cmd")
+    import json
+    d = json.load(open(tmp_path / "profiles" / "gate_up_unit_traffic.json"))
+    assert d["launches"] == [2, 2]
+    assert d["copy_calibration"]["fetch_factor"] == 2.0 and d["copy_calibration"]["write_factor"] == 1.0
+    assert d["hbm_bytes_per_launch"] == 1100.0 * 1024 * 2 + 20.0 * 1024
+    assert bench.measured_traffic("gate_up", "unit") == d["hbm_bytes_per_launch"]
+    (src / "gemm_skinny.hip").write_text("int y;\n")  # the code changed: the figure no longer applies
+    assert bench.measured_traffic("gate_up", "unit") is None
