@@ -91,3 +91,25 @@ def test_write_traffic_scales_counters_by_the_copy_calibration(tmp_path, monkeyp
     assert bench.measured_traffic("gate_up", "unit") == d["hbm_bytes_per_launch"]
     (src / "gemm_skinny.hip").write_text("int y;\n")  # the code changed: the figure no longer applies
     assert bench.measured_traffic("gate_up", "unit") is None
+
+
+def test_roofline_of_decode_and_prefill():
+    dec = W.BY_NAME["phimoe_decode"]
+    res = dict(wl=dec, counts=[4] * dec.E, weights="bf16", dominant="gate_up",
+               stages={"gate_up": 0.25, "down": 0.13})
+    r, w = bench.roofline_of(res)
+    assert r["bound"] == "hbm" and r["unit"] == "GB/s" and r["kernel"] == "gate_up" and r["peak"] == 8000.0
+    expect = w["bytes_gate_up"] / 0.25e-3 / 1e9
+    assert abs(r["achieved"] - round(expect, 1)) < 1e-6 and abs(r["frac"] - expect / 8000.0) < 1e-4
+    assert w["bytes_gate_up"] > 16 * 2 * dec.I * dec.H * 2  # every expert's weights once, plus activations
+    pre = W.BY_NAME["phimoe_prefill"]
+    res = dict(wl=pre, counts=[512] * pre.E, weights="bf16", dominant="gate_up",
+               stages={"gate_up": 0.9, "down": 0.47})
+    r, w = bench.roofline_of(res)
+    assert r["bound"] == "mfma" and r["kernel"] == "gate_up" and r["peak"] == 2500.0
+    assert abs(r["achieved"] - round(2.0 * pre.T * pre.k * 2 * pre.I * pre.H / 0.9e-3 / 1e12, 1)) < 1e-6
+    # a dominant stage that is not an expert GEMM falls back to the slower of the two
+    res.update(dominant="router", stages={"router": 2.0, "gate_up": 0.4, "down": 0.47})
+    r, _ = bench.roofline_of(res)
+    assert r["kernel"] == "down"
+    assert abs(r["achieved"] - round(2.0 * pre.T * pre.k * pre.H * pre.I / 0.47e-3 / 1e12, 1)) < 1e-6
