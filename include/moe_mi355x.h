@@ -233,6 +233,11 @@ int64_t moe_workspace_bytes(int64_t T, int64_t H, int64_t I, int64_t E, int32_t 
  * down     [E, H, I]    down projection (nn.Linear layout [out, in])
  * out      [T, H]       written in full; must not overlap any input
  *
+ * The workspace must not overlap any input; out, the workspace and the
+ * optional outputs must not overlap each other (MOE_ERR_INVALID_ARG).
+ * The number of compute units of the current device is queried on every
+ * call (it sizes the persistent launches); nothing is cached between calls.
+ *
  * Sizes: T >= 0 (T = 0 is a successful no-op), 1 <= k <= E <= 256, H, I >= 8
  * and multiples of 8, T*k < 2^31; one expert (2*I*H, 2*shared_I*H) and one
  * activation tensor (T*H, T*k*I, T*shared_I) below 2^31 elements, H, I and

@@ -681,16 +681,12 @@ __global__ __launch_bounds__(64) void tiled_split_finish_kernel(TiledParams p)
     }
 }
 
-// Persistent grid: OCC workgroups per CU, rounded to whole XCD rounds.
-int persistent_grid(int occ)
+// Persistent grid: OCC workgroups per CU, rounded to whole XCD rounds. The
+// caller queries the CU count of the current device on every call, so the
+// library keeps no cached device state.
+int persistent_grid(int cus, int occ)
 {
-    static int cus = 0;
-    if (!cus) {
-        int dev = 0;
-        if (hipGetDevice(&dev) != hipSuccess ||
-            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-            cus = 256;
-    }
+    if (cus <= 0) cus = 256;
     return ((cus + 7) / 8) * 8 * occ;
 }
 
@@ -722,7 +718,7 @@ hipError_t launch_cfg(const GemmProblem &g, hipStream_t st)
 {
     const int cols = GATEUP ? BN / 2 : BN;  // output columns per N-block
     TiledParams t = make_params(g, (int)((g.N + cols - 1) / cols));
-    t.G = persistent_grid(OCC);
+    t.G = persistent_grid(g.cus, OCC);
     // pieces of this tile shape that fit the buffer (sized for kSplitPieces
     // routed 256x256 pieces), at most one round of the launch
     constexpr int64_t piece_bytes = (int64_t)WM * WN * ((BM / WM / 32) * (BN / WN / 32) + (XT > 0 ? 1 : 0)) * 1024 * 4;

@@ -277,6 +277,30 @@ int moe_forward(const void *hidden, const void *router_w, const void *gate_up, c
                {opts->workspace, opts->workspace_bytes}};
     for (const Range &r : ins)
         if (overlaps(out, out_bytes, r.p, r.n)) return fail(MOE_ERR_INVALID_ARG, "out overlaps an input or the workspace");
+    // the workspace is written by every call: it must not overlap an input
+    const size_t nins = sizeof ins / sizeof ins[0];  // the last entry is the workspace itself
+    for (size_t i = 0; i + 1 < nins; i++)
+        if (overlaps(opts->workspace, opts->workspace_bytes, ins[i].p, ins[i].n))
+            return fail(MOE_ERR_INVALID_ARG, "the workspace overlaps an input");
+    // optional outputs: none may overlap an input, the workspace, out or another output
+    const uint64_t TK = (uint64_t)T * k;
+    const Range outs[] = {{opts->router_logits, (uint64_t)T * E * 4}, {opts->topk_ids, TK * 4},
+                          {opts->topk_weights, TK * 4},           {opts->expert_counts, (uint64_t)E * 4},
+                          {opts->expert_offsets, (uint64_t)(E + 1) * 4}, {opts->perm, TK * 4},
+                          {opts->inv_perm, TK * 4},               {opts->router_prob_mean, (uint64_t)E * 4},
+                          {opts->expert_load, (uint64_t)E * 4},   {opts->aux_loss, 4}};
+    const size_t nouts = sizeof outs / sizeof outs[0];
+    for (size_t i = 0; i < nouts; i++) {
+        if (!outs[i].p) continue;
+        if (overlaps(outs[i].p, outs[i].n, out, out_bytes))
+            return fail(MOE_ERR_INVALID_ARG, "an optional output overlaps out");
+        for (const Range &r : ins)
+            if (overlaps(outs[i].p, outs[i].n, r.p, r.n))
+                return fail(MOE_ERR_INVALID_ARG, "an optional output overlaps an input or the workspace");
+        for (size_t j = 0; j < i; j++)
+            if (overlaps(outs[i].p, outs[i].n, outs[j].p, outs[j].n))
+                return fail(MOE_ERR_INVALID_ARG, "two optional outputs overlap");
+    }
 
     const moe::Shape s = make_shape(T, H, I, E, k, opts);
     const int64_t need = moe::workspace_layout(s, nullptr, nullptr);
@@ -288,6 +312,12 @@ int moe_forward(const void *hidden, const void *router_w, const void *gate_up, c
     moe::Workspace ws;
     moe::workspace_layout(s, opts->workspace, &ws);
     hipStream_t st = (hipStream_t)opts->stream;
+    // compute units of the current device, queried on every call (sizes the
+    // persistent launches; nothing is cached between calls)
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+        return fail(MOE_ERR_HIP, "cannot query the compute units of the current device");
 
     const bool f32 = opts->dtype == MOE_F32;
     const bool skinny = use_skinny(T, k, E, opts);
@@ -365,6 +395,7 @@ int moe_forward(const void *hidden, const void *router_w, const void *gate_up, c
     gu.ids = direct ? ws.ids : nullptr;
     gu.wts = direct ? ws.wts : nullptr;
     gu.k = k;
+    gu.cus = cus;
 
     moe::GemmProblem dn = gu;
     dn.A = ws.h;

@@ -156,6 +156,7 @@ struct GemmProblem {
     const int32_t *ids = nullptr;
     const float *wts = nullptr;
     int k = 0;
+    int cus = 0;             // compute units of the device (persistent grids)
 };
 
 // Largest T*k for which the weight-streaming kernels route directly from the ids.

@@ -310,3 +310,77 @@ def test_rejects_shared_expert_past_32_bit_offsets():
         moe.workspace_bytes(4, 4096, 64, 4, 2, shared_I=1 << 18)
     assert ei.value.status == -2 and "shared expert" in str(ei.value)
     assert moe.workspace_bytes(4, 4096, 64, 4, 2, shared_I=(1 << 18) - 8) > 0
+
+
+def test_rejects_workspace_overlapping_an_input():
+    base = 1 << 40
+    o = good_opts()
+    o.workspace = base + (3 << 30)  # on top of down
+    rc, msg = call(opts=o)
+    assert rc == -1 and "workspace overlaps" in msg
+
+
+def test_rejects_optional_outputs_overlapping_inputs_workspace_out_or_each_other():
+    base = 1 << 40
+    o = good_opts(nbytes=100)
+    o.topk_ids = base + (8 << 30) + 32  # inside the workspace
+    rc, msg = call(opts=o)
+    assert rc == -1 and "optional output" in msg
+    o = good_opts(nbytes=100)
+    o.perm = base + 256  # inside hidden
+    rc, msg = call(opts=o)
+    assert rc == -1 and "optional output" in msg
+    o = good_opts(nbytes=100)
+    o.router_logits = base + (4 << 30) + 64  # inside out
+    rc, msg = call(opts=o)
+    assert rc == -1 and "overlaps out" in msg
+    o = good_opts(nbytes=100)
+    o.expert_counts = base + (9 << 30)
+    o.expert_offsets = base + (9 << 30) + 8  # E = 4: counts span 16 bytes
+    rc, msg = call(opts=o)
+    assert rc == -1 and "two optional outputs" in msg
+    o = good_opts(nbytes=100)
+    o.expert_counts = base + (9 << 30)
+    o.expert_offsets = base + (9 << 30) + 16  # adjacent, not overlapping: reaches the workspace check
+    assert call(opts=o)[0] == -3
+
+
+CONCURRENT_FIRST_CALLS = r"""
+import ctypes, sys, threading
+sys.path.insert(0, sys.argv[1])
+import sparse_mixture_experts_logits_amd as moe
+lib = moe.load_library()
+vp = ctypes.c_void_p
+base = 1 << 40
+cases = [(5, -1, "k = 5"), (0, -1, "k = 0"), (3, -3, "needed"), (2, -3, "needed")] * 8
+start = threading.Barrier(len(cases))
+bad = []
+def run(i, k, want_rc, want_msg):
+    o = moe.MoeOpts()
+    lib.moe_opts_init(ctypes.byref(o))
+    o.workspace = base + (8 << 30)
+    o.workspace_bytes = 64
+    start.wait()
+    for _ in range(200):
+        rc = lib.moe_forward(vp(base), vp(base + (1 << 30)), vp(base + (2 << 30)), vp(base + (3 << 30)),
+                             16, 64, 32, 4, k, ctypes.byref(o), vp(base + (4 << 30)))
+        msg = lib.moe_last_error().decode()
+        if rc != want_rc or want_msg not in msg:
+            bad.append((i, k, rc, msg))
+            return
+threads = [threading.Thread(target=run, args=(i, *c)) for i, c in enumerate(cases)]
+for t in threads: t.start()
+for t in threads: t.join()
+print("BAD" if bad else "OK", bad[:3])
+"""
+
+
+def test_concurrent_first_calls_on_check_paths():
+    """Many host threads make their first calls at once (a fresh process):
+    each sees its own status and its own thread-local message."""
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, "-c", CONCURRENT_FIRST_CALLS, ROOT], capture_output=True, text=True,
+                       timeout=120)
+    assert r.returncode == 0, r.stderr
+    assert r.stdout.startswith("OK"), r.stdout
