@@ -1,26 +1,30 @@
 """Benchmark of the MI355X sparse-MoE layer (one GPU).
 
 One step is one moe_forward call -- router, top-k, permutation, gate_up GEMM
-with fused SiLU*up, down GEMM with the weighted scatter, combine -- over one
-batch of seeded synthetic tokens already resident in HBM. Prints ONE JSON
-line on stdout.
+with fused SiLU*up, down GEMM with the weighted scatter, shared expert,
+combine -- over one batch of seeded synthetic tokens already resident in HBM.
+Prints ONE JSON line on stdout.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
-Default workload: the PhiMoE decode step (T=32, H=4096, I=6400, E=16, top-2),
-a weight-bandwidth-bound case. The PhiMoE prefill chunk (T=4096) is measured
-in the same run and reported under "prefill" (MFMA-bound), and the decode
+Default workload (the headline ``value``): the PhiMoE decode step (T=32,
+H=4096, I=6400, E=16, top-2), bound by the bandwidth of streaming the
+selected experts' weights. Every other workload is measured in the same run
+with the same steps and warm-up and nested in the line under its own name:
+``phimoe_prefill`` (T=4096), ``instella_fine`` (T=2048, 64 experts, top-6,
+scale 2.5, two shared experts), ``phimoe_skewed`` (T=16384, router bias: half
+of all assignments to one expert) and ``tiny_f32`` (fp32), plus the decode
 step with FP8 (E4M3, per-row scaled) and MXFP4 (E2M1, E8M0 scale per 32)
-expert weights under "decode_fp8" and "decode_mxfp4" (different weight
-storage, so never the headline value; --weights fp8|mxfp4 makes one of them
-the main line, marked in its config). A short untimed
-pilot with events at every stage boundary finds the dominant kernel; every
-timed call then records HIP events around that kernel on the library's
-stream, so the roofline figures come from the timed region itself.
+expert weights under ``decode_fp8`` and ``decode_mxfp4`` (different weight
+storage, so never the headline value). Each carries a ``roofline`` of its
+dominant kernel, bound by max(FLOP / MFMA peak, bytes / HBM bandwidth). A
+short untimed pilot with events at every stage boundary finds the dominant
+kernel; every timed call then records HIP events around that kernel on the
+library's stream, so the roofline figures come from the timed region itself.
 
 Other modes: --copy-calibration (a 1 GiB device copy, for scaling rocprofv3
-FETCH_SIZE / WRITE_SIZE) and --write-traffic (summarise those counter runs
-into profiles/).
+FETCH_SIZE / WRITE_SIZE), --write-traffic, --write-stats and --write-counters
+(summarise rocprofv3 runs into profiles/).
 """
 from __future__ import annotations
 
@@ -170,6 +174,85 @@ def write_traffic(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, kernel, 
     with open(out, "w") as fh:
         json.dump(d, fh, indent=1)
     print(json.dumps(d))
+
+
+def _csv_rows(path, suffix):
+    import csv
+    import glob
+    rows = []
+    for f in glob.glob(os.path.join(path, "**", "*" + suffix), recursive=True):
+        rows += list(csv.DictReader(open(f)))
+    return rows
+
+
+def _short_kernel_name(name):
+    """A kernel's name without its parameter list (template arguments kept)."""
+    depth = 0
+    for i, ch in enumerate(name):
+        if ch == "<":
+            depth += 1
+        elif ch == ">":
+            depth -= 1
+        elif ch == "(" and depth == 0:
+            return name[:i]
+    return name
+
+
+def write_stats(trace_dir, title, out_name, command):
+    """Summarise a rocprofv3 --kernel-trace --stats run (its *kernel_stats.csv)
+    into profiles/<out_name>.md: calls, average, min and max duration and the
+    share of GPU time of every kernel."""
+    rows = _csv_rows(trace_dir, "kernel_stats.csv")
+    if not rows:
+        raise SystemExit(f"no kernel_stats.csv under {trace_dir}")
+    rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
+    lines = [f"# rocprofv3 kernel statistics: {title}", "", "Command (run from the repository root on one MI355X):",
+             "", "```", command, "```", "",
+             "| kernel | calls | average (us) | min (us) | max (us) | share of GPU time |",
+             "|---|---|---|---|---|---|"]
+    for r in rows:
+        lines.append(f"| `{_short_kernel_name(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                     f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.1f}% |")
+    out = os.path.join(ROOT, "profiles", out_name + ".md")
+    with open(out, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print(out)
+
+
+def write_counters(pmc_dir, title, out_name, command):
+    """Summarise a rocprofv3 --pmc run (its *counter_collection.csv) into
+    profiles/<out_name>.md: every counter averaged over the dispatches of each
+    kernel (kernels below 1% of the largest counter total are left out)."""
+    rows = _csv_rows(pmc_dir, "counter_collection.csv")
+    if not rows:
+        raise SystemExit(f"no counter_collection.csv under {pmc_dir}")
+    acc = {}
+    for r in rows:
+        key = (_short_kernel_name(r["Kernel_Name"]), r["Counter_Name"])
+        a = acc.setdefault(key, [0.0, 0])
+        a[0] += float(r["Counter_Value"])
+        a[1] += 1
+    kernels = sorted({k for k, _ in acc})
+    counters = sorted({c for _, c in acc})
+    total = {k: max(acc[(k, c)][0] for c in counters if (k, c) in acc) for k in kernels}
+    top = max(total.values())
+    kernels = [k for k in kernels if total[k] >= 0.01 * top]
+    lines = [f"# rocprofv3 counters: {title}", "", "Command (run from the repository root on one MI355X):", "",
+             "```", command, "```", "", "Averages per dispatch.", "",
+             "| counter | " + " | ".join(f"`{k}`" for k in kernels) + " |",
+             "|---|" + "---|" * len(kernels)]
+    for c in counters:
+        vals = []
+        for k in kernels:
+            v = acc.get((k, c))
+            vals.append(f"{v[0] / v[1]:.4g} ({v[1]})" if v else "-")
+        lines.append(f"| {c} | " + " | ".join(vals) + " |")
+    lines.append("")
+    lines.append("(n) = dispatches averaged.")
+    out = os.path.join(ROOT, "profiles", out_name + ".md")
+    with open(out, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print(out)
 
 
 def measured_traffic(kernel, workload):
@@ -334,16 +417,65 @@ def run_workload(name, steps, warmup, weights="bf16"):
     dom_ms = sum(a.elapsed_time(b) for a, b in events) / steps
     stages = dict(zip(moe.STAGES, stage_ms.tolist()))
     stages[moe.STAGES[dom]] = dom_ms  # live value from the timed region
-    return dict(wl=wl, counts=counts, wall_s=wall, gpu_ms=gpu_ms, steps=steps, stages=stages,
-                dominant=moe.STAGES[dom], inp=inp, weights=weights)
+    return dict(wl=wl, counts=counts, wall_s=wall, gpu_ms=gpu_ms, steps=steps, warmup=warmup, stages=stages,
+                dominant=moe.STAGES[dom], inp=inp, weights=weights, schedule=schedule_of(wl, weights))
 
 
 _INPUT_CACHE = {}
 _DEV_CACHE = {}
 
 
+def schedule_of(wl, weights="bf16"):
+    """Which expert-GEMM kernels the library runs for this workload (its
+    default rule, for reporting): fp32 VALU kernels, the weight-streaming
+    kernels for low-precision weights or about 32 rows per expert or fewer,
+    else the large-M tiled kernels."""
+    if wl.dtype == "f32":
+        return "f32"
+    if weights != "bf16" or wl.T * wl.k <= 32 * wl.E:
+        return "skinny"
+    return "tiled"
+
+
+def peak_flops(wl):
+    """Dense MFMA peak of the workload's arithmetic type, FLOP/s."""
+    return (BF16_PEAK_TFLOPS if wl.dtype == "bf16" else FP32_PEAK_TFLOPS) * 1e12
+
+
+def bound_of(flop, nbytes, wl):
+    """The roofline bound of a piece of work: whichever of MFMA time and HBM
+    time is longer. Returns (bound, roofline seconds)."""
+    t_flop = flop / peak_flops(wl)
+    t_bytes = nbytes / (HBM_PEAK_GBPS * 1e9)
+    return ("hbm", t_bytes) if t_bytes >= t_flop else ("mfma", t_flop)
+
+
+def tiled_executed_flops(wl, counts, tile_m=256, tile_xt=32, block=32, nblk_cols=128):
+    """MFMA FLOPs the large-M schedule executes for the routed expert GEMMs:
+    an expert's rows go to as few M-tiles as hold them at up to tile_m +
+    tile_xt rows; a tile runs whole 32-row blocks (a tile with extra rows runs
+    tile_m + 32), and N is padded to whole column blocks (gate_up: 128 h
+    columns, i.e. 128 gate + 128 up rows; down: 256 output rows)."""
+    rows_exec = 0
+    for c in counts:
+        c = int(c)
+        if c == 0:
+            continue
+        n = (c + tile_m + tile_xt - 1) // (tile_m + tile_xt)
+        extra = max(c - n * tile_m, 0)
+        for i in range(n):
+            rows = tile_m + min(max(extra - i * tile_xt, 0), tile_xt) if extra > 0 else \
+                (c - i * tile_m if i == n - 1 else tile_m)
+            rows_exec += tile_m + block if rows > tile_m else -(-rows // block) * block
+    n_gu = -(-wl.I // nblk_cols) * nblk_cols
+    n_dn = -(-wl.H // 256) * 256
+    return dict(gate_up=2.0 * rows_exec * 2 * n_gu * wl.H, down=2.0 * rows_exec * n_dn * wl.I)
+
+
 def roofline_of(res):
-    """Roofline of the dominant expert GEMM (the stage with the largest time)."""
+    """Roofline of the dominant expert GEMM (the stage with the largest time),
+    bound by max(FLOP / peak, bytes / HBM bandwidth) of that kernel's
+    algorithmic work."""
     wl = res["wl"]
     w = work(wl, res["counts"], weights=res["weights"])
     st = res["stages"]
@@ -351,13 +483,13 @@ def roofline_of(res):
     if kernel not in ("gate_up", "down"):  # the expert GEMMs dominate every workload here
         kernel = "gate_up" if st["gate_up"] >= st["down"] else "down"
     dur_s = st[kernel] / 1e3
-    decode = wl.T * wl.k <= 32 * wl.E
-    if decode:
+    bound, _ = bound_of(w[f"flop_{kernel}"], w[f"bytes_{kernel}"], wl)
+    if bound == "hbm":
         achieved = w[f"bytes_{kernel}"] / dur_s / 1e9
         r = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBPS, unit="GB/s",
                  frac=round(achieved / HBM_PEAK_GBPS, 4))
     else:
-        peak = BF16_PEAK_TFLOPS if wl.dtype == "bf16" else FP32_PEAK_TFLOPS
+        peak = peak_flops(wl) / 1e12
         achieved = w[f"flop_{kernel}"] / dur_s / 1e12
         r = dict(bound="mfma", achieved=round(achieved, 1), peak=peak, unit="TFLOP/s",
                  frac=round(achieved / peak, 4))
@@ -365,7 +497,12 @@ def roofline_of(res):
     r["traffic"] = tr
     r["kernel"] = kernel
     r["avg_launch_ms"] = round(st[kernel], 4)
+    r["algorithmic"] = {"flop": w[f"flop_{kernel}"], "bytes": w[f"bytes_{kernel}"]}
     r["timing"] = "HIP events around this kernel on the library's stream, every timed step"
+    if res.get("schedule") == "tiled":
+        ex = tiled_executed_flops(wl, res["counts"])[kernel]
+        r["mfma_flop_executed"] = ex
+        r["padded_flop_frac"] = round(1.0 - w[f"flop_{kernel}"] / ex, 4)
     return r, w
 
 
@@ -373,10 +510,13 @@ def layer_summary(res, w):
     wl = res["wl"]
     ms = res["wall_s"] * 1e3 / res["steps"]
     s = ms / 1e3
+    bound, t_roof = bound_of(w["flop_layer"], w["bytes_layer"], wl)
     return dict(ms_per_step=round(ms, 4), tokens_per_s=round(wl.T / s, 1),
                 tflops=round(w["flop_layer"] / s / 1e12, 2), gbps=round(w["bytes_layer"] / s / 1e9, 1),
                 frac_hbm=round(w["bytes_layer"] / s / 1e9 / HBM_PEAK_GBPS, 4),
-                frac_mfma=round(w["flop_layer"] / s / 1e12 / BF16_PEAK_TFLOPS, 4),
+                frac_mfma=round(w["flop_layer"] / s / peak_flops(wl), 4),
+                bound=bound, roofline_ms=round(t_roof * 1e3, 4), roofline_frac=round(t_roof / s, 4),
+                schedule=res.get("schedule"),
                 experts_hit=w["hit"], stages_ms={k: round(v, 4) for k, v in res["stages"].items()})
 
 
@@ -409,20 +549,34 @@ def cpu_baseline(res, max_tokens, min_seconds=10.0):
 
 # ------------------------------------------------------------------ main
 
+# PhiMoE-shaped workloads first: they share one set of device weights
+NESTED = ("phimoe_prefill", "phimoe_skewed", "instella_fine", "tiny_f32")
+
+
+def nested_line(res):
+    roof, w = roofline_of(res)
+    wl = res["wl"]
+    d = dict(workload=wl.name, steps=res["steps"], warmup=res["warmup"], dtype=wl.dtype,
+             config={"T": wl.T, "H": wl.H, "I": wl.I, "E": wl.E, "k": wl.k, "routed_scale": wl.routed_scale,
+                     "shared_I": wl.n_shared * wl.shared_I},
+             roofline=roof, layer=layer_summary(res, w))
+    if res["weights"] != "bf16":
+        d["weights"] = WEIGHT_FORMATS[res["weights"]]
+    return d
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="phimoe_decode")
-    ap.add_argument("--prefill-steps", type=int, default=50)
-    ap.add_argument("--no-prefill", action="store_true", help="skip the secondary prefill measurement")
+    ap.add_argument("--only", action="store_true", help="measure the main workload only (no nested lines)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--no-fp8", action="store_true", help="skip the secondary FP8-weight decode measurement")
-    ap.add_argument("--no-mxfp4", action="store_true", help="skip the secondary MXFP4-weight decode measurement")
+    ap.add_argument("--skip", nargs="*", default=[], help="nested lines to leave out (workload names, "
+                                                           "decode_fp8, decode_mxfp4)")
     ap.add_argument("--weights", choices=sorted(WEIGHT_FORMATS), default="bf16",
                     help="expert weight storage of the main workload (fp8 / mxfp4: decode-shaped work only)")
-    ap.add_argument("--fp8", action="store_true", help="same as --weights fp8")
     ap.add_argument("--cpu-tokens", type=int, default=32)
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="whole oracle passes over the CPU sample until this many seconds have passed")
@@ -431,11 +585,21 @@ def main(argv=None):
     ap.add_argument("--write-traffic", nargs=7, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR",
                                                          "COPY_WRITE_DIR", "KERNEL", "WORKLOAD", "REGEX"),
                     help="summarise rocprofv3 FETCH_SIZE/WRITE_SIZE runs into profiles/")
-    ap.add_argument("--command", default="", help="command line recorded with --write-traffic")
+    ap.add_argument("--write-stats", nargs=3, metavar=("TRACE_DIR", "TITLE", "OUT_NAME"),
+                    help="summarise a rocprofv3 --kernel-trace --stats run into profiles/OUT_NAME.md")
+    ap.add_argument("--write-counters", nargs=3, metavar=("PMC_DIR", "TITLE", "OUT_NAME"),
+                    help="summarise a rocprofv3 --pmc run (averages per kernel) into profiles/OUT_NAME.md")
+    ap.add_argument("--command", default="", help="command line recorded with the --write-* modes")
     args = ap.parse_args(argv)
     if args.write_traffic:
         fd, wd, cfd, cwd, kernel, workload, regex = args.write_traffic
         write_traffic(fd, wd, cfd, cwd, kernel, workload, regex, 1 << 30, args.command)
+        return 0
+    if args.write_stats:
+        write_stats(*args.write_stats, args.command)
+        return 0
+    if args.write_counters:
+        write_counters(*args.write_counters, args.command)
         return 0
     if args.copy_calibration:
         copy_calibration()
@@ -450,8 +614,6 @@ def main(argv=None):
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
 
-    if args.fp8:
-        args.weights = "fp8"
     res = run_workload(args.workload, args.steps, args.warmup, weights=args.weights)
     roof, w = roofline_of(res)
     lay = layer_summary(res, w)
@@ -478,17 +640,16 @@ def main(argv=None):
     }
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(res, args.cpu_tokens, args.cpu_seconds)
-    for fmt, skip in (("fp8", args.no_fp8), ("mxfp4", args.no_mxfp4)):
-        if skip or args.weights != "bf16" or args.workload != "phimoe_decode":
-            continue
-        fres = run_workload("phimoe_decode", args.steps, args.warmup, weights=fmt)
-        froof, fw = roofline_of(fres)
-        line["decode_" + fmt] = dict(workload="phimoe_decode", weights=WEIGHT_FORMATS[fmt],
-                                     roofline=froof, layer=layer_summary(fres, fw))
-    if not args.no_prefill and args.workload != "phimoe_prefill":
-        pres = run_workload("phimoe_prefill", args.prefill_steps, 3)
-        proof, pw = roofline_of(pres)
-        line["prefill"] = dict(workload="phimoe_prefill", roofline=proof, layer=layer_summary(pres, pw))
+    if not args.only:
+        if args.weights == "bf16" and args.workload == "phimoe_decode":
+            for fmt in ("fp8", "mxfp4"):
+                if "decode_" + fmt not in args.skip:
+                    line["decode_" + fmt] = nested_line(run_workload("phimoe_decode", args.steps, args.warmup,
+                                                                     weights=fmt))
+        for name in NESTED:
+            if name != args.workload and name not in args.skip:
+                line[name] = nested_line(run_workload(name, args.steps, args.warmup))
+                log(f"[bench] {name}: {line[name]['layer']['ms_per_step']} ms per step")
     print(json.dumps(line), flush=True)
     return 0
 

@@ -113,3 +113,63 @@ def test_roofline_of_decode_and_prefill():
     r, _ = bench.roofline_of(res)
     assert r["kernel"] == "down"
     assert abs(r["achieved"] - round(2.0 * pre.T * pre.k * pre.H * pre.I / 0.47e-3 / 1e12, 1)) < 1e-6
+
+
+def test_bound_is_the_longer_of_mfma_and_hbm_time():
+    # the Instella-style gate_up moves more bytes than its FLOPs take at peak
+    # (intensity below the ridge): HBM bound, although many rows share each expert
+    fine = W.BY_NAME["instella_fine"]
+    res = dict(wl=fine, counts=[192] * fine.E, weights="bf16", dominant="gate_up", schedule="tiled",
+               stages={"gate_up": 0.18, "down": 0.1})
+    r, w = bench.roofline_of(res)
+    assert w["flop_gate_up"] / 2.5e15 < w["bytes_gate_up"] / 8e12
+    assert r["bound"] == "hbm" and r["unit"] == "GB/s"
+    assert abs(r["achieved"] - round(w["bytes_gate_up"] / 0.18e-3 / 1e9, 1)) < 1e-6
+    lay = bench.layer_summary(dict(res, wall_s=0.5e-3 * 10, steps=10), w)
+    assert lay["bound"] == "hbm" and abs(lay["roofline_frac"] - w["bytes_layer"] / 8e12 / 0.5e-3) < 1e-4
+    assert bench.bound_of(1e12, 1e6, fine)[0] == "mfma" and bench.bound_of(1e6, 1e9, fine)[0] == "hbm"
+
+
+def test_tiled_executed_flops_counts_padded_tiles():
+    pre = W.BY_NAME["phimoe_prefill"]
+    # 512 rows: two full 256-row tiles; I = 6400 is 50 whole column blocks: no padding
+    ex = bench.tiled_executed_flops(pre, [512] * pre.E)
+    assert ex["gate_up"] == 2.0 * pre.T * pre.k * 2 * pre.I * pre.H
+    assert ex["down"] == 2.0 * pre.T * pre.k * pre.H * pre.I
+    # 557 rows: tiles of 288 (256 + 32 extra) and 269 (256 + 13 extra) both run 288 rows;
+    # 20 rows: one 32-row block; 0 rows: nothing
+    counts = [557, 20, 0] + [0] * (pre.E - 3)
+    ex = bench.tiled_executed_flops(pre, counts)
+    assert ex["down"] == 2.0 * (576 + 32) * pre.H * pre.I
+    import dataclasses
+    one = dataclasses.replace(pre, T=577, k=1)  # T*k = the 577 rows above
+    res = dict(wl=one, counts=counts, weights="bf16", dominant="down", schedule="tiled",
+               stages={"gate_up": 0.1, "down": 0.2})
+    r, w = bench.roofline_of(res)
+    assert abs(r["padded_flop_frac"] - (1 - 577 / 608)) < 1e-4
+
+
+def test_write_stats_and_counters_summaries(tmp_path, monkeypatch):
+    import csv
+    (tmp_path / "profiles").mkdir()
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    d = tmp_path / "trace" / "host" / "123"
+    d.mkdir(parents=True)
+    with open(d / "t_kernel_stats.csv", "w", newline="") as fh:
+        w = csv.DictWriter(fh, fieldnames=["Name", "Calls", "TotalDurationNs", "AverageNs", "Percentage",
+                                           "MinNs", "MaxNs", "StdDev"])
+        w.writeheader()
+        w.writerow(dict(Name="small_kernel(int)", Calls=4, TotalDurationNs=4000, AverageNs=1000, Percentage=10,
+                        MinNs=900, MaxNs=1100, StdDev=1))
+        w.writerow(dict(Name="void big<1, true>(P)", Calls=4, TotalDurationNs=36000, AverageNs=9000,
+                        Percentage=90, MinNs=8000, MaxNs=9500, StdDev=1))
+    bench.write_stats(str(tmp_path / "trace"), "unit", "unit_stats", "cmd --x")
+    text = (tmp_path / "profiles" / "unit_stats.md").read_text()
+    assert "cmd --x" in text and text.index("`void big<1, true>`") < text.index("`small_kernel`")
+    assert "| 4 | 9.0 | 8.0 | 9.5 | 90.0% |" in text
+    _pmc(tmp_path / "pmc", [("void big<1, true>(P)", "SQ_BUSY_CYCLES", 10.0),
+                            ("void big<1, true>(P)", "SQ_BUSY_CYCLES", 30.0),
+                            ("tiny(int)", "SQ_BUSY_CYCLES", 0.01)])
+    bench.write_counters(str(tmp_path / "pmc"), "unit", "unit_pmc", "cmd")
+    text = (tmp_path / "profiles" / "unit_pmc.md").read_text()
+    assert "| SQ_BUSY_CYCLES | 20 (2) |" in text and "tiny" not in text

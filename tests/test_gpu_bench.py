@@ -1,6 +1,7 @@
 """The benchmark's output contract on a GPU: one JSON line with the metric,
 the whole-step throughput, the roofline of the dominant kernel, the CPU
-oracle baseline and the secondary lines (a short run: few steps)."""
+oracle baseline and a nested line for every other workload (a short run:
+few steps)."""
 import json
 
 import pytest
@@ -15,8 +16,7 @@ def test_bench_prints_one_json_line_with_roofline_and_cpu_baseline(capsys):
     print("case bench.py short run", flush=True)
     import bench  # in this process: no second program is started
     try:
-        rc = bench.main(["--steps", "5", "--warmup", "1", "--prefill-steps", "3", "--cpu-tokens", "2",
-                         "--cpu-seconds", "0.2"])
+        rc = bench.main(["--steps", "5", "--warmup", "1", "--cpu-tokens", "2", "--cpu-seconds", "0.2"])
     finally:  # the full-size weights it keeps on the device
         bench._INPUT_CACHE.clear()
         bench._DEV_CACHE.clear()
@@ -36,5 +36,10 @@ def test_bench_prints_one_json_line_with_roofline_and_cpu_baseline(capsys):
     assert 0 < roof["frac"] < 1.2 and abs(roof["frac"] - roof["achieved"] / roof["peak"]) < 1e-3
     cpu = d["cpu_baseline"]
     assert cpu["kind"] == "oracle" and cpu["value"] > 0 and cpu["cores"] >= 1 and "tokens" in cpu["sample"]
-    for sec, bound in (("decode_fp8", "hbm"), ("decode_mxfp4", "hbm"), ("prefill", "mfma")):
-        assert d[sec]["roofline"]["bound"] == bound and d[sec]["layer"]["tokens_per_s"] > 0
+    for sec, bound in (("decode_fp8", "hbm"), ("decode_mxfp4", "hbm"), ("phimoe_prefill", "mfma"),
+                       ("phimoe_skewed", "mfma"), ("instella_fine", "hbm")):
+        sub = d[sec]
+        assert sub["roofline"]["bound"] == bound and sub["layer"]["tokens_per_s"] > 0, sec
+        assert sub["steps"] == 5 and sub["warmup"] == 1, sec
+    assert d["tiny_f32"]["dtype"] == "f32" and d["tiny_f32"]["layer"]["tokens_per_s"] > 0
+    assert 0 <= d["phimoe_skewed"]["roofline"]["padded_flop_frac"] < 0.2
