@@ -19,7 +19,8 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(_HERE, "moe_oracle.c")
-LIB = os.path.join(_HERE, "libmoe_oracle.so")
+# MOE_ORACLE_LIB may name another build of the same source (the sanitizer build)
+LIB = os.environ.get("MOE_ORACLE_LIB") or os.path.join(_HERE, "libmoe_oracle.so")
 
 _lib = None
 
@@ -33,6 +34,16 @@ def build(force: bool = True) -> str:
         subprocess.run(cmd, check=True)
         os.replace(tmp, LIB)
     return LIB
+
+
+def build_sanitized(out: str) -> str:
+    """The same source built with AddressSanitizer and UndefinedBehaviorSanitizer
+    (gcc; every finding fatal), for running the oracle's pins under them."""
+    cmd = ["gcc", "-O1", "-g", "-mfma", "-ffp-contract=off", "-fno-fast-math", "-fopenmp", "-fPIC", "-shared",
+           "-std=c11", "-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-fno-omit-frame-pointer",
+           SRC, "-o", out, "-lm"]
+    subprocess.run(cmd, check=True)
+    return out
 
 
 def _load():

@@ -57,6 +57,36 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+def build_host_sanitized(out: str, verbose: bool = False) -> str:
+    """A copy of the library whose host code in moe_api.hip (argument checks,
+    workspace layout, entry points) is built with AddressSanitizer and
+    UndefinedBehaviorSanitizer (host pass only; device code unchanged). The
+    other translation units are the regular objects. For CPU runs of the
+    argument-check paths; never loaded by the tests' GPU code."""
+    os.makedirs(BUILD, exist_ok=True)
+    objs = []
+    for src in sources():
+        obj = os.path.join(BUILD, src.replace(".hip", ".o"))
+        if src == "moe_api.hip":
+            obj = os.path.join(BUILD, "moe_api_hostsan.o")
+            san = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                   "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host", "-fno-omit-frame-pointer"]
+            cmd = [HIPCC, *COMMON, *san, "-c", os.path.join(CSRC, src), "-o", obj]
+            r = subprocess.run(cmd, capture_output=True, text=True)
+            if r.returncode != 0:
+                raise RuntimeError(f"hipcc failed on {src}:\n{r.stdout}\n{r.stderr}")
+        elif not os.path.exists(obj) or os.path.getmtime(obj) < os.path.getmtime(os.path.join(CSRC, src)):
+            obj = _compile(src)
+        objs.append(obj)
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", out]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
+    if verbose:
+        print(f"built {out}")
+    return out
+
+
 if __name__ == "__main__":
     build(verbose=True)
     sys.exit(0)
