@@ -262,6 +262,35 @@ int moe_forward(const void *hidden, const void *router_w, const void *gate_up, c
                 int64_t T, int64_t H, int64_t I, int64_t E, int32_t k, const moe_opts *opts,
                 void *out);
 
+/* Scratch bytes that moe_forward_noalloc holds on each GPU it runs on. */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/*
+ * moe_forward without a caller workspace, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops and
+ * harnesses that forbid hipMalloc. Same arguments, results and checks as
+ * moe_forward, except:
+ *   - opts->workspace must be NULL and opts->workspace_bytes 0
+ *     (MOE_ERR_INVALID_ARG otherwise); the layer's scratch lives in a device
+ *     array of MOE_NOALLOC_SCRATCH_BYTES inside the library, one per GPU,
+ *     held until the process ends;
+ *   - sizes whose workspace (moe_workspace_bytes) exceeds that array are
+ *     rejected with MOE_ERR_UNSUPPORTED (the PhiMoE decode step, T = 32,
+ *     H = 4096, I = 6400, E = 16, k = 2, needs about 2 MB; large-M tiled
+ *     calls need more: use moe_forward for those);
+ *   - no call allocates or frees memory; the first call on a device looks up
+ *     the array's address on that device once (hipGetSymbolAddress, with
+ *     that device current) and keeps it for later calls;
+ *   - every call on one GPU uses the same array, which keeps the last call's
+ *     contents (every call writes what it reads first, nothing needs
+ *     clearing). Calls that overlap in time on one GPU (other streams, or
+ *     other host threads without ordering) race on it; calls ordered on one
+ *     stream do not.
+ */
+int moe_forward_noalloc(const void *hidden, const void *router_w, const void *gate_up, const void *down,
+                        int64_t T, int64_t H, int64_t I, int64_t E, int32_t k, const moe_opts *opts,
+                        void *out);
+
 /*
  * Per-row FP8 quantisation of a bf16 matrix w [rows, cols] (for instance the
  * packed gate_up viewed as [E*2I, H], or down as [E*H, I]):

@@ -31,8 +31,9 @@ WEIGHTS_MXFP4 = 2
 SCORE_SOFTMAX = 0
 SCORE_SIGMOID = 1
 SCORE_SPARSEMIXER = 2
-EXPORTS = ("moe_opts_init", "moe_workspace_bytes", "moe_forward", "moe_quantize_fp8_rows",
+EXPORTS = ("moe_opts_init", "moe_workspace_bytes", "moe_forward", "moe_forward_noalloc", "moe_quantize_fp8_rows",
            "moe_quantize_mxfp4_rows", "moe_last_error")
+NOALLOC_SCRATCH_BYTES = 64 << 20  # MOE_NOALLOC_SCRATCH_BYTES
 STAGES = ("router", "scan", "permute", "gate_up", "down", "shared_gate_up", "shared_down", "combine")
 STAGE_EVENTS = len(STAGES) + 1
 
@@ -107,6 +108,8 @@ def load_library():
         lib.moe_workspace_bytes.restype = i64
         lib.moe_forward.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i32, ctypes.POINTER(MoeOpts), vp]
         lib.moe_forward.restype = ctypes.c_int
+        lib.moe_forward_noalloc.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i32, ctypes.POINTER(MoeOpts), vp]
+        lib.moe_forward_noalloc.restype = ctypes.c_int
         lib.moe_quantize_fp8_rows.argtypes = [vp, i64, i64, vp, vp, vp]
         lib.moe_quantize_fp8_rows.restype = ctypes.c_int
         lib.moe_quantize_mxfp4_rows.argtypes = [vp, i64, i64, vp, vp, vp]
@@ -197,7 +200,7 @@ def moe_forward(hidden, router_w, gate_up, down, k: int, *, routed_scale: float 
                 out=None, workspace=None, stream=None, stage_events=None, gate_up_scale=None, down_scale=None,
                 router_stats: bool = False, stats_mask=None, score_func: str = "softmax",
                 selection_bias=None, n_group: int = 0, topk_group: int = 0, jitter_eps: float | None = None,
-                gate_up_block_scale=None, down_block_scale=None):
+                gate_up_block_scale=None, down_block_scale=None, no_alloc: bool = False):
     """Run the MoE layer on torch tensors already on the GPU.
 
     hidden [T, H], router_w [E, H], gate_up [E, 2I, H], down [E, H, I] (all
@@ -207,7 +210,9 @@ def moe_forward(hidden, router_w, gate_up, down, k: int, *, routed_scale: float 
     from quantize_fp8_rows); activations bf16. MXFP4 expert weights: gate_up
     [E, 2I, H/2] and down [E, H, I/2] uint8 (two E2M1 codes per byte) with
     gate_up_block_scale [E, 2I, H/32] and down_block_scale [E, H, I/32] uint8
-    (from quantize_mxfp4_rows). ``router_stats`` adds the
+    (from quantize_mxfp4_rows). ``no_alloc`` calls moe_forward_noalloc: the
+    library's own scratch instead of a workspace (``workspace`` must be None;
+    pass ``out`` so that nothing is allocated here either). ``router_stats`` adds the
     load-balancing statistics (prob_mean [E], load [E], aux_loss [1]) to the
     routing dict, over the tokens with ``stats_mask`` != 0 (int32 [T]; all
     tokens if None). ``score_func`` "sigmoid" scores experts by the sigmoid of
@@ -332,14 +337,18 @@ def moe_forward(hidden, router_w, gate_up, down, k: int, *, routed_scale: float 
     need = lib.moe_workspace_bytes(T, H, I, E, k, ctypes.byref(o))
     if need < 0:
         raise MoeError(int(need), last_error())
-    if workspace is None:
+    if no_alloc:
+        if workspace is not None:
+            raise ValueError("no_alloc uses the library's scratch: pass no workspace")
+    elif workspace is None:
         workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
     elif workspace.numel() * workspace.element_size() < need or not workspace.is_cuda:
         # a caller that passes a workspace relies on the call allocating nothing
         raise ValueError(f"workspace holds {workspace.numel() * workspace.element_size()} bytes; "
                          f"{need} are needed (workspace_bytes with the same flags and dtype)")
-    o.workspace = workspace.data_ptr()
-    o.workspace_bytes = workspace.numel() * workspace.element_size()
+    if not no_alloc:
+        o.workspace = workspace.data_ptr()
+        o.workspace_bytes = workspace.numel() * workspace.element_size()
     current = torch.cuda.current_stream(dev)
     if stream is None:
         stream = current
@@ -353,8 +362,8 @@ def moe_forward(hidden, router_w, gate_up, down, k: int, *, routed_scale: float 
     o.stream = stream.cuda_stream
     if stage_events is not None:
         o.stage_events = ctypes.cast(stage_events, ctypes.c_void_p)
-    rc = lib.moe_forward(_ptr(hidden), _ptr(router_w), _ptr(gate_up), _ptr(down), T, H, I, E, int(k),
-                         ctypes.byref(o), _ptr(out))
+    fn = lib.moe_forward_noalloc if no_alloc else lib.moe_forward
+    rc = fn(_ptr(hidden), _ptr(router_w), _ptr(gate_up), _ptr(down), T, H, I, E, int(k), ctypes.byref(o), _ptr(out))
     if rc != 0:
         raise MoeError(rc, last_error())
     if return_routing:

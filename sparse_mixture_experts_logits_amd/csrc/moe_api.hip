@@ -4,6 +4,7 @@
 #include "moe_internal.h"
 
 #include <math.h>
+#include <mutex>
 #include <stdarg.h>
 #include <stdio.h>
 #include <stdlib.h>
@@ -199,6 +200,43 @@ int64_t workspace_layout(const Shape &s, void *base, Workspace *ws)
 
 }  // namespace moe
 
+namespace {
+
+// Scratch memory of moe_forward_noalloc, for callers that cannot allocate
+// (code under graph capture, serving loops, harnesses that forbid hipMalloc).
+// Each GPU holds its own copy for the life of the process. In host code the
+// array's name is only a stand-in: its device address comes from
+// hipGetSymbolAddress, once per device with that device current, and only
+// that address is ever passed to kernels.
+constexpr size_t kScratchBytes = MOE_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+void *g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+
+int scratch_on_current_device(void **ptr)
+{
+    int dev = -1;
+    hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess) return fail(MOE_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(err));
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(MOE_ERR_UNSUPPORTED, "device %d: moe_forward_noalloc serves devices 0..%d", dev, kMaxDevices - 1);
+    std::call_once(g_scratch_once[dev], [dev] {
+        void *p = nullptr;
+        g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        g_scratch_ptr[dev] = g_scratch_err[dev] == hipSuccess ? p : nullptr;
+    });
+    if (g_scratch_err[dev] != hipSuccess || !g_scratch_ptr[dev])
+        return fail(MOE_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d failed: %s", dev,
+                    hipGetErrorString(g_scratch_err[dev]));
+    *ptr = g_scratch_ptr[dev];
+    return MOE_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 void moe_opts_init(moe_opts *opts)
@@ -222,10 +260,10 @@ int64_t moe_workspace_bytes(int64_t T, int64_t H, int64_t I, int64_t E, int32_t 
     return moe::workspace_layout(s, nullptr, nullptr);
 }
 
-int moe_forward(const void *hidden, const void *router_w, const void *gate_up, const void *down,
-                int64_t T, int64_t H, int64_t I, int64_t E, int32_t k, const moe_opts *opts, void *out)
+// The layer on the caller's stream with the workspace in opts (both entry points).
+static int forward_impl(const void *hidden, const void *router_w, const void *gate_up, const void *down,
+                        int64_t T, int64_t H, int64_t I, int64_t E, int32_t k, const moe_opts *opts, void *out)
 {
-    g_err[0] = 0;
     if (!opts) return fail(MOE_ERR_INVALID_ARG, "opts is NULL");
     int rc = check_shape(T, H, I, E, k, opts);
     if (rc != MOE_OK) return rc;
@@ -459,6 +497,38 @@ int moe_forward(const void *hidden, const void *router_w, const void *gate_up, c
         (rc = mark(1 + MOE_STAGE_COMBINE)))
         return rc;
     return MOE_OK;
+}
+
+int moe_forward(const void *hidden, const void *router_w, const void *gate_up, const void *down,
+                int64_t T, int64_t H, int64_t I, int64_t E, int32_t k, const moe_opts *opts, void *out)
+{
+    g_err[0] = 0;
+    return forward_impl(hidden, router_w, gate_up, down, T, H, I, E, k, opts, out);
+}
+
+int moe_forward_noalloc(const void *hidden, const void *router_w, const void *gate_up, const void *down,
+                        int64_t T, int64_t H, int64_t I, int64_t E, int32_t k, const moe_opts *opts, void *out)
+{
+    g_err[0] = 0;
+    if (!opts) return fail(MOE_ERR_INVALID_ARG, "opts is NULL");
+    int rc = check_shape(T, H, I, E, k, opts);
+    if (rc != MOE_OK) return rc;
+    if (opts->workspace || opts->workspace_bytes)
+        return fail(MOE_ERR_INVALID_ARG, "moe_forward_noalloc uses the library's scratch: opts->workspace must be "
+                                         "NULL and workspace_bytes 0");
+    const moe::Shape s = make_shape(T, H, I, E, k, opts);
+    const int64_t need = moe::workspace_layout(s, nullptr, nullptr);
+    if (need > (int64_t)kScratchBytes)
+        return fail(MOE_ERR_UNSUPPORTED, "these sizes need %lld bytes of scratch; moe_forward_noalloc holds %lld "
+                                         "(use moe_forward with a workspace)",
+                    (long long)need, (long long)kScratchBytes);
+    if (T == 0) return forward_impl(hidden, router_w, gate_up, down, T, H, I, E, k, opts, out);
+    void *ptr = nullptr;
+    if ((rc = scratch_on_current_device(&ptr)) != MOE_OK) return rc;
+    moe_opts o = *opts;  // struct_size checked above: the whole struct is the caller's
+    o.workspace = ptr;
+    o.workspace_bytes = kScratchBytes;
+    return forward_impl(hidden, router_w, gate_up, down, T, H, I, E, k, &o, out);
 }
 
 int moe_quantize_fp8_rows(const void *w, int64_t rows, int64_t cols, void *q, float *scale, void *stream)

@@ -384,3 +384,27 @@ def test_concurrent_first_calls_on_check_paths():
                        timeout=120)
     assert r.returncode == 0, r.stderr
     assert r.stdout.startswith("OK"), r.stdout
+
+
+def test_noalloc_entry_point_checks_arguments():
+    # the allocation-free entry point takes no workspace and rejects sizes its
+    # scratch cannot hold, before any HIP call
+    o = moe.new_opts()
+    o.workspace = (1 << 40) + (8 << 30)
+    o.workspace_bytes = 1 << 20
+    lib = moe.load_library()
+    vp = ctypes.c_void_p
+    base = 1 << 40
+    args = (vp(base), vp(base + (1 << 30)), vp(base + (2 << 30)), vp(base + (3 << 30)))
+    rc = lib.moe_forward_noalloc(*args, 4, 64, 32, 4, 2, ctypes.byref(o), vp(base + (4 << 30)))
+    assert rc == -1 and "workspace must be NULL" in moe.last_error()
+    o = moe.new_opts()
+    rc = lib.moe_forward_noalloc(*args, 4096, 4096, 6400, 16, 2, ctypes.byref(o), vp(base + (4 << 30)))
+    assert rc == -2 and "scratch" in moe.last_error()
+    assert moe.workspace_bytes(4096, 4096, 6400, 16, 2) > moe.NOALLOC_SCRATCH_BYTES
+    assert lib.moe_forward_noalloc(*args, 4, 64, 32, 4, 0, ctypes.byref(o), vp(base + (4 << 30))) == -1
+    assert lib.moe_forward_noalloc(*args, 4, 64, 32, 4, 2, None, vp(base + (4 << 30))) == -1
+    # T = 0 succeeds without touching the device
+    assert lib.moe_forward_noalloc(None, None, None, None, 0, 64, 32, 4, 2, ctypes.byref(o), None) == 0
+    # the decode step fits
+    assert moe.workspace_bytes(32, 4096, 6400, 16, 2) <= moe.NOALLOC_SCRATCH_BYTES
