@@ -44,7 +44,18 @@ HBM_PEAK_GBPS = 8000.0         # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 FP32_PEAK_TFLOPS = 157.3       # MI355X fp32 vector
 METRIC = "MoE layer tokens/sec + % of bf16 MFMA peak (prefill) / % HBM BW (decode)"
-KERNEL_SOURCES = {k: ("gemm_skinny.hip", "gemm_tiled.hip", "moe_internal.h") for k in ("gate_up", "down")}
+# the sources a counter figure depends on, by the kernel family it was taken on
+SCHEDULE_SOURCES = {"skinny": ("gemm_skinny.hip", "moe_internal.h"), "tiled": ("gemm_tiled.hip", "moe_internal.h"),
+                    "f32": ("gemm_f32.hip", "moe_internal.h")}
+
+
+def schedule_of_kernel(regex):
+    """Kernel family of a kernel-name pattern (skinny_gemm / tiled_gemm / f32_*)."""
+    if "skinny" in regex:
+        return "skinny"
+    if "tiled" in regex:
+        return "tiled"
+    return "f32"
 
 
 def decode_tokens_per_s_bound(bandwidth_Bps: float, bytes_per_token: float) -> float:
@@ -167,7 +178,8 @@ def write_traffic(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, kernel, 
         "copy_calibration": {"bytes": copy_bytes, "fetch_kib": f_c, "write_kib": w_c,
                              "fetch_factor": ff, "write_factor": fw},
         "hbm_bytes_per_launch": f_k * 1024.0 * ff + w_k * 1024.0 * fw,
-        "source_hash": source_hash(KERNEL_SOURCES[kernel]),
+        "schedule": schedule_of_kernel(regex),
+        "source_hash": source_hash(SCHEDULE_SOURCES[schedule_of_kernel(regex)]),
         "command": command,
     }
     out = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.json")
@@ -186,7 +198,26 @@ def _csv_rows(path, suffix):
 
 
 def _short_kernel_name(name):
-    """A kernel's name without its parameter list (template arguments kept)."""
+    """A kernel's name without its namespace and parameter list (template
+    arguments kept); mangled names are demangled first."""
+    if name.startswith("_Z"):
+        import re
+        import subprocess
+        try:
+            dem = subprocess.run(["c++filt", name], capture_output=True, text=True, timeout=10).stdout.strip()
+        except (OSError, subprocess.SubprocessError):
+            dem = name
+        if dem and dem != name:
+            name = dem
+        else:  # a mangling the tool does not know (bf16 template arguments): name and first template argument
+            m = re.match(r"_ZN3moe12_GLOBAL__N_1(\d+)", name)
+            if m:
+                n = int(m.group(1))
+                ident = name[m.end():m.end() + n]
+                rest = name[m.end() + n:]
+                targ = "bf16" if rest.startswith("IDF16b") else "float" if rest.startswith("If") else ""
+                name = ident + (f" [{targ}]" if targ else "")
+    name = name.replace("moe::(anonymous namespace)::", "")
     depth = 0
     for i, ch in enumerate(name):
         if ch == "<":
@@ -265,7 +296,8 @@ def measured_traffic(kernel, workload):
         d = json.load(open(path))
     except (OSError, ValueError):
         return None
-    if d.get("source_hash") != source_hash(KERNEL_SOURCES[kernel]):
+    sched = d.get("schedule") or schedule_of_kernel(d.get("kernel_regex", ""))
+    if d.get("source_hash") != source_hash(SCHEDULE_SOURCES[sched]):
         return None
     return d.get("hbm_bytes_per_launch")
 

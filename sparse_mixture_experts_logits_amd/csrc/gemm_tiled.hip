@@ -40,6 +40,7 @@ constexpr int STAGES = MOE_TILED_STAGES;  // LDS ring depth
 constexpr int CH = BK / 8;                // 16-byte chunks per row of a stage
 constexpr int RPI = 64 / CH;              // rows filled by one 64-lane copy instruction
 static_assert(CH == 4 || CH == 8, "stage rows of 64 or 128 bytes");
+static_assert(STAGES >= 2, "at least a double buffer");
 
 struct TiledParams {
     const __bf16 *A;
@@ -59,6 +60,7 @@ struct TiledParams {
     float *part;  // partial sums of split tiles (null: no splitting)
     int G;      // workgroups of the persistent launch
     int cap;    // pieces the partial-sum buffer holds for this tile shape
+    uint32_t a_bytes;  // bytes of A the rows may reach (buffer resource bound)
 };
 
 // The last, partial round of a persistent launch leaves most CUs idle when
@@ -229,17 +231,32 @@ __device__ __forceinline__ void wait_vm_barrier()
     asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
-// Direct-to-LDS copy of 16 bytes per lane: lane i writes LDS bytes
-// [lds + 16 i, lds + 16 i + 16). Issued from inline assembly so that the
-// compiler does not treat every later LDS read as possibly aliasing the copy
-// (it would wait for all copies in flight before each read and serialize the
-// ring); completion is tracked by wait_vm_barrier's explicit vmcnt instead.
-// The copy has no register result; it only reads the address operands.
-__device__ __forceinline__ void dma16(const void *gptr, uint32_t lds)
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+
+// Raw buffer resource over n bytes at base (gfx9 layout: base, stride 0,
+// num_records, untyped), wave-uniform: it lives in scalar registers.
+__device__ __forceinline__ i32x4_t buf_rsrc(const void *base, uint32_t n)
 {
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(lds)
+    const uint64_t a = (uint64_t)(uintptr_t)base;
+    return i32x4_t{(int)(uint32_t)a, (int)((uint32_t)(a >> 32) & 0xffffu), (int)n, 0x00020000};
+}
+
+// Direct-to-LDS copy of 16 bytes per lane: lane i reads the buffer at byte
+// voff (its own) + soff (the stage's K offset, wave-uniform) and writes LDS
+// bytes [lds + 16 i, lds + 16 i + 16). Issued from inline assembly so that
+// the compiler does not treat every later LDS read as possibly aliasing the
+// copy (it would wait for all copies in flight before each read and
+// serialize the ring); completion is tracked by wait_vm_barrier's explicit
+// vmcnt instead. The copy has no register result; it only reads its
+// operands. A lane's address is one 32-bit offset, so a stage's copies cost
+// no address arithmetic in vector registers.
+__device__ __forceinline__ void dma16(i32x4_t rsrc, uint32_t voff, uint32_t soff, uint32_t lds)
+{
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, %3 offen lds" ::"v"(voff), "s"(rsrc),
+                 "s"(lds), "s"(soff)
                  : "memory", "m0");
 }
+
 
 __device__ __forceinline__ uint32_t lds_addr(const void *p) { return (uint32_t)(uintptr_t)p; }
 
@@ -331,29 +348,34 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void tiled_gemm_kernel(TiledParam
         decode_tile<BM>(p, id, n_mtiles, e, nb, row0, rows);
         const bool xtra = XT > 0 && rows > BM;  // tile-uniform
 
-        // ---- per-lane DMA source rows (rows past the tile repeat row 0; dropped later)
+        // ---- per-lane DMA sources (rows past the tile repeat row 0; dropped
+        // later) as byte offsets into a buffer resource over A, or over the
+        // expert's weights; a stage adds its K offset in a scalar register
         // logical chunk (of 8 elements) a lane copies for LDS row rr
         auto chunk_of = [&](int rr) { return (lane % CH) ^ lds_swz(rr); };
-        const __bf16 *asrc[A_INS];
+        const uint32_t krow = (uint32_t)p.K * 2u;  // bytes per row
+        const i32x4_t ra = buf_rsrc(p.A, p.a_bytes);
+        uint32_t aoff[A_INS];
 #pragma unroll
         for (int i = 0; i < A_INS; i++) {
             const int rr = RPI * (wave * A_INS + i) + drow;
             const int rc = rr < rows ? rr : 0;
-            const int64_t src = p.a_rows ? (int64_t)p.a_rows[row0 + rc] : (int64_t)(row0 + rc);
-            asrc[i] = p.A + src * p.K + kbase + chunk_of(rr) * 8;
+            const uint32_t src = p.a_rows ? (uint32_t)p.a_rows[row0 + rc] : (uint32_t)(row0 + rc);
+            aoff[i] = src * krow + (uint32_t)kbase * 2u + (uint32_t)chunk_of(rr) * 16u;
         }
         // extra rows BM + XR*wave + lane/CH, lanes below XR*CH (rows past the
         // tile repeat row BM)
-        const __bf16 *xsrc = p.A;
+        uint32_t xoff = 0;
         const bool xlane = lane < XR * CH;
         const int xrr = BM + XR * wave + (xlane ? drow : 0);
         if (XT > 0 && xtra) {
             const int rc = xrr < rows ? xrr : BM;
-            const int64_t src = p.a_rows ? (int64_t)p.a_rows[row0 + rc] : (int64_t)(row0 + rc);
-            xsrc = p.A + src * p.K + kbase + chunk_of(xrr) * 8;
+            const uint32_t src = p.a_rows ? (uint32_t)p.a_rows[row0 + rc] : (uint32_t)(row0 + rc);
+            xoff = src * krow + (uint32_t)kbase * 2u + (uint32_t)chunk_of(xrr) * 16u;
         }
-        const __bf16 *wbase = p.W + (int64_t)e * p.w_expert_stride;
-        const __bf16 *bsrc[B_INS];
+        const i32x4_t rb = buf_rsrc(p.W + (int64_t)e * p.w_expert_stride,
+                                    (uint32_t)(GATEUP ? 2 * p.N : p.N) * krow);
+        uint32_t boff[B_INS];
 #pragma unroll
         for (int i = 0; i < B_INS; i++) {
             const int rr = RPI * (wave * B_INS + i) + drow;
@@ -367,28 +389,27 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void tiled_gemm_kernel(TiledParam
                 const int n = nb * BN + rr;
                 wrow = n < p.N ? n : 0;
             }
-            bsrc[i] = wbase + (int64_t)wrow * p.K + kbase + chunk_of(rr) * 8;
+            boff[i] = (uint32_t)wrow * krow + (uint32_t)kbase * 2u + (uint32_t)chunk_of(rr) * 16u;
         }
 
         // stage kt -> LDS buffer b: every lane copies 16 bytes. Only a final
         // partial stage (K not a multiple of BK) masks lanes; they zero-fill.
         auto issue = [&](int kt, int b) {
-            const int k0 = kt * BK;
+            const uint32_t k0 = (uint32_t)(kt * BK) * 2u;
 #pragma unroll
-            for (int i = 0; i < A_INS; i++)
-                dma16(asrc[i] + k0, lds_addr(&sA[b][(wave * A_INS + i) * 64]));
+            for (int i = 0; i < A_INS; i++) dma16(ra, aoff[i], k0, lds_addr(&sA[b][(wave * A_INS + i) * 64]));
 #pragma unroll
-            for (int i = 0; i < B_INS; i++)
-                dma16(bsrc[i] + k0, lds_addr(&sB[b][(wave * B_INS + i) * 64]));
-            if (XT > 0 && xtra && xlane) dma16(xsrc + k0, lds_addr(&sA[b][(BM + XR * wave) * CH]));
+            for (int i = 0; i < B_INS; i++) dma16(rb, boff[i], k0, lds_addr(&sB[b][(wave * B_INS + i) * 64]));
+            if (XT > 0 && xtra && xlane) dma16(ra, xoff, k0, lds_addr(&sA[b][(BM + XR * wave) * CH]));
         };
         auto issue_tail = [&](int kt, int b) {
             const int k0 = kt * BK;
+            const uint32_t k0b = (uint32_t)k0 * 2u;
 #pragma unroll
             for (int i = 0; i < A_INS; i++) {
                 u32x4 *dst = &sA[b][(wave * A_INS + i) * 64];
                 if (k0 + chunk_of(RPI * (wave * A_INS + i) + drow) * 8 < Kl)
-                    dma16(asrc[i] + k0, lds_addr(dst));
+                    dma16(ra, aoff[i], k0b, lds_addr(dst));
                 else
                     dst[lane] = u32x4{0u, 0u, 0u, 0u};
             }
@@ -396,14 +417,14 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void tiled_gemm_kernel(TiledParam
             for (int i = 0; i < B_INS; i++) {
                 u32x4 *dst = &sB[b][(wave * B_INS + i) * 64];
                 if (k0 + chunk_of(RPI * (wave * B_INS + i) + drow) * 8 < Kl)
-                    dma16(bsrc[i] + k0, lds_addr(dst));
+                    dma16(rb, boff[i], k0b, lds_addr(dst));
                 else
                     dst[lane] = u32x4{0u, 0u, 0u, 0u};
             }
             if (XT > 0 && xtra && xlane) {
                 u32x4 *dst = &sA[b][(BM + XR * wave) * CH];
                 if (k0 + chunk_of(xrr) * 8 < Kl)
-                    dma16(xsrc + k0, lds_addr(dst));
+                    dma16(ra, xoff, k0b, lds_addr(dst));
                 else
                     dst[lane] = u32x4{0u, 0u, 0u, 0u};
             }
@@ -424,12 +445,29 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void tiled_gemm_kernel(TiledParam
 #pragma unroll
         for (int q = 0; q < 16; q++) accx[q] = 0.0f;
 
+        // Every fragment row is a multiple of 32 plus lane % 32, and the LDS
+        // swizzle only looks at the row's low five bits, so a fragment's
+        // address is a per-lane base (one per k-step and operand, wave part
+        // included) plus a compile-time offset (buffer, row block).
+        constexpr int KSTEPS = BK / 16;  // MFMA k-steps per stage
+        const int l32 = lane & 31;
+        auto laneoff = [&](int kk) { return l32 * CH + ((kk * 2 + (lane >> 5)) ^ lds_swz(l32)); };
+        constexpr int HWB = GATEUP ? BN / 2 / WN : BN / WN;  // B rows per wave (per half for gate_up)
+        int va[KSTEPS], vb[KSTEPS], vxa[KSTEPS], vxb[KSTEPS];
+#pragma unroll
+        for (int kk = 0; kk < KSTEPS; kk++) {
+            va[kk] = wm * (BM / WM) * CH + laneoff(kk);
+            vb[kk] = wn * HWB * CH + laneoff(kk);
+            vxa[kk] = BM * CH + laneoff(kk);
+            vxb[kk] = (xrow - l32) * CH + laneoff(kk);
+        }
+
         // copy instruction q (A rows, then B rows, then the extra rows) of stage kt into buffer b
         auto issue_one = [&](int kt, int b, int q) {
-            const int k0 = kt * BK;
-            if (q < A_INS) dma16(asrc[q] + k0, lds_addr(&sA[b][(wave * A_INS + q) * 64]));
-            else if (q < LOADS) dma16(bsrc[q - A_INS] + k0, lds_addr(&sB[b][(wave * B_INS + q - A_INS) * 64]));
-            else if (xlane) dma16(xsrc + k0, lds_addr(&sA[b][(BM + XR * wave) * CH]));
+            const uint32_t k0 = (uint32_t)(kt * BK) * 2u;
+            if (q < A_INS) dma16(ra, aoff[q], k0, lds_addr(&sA[b][(wave * A_INS + q) * 64]));
+            else if (q < LOADS) dma16(rb, boff[q - A_INS], k0, lds_addr(&sB[b][(wave * B_INS + q - A_INS) * 64]));
+            else if (xlane) dma16(ra, xoff, k0, lds_addr(&sA[b][(BM + XR * wave) * CH]));
         };
         // Consume stage buffer b. When nkt >= 0, the LX copies of stage nkt
         // into buffer nbuf are spread between the MFMAs, one copy per PER
@@ -446,36 +484,34 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void tiled_gemm_kernel(TiledParam
             constexpr int NMMA = (BK / 16) * (RM * RN + (EX ? 1 : 0));
             constexpr int PER = NMMA / LX > 0 ? NMMA / LX : 1;
             static_assert(PER * LX <= NMMA, "every copy finds an MFMA slot");
+            // with a double buffer the next stage has only this stage to land:
+            // its copies go out together, before the first fragment read
+            constexpr bool BURST = STAGES <= 2;
+            if (CP && BURST) {
+#pragma unroll
+                for (int q = 0; q < LX; q++) issue_one(nkt, nbuf, q);
+            }
+            const u32x4 *A = &sA[b][0];
+            const u32x4 *Bw = &sB[b][0];
 #pragma unroll
             for (int kk = 0; kk < BK / 16; kk++) {
                 bf16x8_t af[RM], bf[RN], ax, bx;
-                const int c = kk * 2 + (lane >> 5);
 #pragma unroll
-                for (int i = 0; i < NB; i++) {
-                    const int row = wm * (BM / WM) + i * 32 + (lane & 31);
-                    af[i] = as_bf16x8(sA[b][lds_slot(row, c)]);
-                }
+                for (int i = 0; i < NB; i++) af[i] = as_bf16x8(A[va[kk] + i * 32 * CH]);
                 if (EX) {
                     // the extra rows and this wave's B block jx for them (read
                     // again rather than picked from bf[] with a runtime index)
-                    ax = as_bf16x8(sA[b][lds_slot(BM + (lane & 31), c)]);
-                    bx = as_bf16x8(sB[b][lds_slot(xrow, c)]);
+                    ax = as_bf16x8(A[vxa[kk]]);
+                    bx = as_bf16x8(Bw[vxb[kk]]);
                 }
 #pragma unroll
                 for (int j = 0; j < RN; j++) {
                     if (NB == 0) break;
-                    int row;
-                    if (GATEUP) {
-                        constexpr int HW = BN / 2 / WN;
-                        row = (j < RN / 2) ? wn * HW + j * 32 : BN / 2 + wn * HW + (j - RN / 2) * 32;
-                    } else {
-                        row = wn * (BN / WN) + j * 32;
-                    }
-                    row += lane & 31;
-                    bf[j] = as_bf16x8(sB[b][lds_slot(row, c)]);
+                    const int row = GATEUP ? ((j < RN / 2) ? j * 32 : BN / 2 + (j - RN / 2) * 32) : j * 32;
+                    bf[j] = as_bf16x8(Bw[vb[kk] + row * CH]);
                 }
                 auto slot = [&](int mi) {  // compile-time after unrolling
-                    if (CP && (mi + 1) % PER == 0 && (mi + 1) / PER - 1 < LX)
+                    if (CP && !BURST && (mi + 1) % PER == 0 && (mi + 1) / PER - 1 < LX)
                         issue_one(nkt, nbuf, (mi + 1) / PER - 1);
                 };
 #pragma unroll
@@ -710,6 +746,7 @@ TiledParams make_params(const GemmProblem &g, int NB)
     t.part = nullptr;
     t.G = 0;
     t.cap = 0;
+    t.a_bytes = (uint32_t)std::min<int64_t>(g.a_rows_total * g.K * 2, 0xFFFFFFFFll);
     return t;
 }
 

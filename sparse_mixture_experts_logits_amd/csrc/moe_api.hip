@@ -434,6 +434,7 @@ static int forward_impl(const void *hidden, const void *router_w, const void *ga
     gu.wts = direct ? ws.wts : nullptr;
     gu.k = k;
     gu.cus = cus;
+    gu.a_rows_total = T;
 
     moe::GemmProblem dn = gu;
     dn.A = ws.h;
@@ -447,6 +448,7 @@ static int forward_impl(const void *hidden, const void *router_w, const void *ga
     dn.C = ws.slot;
     dn.c_rows = ws.perm;
     dn.c_scale = ws.row_weight;
+    dn.a_rows_total = T * k;
 
     if (f32) rc = check(moe::launch_gate_up_f32(gu, st), "gate_up f32");
     else if (skinny) rc = check(moe::launch_gate_up_skinny(gu, st), "gate_up skinny");
@@ -474,6 +476,7 @@ static int forward_impl(const void *hidden, const void *router_w, const void *ga
         sg.part = ws.part;  // free again: the routed launches have finished with it
         sg.ids = nullptr;
         sg.wts = nullptr;
+        sg.a_rows_total = T;
         moe::GemmProblem sd = sg;
         sd.A = ws.sh_h;
         sd.W = opts->shared_down;

@@ -157,6 +157,7 @@ struct GemmProblem {
     const float *wts = nullptr;
     int k = 0;
     int cus = 0;             // compute units of the device (persistent grids)
+    int64_t a_rows_total = 0;  // rows of A (gate_up: tokens; down: assignments or tokens)
 };
 
 // Largest T*k for which the weight-streaming kernels route directly from the ids.

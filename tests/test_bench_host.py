@@ -74,6 +74,7 @@ def test_write_traffic_scales_counters_by_the_copy_calibration(tmp_path, monkeyp
     src.mkdir(parents=True)
     for n in ("gemm_skinny.hip", "gemm_tiled.hip", "moe_internal.h"):
         (src / n).write_text("int x;\n")
+    # a change to the other schedule's kernel leaves the figure valid (checked below)
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
     k = "void skinny_gemm_kernel<true, 0, true>(p)"
     _pmc(tmp_path / "f", [(k, "FETCH_SIZE", 1000.0), (k, "FETCH_SIZE", 1200.0), ("other", "FETCH_SIZE", 9e9)])
@@ -88,6 +89,8 @@ def test_write_traffic_scales_counters_by_the_copy_calibration(tmp_path, monkeyp
     assert d["launches"] == [2, 2]
     assert d["copy_calibration"]["fetch_factor"] == 2.0 and d["copy_calibration"]["write_factor"] == 1.0
     assert d["hbm_bytes_per_launch"] == 1100.0 * 1024 * 2 + 20.0 * 1024
+    assert bench.measured_traffic("gate_up", "unit") == d["hbm_bytes_per_launch"]
+    (src / "gemm_tiled.hip").write_text("int z;\n")  # another schedule's kernel: still valid
     assert bench.measured_traffic("gate_up", "unit") == d["hbm_bytes_per_launch"]
     (src / "gemm_skinny.hip").write_text("int y;\n")  # the code changed: the figure no longer applies
     assert bench.measured_traffic("gate_up", "unit") is None
