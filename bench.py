@@ -13,7 +13,8 @@ selected experts' weights. Every other workload is measured in the same run
 with the same steps and warm-up and nested in the line under its own name:
 ``phimoe_prefill`` (T=4096), ``instella_fine`` (T=2048, 64 experts, top-6,
 scale 2.5, two shared experts), ``phimoe_skewed`` (T=16384, router bias: half
-of all assignments to one expert) and ``tiny_f32`` (fp32), plus the decode
+of all assignments to one expert), ``phimoe_skewed_small`` (the same bias on a
+256-token batch: the mixed schedule) and ``tiny_f32`` (fp32), plus the decode
 step with FP8 (E4M3, per-row scaled) and MXFP4 (E2M1, E8M0 scale per 32)
 expert weights under ``decode_fp8`` and ``decode_mxfp4`` (different weight
 storage, so never the headline value). Each carries a ``roofline`` of its
@@ -459,13 +460,17 @@ _DEV_CACHE = {}
 
 def schedule_of(wl, weights="bf16"):
     """Which expert-GEMM kernels the library runs for this workload (its
-    default rule, for reporting): fp32 VALU kernels, the weight-streaming
-    kernels for low-precision weights or about 32 rows per expert or fewer,
-    else the large-M tiled kernels."""
+    default rule, for reporting): fp32 VALU kernels; the weight-streaming
+    kernels for low-precision weights, or about 32 rows per expert or fewer
+    with at most 32 tokens; "mixed" (streaming plus tiled for experts past 32
+    rows) for about 32 rows per expert or fewer with more tokens; else the
+    large-M tiled kernels."""
     if wl.dtype == "f32":
         return "f32"
-    if weights != "bf16" or wl.T * wl.k <= 32 * wl.E:
+    if weights != "bf16":
         return "skinny"
+    if wl.T * wl.k <= 32 * wl.E:
+        return "skinny" if wl.T <= 32 else "mixed"
     return "tiled"
 
 
@@ -582,7 +587,7 @@ def cpu_baseline(res, max_tokens, min_seconds=10.0):
 # ------------------------------------------------------------------ main
 
 # PhiMoE-shaped workloads first: they share one set of device weights
-NESTED = ("phimoe_prefill", "phimoe_skewed", "instella_fine", "tiny_f32")
+NESTED = ("phimoe_prefill", "phimoe_skewed", "phimoe_skewed_small", "instella_fine", "tiny_f32")
 
 
 def nested_line(res):

@@ -263,7 +263,7 @@ int moe_forward(const void *hidden, const void *router_w, const void *gate_up, c
                 void *out);
 
 /* Scratch bytes that moe_forward_noalloc holds on each GPU it runs on. */
-#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
 
 /*
  * moe_forward without a caller workspace, for callers that cannot allocate
@@ -276,8 +276,9 @@ int moe_forward(const void *hidden, const void *router_w, const void *gate_up, c
  *     held until the process ends;
  *   - sizes whose workspace (moe_workspace_bytes) exceeds that array are
  *     rejected with MOE_ERR_UNSUPPORTED (the PhiMoE decode step, T = 32,
- *     H = 4096, I = 6400, E = 16, k = 2, needs about 2 MB; large-M tiled
- *     calls need more: use moe_forward for those);
+ *     H = 4096, I = 6400, E = 16, k = 2, needs about 2 MB, a 256-token
+ *     batch of the same layer about 91 MB; large prefill calls need more:
+ *     use moe_forward for those);
  *   - no call allocates or frees memory; the first call on a device looks up
  *     the array's address on that device once (hipGetSymbolAddress, with
  *     that device current) and keeps it for later calls;

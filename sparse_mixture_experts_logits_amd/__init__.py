@@ -33,7 +33,7 @@ SCORE_SIGMOID = 1
 SCORE_SPARSEMIXER = 2
 EXPORTS = ("moe_opts_init", "moe_workspace_bytes", "moe_forward", "moe_forward_noalloc", "moe_quantize_fp8_rows",
            "moe_quantize_mxfp4_rows", "moe_last_error")
-NOALLOC_SCRATCH_BYTES = 64 << 20  # MOE_NOALLOC_SCRATCH_BYTES
+NOALLOC_SCRATCH_BYTES = 128 << 20  # MOE_NOALLOC_SCRATCH_BYTES
 STAGES = ("router", "scan", "permute", "gate_up", "down", "shared_gate_up", "shared_down", "combine")
 STAGE_EVENTS = len(STAGES) + 1
 

@@ -132,6 +132,7 @@ struct SkinnyParams {
     const float *wts;
     int k;
     int TK;
+    int max_rows;  // > 0: experts with more rows are left to the tiled kernel
 };
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8_t, v); }
@@ -200,7 +201,7 @@ __device__ __forceinline__ int tswz(int r, int c) { return r * 16 + (c ^ (r & 15
 // 3 MXFP4 whose rows of block scales start 4-byte aligned (K % 128 == 0), so
 // a lane reads one row's 16 scales of a step with one 16-byte load.
 // DIRECT: route straight from the top-k ids (see SkinnyParams).
-template <bool GATEUP, int FMT, bool DIRECT>
+template <bool GATEUP, int FMT, bool DIRECT, int G>
 __global__ __launch_bounds__(skinny_waves(GATEUP, FMT) * 64,
                              FMT >= 2 ? MOE_SKINNY_W4_OCC : FMT ? MOE_SKINNY_W8_OCC : MOE_SKINNY_BF_OCC) void skinny_gemm_kernel(SkinnyParams p)
 {
@@ -260,7 +261,9 @@ __global__ __launch_bounds__(skinny_waves(GATEUP, FMT) * 64,
         M = p.counts ? p.counts[e] : p.dense_rows;
         row0 = p.counts ? p.offsets[e] : 0;
     }
-    if (M <= 0) return;  // workgroup-uniform
+    // workgroup-uniform: no rows, or more than this launch serves (those
+    // experts run on the large-M tiled kernel)
+    if (M <= 0 || (p.max_rows > 0 && M > p.max_rows)) return;
     const int n0 = blockIdx.x * skinny_cols(GATEUP, FMT);
     const int lgrp = lane >> 4;
     const int l16 = lane & 15;
@@ -293,152 +296,10 @@ __global__ __launch_bounds__(skinny_waves(GATEUP, FMT) * 64,
     u32x4 *tile = s_w[wave];
     const u32x4 zero = {0u, 0u, 0u, 0u};
 
-    for (int pass = 0; pass < M; pass += 16) {
-        const int q = pass + l16;
-        const bool xv = q < M;
-        const int qc = xv ? q : M - 1;
-        const int64_t src = (GATEUP && DIRECT) ? (int64_t)s_rows[qc]
-                            : p.a_rows ? (int64_t)p.a_rows[row0 + qc] : (int64_t)(row0 + qc);
-        const __bf16 *xp = p.A + src * p.K;  // the token's row; lanes add their chunk offsets
-
-        f32x4_t acc[NW];
-#pragma unroll
-        for (int w = 0; w < NW; w++) acc[w] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-        u32x4 st[PD][NL];
-        uint32_t bs[PD][FMT == 2 ? NL : 1];  // MXFP4 block scale bytes of the staged chunks
-        u32x4 sc[PD];                        // MXFP4, aligned scale rows: this lane's row's 16 scales
-        u32x4 xs[PD][XF];
-        // weights of step kb and the token fragments it needs: MFMA j takes
-        // chunk 4j + lgrp (bf16: 8 elements; E4M3: 16 elements, as two MFMAs
-        // over its halves, fragment 2j + half; MXFP4: 32 elements, as four
-        // MFMAs over its words, fragment 4j + word)
-        // Loads are unconditional and whole 16-byte loads: a chunk past K (or
-        // a token past the expert's rows) reads the row's first chunk instead,
-        // and the consumer zeroes it. With no branches or selects between a
-        // load and its use, the compiler's wait counts stay exact and every
-        // load of a step is in flight together.
-        // (plain '&' and masks below, not '&&' or '?:', so that no branch is formed)
-        auto w_ok = [&](int kb) { return kb * KS + l16 * EPC < p.K; };
-        auto x_ok = [&](int kb, int f) { return xv & (kb * KS + (4 * (f / FPC) + lgrp) * EPC < p.K); };
-        // (a chunk that is not read falls back to the row's first chunk, so
-        // every address stays inside a row that exists)
-        auto gload_w = [&](int kb, int b) {
-            const uint32_t okm = 0u - (uint32_t)w_ok(kb);
-            const uint32_t kbytes = wbytes((uint32_t)(kb * KS + l16 * EPC)) & okm;
-            const uint32_t lw = wbytes((uint32_t)lgrp * (uint32_t)p.K) + kbytes;
-            const uint32_t ls = (uint32_t)lgrp * (uint32_t)(p.K / 32) + ((uint32_t)(kb * 16 + l16) & okm);
-#pragma unroll
-            for (int i = 0; i < NL; i++) {
-                st[b][i] = buffer_load_nt16(rw, lw, wbytes(urow(i) * (uint32_t)p.K));
-                if (FMT == 2) bs[b][i] = __builtin_amdgcn_raw_buffer_load_b8(rs, ls, urow(i) * (uint32_t)(p.K / 32), 0);
-            }
-            if (SC4) {
-                // lane r (mod NR) reads tile row r's 16 scales of the step (a
-                // row past N reads row N - 1; its columns are never written)
-                constexpr int half = GATEUP ? NR / 2 : NR;
-                const int r = lane % NR;
-                const int n = min(n0 + r % half, p.N - 1);
-                const uint32_t grow = (GATEUP && r >= half) ? p.N + n : n;
-                const u32x4v_t v = __builtin_amdgcn_raw_buffer_load_b128(rs, grow * (uint32_t)(p.K / 32) + kb * 16, 0, 0);
-                sc[b] = u32x4{v.x, v.y, v.z, v.w};
-            }
-        };
-        auto gload_x = [&](int kb, int b) {
-#pragma unroll
-            for (int f = 0; f < XF; f++) {
-                // fragment f: chunk 4 * (f / FPC) + lgrp, its 8 elements (f % FPC)
-                const int off = (f / FPC) * 4 * EPC + (f % FPC) * 8;
-                xs[b][f] = load16(xp + ((kb * KS + lgrp * EPC + off) & (0 - (int)x_ok(kb, f))));
-            }
-        };
-        // One reduction step from staging buffer b (a compile-time index after
-        // unrolling). The next weights (from HBM, the long wait) are requested
-        // as soon as this step's are in LDS; the next token fragments (L2
-        // hits) only after this step's MFMAs have consumed the current ones, so
-        // they need no second register copy and more waves fit on a SIMD.
-        auto step = [&](int kb, int b) {
-            const bool okw = w_ok(kb);
-#pragma unroll
-            for (int i = 0; i < NL; i++) tile[tswz(4 * i + lgrp, l16)] = keep_if(okw, st[b][i]);
-            if (FMT == 2) {
-                uint8_t *sb = reinterpret_cast<uint8_t *>(s_bs[W4 ? wave : 0]);
-#pragma unroll
-                for (int i = 0; i < NL; i++) sb[(4 * i + lgrp) * 16 + l16] = (uint8_t)bs[b][i];
-            }
-            if (SC4) {
-                // scales of blocks past K (a ragged last step) read the next
-                // row's; they become 127 (factor 1) so that the zero weights
-                // there stay zero whatever those bytes hold
-                const int nb = p.K / 32 - kb * 16;  // blocks of this step inside K
-                auto keep = [&](uint32_t v, int d) {
-                    const int nv = nb - 4 * d;
-                    const uint32_t m = nv >= 4 ? 0xFFFFFFFFu : nv <= 0 ? 0u : (1u << (8 * nv)) - 1u;
-                    return (v & m) | (0x7F7F7F7Fu & ~m);
-                };
-                if (lane < NR)
-                    reinterpret_cast<u32x4 *>(s_bs[W4 ? wave : 0])[lane] =
-                        u32x4{keep(sc[b].x, 0), keep(sc[b].y, 1), keep(sc[b].z, 2), keep(sc[b].w, 3)};
-            }
-            const bool more = kb + PD < kb_hi;
-            if (more) gload_w(kb + PD, b);
-            u32x4 xb[XF];
-#pragma unroll
-            for (int f = 0; f < XF; f++) xb[f] = W4 ? xs[b][f] : keep_if(x_ok(kb, f), xs[b][f]);
-#pragma unroll
-            for (int j = 0; j < 4; j++) {
-#pragma unroll
-                for (int w = 0; w < NW; w++) {
-                    const u32x4 a = tile[tswz(16 * w + l16, 4 * j + lgrp)];
-                    if (W4) {
-                        const uint8_t *sb = reinterpret_cast<const uint8_t *>(s_bs[W4 ? wave : 0]);
-                        const float sf = e8m0_factor(sb[(16 * w + l16) * 16 + 4 * j + lgrp]);
-                        acc[w] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(e2m1x8_to_bf16(a.x, sf)),
-                                                                         as_bf16x8(xb[4 * j]), acc[w], 0, 0, 0);
-                        acc[w] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(e2m1x8_to_bf16(a.y, sf)),
-                                                                         as_bf16x8(xb[4 * j + 1]), acc[w], 0, 0, 0);
-                        acc[w] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(e2m1x8_to_bf16(a.z, sf)),
-                                                                         as_bf16x8(xb[4 * j + 2]), acc[w], 0, 0, 0);
-                        acc[w] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(e2m1x8_to_bf16(a.w, sf)),
-                                                                         as_bf16x8(xb[4 * j + 3]), acc[w], 0, 0, 0);
-                    } else if (W8) {
-                        acc[w] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(e4m3x8_to_bf16(a.x, a.y)),
-                                                                         as_bf16x8(xb[2 * j]), acc[w], 0, 0, 0);
-                        acc[w] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(e4m3x8_to_bf16(a.z, a.w)),
-                                                                         as_bf16x8(xb[2 * j + 1]), acc[w], 0, 0, 0);
-                    } else {
-                        acc[w] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(xb[j]), acc[w], 0, 0, 0);
-                    }
-                }
-                // MXFP4: convert each chunk just before its MFMAs; hoisting
-                // every conversion of a step would need 256 more registers
-                if (W4) __builtin_amdgcn_sched_barrier(0);
-            }
-            if (more) gload_x(kb + PD, b);
-        };
-#pragma unroll
-        for (int b = 0; b < PD; b++)
-            if (kb_lo + b < kb_hi) {
-                gload_w(kb_lo + b, b);
-                gload_x(kb_lo + b, b);
-            }
-        int kb = kb_lo;
-        for (; kb + PD <= kb_hi; kb += PD) {
-#pragma unroll
-            for (int b = 0; b < PD; b++) step(kb + b, b);
-        }
-#pragma unroll
-        for (int b = 0; b < PD - 1; b++)
-            if (kb + b < kb_hi) step(kb + b, b);
-
-        // ---- split-K reduction across the waves, in wave order (each wave's
-        // partial sums go to its own tile, which it no longer reads)
-        static_assert(NW * 64 * sizeof(f32x4_t) <= NR * 16 * sizeof(u32x4), "partials fit the tile");
-        auto red = [&](int v) { return reinterpret_cast<f32x4_t *>(s_w[v]); };
-#pragma unroll
-        for (int w = 0; w < NW; w++) red(wave)[w * 64 + lane] = acc[w];
-        __syncthreads();
-        if (wave == 0) {
+    // wave 0: sum the waves' partials of one token group (rows q, valid xv)
+    // and write them out
+    auto red = [&](int v) { return reinterpret_cast<f32x4_t *>(s_w[v]); };
+    auto epilogue = [&](const int q, const bool xv) {
             f32x4_t sm[NW];
 #pragma unroll
             for (int w = 0; w < NW; w++) {
@@ -490,6 +351,182 @@ __global__ __launch_bounds__(skinny_waves(GATEUP, FMT) * 64,
                     }
                 }
             }
+    };
+
+    // G groups of 16 tokens per pass share every weight step, so an expert
+    // with up to 16 * G rows streams its weights exactly once; a group with
+    // no rows skips its loads and MFMAs (pass-uniform).
+    for (int pass = 0; pass < M; pass += 16 * G) {
+        bool gon[G];
+        int q[G];
+        bool xv[G];
+        const __bf16 *xp[G];
+#pragma unroll
+        for (int g = 0; g < G; g++) {
+            gon[g] = pass + 16 * g < M;
+            q[g] = pass + 16 * g + l16;
+            xv[g] = q[g] < M;
+            const int qc = xv[g] ? q[g] : M - 1;
+            const int64_t src = (GATEUP && DIRECT) ? (int64_t)s_rows[qc]
+                                : p.a_rows ? (int64_t)p.a_rows[row0 + qc] : (int64_t)(row0 + qc);
+            xp[g] = p.A + src * p.K;  // the token's row; lanes add their chunk offsets
+        }
+
+        f32x4_t acc[G][NW];
+#pragma unroll
+        for (int g = 0; g < G; g++)
+#pragma unroll
+            for (int w = 0; w < NW; w++) acc[g][w] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+        u32x4 st[PD][NL];
+        uint32_t bs[PD][FMT == 2 ? NL : 1];  // MXFP4 block scale bytes of the staged chunks
+        u32x4 sc[PD];                        // MXFP4, aligned scale rows: this lane's row's 16 scales
+        u32x4 xs[G][PD][XF];
+        // weights of step kb and the token fragments it needs: MFMA j takes
+        // chunk 4j + lgrp (bf16: 8 elements; E4M3: 16 elements, as two MFMAs
+        // over its halves, fragment 2j + half; MXFP4: 32 elements, as four
+        // MFMAs over its words, fragment 4j + word)
+        // Loads are unconditional and whole 16-byte loads: a chunk past K (or
+        // a token past the expert's rows) reads the row's first chunk instead,
+        // and the consumer zeroes it. With no branches or selects between a
+        // load and its use, the compiler's wait counts stay exact and every
+        // load of a step is in flight together.
+        // (plain '&' and masks below, not '&&' or '?:', so that no branch is formed)
+        auto w_ok = [&](int kb) { return kb * KS + l16 * EPC < p.K; };
+        auto x_ok = [&](int kb, int f, int g) { return xv[g] & (kb * KS + (4 * (f / FPC) + lgrp) * EPC < p.K); };
+        // (a chunk that is not read falls back to the row's first chunk, so
+        // every address stays inside a row that exists)
+        auto gload_w = [&](int kb, int b) {
+            const uint32_t okm = 0u - (uint32_t)w_ok(kb);
+            const uint32_t kbytes = wbytes((uint32_t)(kb * KS + l16 * EPC)) & okm;
+            const uint32_t lw = wbytes((uint32_t)lgrp * (uint32_t)p.K) + kbytes;
+            const uint32_t ls = (uint32_t)lgrp * (uint32_t)(p.K / 32) + ((uint32_t)(kb * 16 + l16) & okm);
+#pragma unroll
+            for (int i = 0; i < NL; i++) {
+                st[b][i] = buffer_load_nt16(rw, lw, wbytes(urow(i) * (uint32_t)p.K));
+                if (FMT == 2) bs[b][i] = __builtin_amdgcn_raw_buffer_load_b8(rs, ls, urow(i) * (uint32_t)(p.K / 32), 0);
+            }
+            if (SC4) {
+                // lane r (mod NR) reads tile row r's 16 scales of the step (a
+                // row past N reads row N - 1; its columns are never written)
+                constexpr int half = GATEUP ? NR / 2 : NR;
+                const int r = lane % NR;
+                const int n = min(n0 + r % half, p.N - 1);
+                const uint32_t grow = (GATEUP && r >= half) ? p.N + n : n;
+                const u32x4v_t v = __builtin_amdgcn_raw_buffer_load_b128(rs, grow * (uint32_t)(p.K / 32) + kb * 16, 0, 0);
+                sc[b] = u32x4{v.x, v.y, v.z, v.w};
+            }
+        };
+        auto gload_x = [&](int kb, int b) {
+#pragma unroll
+            for (int g = 0; g < G; g++) {
+                if (g > 0 && !gon[g]) break;
+#pragma unroll
+                for (int f = 0; f < XF; f++) {
+                    // fragment f: chunk 4 * (f / FPC) + lgrp, its 8 elements (f % FPC)
+                    const int off = (f / FPC) * 4 * EPC + (f % FPC) * 8;
+                    xs[g][b][f] = load16(xp[g] + ((kb * KS + lgrp * EPC + off) & (0 - (int)x_ok(kb, f, g))));
+                }
+            }
+        };
+        // One reduction step from staging buffer b (a compile-time index after
+        // unrolling). The next weights (from HBM, the long wait) are requested
+        // as soon as this step's are in LDS; the next token fragments (L2
+        // hits) only after this step's MFMAs have consumed the current ones, so
+        // they need no second register copy and more waves fit on a SIMD.
+        auto step = [&](int kb, int b) {
+            const bool okw = w_ok(kb);
+#pragma unroll
+            for (int i = 0; i < NL; i++) tile[tswz(4 * i + lgrp, l16)] = keep_if(okw, st[b][i]);
+            if (FMT == 2) {
+                uint8_t *sb = reinterpret_cast<uint8_t *>(s_bs[W4 ? wave : 0]);
+#pragma unroll
+                for (int i = 0; i < NL; i++) sb[(4 * i + lgrp) * 16 + l16] = (uint8_t)bs[b][i];
+            }
+            if (SC4) {
+                // scales of blocks past K (a ragged last step) read the next
+                // row's; they become 127 (factor 1) so that the zero weights
+                // there stay zero whatever those bytes hold
+                const int nb = p.K / 32 - kb * 16;  // blocks of this step inside K
+                auto keep = [&](uint32_t v, int d) {
+                    const int nv = nb - 4 * d;
+                    const uint32_t m = nv >= 4 ? 0xFFFFFFFFu : nv <= 0 ? 0u : (1u << (8 * nv)) - 1u;
+                    return (v & m) | (0x7F7F7F7Fu & ~m);
+                };
+                if (lane < NR)
+                    reinterpret_cast<u32x4 *>(s_bs[W4 ? wave : 0])[lane] =
+                        u32x4{keep(sc[b].x, 0), keep(sc[b].y, 1), keep(sc[b].z, 2), keep(sc[b].w, 3)};
+            }
+            const bool more = kb + PD < kb_hi;
+            if (more) gload_w(kb + PD, b);
+            u32x4 xb[G][XF];
+#pragma unroll
+            for (int g = 0; g < G; g++)
+#pragma unroll
+                for (int f = 0; f < XF; f++) xb[g][f] = W4 ? xs[g][b][f] : keep_if(x_ok(kb, f, g), xs[g][b][f]);
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+#pragma unroll
+                for (int w = 0; w < NW; w++) {
+                    const u32x4 a = tile[tswz(16 * w + l16, 4 * j + lgrp)];
+                    // this chunk's weights as bf16 MFMA fragments, shared by every token group
+                    constexpr int NF = W4 ? 4 : W8 ? 2 : 1;
+                    bf16x8_t wf[NF];
+                    if (W4) {
+                        const uint8_t *sb = reinterpret_cast<const uint8_t *>(s_bs[W4 ? wave : 0]);
+                        const float sf = e8m0_factor(sb[(16 * w + l16) * 16 + 4 * j + lgrp]);
+                        wf[0] = as_bf16x8(e2m1x8_to_bf16(a.x, sf));
+                        wf[NF > 1 ? 1 : 0] = as_bf16x8(e2m1x8_to_bf16(a.y, sf));
+                        wf[NF > 2 ? 2 : 0] = as_bf16x8(e2m1x8_to_bf16(a.z, sf));
+                        wf[NF > 3 ? 3 : 0] = as_bf16x8(e2m1x8_to_bf16(a.w, sf));
+                    } else if (W8) {
+                        wf[0] = as_bf16x8(e4m3x8_to_bf16(a.x, a.y));
+                        wf[NF > 1 ? 1 : 0] = as_bf16x8(e4m3x8_to_bf16(a.z, a.w));
+                    } else {
+                        wf[0] = as_bf16x8(a);
+                    }
+#pragma unroll
+                    for (int g = 0; g < G; g++) {
+                        if (g > 0 && !gon[g]) break;
+#pragma unroll
+                        for (int h = 0; h < NF; h++)
+                            acc[g][w] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[h], as_bf16x8(xb[g][NF * j + h]),
+                                                                                acc[g][w], 0, 0, 0);
+                    }
+                }
+                // MXFP4: convert each chunk just before its MFMAs; hoisting
+                // every conversion of a step would need 256 more registers
+                if (W4) __builtin_amdgcn_sched_barrier(0);
+            }
+            if (more) gload_x(kb + PD, b);
+        };
+#pragma unroll
+        for (int b = 0; b < PD; b++)
+            if (kb_lo + b < kb_hi) {
+                gload_w(kb_lo + b, b);
+                gload_x(kb_lo + b, b);
+            }
+        int kb = kb_lo;
+        for (; kb + PD <= kb_hi; kb += PD) {
+#pragma unroll
+            for (int b = 0; b < PD; b++) step(kb + b, b);
+        }
+#pragma unroll
+        for (int b = 0; b < PD - 1; b++)
+            if (kb + b < kb_hi) step(kb + b, b);
+
+        // ---- split-K reduction across the waves, in wave order (each wave's
+        // partial sums go to its own tile, which it no longer reads), one
+        // token group at a time
+        static_assert(NW * 64 * sizeof(f32x4_t) <= NR * 16 * sizeof(u32x4), "partials fit the tile");
+#pragma unroll
+        for (int g = 0; g < G; g++) {
+            if (g > 0 && !gon[g]) break;
+            if (g > 0) __syncthreads();  // wave 0 is done with the previous group's partials
+#pragma unroll
+            for (int w = 0; w < NW; w++) red(wave)[w * 64 + lane] = acc[g][w];
+            __syncthreads();
+            if (wave == 0) epilogue(q[g], xv[g]);
         }
         __syncthreads();
     }
@@ -517,6 +554,7 @@ SkinnyParams make_params(const GemmProblem &g)
     s.wts = direct ? g.wts : nullptr;
     s.k = g.k;
     s.TK = (int)g.total_rows;
+    s.max_rows = g.dense_rows > 0 ? 0 : g.skinny_max_rows;
     return s;
 }
 
@@ -524,12 +562,21 @@ SkinnyParams make_params(const GemmProblem &g)
 
 namespace {
 
+// Token groups per pass: one when no expert can have more than 16 rows
+// (max_rows, the host's bound), else two, so that an expert with up to 32
+// rows streams its weights once (bf16 weights; the FP8 and MXFP4 variants
+// keep one group: a second would not fit their registers).
 template <bool GATEUP, int FMT>
-void launch_fmt(dim3 grid, const SkinnyParams &s, hipStream_t st)
+void launch_fmt(dim3 grid, const SkinnyParams &s, int max_rows, hipStream_t st)
 {
     const dim3 block(skinny_waves(GATEUP, FMT) * 64);
-    if (s.ids) hipLaunchKernelGGL((skinny_gemm_kernel<GATEUP, FMT, true>), grid, block, 0, st, s);
-    else hipLaunchKernelGGL((skinny_gemm_kernel<GATEUP, FMT, false>), grid, block, 0, st, s);
+    if (FMT != 0 || max_rows <= 16) {  // the low-precision formats keep one group (register budget)
+        if (s.ids) hipLaunchKernelGGL((skinny_gemm_kernel<GATEUP, FMT, true, 1>), grid, block, 0, st, s);
+        else hipLaunchKernelGGL((skinny_gemm_kernel<GATEUP, FMT, false, 1>), grid, block, 0, st, s);
+    } else {
+        if (s.ids) hipLaunchKernelGGL((skinny_gemm_kernel<GATEUP, FMT, true, 2>), grid, block, 0, st, s);
+        else hipLaunchKernelGGL((skinny_gemm_kernel<GATEUP, FMT, false, 2>), grid, block, 0, st, s);
+    }
 }
 
 template <bool GATEUP>
@@ -542,11 +589,17 @@ hipError_t launch_skinny(const GemmProblem &g, hipStream_t st)
     const int fmt = g.w_bscale ? (sc4 ? 3 : 2) : g.w_scale ? 1 : 0;
     const int cols = skinny_cols(GATEUP, fmt);
     const dim3 grid((unsigned)((g.N + cols - 1) / cols), g.dense_rows > 0 ? 1u : (unsigned)g.E);
+    // most rows one expert can hold: every row of a dense problem, at most
+    // one per token otherwise (a token's k experts are distinct), and no
+    // more than the launch serves
+    int64_t mr = g.dense_rows > 0 ? g.dense_rows : g.total_rows / (g.k > 0 ? g.k : 1);
+    if (s.max_rows > 0 && mr > s.max_rows) mr = s.max_rows;
+    const int max_rows = (int)(mr < (1 << 30) ? mr : (1 << 30));
     switch (fmt) {
-    case 3: launch_fmt<GATEUP, 3>(grid, s, st); break;
-    case 2: launch_fmt<GATEUP, 2>(grid, s, st); break;
-    case 1: launch_fmt<GATEUP, 1>(grid, s, st); break;
-    default: launch_fmt<GATEUP, 0>(grid, s, st); break;
+    case 3: launch_fmt<GATEUP, 3>(grid, s, max_rows, st); break;
+    case 2: launch_fmt<GATEUP, 2>(grid, s, max_rows, st); break;
+    case 1: launch_fmt<GATEUP, 1>(grid, s, max_rows, st); break;
+    default: launch_fmt<GATEUP, 0>(grid, s, max_rows, st); break;
     }
     return hipGetLastError();
 }

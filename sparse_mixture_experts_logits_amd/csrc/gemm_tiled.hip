@@ -14,9 +14,10 @@
 //   * down: the epilogue multiplies each row by its routing weight and
 //     writes it to that assignment's slot in token order (the weighted
 //     un-permute); a later pass sums the k slots of each token in order.
-//   * tiles are visited expert-major, then N-block, then M-tile, and each
-//     XCD takes a contiguous run of tile ids per round, so the M-tiles that
-//     share an expert's weight block run together on one XCD's L2;
+//   * tiles are visited expert-major, then in bands of a few M-tiles that
+//     run through every N-block, and each XCD takes a contiguous run of tile
+//     ids per round, so the tiles running together on one XCD share both
+//     their token rows and their weight blocks through its L2;
 //   * an expert's last few rows ride in its previous tile (XT below) and the
 //     tiles of a short last round are split along K (SplitPlan below), so
 //     neither a handful of rows nor a handful of tiles holds the launch.
@@ -96,8 +97,29 @@ __device__ __forceinline__ SplitPlan split_plan(int total, int G, int cap, int n
     return sp;
 }
 
-// tile id -> (expert, N-block, first row, rows); M-tiles of one expert are
-// consecutive within each N-block
+#ifndef MOE_TILED_BAND
+#define MOE_TILED_BAND 8
+#endif
+// Tile order inside an expert (or the dense problem): its M-tiles are taken
+// in bands of BAND; a band runs through every N-block with its M-tiles
+// innermost. Each XCD takes a contiguous run of tile ids per round (see the
+// persistent loop), so the run covers a few M-tiles times several N-blocks
+// and both the token rows and the weight blocks it streams are shared
+// through that XCD's L2, instead of one operand being fetched anew by every
+// tile. Returns the M-tile index and the N-block of local tile id `local`
+// among nte M-tiles and NB N-blocks.
+__device__ __forceinline__ void band_order(int local, int nte, int NB, int &mt, int &nb)
+{
+    constexpr int BAND = MOE_TILED_BAND;
+    const int band = local / (BAND * NB);
+    const int mbase = band * BAND;
+    const int sm = min(BAND, nte - mbase);  // M-tiles in this band (the last may be short)
+    const int within = local - band * BAND * NB;
+    nb = within / sm;
+    mt = mbase + (within - nb * sm);
+}
+
+// tile id -> (expert, N-block, first row, rows)
 template <int BM>
 __device__ __forceinline__ void decode_tile(const TiledParams &p, int id, int n_mtiles, int &e, int &nb, int &row0,
                                             int &rows)
@@ -110,16 +132,15 @@ __device__ __forceinline__ void decode_tile(const TiledParams &p, int id, int n_
             if (s_ts[mid] * p.NB <= id) lo = mid; else hi = mid;
         }
         e = lo;
-        const int nte = s_ts[e + 1] - s_ts[e];
-        const int local = id - s_ts[e] * p.NB;
-        nb = local / nte;
-        const MTile t = p.tiles[s_ts[e] + (local - nb * nte)];
+        int mt;
+        band_order(id - s_ts[e] * p.NB, s_ts[e + 1] - s_ts[e], p.NB, mt, nb);
+        const MTile t = p.tiles[s_ts[e] + mt];
         row0 = t.row0;
         rows = t.rows;
     } else {
         e = 0;
-        nb = id / n_mtiles;
-        const int mt = id - nb * n_mtiles;
+        int mt;
+        band_order(id, n_mtiles, p.NB, mt, nb);
         row0 = mt * BM;
         rows = min(BM, p.dense_rows - row0);
     }

@@ -112,6 +112,10 @@ int check_shape(int64_t T, int64_t H, int64_t I, int64_t E, int32_t k, const moe
                 return fail(MOE_ERR_UNSUPPORTED, "MXFP4 expert weights need H and I multiples of 32");
             if (opts->flags & MOE_FLAG_FORCE_TILED)
                 return fail(MOE_ERR_UNSUPPORTED, "MXFP4 expert weights run on the weight-streaming kernels only");
+            if (T * (int64_t)k > 32 * E)
+                return fail(MOE_ERR_UNSUPPORTED, "MXFP4 expert weights serve batches of T*k <= 32*E (the "
+                                                 "weight-streaming schedule); T*k = %lld",
+                            (long long)(T * k));
         }
         if (opts->weight_format == MOE_WEIGHTS_FP8_E4M3) {
             if (dtype != MOE_BF16)
@@ -120,20 +124,34 @@ int check_shape(int64_t T, int64_t H, int64_t I, int64_t E, int32_t k, const moe
                 return fail(MOE_ERR_UNSUPPORTED, "FP8 expert weights need H and I multiples of 16");
             if (opts->flags & MOE_FLAG_FORCE_TILED)
                 return fail(MOE_ERR_UNSUPPORTED, "FP8 expert weights run on the weight-streaming kernels only");
+            if (T * (int64_t)k > 32 * E)
+                return fail(MOE_ERR_UNSUPPORTED, "FP8 expert weights serve batches of T*k <= 32*E (the "
+                                                 "weight-streaming schedule); T*k = %lld",
+                            (long long)(T * k));
         }
     }
     return MOE_OK;
 }
 
-// Routed experts on the weight-streaming kernels (few rows per expert, FP8
-// weights, or forced) rather than the large-M tiled schedule.
-bool use_skinny(int64_t T, int32_t k, int64_t E, const moe_opts *opts)
+// Schedule of the routed experts' GEMMs.
+//   SKINNY: the weight-streaming kernels (few rows per expert, low-precision
+//           weights, or forced); with no more than 32 tokens no expert can
+//           hold more than 32 rows, so every expert's weights stream once.
+//   MIXED:  the weight-streaming kernels for experts with up to 32 rows and
+//           the tiled kernel for the others (few rows per expert on average,
+//           but more than 32 tokens: one expert may take many of them).
+//   TILED:  the large-M tiled kernel for every expert.
+enum class Sched { SKINNY, MIXED, TILED };
+
+Sched schedule(int64_t T, int32_t k, int64_t E, const moe_opts *opts)
 {
     const uint32_t flags = opts ? opts->flags : 0;
-    if (opts && opts->weight_format != MOE_WEIGHTS_NATIVE) return true;  // low-precision weights
-    if (flags & MOE_FLAG_FORCE_SKINNY) return true;
-    if (flags & MOE_FLAG_FORCE_TILED) return false;
-    return T * k <= 32 * E;  // about 32 rows per expert or fewer: stream the weights
+    if (opts && opts->weight_format != MOE_WEIGHTS_NATIVE) return Sched::SKINNY;  // low-precision weights
+    if (opts && opts->dtype == MOE_F32) return Sched::SKINNY;  // the fp32 kernels (one schedule)
+    if (flags & MOE_FLAG_FORCE_SKINNY) return Sched::SKINNY;
+    if (flags & MOE_FLAG_FORCE_TILED) return Sched::TILED;
+    if (T * k > 32 * E) return Sched::TILED;  // more than about 32 rows per expert
+    return T <= moe::kSkinnyMaxRows ? Sched::SKINNY : Sched::MIXED;
 }
 
 moe::Shape make_shape(int64_t T, int64_t H, int64_t I, int64_t E, int32_t k, const moe_opts *opts)
@@ -153,7 +171,13 @@ moe::Shape make_shape(int64_t T, int64_t H, int64_t I, int64_t E, int32_t k, con
     s.tileBM = moe::tiled_block_m();
     s.tileXT = moe::tiled_tail_m();
     s.maxTiles = (T * k) / s.tileBM + E + 1;
-    s.partBytes = (s.dtype == MOE_BF16 && !use_skinny(T, k, E, opts)) ? moe::tiled_split_bytes() : 0;
+    // experts with fewer rows than tileMinRows get no M-tile (the streaming kernels serve them)
+    const Sched sc = schedule(T, k, E, opts);
+    s.tileMinRows = sc == Sched::MIXED ? moe::kSkinnyMaxRows + 1 : 0;
+    // the partial sums of split tiles (a launch with a short last round, or
+    // the few tiles of the mixed schedule's large experts, spreads them over
+    // every CU along K)
+    s.partBytes = (s.dtype == MOE_BF16 && sc != Sched::SKINNY) ? moe::tiled_split_bytes() : 0;
     return s;
 }
 
@@ -358,7 +382,9 @@ static int forward_impl(const void *hidden, const void *router_w, const void *ga
         return fail(MOE_ERR_HIP, "cannot query the compute units of the current device");
 
     const bool f32 = opts->dtype == MOE_F32;
-    const bool skinny = use_skinny(T, k, E, opts);
+    const Sched sched = schedule(T, k, E, opts);
+    const bool skinny = sched != Sched::TILED;  // the weight-streaming kernels run
+    const bool tiled = sched != Sched::SKINNY;  // the tiled kernel runs
 
     int step = 0;
     auto check = [&](hipError_t err, const char *what) -> int {
@@ -396,7 +422,7 @@ static int forward_impl(const void *hidden, const void *router_w, const void *ga
     // Few assignments on the weight-streaming kernels, with no sorted routing
     // tables or statistics asked for: those kernels route straight from the
     // top-k ids, and the scan and permute launches are skipped.
-    const bool direct = skinny && !f32 && T * k <= moe::kSkinnyDirectMax && !opts->expert_counts &&
+    const bool direct = sched == Sched::SKINNY && !f32 && T * k <= moe::kSkinnyDirectMax && !opts->expert_counts &&
                         !opts->expert_offsets && !opts->perm && !opts->inv_perm && !rs.on();
     if (!direct) {
         if ((rc = check(moe::launch_route_scan(s, opts->expert_counts, opts->expert_offsets, rs, ws, st),
@@ -435,6 +461,7 @@ static int forward_impl(const void *hidden, const void *router_w, const void *ga
     gu.k = k;
     gu.cus = cus;
     gu.a_rows_total = T;
+    gu.skinny_max_rows = sched == Sched::MIXED ? moe::kSkinnyMaxRows : 0;
 
     moe::GemmProblem dn = gu;
     dn.A = ws.h;
@@ -450,13 +477,19 @@ static int forward_impl(const void *hidden, const void *router_w, const void *ga
     dn.c_scale = ws.row_weight;
     dn.a_rows_total = T * k;
 
-    if (f32) rc = check(moe::launch_gate_up_f32(gu, st), "gate_up f32");
-    else if (skinny) rc = check(moe::launch_gate_up_skinny(gu, st), "gate_up skinny");
-    else rc = check(moe::launch_gate_up_tiled(gu, st), "gate_up tiled");
+    if (f32) {
+        rc = check(moe::launch_gate_up_f32(gu, st), "gate_up f32");
+    } else {
+        if (skinny) rc = check(moe::launch_gate_up_skinny(gu, st), "gate_up skinny");
+        if (!rc && tiled) rc = check(moe::launch_gate_up_tiled(gu, st), "gate_up tiled");
+    }
     if (rc || (rc = mark(1 + MOE_STAGE_GATE_UP))) return rc;
-    if (f32) rc = check(moe::launch_down_f32(dn, st), "down f32");
-    else if (skinny) rc = check(moe::launch_down_skinny(dn, st), "down skinny");
-    else rc = check(moe::launch_down_tiled(dn, st), "down tiled");
+    if (f32) {
+        rc = check(moe::launch_down_f32(dn, st), "down f32");
+    } else {
+        if (skinny) rc = check(moe::launch_down_skinny(dn, st), "down skinny");
+        if (!rc && tiled) rc = check(moe::launch_down_tiled(dn, st), "down tiled");
+    }
     if (rc || (rc = mark(1 + MOE_STAGE_DOWN))) return rc;
 
     if (shared) {

@@ -92,6 +92,7 @@ struct Shape {
     int nblk;        // router blocks
     int tileBM;      // rows per M-tile of the large-M schedule
     int tileXT;      // extra rows an expert's last M-tile may take (0: none)
+    int tileMinRows; // experts with fewer rows get no M-tile (mixed schedule; 0: every expert)
     int64_t maxTiles;
     int64_t partBytes;  // partial-sum buffer (0 unless the large-M schedule may run)
 };
@@ -158,10 +159,15 @@ struct GemmProblem {
     int k = 0;
     int cus = 0;             // compute units of the device (persistent grids)
     int64_t a_rows_total = 0;  // rows of A (gate_up: tokens; down: assignments or tokens)
+    int skinny_max_rows = 0;   // > 0: the weight-streaming launch leaves experts with more rows to the tiled one
 };
 
 // Largest T*k for which the weight-streaming kernels route directly from the ids.
 constexpr int kSkinnyDirectMax = 1024;
+// Rows of one expert the weight-streaming kernels serve with its weights
+// streamed once (two groups of 16 tokens per pass); in the mixed schedule,
+// experts with more rows run on the tiled kernel.
+constexpr int kSkinnyMaxRows = 32;
 
 hipError_t launch_gate_up_tiled(const GemmProblem &p, hipStream_t st);
 hipError_t launch_down_tiled(const GemmProblem &p, hipStream_t st);

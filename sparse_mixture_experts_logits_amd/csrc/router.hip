@@ -428,7 +428,7 @@ __global__ __launch_bounds__(256) void router_topk_kernel(
 // One workgroup: expert totals, exclusive offsets, per-block bases and the
 // M-tile list of the large-M schedule.
 __global__ __launch_bounds__(1024) void route_scan_kernel(
-    const int32_t *__restrict__ blk_counts, int nblk, int E, int BM, int XT, int32_t *__restrict__ counts,
+    const int32_t *__restrict__ blk_counts, int nblk, int E, int BM, int XT, int min_rows, int32_t *__restrict__ counts,
     int32_t *__restrict__ offsets, int32_t *__restrict__ blk_base, int32_t *__restrict__ tile_start,
     MTile *__restrict__ tiles, int32_t *__restrict__ counts_out, int32_t *__restrict__ offsets_out,
     const float *__restrict__ blk_prob, const int32_t *__restrict__ blk_mcnt, const int32_t *__restrict__ blk_ntok,
@@ -443,7 +443,9 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(
     // first tiles (XT each, the rest in the next), so no tile is left with a
     // handful of rows that would stream a whole weight block for them; else
     // the tiles hold BM rows and the last one the remainder.
-    auto n_tiles = [&](int c) { return (c + BM + XT - 1) / (BM + XT); };
+    // Experts with fewer than min_rows rows get no tile: the weight-streaming
+    // kernel serves them (mixed schedule).
+    auto n_tiles = [&](int c) { return c < min_rows ? 0 : (c + BM + XT - 1) / (BM + XT); };
     // first row (relative to the expert's offset) and rows of its tile i of n
     auto tile_rows = [&](int c, int n, int i, int &r0, int &rows) {
         const int extra = max(c - n * BM, 0);
@@ -637,7 +639,7 @@ hipError_t launch_route_scan(const Shape &s, int32_t *counts_out, int32_t *offse
                              const RouterStats &rs, const Workspace &ws, hipStream_t st)
 {
     hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(1024), 0, st, ws.blk_counts, s.nblk,
-                       (int)s.E, s.tileBM, s.tileXT, ws.counts, ws.offsets, ws.blk_base, ws.tile_start,
+                       (int)s.E, s.tileBM, s.tileXT, s.tileMinRows, ws.counts, ws.offsets, ws.blk_base, ws.tile_start,
                        ws.tiles, counts_out, offsets_out, rs.on() ? ws.blk_prob : nullptr, ws.blk_mcnt,
                        ws.blk_ntok, rs.prob_mean, rs.load, rs.aux);
     return hipGetLastError();

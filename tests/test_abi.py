@@ -408,3 +408,28 @@ def test_noalloc_entry_point_checks_arguments():
     assert lib.moe_forward_noalloc(None, None, None, None, 0, 64, 32, 4, 2, ctypes.byref(o), None) == 0
     # the decode step fits
     assert moe.workspace_bytes(32, 4096, 6400, 16, 2) <= moe.NOALLOC_SCRATCH_BYTES
+
+
+def test_low_precision_weights_serve_the_streaming_schedule_only():
+    # FP8 / MXFP4 weights have no tiled kernel: batches past T*k <= 32*E are
+    # refused (before any HIP call) instead of re-streaming every expert's
+    # weights once per 16 rows
+    for make in (fp8_opts, mxfp4_opts):
+        rc, msg = call(T=64, E=4, k=2, opts=make())  # 128 <= 128: reaches the workspace check
+        assert rc == -3, msg
+        rc, msg = call(T=65, E=4, k=2, opts=make())
+        assert rc == -2 and "T*k <= 32*E" in msg
+
+
+def test_workspace_of_each_schedule():
+    # at most 32 tokens: the streaming kernels alone, no split-tile buffer;
+    # more tokens but few rows per expert on average: the mixed schedule,
+    # whose tiled launch may split its few tiles along K (the buffer), and
+    # which still fits the allocation-free entry point's scratch
+    split = 256 * 8 * 9 * 4096  # partial sums of 256 split pieces
+    decode = moe.workspace_bytes(32, 4096, 6400, 16, 2)
+    assert decode < split
+    mixed = moe.workspace_bytes(256, 4096, 6400, 16, 2)
+    forced = moe.workspace_bytes(256, 4096, 6400, 16, 2, flags=moe.FLAG_FORCE_SKINNY)
+    assert mixed - forced >= split
+    assert mixed <= moe.NOALLOC_SCRATCH_BYTES

@@ -132,7 +132,7 @@ def check_against_oracle(inp, tokens, what, flags=0):
 
 SMALL = [
     ("tiny", dict(T=40, H=64, I=48, E=5, k=2)),
-    ("multi_pass", dict(T=300, H=256, I=128, E=8, k=3)),          # > 16 rows per expert: several passes
+    ("multi_pass", dict(T=100, H=256, I=128, E=8, k=2)),          # > 16 rows per expert: several passes
     ("ragged_k", dict(T=50, H=272, I=80, E=4, k=2)),               # K not a multiple of the 256-wide step
     ("fine", dict(T=96, H=192, I=64, E=32, k=6, routed_scale=2.5)),
     ("shared_bias", dict(T=70, H=128, I=64, E=16, k=2, n_shared=2, shared_I=32,
@@ -156,7 +156,7 @@ def test_fp8_decode_full_size():
 
 def test_fp8_layer_run_to_run_identical():
     _say("case fp8 run to run")
-    inp = W.custom_inputs(T=300, H=256, I=128, E=8, k=3)
+    inp = W.custom_inputs(T=100, H=256, I=128, E=8, k=2)
     gq, gs = gpu_quantize(inp.gate_up)
     dq, ds = gpu_quantize(inp.down)
     a, _ = run_fp8(inp, gq, gs, dq, ds)

@@ -326,6 +326,34 @@ def test_direct_routing_matches_sorted_tables(kw):
     check_out(out_direct, oracle_out(inp, ref, np.arange(inp.wl.T, dtype=np.int32)), "direct routing")
 
 
+@pytest.mark.parametrize("kw", [
+    # a small skewed batch (the skewed workload's router bias): about 32 rows
+    # per expert on average, so the weight-streaming schedule, but expert 0
+    # takes nearly every token; it runs on the tiled kernel, the others stream
+    dict(T=256, H=512, I=256, E=16, k=2, bias=((0, 6.0), (13, -30.0), (14, -30.0), (15, -30.0))),
+    # between 16 and 32 rows per expert: two token groups per streaming pass
+    dict(T=200, H=256, I=128, E=16, k=2),
+    # k = 1 and a strong bias: nearly all of 40 tokens on expert 3 (past 32
+    # rows: the tiled launch), a handful on others
+    dict(T=40, H=256, I=128, E=32, k=1, bias=((3, 8.0),)),
+], ids=["skewed_small_batch", "two_groups", "threshold"])
+def test_mixed_schedule(kw):
+    _say(f"case mixed schedule {kw}")
+    inp = W.custom_inputs(**kw, std_weight=0.05)
+    ref = oracle_routing(inp)
+    _say(f"  counts {ref['counts'].tolist()}")
+    out, got = run_gpu(inp)
+    check_routing(got, ref, "mixed")
+    r_out = oracle_out(inp, ref, np.arange(inp.wl.T, dtype=np.int32))
+    check_out(out, r_out, "mixed")
+    plain = run_gpu_plain(inp)
+    assert np.array_equal(plain.view(np.uint32), out.view(np.uint32))
+    assert np.array_equal(run_gpu_plain(inp).view(np.uint32), plain.view(np.uint32))
+    # the same layer on the streaming kernels alone (experts re-streamed per 32 rows) agrees
+    forced, _ = run_gpu(inp, flags=moe.FLAG_FORCE_SKINNY)
+    check_out(forced, r_out, "streaming only")
+
+
 # ------------------------------------------------------------------ full-size workloads
 
 FULL = ["phimoe_decode", "phimoe_prefill", "instella_fine", "phimoe_skewed"]

@@ -33,9 +33,10 @@ def _run(inp, no_alloc, **kw):
         gu, dn = inp.shared_concat()
         sgu, sdn = _dev(gu), _dev(dn)
     out = torch.empty((wl.T, wl.H), dtype=torch.bfloat16, device="cuda:0")
+    bias = None if inp.bias is None else torch.from_numpy(inp.bias).to("cuda:0")
     res = moe.moe_forward(_dev(inp.hidden), _dev(inp.router_w), _dev(inp.gate_up), _dev(inp.down), wl.k,
-                          routed_scale=wl.routed_scale, shared_gate_up=sgu, shared_down=sdn, out=out,
-                          no_alloc=no_alloc, **kw)
+                          routed_scale=wl.routed_scale, router_bias=bias, shared_gate_up=sgu, shared_down=sdn,
+                          out=out, no_alloc=no_alloc, **kw)
     torch.cuda.synchronize()
     return res
 
@@ -49,15 +50,17 @@ def _oracle(inp):
     return ids, ref
 
 
-@pytest.mark.parametrize("kw", [
-    dict(H=1024, I=768, E=8, k=2),
-    dict(H=512, I=256, E=16, k=4, n_shared=1, shared_I=128, routed_scale=2.5),
-], ids=["plain", "shared"])
-def test_noalloc_matches_workspace_entry_point_twice(kw):
-    print(f"case noalloc {kw}", flush=True)
-    full = W.custom_inputs(T=32, **kw, std_weight=0.05)
-    for T in (32, 5):  # the second call is smaller
-        inp = full if T == 32 else W.custom_inputs(T=T, **kw, std_weight=0.05, seed=1)
+@pytest.mark.parametrize("Ts,kw", [
+    ((32, 5), dict(H=1024, I=768, E=8, k=2)),
+    ((32, 5), dict(H=512, I=256, E=16, k=4, n_shared=1, shared_I=128, routed_scale=2.5)),
+    # more than 32 tokens, few rows per expert on average: the mixed schedule
+    # (streaming kernels, plus the tiled kernel for experts past 32 rows)
+    ((200, 48), dict(H=512, I=256, E=16, k=2, bias=((0, 6.0),))),
+], ids=["plain", "shared", "mixed"])
+def test_noalloc_matches_workspace_entry_point_twice(Ts, kw):
+    print(f"case noalloc {Ts} {kw}", flush=True)
+    for i, T in enumerate(Ts):  # the second call is smaller
+        inp = W.custom_inputs(T=T, **kw, std_weight=0.05, seed=i)
         a, ra = _run(inp, no_alloc=True, return_routing=True)
         b, rb = _run(inp, no_alloc=False, return_routing=True)
         assert torch.equal(a.view(torch.int16), b.view(torch.int16)), f"T={T}: outputs differ"
@@ -80,8 +83,8 @@ def test_noalloc_rejects_a_workspace_and_oversized_calls():
     args = (_dev(inp.hidden), _dev(inp.router_w), _dev(inp.gate_up), _dev(inp.down), 2)
     with pytest.raises(ValueError, match="no workspace"):
         moe.moe_forward(*args, no_alloc=True, workspace=torch.empty(1 << 20, dtype=torch.uint8, device="cuda"))
-    # a tiled-schedule call needs more scratch than the library holds
-    big = W.custom_inputs(T=2048, H=1024, I=512, E=4, k=2)
-    assert moe.workspace_bytes(2048, 1024, 512, 4, 2) > moe.NOALLOC_SCRATCH_BYTES
+    # a large prefill call needs more scratch than the library holds
+    big = W.custom_inputs(T=8192, H=4096, I=64, E=4, k=2)
+    assert moe.workspace_bytes(8192, 4096, 64, 4, 2) > moe.NOALLOC_SCRATCH_BYTES
     with pytest.raises(moe.MoeError, match="scratch"):
         moe.moe_forward(_dev(big.hidden), _dev(big.router_w), _dev(big.gate_up), _dev(big.down), 2, no_alloc=True)

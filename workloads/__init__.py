@@ -78,6 +78,10 @@ WORKLOADS = [
              bias=((0, 6.0), (13, -30.0), (14, -30.0), (15, -30.0)),
              description="PhiMoE shapes with a router bias: about half of all assignments "
                          "to expert 0, experts 13-15 empty"),
+    Workload("phimoe_skewed_small", 5, T=256, H=4096, I=6400, E=16, k=2, dtype="bf16",
+             bias=((0, 6.0), (13, -30.0), (14, -30.0), (15, -30.0)),
+             description="a decode-sized batch with the skewed router bias: about 32 rows per expert on "
+                         "average, nearly every token on expert 0"),
 ]
 BY_NAME = {w.name: w for w in WORKLOADS}
 
