@@ -36,12 +36,10 @@ namespace {
 #ifndef MOE_TILED_STAGES
 #define MOE_TILED_STAGES 4
 #endif
-constexpr int BK = MOE_TILED_BK;          // bf16 elements per k-stage (2*BK bytes per row)
-constexpr int STAGES = MOE_TILED_STAGES;  // LDS ring depth
-constexpr int CH = BK / 8;                // 16-byte chunks per row of a stage
-constexpr int RPI = 64 / CH;              // rows filled by one 64-lane copy instruction
-static_assert(CH == 4 || CH == 8, "stage rows of 64 or 128 bytes");
-static_assert(STAGES >= 2, "at least a double buffer");
+// Routed launches: BK bf16 elements per k-stage (2*BK bytes per row) and an
+// LDS ring of STAGES stages. Every launch configuration takes its own pair.
+constexpr int kRoutedBK = MOE_TILED_BK;
+constexpr int kRoutedStages = MOE_TILED_STAGES;
 
 struct TiledParams {
     const __bf16 *A;
@@ -80,13 +78,13 @@ struct SplitPlan {
     int nwork;  // work items of the persistent loop
 };
 
-__device__ __forceinline__ SplitPlan split_plan(int total, int G, int cap, int nk, bool enabled)
+__host__ __device__ __forceinline__ SplitPlan split_plan(int total, int G, int cap, int nk, bool enabled)
 {
     SplitPlan sp{total, 1, nk, total};
-    cap = min(G, cap);
+    cap = std::min(G, cap);
     const int rem = total % G;
     if (!enabled || rem == 0 || 2 * rem > cap || nk < 2) return sp;
-    int split = min(min(cap / rem, kMaxSplit), nk);
+    int split = std::min(std::min(cap / rem, kMaxSplit), nk);
     const int nks = (nk + split - 1) / split;
     split = (nk + nks - 1) / nks;  // every piece holds at least one stage
     if (split < 2) return sp;
@@ -233,13 +231,13 @@ __device__ __forceinline__ void tile_epilogue(const TiledParams &p, const f32x16
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) void global_void_t;
 
-// LDS stage layout: rows of CH chunks of 16 bytes; chunk c of row r sits at
+// LDS stage layout: rows of CH = BK / 8 chunks of 16 bytes; chunk c of row r sits at
 // slot c ^ swz(r) with swz(r) = (r >> 2) & 3 for 64-byte rows and (r >> 1) & 7
 // for 128-byte rows, so the 16 lanes a ds_read_b128 serves per cycle (16
 // consecutive rows, one chunk column) hit 16 distinct 16-byte bank groups of
 // the 64-bank LDS.
+template <int CH>
 __device__ __forceinline__ int lds_swz(int r) { return CH == 4 ? ((r >> 2) & 3) : ((r >> 1) & 7); }
-__device__ __forceinline__ int lds_slot(int r, int c) { return r * CH + (c ^ lds_swz(r)); }
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8_t, v); }
 
@@ -291,9 +289,13 @@ __device__ __forceinline__ uint32_t lds_addr(const void *p) { return (uint32_t)(
 // gate_up: the four waves of a column half take the gate and the up block of
 // its two output column blocks, and the gate blocks reach the matching up
 // waves through LDS in the epilogue.
-template <int BM, int BN, int WM, int WN, int OCC, bool GATEUP, int XT = 0>
+template <int BM, int BN, int WM, int WN, int OCC, bool GATEUP, int XT, int BK, int STAGES>
 __global__ __launch_bounds__(WM *WN * 64, OCC) void tiled_gemm_kernel(TiledParams p)
 {
+    constexpr int CH = BK / 8;    // 16-byte chunks per row of a stage
+    constexpr int RPI = 64 / CH;  // rows filled by one 64-lane copy instruction
+    static_assert(CH == 4 || CH == 8, "stage rows of 64 or 128 bytes");
+    static_assert(STAGES >= 2, "at least a double buffer");
     constexpr int NT = WM * WN * 64;
     constexpr int NWAVE = WM * WN;
     constexpr int RM = BM / WM / 32;
@@ -373,7 +375,7 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void tiled_gemm_kernel(TiledParam
         // later) as byte offsets into a buffer resource over A, or over the
         // expert's weights; a stage adds its K offset in a scalar register
         // logical chunk (of 8 elements) a lane copies for LDS row rr
-        auto chunk_of = [&](int rr) { return (lane % CH) ^ lds_swz(rr); };
+        auto chunk_of = [&](int rr) { return (lane % CH) ^ lds_swz<CH>(rr); };
         const uint32_t krow = (uint32_t)p.K * 2u;  // bytes per row
         const i32x4_t ra = buf_rsrc(p.A, p.a_bytes);
         uint32_t aoff[A_INS];
@@ -472,7 +474,7 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void tiled_gemm_kernel(TiledParam
         // included) plus a compile-time offset (buffer, row block).
         constexpr int KSTEPS = BK / 16;  // MFMA k-steps per stage
         const int l32 = lane & 31;
-        auto laneoff = [&](int kk) { return l32 * CH + ((kk * 2 + (lane >> 5)) ^ lds_swz(l32)); };
+        auto laneoff = [&](int kk) { return l32 * CH + ((kk * 2 + (lane >> 5)) ^ lds_swz<CH>(l32)); };
         constexpr int HWB = GATEUP ? BN / 2 / WN : BN / WN;  // B rows per wave (per half for gate_up)
         int va[KSTEPS], vb[KSTEPS], vxa[KSTEPS], vxb[KSTEPS];
 #pragma unroll
@@ -627,7 +629,7 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void tiled_gemm_kernel(TiledParam
 // the tile as the main kernel's epilogue would (the extra rows go with row
 // block 0; for gate_up an up wave sums its gate partner's partials as well). The split plan is recomputed from the
 // same inputs as the main kernel's.
-template <int BM, int BN, int WM, int WN, bool GATEUP, int XT>
+template <int BM, int BN, int WM, int WN, bool GATEUP, int XT, int BK>
 __global__ __launch_bounds__(64) void tiled_split_finish_kernel(TiledParams p)
 {
     constexpr int NWAVE = WM * WN;
@@ -771,7 +773,7 @@ TiledParams make_params(const GemmProblem &g, int NB)
     return t;
 }
 
-template <int BM, int BN, int WM, int WN, int OCC, bool GATEUP, int XT = 0>
+template <int BM, int BN, int WM, int WN, int OCC, bool GATEUP, int XT, int BK, int STAGES>
 hipError_t launch_cfg(const GemmProblem &g, hipStream_t st)
 {
     const int cols = GATEUP ? BN / 2 : BN;  // output columns per N-block
@@ -782,10 +784,16 @@ hipError_t launch_cfg(const GemmProblem &g, hipStream_t st)
     constexpr int64_t piece_bytes = (int64_t)WM * WN * ((BM / WM / 32) * (BN / WN / 32) + (XT > 0 ? 1 : 0)) * 1024 * 4;
     t.cap = (int)std::min<int64_t>(t.G, tiled_split_bytes() / piece_bytes);
     t.part = g.part;
-    hipLaunchKernelGGL((tiled_gemm_kernel<BM, BN, WM, WN, OCC, GATEUP, XT>), dim3(t.G), dim3(WM * WN * 64), 0, st, t);
+    // a dense problem's tile count is known here: no second launch when no tile is split
+    if (t.part && g.dense_rows > 0) {
+        const int total = (int)((g.dense_rows + BM - 1) / BM) * t.NB;
+        if (split_plan(total, t.G, t.cap, (int)((g.K + BK - 1) / BK), true).split < 2) t.part = nullptr;
+    }
+    hipLaunchKernelGGL((tiled_gemm_kernel<BM, BN, WM, WN, OCC, GATEUP, XT, BK, STAGES>), dim3(t.G), dim3(WM * WN * 64), 0,
+                       st, t);
     if (t.part) {
         // at most cap / 2 tiles are split (two pieces or more each)
-        hipLaunchKernelGGL((tiled_split_finish_kernel<BM, BN, WM, WN, GATEUP, XT>),
+        hipLaunchKernelGGL((tiled_split_finish_kernel<BM, BN, WM, WN, GATEUP, XT, BK>),
                            dim3(t.cap / 2 * WM * WN * (BM / WM / 32)), dim3(64), 0, st, t);
     }
     return hipGetLastError();
@@ -794,14 +802,22 @@ hipError_t launch_cfg(const GemmProblem &g, hipStream_t st)
 #ifndef MOE_TILED_TAIL
 #define MOE_TILED_TAIL 32
 #endif
+#ifndef MOE_DENSE_GATE_UP_CFG
+#define MOE_DENSE_GATE_UP_CFG launch_cfg<128, 256, 2, 2, 1, true, 0, 64, 3>
+#endif
+#ifndef MOE_DENSE_DOWN_CFG
+#define MOE_DENSE_DOWN_CFG launch_cfg<128, 128, 2, 2, 1, false, 0, 64, 4>
+#endif
 
 }  // namespace
 
 // Routed experts: 256x256 tiles (up to 32 more token rows in an expert's
-// last tile), 8 waves, one workgroup per CU; the M-tile list is built for
-// these sizes. Dense problems (the shared expert, all T rows) use smaller
-// tiles so that a few thousand rows still fill the CUs: 128x256 (gate_up)
-// and 128x128 with two workgroups per CU (down).
+// last tile), 8 waves, one workgroup per CU, 64-byte row segments per stage
+// in a 4-deep ring; the M-tile list is built for these sizes. Dense problems
+// (the shared expert, all T rows) use smaller tiles so that a few thousand
+// rows still fill the CUs, with 128-byte row segments (half the address work
+// per byte copied): 128x256 in a 3-deep ring (gate_up) and 128x128 in a
+// 4-deep ring (down).
 int tiled_block_m() { return 256; }
 // partial-sum buffer of split tiles for the routed launches (256x256 tiles,
 // 8 waves, 9 accumulator blocks of 32x32 per wave)
@@ -810,14 +826,14 @@ int tiled_tail_m() { return MOE_TILED_TAIL; }
 
 hipError_t launch_gate_up_tiled(const GemmProblem &g, hipStream_t st)
 {
-    if (g.dense_rows > 0) return launch_cfg<128, 256, 2, 2, 1, true>(g, st);
-    return launch_cfg<256, 256, 4, 2, 1, true, MOE_TILED_TAIL>(g, st);
+    if (g.dense_rows > 0) return MOE_DENSE_GATE_UP_CFG(g, st);
+    return launch_cfg<256, 256, 4, 2, 1, true, MOE_TILED_TAIL, kRoutedBK, kRoutedStages>(g, st);
 }
 
 hipError_t launch_down_tiled(const GemmProblem &g, hipStream_t st)
 {
-    if (g.dense_rows > 0) return launch_cfg<128, 128, 2, 2, 2, false>(g, st);
-    return launch_cfg<256, 256, 4, 2, 1, false, MOE_TILED_TAIL>(g, st);
+    if (g.dense_rows > 0) return MOE_DENSE_DOWN_CFG(g, st);
+    return launch_cfg<256, 256, 4, 2, 1, false, MOE_TILED_TAIL, kRoutedBK, kRoutedStages>(g, st);
 }
 
 }  // namespace moe

@@ -138,3 +138,27 @@ def test_scoring_instella_full_size(T):
     sc = dict(score_func="sigmoid", selection_bias=sel_bias(inp.wl.E, 9, 0.01), n_group=8, topk_group=4)
     tokens = np.arange(T, dtype=np.int32) if T <= 32 else np.linspace(0, T - 1, 24).astype(np.int32)
     check(inp, sc, tokens, f"instella T={T}")
+
+
+# Routing at sizes past the small cases: hidden sizes that are not a multiple
+# of the 512-element chunk a wave sums (absent slices in the last chunk),
+# expert counts that leave the last group of four experts partly empty, 16k
+# tokens with ragged last router blocks, and the largest k next to E.
+LARGER = [
+    ("h3000_e20", dict(T=1000, H=3000, I=32, E=20, k=3), dict(score_func="softmax")),
+    ("t16500_groups", dict(T=16500, H=1000, I=32, E=64, k=4, routed_scale=2.5),
+     dict(score_func="sigmoid", selection_bias=sel_bias(64, 10), n_group=8, topk_group=3)),
+    ("t16400_k16", dict(T=16400, H=4096, I=16, E=40, k=16), dict(score_func="softmax")),
+    ("t16400_k17", dict(T=16400, H=512, I=16, E=24, k=17), dict(score_func="softmax")),
+    ("h2056_sparsemixer", dict(T=777, H=2056, I=32, E=16, k=2), dict(score_func="sparsemixer")),
+]
+
+
+@pytest.mark.parametrize("name,kw,sc", LARGER, ids=[s[0] for s in LARGER])
+def test_routing_larger_shapes(name, kw, sc):
+    _say(f"case routing {name}")
+    inp = W.custom_inputs(**kw, std_weight=0.05)
+    T = kw["T"]
+    tokens = np.unique(np.concatenate([np.linspace(0, T - 1, 20).astype(np.int32),
+                                       np.arange(max(0, T - 5), T, dtype=np.int32)]))
+    check(inp, sc, tokens, name)
