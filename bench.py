@@ -219,6 +219,9 @@ def _short_kernel_name(name):
                 targ = "bf16" if rest.startswith("IDF16b") else "float" if rest.startswith("If") else ""
                 name = ident + (f" [{targ}]" if targ else "")
     name = name.replace("moe::(anonymous namespace)::", "")
+    if "_Accum" in name:  # a profiler's demangling of bf16 template arguments ("bool _Accum, int, E")
+        import re
+        name = re.sub(r"<[^()]*>", " [bf16]", name, count=1)
     depth = 0
     for i, ch in enumerate(name):
         if ch == "<":

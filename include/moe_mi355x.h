@@ -119,8 +119,11 @@ typedef struct moe_opts {
      * halves the bytes a decode step streams (MoEs in Transformers page,
      * section on why MoEs are fast: decode speed ~ bandwidth / bytes of the
      * active weights; per-expert quantisation once experts are packed). The
-     * shared expert stays in opts->dtype. Every schedule streams the weights
-     * (the weight-streaming kernels), so MOE_FLAG_FORCE_TILED is rejected. */
+     * shared expert stays in opts->dtype. These weights run on the
+     * weight-streaming kernels only: MOE_FLAG_FORCE_TILED is rejected, and so
+     * are batches with T*k > 32*E (more than about 32 rows per expert, where
+     * an expert's weights would be streamed once per 32 of its rows), with
+     * MOE_ERR_UNSUPPORTED; the same holds for MOE_WEIGHTS_MXFP4. */
     int32_t weight_format;
     const float *gate_up_scale;
     const float *down_scale;
