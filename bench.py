@@ -16,8 +16,10 @@ scale 2.5, two shared experts), ``phimoe_skewed`` (T=16384, router bias: half
 of all assignments to one expert), ``phimoe_skewed_small`` (the same bias on a
 256-token batch: the mixed schedule) and ``tiny_f32`` (fp32), plus the decode
 step with FP8 (E4M3, per-row scaled) and MXFP4 (E2M1, E8M0 scale per 32)
-expert weights under ``decode_fp8`` and ``decode_mxfp4`` (different weight
-storage, so never the headline value). Each carries a ``roofline`` of its
+expert weights under ``decode_fp8`` and ``decode_mxfp4``, and the prefill,
+skewed and Instella-style workloads with their bf16 routed weights packed in
+tile blocks under ``<workload>_tile_blocks`` (other weight storage, so never
+the headline value). Each carries a ``roofline`` of its
 dominant kernel, bound by max(FLOP / MFMA peak, bytes / HBM bandwidth). A
 short untimed pilot with events at every stage boundary finds the dominant
 kernel; every timed call then records HIP events around that kernel on the
@@ -71,7 +73,8 @@ def log(*a):
 # ------------------------------------------------------------------ algorithmic work
 
 WEIGHT_FORMATS = {"bf16": "bf16 as given", "fp8": "OCP FP8 E4M3, one fp32 scale per row",
-                  "mxfp4": "OCP MXFP4: FP4 E2M1, one E8M0 scale per 32 weights of a row"}
+                  "mxfp4": "OCP MXFP4: FP4 E2M1, one E8M0 scale per 32 weights of a row",
+                  "tile_blocks": "bf16 in tile blocks (packed once; read by the tiled kernels)"}
 
 
 def weight_bytes(rows, cols, es, weights):
@@ -80,7 +83,7 @@ def weight_bytes(rows, cols, es, weights):
         return rows * cols + rows * 4
     if weights == "mxfp4":
         return rows * cols // 2 + rows * cols // 32
-    return rows * cols * es
+    return rows * cols * es  # bf16, in either layout
 
 
 def work(wl, counts, weights="bf16"):
@@ -386,6 +389,9 @@ def run_workload(name, steps, warmup, weights="bf16"):
         gate_up, gs = moe.quantize_mxfp4_rows(gate_up)
         down, ds = moe.quantize_mxfp4_rows(down)
         scales = dict(gate_up_block_scale=gs, down_block_scale=ds)
+    elif weights == "tile_blocks":  # the routed experts are packed once, outside the timed region
+        gate_up = moe.pack_tile_blocks(gate_up, moe.PACK_GATE_UP)
+        down = moe.pack_tile_blocks(down, moe.PACK_DOWN)
     sgu = sdn = None
     if inp.shared_gate_up:
         gu, dn = inp.shared_concat()
@@ -395,7 +401,8 @@ def run_workload(name, steps, warmup, weights="bf16"):
 
     out = torch.empty((wl.T, wl.H), dtype=hidden.dtype, device=dev)
     need = moe.workspace_bytes(wl.T, wl.H, wl.I, wl.E, wl.k, shared_I=sgu.shape[0] // 2 if sgu is not None else 0,
-                               dtype=0 if wl.dtype == "bf16" else 1)
+                               dtype=0 if wl.dtype == "bf16" else 1,
+                               weight_layout=moe.LAYOUT_TILE_BLOCKS if weights == "tile_blocks" else moe.LAYOUT_ROWS)
     ws = torch.empty((need,), dtype=torch.uint8, device=dev)
     _, routing = moe.moe_forward(hidden, router_w, gate_up, down, wl.k, return_routing=True, out=out,
                                  workspace=ws, **kw)
@@ -470,6 +477,8 @@ def schedule_of(wl, weights="bf16"):
     large-M tiled kernels."""
     if wl.dtype == "f32":
         return "f32"
+    if weights == "tile_blocks":
+        return "tiled"
     if weights != "bf16":
         return "skinny"
     if wl.T * wl.k <= 32 * wl.E:
@@ -591,6 +600,7 @@ def cpu_baseline(res, max_tokens, min_seconds=10.0):
 
 # PhiMoE-shaped workloads first: they share one set of device weights
 NESTED = ("phimoe_prefill", "phimoe_skewed", "phimoe_skewed_small", "instella_fine", "tiny_f32")
+TILE_BLOCK_NESTED = ("phimoe_prefill", "phimoe_skewed", "instella_fine")
 
 
 def nested_line(res):
@@ -614,7 +624,7 @@ def main(argv=None):
     ap.add_argument("--only", action="store_true", help="measure the main workload only (no nested lines)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--skip", nargs="*", default=[], help="nested lines to leave out (workload names, "
-                                                           "decode_fp8, decode_mxfp4)")
+                                                           "decode_fp8, decode_mxfp4, <workload>_tile_blocks)")
     ap.add_argument("--weights", choices=sorted(WEIGHT_FORMATS), default="bf16",
                     help="expert weight storage of the main workload (fp8 / mxfp4: decode-shaped work only)")
     ap.add_argument("--cpu-tokens", type=int, default=32)
@@ -690,6 +700,12 @@ def main(argv=None):
             if name != args.workload and name not in args.skip:
                 line[name] = nested_line(run_workload(name, args.steps, args.warmup))
                 log(f"[bench] {name}: {line[name]['layer']['ms_per_step']} ms per step")
+        # the tiled workloads again with their routed weights packed in tile blocks
+        for name in TILE_BLOCK_NESTED:
+            key = name + "_tile_blocks"
+            if key not in args.skip:
+                line[key] = nested_line(run_workload(name, args.steps, args.warmup, weights="tile_blocks"))
+                log(f"[bench] {key}: {line[key]['layer']['ms_per_step']} ms per step")
     print(json.dumps(line), flush=True)
     return 0
 

@@ -80,6 +80,16 @@ typedef enum moe_weight_format {
                              /* moe_quantize_mxfp4_rows); bf16 activations only     */
 } moe_weight_format;
 
+/* Storage order of the routed experts' bf16 weights (opts->weight_layout). */
+typedef enum moe_weight_layout {
+    MOE_LAYOUT_ROWS = 0,       /* gate_up [E, 2I, H], down [E, H, I]: nn.Linear rows */
+    MOE_LAYOUT_TILE_BLOCKS = 1 /* the blocks moe_pack_tile_blocks writes            */
+} moe_weight_layout;
+
+/* which matrix moe_pack_tile_blocks / moe_tile_blocks_bytes describe */
+#define MOE_PACK_GATE_UP 0
+#define MOE_PACK_DOWN 1
+
 /* opts->flags bits: choose the expert-GEMM schedule (default: by shape). */
 #define MOE_FLAG_FORCE_TILED 0x1u  /* large-M tiles (prefill schedule)          */
 #define MOE_FLAG_FORCE_SKINNY 0x2u /* weight-streaming tiles (decode schedule)  */
@@ -197,6 +207,17 @@ typedef struct moe_opts {
      * weight-streaming kernels only (MOE_FLAG_FORCE_TILED is rejected). */
     const uint8_t *gate_up_block_scale;
     const uint8_t *down_block_scale;
+    /* MOE_LAYOUT_TILE_BLOCKS: gate_up and down hold the routed experts' bf16
+     * weights as moe_pack_tile_blocks wrote them (bytes as
+     * moe_tile_blocks_bytes gives). Every batch then runs on the large-M
+     * tiled kernels, whose weight copies each read 1 KB contiguous instead of
+     * 16 rows x 64 bytes ("Transformer中的混合专家架构详解" page, experts
+     * backends: grouped_mm over packed expert weights; the packing here is a
+     * storage order of the same weights). bf16, MOE_WEIGHTS_NATIVE only;
+     * MOE_FLAG_FORCE_SKINNY is rejected; the shared expert keeps
+     * MOE_LAYOUT_ROWS. Results are bit for bit those of MOE_LAYOUT_ROWS on the
+     * tiled schedule (MOE_FLAG_FORCE_TILED). */
+    int32_t weight_layout;
 } moe_opts;
 
 /* Stages of moe_forward, in launch order. */
@@ -312,7 +333,29 @@ int moe_forward_noalloc(const void *hidden, const void *router_w, const void *ga
  */
 int moe_quantize_fp8_rows(const void *w, int64_t rows, int64_t cols, void *q, float *scale, void *stream);
 
-/* Message describing the last failing call on this thread ("" if none). */
+/*
+ * The routed experts' bf16 weights in tile blocks (MOE_LAYOUT_TILE_BLOCKS),
+ * written once from the nn.Linear layout; every block is one 32-column
+ * k-stage of one 256-row weight block of the tiled kernels, so each stage of
+ * a tile streams one contiguous 16 KB run. Zero where a row or column lies
+ * past the matrix.
+ *   MOE_PACK_GATE_UP, w = gate_up [E, 2I, H]: out [E][NB = ceil(I/128)]
+ *     [NK = ceil(H/32)][256][32]; in block (e, nb, kt), row r < 128 holds gate
+ *     row nb*128 + r of expert e and row 128 + r holds up row
+ *     I + nb*128 + r, columns kt*32 .. kt*32 + 31;
+ *   MOE_PACK_DOWN, w = down [E, H, I]: out [E][NB = ceil(H/256)]
+ *     [NK = ceil(I/32)][256][32]; row r of block (e, nb, kt) holds row
+ *     nb*256 + r of expert e, columns kt*32 .. kt*32 + 31.
+ * moe_tile_blocks_bytes returns E * NB * NK * 16384 (or a negative
+ * moe_status for bad arguments: which, E >= 1, H and I positive multiples
+ * of 8, one expert's blocks below 2^31 bytes). moe_pack_tile_blocks writes
+ * them: w and out device buffers, 16-byte aligned, not overlapping;
+ * asynchronous on stream (hipStream_t, NULL = default); argument errors are
+ * returned before any HIP call.
+ */
+int64_t moe_tile_blocks_bytes(int32_t which, int64_t E, int64_t I, int64_t H);
+int moe_pack_tile_blocks(int32_t which, const void *w, int64_t E, int64_t I, int64_t H, void *out, void *stream);
+
 /*
  * MXFP4 quantisation (OCP Microscaling Formats v1.0, MXFP4) of a bf16 matrix
  * w [rows, cols], in blocks of 32 consecutive elements of a row:
@@ -332,6 +375,7 @@ int moe_quantize_fp8_rows(const void *w, int64_t rows, int64_t cols, void *q, fl
  */
 int moe_quantize_mxfp4_rows(const void *w, int64_t rows, int64_t cols, void *q, void *scale, void *stream);
 
+/* Message describing the last failing call on this thread ("" if none). */
 const char *moe_last_error(void);
 
 #ifdef __cplusplus

@@ -14,8 +14,8 @@ import numpy as np
 
 __all__ = ["moe_forward", "workspace_bytes", "quantize_fp8_rows", "MoeError", "load_library", "LIB_PATH",
            "FLAG_FORCE_TILED", "FLAG_FORCE_SKINNY", "WEIGHTS_NATIVE", "WEIGHTS_FP8_E4M3", "WEIGHTS_MXFP4", "quantize_mxfp4_rows",
-           "SCORE_SOFTMAX", "SCORE_SIGMOID", "SCORE_SPARSEMIXER",
-           "bf16_bits_to_tensor", "EXPORTS"]
+           "SCORE_SOFTMAX", "SCORE_SIGMOID", "SCORE_SPARSEMIXER", "TileBlocks", "pack_tile_blocks",
+           "tile_blocks_bytes", "bf16_bits_to_tensor", "EXPORTS"]
 
 # MOE_MI355X_LIB may point at another build of the same library (tuning builds)
 LIB_PATH = os.environ.get("MOE_MI355X_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
@@ -31,8 +31,12 @@ WEIGHTS_MXFP4 = 2
 SCORE_SOFTMAX = 0
 SCORE_SIGMOID = 1
 SCORE_SPARSEMIXER = 2
+LAYOUT_ROWS = 0
+LAYOUT_TILE_BLOCKS = 1
+PACK_GATE_UP = 0
+PACK_DOWN = 1
 EXPORTS = ("moe_opts_init", "moe_workspace_bytes", "moe_forward", "moe_forward_noalloc", "moe_quantize_fp8_rows",
-           "moe_quantize_mxfp4_rows", "moe_last_error")
+           "moe_quantize_mxfp4_rows", "moe_tile_blocks_bytes", "moe_pack_tile_blocks", "moe_last_error")
 NOALLOC_SCRATCH_BYTES = 128 << 20  # MOE_NOALLOC_SCRATCH_BYTES
 STAGES = ("router", "scan", "permute", "gate_up", "down", "shared_gate_up", "shared_down", "combine")
 STAGE_EVENTS = len(STAGES) + 1
@@ -77,6 +81,7 @@ class MoeOpts(ctypes.Structure):
         ("jitter_eps", ctypes.c_float),
         ("gate_up_block_scale", ctypes.c_void_p),
         ("down_block_scale", ctypes.c_void_p),
+        ("weight_layout", ctypes.c_int32),
     ]
 
 
@@ -114,6 +119,10 @@ def load_library():
         lib.moe_quantize_fp8_rows.restype = ctypes.c_int
         lib.moe_quantize_mxfp4_rows.argtypes = [vp, i64, i64, vp, vp, vp]
         lib.moe_quantize_mxfp4_rows.restype = ctypes.c_int
+        lib.moe_tile_blocks_bytes.argtypes = [i32, i64, i64, i64]
+        lib.moe_tile_blocks_bytes.restype = i64
+        lib.moe_pack_tile_blocks.argtypes = [i32, vp, i64, i64, i64, vp, vp]
+        lib.moe_pack_tile_blocks.restype = ctypes.c_int
         lib.moe_last_error.argtypes = []
         lib.moe_last_error.restype = ctypes.c_char_p
         _lib = lib
@@ -130,11 +139,12 @@ def last_error() -> str:
     return load_library().moe_last_error().decode()
 
 
-def workspace_bytes(T, H, I, E, k, dtype=MOE_BF16, shared_I=0, flags=0) -> int:
+def workspace_bytes(T, H, I, E, k, dtype=MOE_BF16, shared_I=0, flags=0, weight_layout=LAYOUT_ROWS) -> int:
     o = new_opts()
     o.dtype = dtype
     o.shared_I = shared_I
     o.flags = flags
+    o.weight_layout = weight_layout
     n = load_library().moe_workspace_bytes(T, H, I, E, k, ctypes.byref(o))
     if n < 0:
         raise MoeError(int(n), last_error())
@@ -174,6 +184,55 @@ def quantize_fp8_rows(w, stream=None):
     return q, scale
 
 
+class TileBlocks:
+    """Routed expert weights in tile blocks (MOE_LAYOUT_TILE_BLOCKS), as
+    ``pack_tile_blocks`` writes them: ``data`` is a flat bf16 CUDA tensor;
+    ``which`` is PACK_GATE_UP (from gate_up [E, 2I, H]) or PACK_DOWN (from
+    down [E, H, I])."""
+
+    def __init__(self, data, which: int, E: int, I: int, H: int):
+        self.data, self.which, self.E, self.I, self.H = data, which, E, I, H
+
+    def data_ptr(self):
+        return self.data.data_ptr()
+
+
+def tile_blocks_bytes(which: int, E: int, I: int, H: int) -> int:
+    n = load_library().moe_tile_blocks_bytes(int(which), E, I, H)
+    if n < 0:
+        raise MoeError(int(n), last_error())
+    return int(n)
+
+
+def pack_tile_blocks(w, which: int, stream=None) -> TileBlocks:
+    """Routed expert weights from the nn.Linear layout into tile blocks:
+    ``which`` PACK_GATE_UP takes gate_up [E, 2I, H], PACK_DOWN takes down
+    [E, H, I] (contiguous bf16 CUDA tensors). Done once per weight set; the
+    layer then reads them with ``moe_forward(..., gate_up=<TileBlocks>,
+    down=<TileBlocks>)``."""
+    import torch
+    if w.dtype != torch.bfloat16 or not w.is_contiguous() or not w.is_cuda or w.dim() != 3:
+        raise ValueError("w must be a contiguous 3-D bf16 CUDA tensor")
+    if which == PACK_GATE_UP:
+        E, twoI, H = w.shape
+        I = twoI // 2
+        if twoI != 2 * I:
+            raise ValueError("gate_up must be [E, 2I, H]")
+    elif which == PACK_DOWN:
+        E, H, I = w.shape
+    else:
+        raise ValueError("which must be PACK_GATE_UP or PACK_DOWN")
+    n = tile_blocks_bytes(which, E, I, H)
+    out = torch.empty((n // 2,), dtype=torch.bfloat16, device=w.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(w.device)
+    rc = load_library().moe_pack_tile_blocks(int(which), _ptr(w), E, I, H, _ptr(out),
+                                             ctypes.c_void_p(stream.cuda_stream))
+    if rc != 0:
+        raise MoeError(rc, last_error())
+    return TileBlocks(out, which, E, I, H)
+
+
 def quantize_mxfp4_rows(w, stream=None):
     """MXFP4 quantisation (OCP MX: E2M1 codes, one E8M0 scale per 32
     consecutive elements of a row) of a contiguous bf16 CUDA tensor viewed as
@@ -210,7 +269,9 @@ def moe_forward(hidden, router_w, gate_up, down, k: int, *, routed_scale: float 
     from quantize_fp8_rows); activations bf16. MXFP4 expert weights: gate_up
     [E, 2I, H/2] and down [E, H, I/2] uint8 (two E2M1 codes per byte) with
     gate_up_block_scale [E, 2I, H/32] and down_block_scale [E, H, I/32] uint8
-    (from quantize_mxfp4_rows). ``no_alloc`` calls moe_forward_noalloc: the
+    (from quantize_mxfp4_rows). Tile-block expert weights: gate_up and down
+    as ``TileBlocks`` from ``pack_tile_blocks`` (bf16; every batch runs on the
+    tiled kernels). ``no_alloc`` calls moe_forward_noalloc: the
     library's own scratch instead of a workspace (``workspace`` must be None;
     pass ``out`` so that nothing is allocated here either). ``router_stats`` adds the
     load-balancing statistics (prob_mean [E], load [E], aux_loss [1]) to the
@@ -228,9 +289,23 @@ def moe_forward(hidden, router_w, gate_up, down, k: int, *, routed_scale: float 
     import torch
     lib = load_library()
     T, H = hidden.shape
-    E, twoI, _ = gate_up.shape
-    I = twoI // 2
+    blocks = isinstance(gate_up, TileBlocks)
+    if blocks != isinstance(down, TileBlocks):
+        raise ValueError("gate_up and down must both be TileBlocks or both tensors")
+    if blocks:
+        if (gate_up.which, down.which) != (PACK_GATE_UP, PACK_DOWN) or \
+                (gate_up.E, gate_up.I, gate_up.H) != (down.E, down.I, down.H) or gate_up.H != H:
+            raise ValueError("tile blocks: gate_up and down of one [E, I, H] weight set, H of hidden")
+        E, I = gate_up.E, gate_up.I
+        gu_shape, dn_shape = (E, 2 * I, H), (E, H, I)
+        gate_up, down = gate_up.data, down.data
+    else:
+        E, twoI, _ = gate_up.shape
+        I = twoI // 2
+        gu_shape, dn_shape = tuple(gate_up.shape), tuple(down.shape)
     o = new_opts()
+    if blocks:
+        o.weight_layout = LAYOUT_TILE_BLOCKS
     if hidden.dtype == torch.bfloat16:
         o.dtype = MOE_BF16
     elif hidden.dtype == torch.float32:
@@ -268,8 +343,8 @@ def moe_forward(hidden, router_w, gate_up, down, k: int, *, routed_scale: float 
         if t.dtype != hidden.dtype:
             raise ValueError("activations, router and native-format weights must share one dtype")
     wcols = 2 if w4 else 1  # MXFP4: two codes per byte
-    if router_w.shape != (E, H) or gate_up.shape != (E, 2 * I, H // wcols) or \
-            down.shape != (E, H, I // wcols) or (w4 and (H % 32 or I % 32)):
+    if router_w.shape != (E, H) or gu_shape != (E, 2 * I, H // wcols) or \
+            dn_shape != (E, H, I // wcols) or (w4 and (H % 32 or I % 32)):
         raise ValueError("shape mismatch among hidden, router_w, gate_up, down")
     o.routed_scale = float(routed_scale)
     o.flags = int(flags)

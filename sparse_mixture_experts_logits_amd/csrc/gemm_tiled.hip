@@ -289,9 +289,12 @@ __device__ __forceinline__ uint32_t lds_addr(const void *p) { return (uint32_t)(
 // gate_up: the four waves of a column half take the gate and the up block of
 // its two output column blocks, and the gate blocks reach the matching up
 // waves through LDS in the epilogue.
-template <int BM, int BN, int WM, int WN, int OCC, bool GATEUP, int XT, int BK, int STAGES>
+template <int BM, int BN, int WM, int WN, int OCC, bool GATEUP, int XT, int BK, int STAGES, bool WPACK>
 __global__ __launch_bounds__(WM *WN * 64, OCC) void tiled_gemm_kernel(TiledParams p)
 {
+    // WPACK: the weights are in tile blocks (one stage of one N-block = 256
+    // rows x 32 columns, contiguous; zero-filled past N and K)
+    static_assert(!WPACK || (BN == kBlockRows && BK == kBlockCols), "tile blocks are 256 x 32");
     constexpr int CH = BK / 8;    // 16-byte chunks per row of a stage
     constexpr int RPI = 64 / CH;  // rows filled by one 64-lane copy instruction
     static_assert(CH == 4 || CH == 8, "stage rows of 64 or 128 bytes");
@@ -397,7 +400,7 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void tiled_gemm_kernel(TiledParam
             xoff = src * krow + (uint32_t)kbase * 2u + (uint32_t)chunk_of(xrr) * 16u;
         }
         const i32x4_t rb = buf_rsrc(p.W + (int64_t)e * p.w_expert_stride,
-                                    (uint32_t)(GATEUP ? 2 * p.N : p.N) * krow);
+                                    WPACK ? (uint32_t)p.w_expert_stride * 2u : (uint32_t)(GATEUP ? 2 * p.N : p.N) * krow);
         uint32_t boff[B_INS];
 #pragma unroll
         for (int i = 0; i < B_INS; i++) {
@@ -412,17 +415,22 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void tiled_gemm_kernel(TiledParam
                 const int n = nb * BN + rr;
                 wrow = n < p.N ? n : 0;
             }
-            boff[i] = (uint32_t)wrow * krow + (uint32_t)kbase * 2u + (uint32_t)chunk_of(rr) * 16u;
+            if (WPACK)  // block (nb, ks): rows rr in LDS order; a stage adds one block (BN * BK * 2 bytes)
+                boff[i] = ((uint32_t)(nb * nk_all + ks) * BN + (uint32_t)rr) * (BK * 2u) + (uint32_t)chunk_of(rr) * 16u;
+            else
+                boff[i] = (uint32_t)wrow * krow + (uint32_t)kbase * 2u + (uint32_t)chunk_of(rr) * 16u;
         }
 
         // stage kt -> LDS buffer b: every lane copies 16 bytes. Only a final
         // partial stage (K not a multiple of BK) masks lanes; they zero-fill.
+        // stage kt's offset into the weights: BK columns of a row, or one tile block
+        auto wstage = [&](int kt) { return WPACK ? (uint32_t)kt * (BN * BK * 2u) : (uint32_t)(kt * BK) * 2u; };
         auto issue = [&](int kt, int b) {
             const uint32_t k0 = (uint32_t)(kt * BK) * 2u;
 #pragma unroll
             for (int i = 0; i < A_INS; i++) dma16(ra, aoff[i], k0, lds_addr(&sA[b][(wave * A_INS + i) * 64]));
 #pragma unroll
-            for (int i = 0; i < B_INS; i++) dma16(rb, boff[i], k0, lds_addr(&sB[b][(wave * B_INS + i) * 64]));
+            for (int i = 0; i < B_INS; i++) dma16(rb, boff[i], wstage(kt), lds_addr(&sB[b][(wave * B_INS + i) * 64]));
             if (XT > 0 && xtra && xlane) dma16(ra, xoff, k0, lds_addr(&sA[b][(BM + XR * wave) * CH]));
         };
         auto issue_tail = [&](int kt, int b) {
@@ -439,7 +447,9 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void tiled_gemm_kernel(TiledParam
 #pragma unroll
             for (int i = 0; i < B_INS; i++) {
                 u32x4 *dst = &sB[b][(wave * B_INS + i) * 64];
-                if (k0 + chunk_of(RPI * (wave * B_INS + i) + drow) * 8 < Kl)
+                if (WPACK)  // the block's columns past K are zeros already
+                    dma16(rb, boff[i], wstage(kt), lds_addr(dst));
+                else if (k0 + chunk_of(RPI * (wave * B_INS + i) + drow) * 8 < Kl)
                     dma16(rb, boff[i], k0b, lds_addr(dst));
                 else
                     dst[lane] = u32x4{0u, 0u, 0u, 0u};
@@ -489,7 +499,7 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void tiled_gemm_kernel(TiledParam
         auto issue_one = [&](int kt, int b, int q) {
             const uint32_t k0 = (uint32_t)(kt * BK) * 2u;
             if (q < A_INS) dma16(ra, aoff[q], k0, lds_addr(&sA[b][(wave * A_INS + q) * 64]));
-            else if (q < LOADS) dma16(rb, boff[q - A_INS], k0, lds_addr(&sB[b][(wave * B_INS + q - A_INS) * 64]));
+            else if (q < LOADS) dma16(rb, boff[q - A_INS], wstage(kt), lds_addr(&sB[b][(wave * B_INS + q - A_INS) * 64]));
             else if (xlane) dma16(ra, xoff, k0, lds_addr(&sA[b][(BM + XR * wave) * CH]));
         };
         // Consume stage buffer b. When nkt >= 0, the LX copies of stage nkt
@@ -773,7 +783,7 @@ TiledParams make_params(const GemmProblem &g, int NB)
     return t;
 }
 
-template <int BM, int BN, int WM, int WN, int OCC, bool GATEUP, int XT, int BK, int STAGES>
+template <int BM, int BN, int WM, int WN, int OCC, bool GATEUP, int XT, int BK, int STAGES, bool WPACK = false>
 hipError_t launch_cfg(const GemmProblem &g, hipStream_t st)
 {
     const int cols = GATEUP ? BN / 2 : BN;  // output columns per N-block
@@ -789,8 +799,8 @@ hipError_t launch_cfg(const GemmProblem &g, hipStream_t st)
         const int total = (int)((g.dense_rows + BM - 1) / BM) * t.NB;
         if (split_plan(total, t.G, t.cap, (int)((g.K + BK - 1) / BK), true).split < 2) t.part = nullptr;
     }
-    hipLaunchKernelGGL((tiled_gemm_kernel<BM, BN, WM, WN, OCC, GATEUP, XT, BK, STAGES>), dim3(t.G), dim3(WM * WN * 64), 0,
-                       st, t);
+    hipLaunchKernelGGL((tiled_gemm_kernel<BM, BN, WM, WN, OCC, GATEUP, XT, BK, STAGES, WPACK>), dim3(t.G),
+                       dim3(WM * WN * 64), 0, st, t);
     if (t.part) {
         // at most cap / 2 tiles are split (two pieces or more each)
         hipLaunchKernelGGL((tiled_split_finish_kernel<BM, BN, WM, WN, GATEUP, XT, BK>),
@@ -809,7 +819,54 @@ hipError_t launch_cfg(const GemmProblem &g, hipStream_t st)
 #define MOE_DENSE_DOWN_CFG launch_cfg<128, 128, 2, 2, 1, false, 0, 64, 4>
 #endif
 
+// Tile blocks from the nn.Linear layout: one thread per 16 bytes (8 columns)
+// of the output, zeros past the matrix. Columns come in whole 8-column
+// chunks (K is a multiple of 8), so a chunk is all inside or all outside.
+__global__ __launch_bounds__(256) void pack_tile_blocks_kernel(const u32x4 *__restrict__ w, int which, int64_t I,
+                                                               int64_t H, int64_t nbk, int64_t nk,
+                                                               u32x4 *__restrict__ out, int64_t nchunks)
+{
+    const int64_t K = which == 0 ? H : I;              // columns of a weight row
+    const int64_t rows = which == 0 ? 2 * I : H;      // weight rows of one expert
+    constexpr int CPR = kBlockCols / 8;                // 16-byte chunks per block row
+    for (int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x; q < nchunks; q += (int64_t)gridDim.x * 256) {
+        const int c8 = (int)(q % CPR);
+        const int64_t rq = q / CPR;
+        const int r = (int)(rq % kBlockRows);
+        const int64_t blk = rq / kBlockRows;  // (e, nb, kt), kt innermost
+        const int64_t kt = blk % nk;
+        const int64_t nb = (blk / nk) % nbk;
+        const int64_t e = blk / (nk * nbk);
+        int64_t row;
+        bool in;
+        if (which == 0) {  // gate rows then the matching up rows
+            const int64_t j = nb * (kBlockRows / 2) + (r % (kBlockRows / 2));
+            in = j < I;
+            row = r < kBlockRows / 2 ? j : I + j;
+        } else {
+            row = nb * kBlockRows + r;
+            in = row < H;
+        }
+        const int64_t col = kt * kBlockCols + c8 * 8;
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (in && col < K) v = w[((e * rows + row) * K + col) / 8];
+        out[q] = v;
+    }
+}
+
 }  // namespace
+
+hipError_t launch_pack_tile_blocks(int which, const void *w, int64_t E, int64_t I, int64_t H, void *out,
+                                   hipStream_t st)
+{
+    const int64_t nbk = which == 0 ? (I + kBlockRows / 2 - 1) / (kBlockRows / 2) : (H + kBlockRows - 1) / kBlockRows;
+    const int64_t nk = which == 0 ? (H + kBlockCols - 1) / kBlockCols : (I + kBlockCols - 1) / kBlockCols;
+    const int64_t nchunks = E * nbk * nk * kBlockRows * (kBlockCols / 8);
+    const int64_t blocks = std::min<int64_t>((nchunks + 255) / 256, 16384);
+    hipLaunchKernelGGL(pack_tile_blocks_kernel, dim3((unsigned)blocks), dim3(256), 0, st, (const u32x4 *)w, which, I,
+                       H, nbk, nk, (u32x4 *)out, nchunks);
+    return hipGetLastError();
+}
 
 // Routed experts: 256x256 tiles (up to 32 more token rows in an expert's
 // last tile), 8 waves, one workgroup per CU, 64-byte row segments per stage
@@ -827,12 +884,14 @@ int tiled_tail_m() { return MOE_TILED_TAIL; }
 hipError_t launch_gate_up_tiled(const GemmProblem &g, hipStream_t st)
 {
     if (g.dense_rows > 0) return MOE_DENSE_GATE_UP_CFG(g, st);
+    if (g.w_blocks) return launch_cfg<256, 256, 4, 2, 1, true, MOE_TILED_TAIL, kBlockCols, kRoutedStages, true>(g, st);
     return launch_cfg<256, 256, 4, 2, 1, true, MOE_TILED_TAIL, kRoutedBK, kRoutedStages>(g, st);
 }
 
 hipError_t launch_down_tiled(const GemmProblem &g, hipStream_t st)
 {
     if (g.dense_rows > 0) return MOE_DENSE_DOWN_CFG(g, st);
+    if (g.w_blocks) return launch_cfg<256, 256, 4, 2, 1, false, MOE_TILED_TAIL, kBlockCols, kRoutedStages, true>(g, st);
     return launch_cfg<256, 256, 4, 2, 1, false, MOE_TILED_TAIL, kRoutedBK, kRoutedStages>(g, st);
 }
 

@@ -129,6 +129,18 @@ int check_shape(int64_t T, int64_t H, int64_t I, int64_t E, int32_t k, const moe
                                                  "weight-streaming schedule); T*k = %lld",
                             (long long)(T * k));
         }
+        if (opts->weight_layout != MOE_LAYOUT_ROWS && opts->weight_layout != MOE_LAYOUT_TILE_BLOCKS)
+            return fail(MOE_ERR_INVALID_ARG, "unknown weight_layout %d", opts->weight_layout);
+        if (opts->weight_layout == MOE_LAYOUT_TILE_BLOCKS) {
+            if (dtype != MOE_BF16 || opts->weight_format != MOE_WEIGHTS_NATIVE)
+                return fail(MOE_ERR_UNSUPPORTED, "tile-block weights are bf16 (dtype MOE_BF16, MOE_WEIGHTS_NATIVE)");
+            if (opts->flags & MOE_FLAG_FORCE_SKINNY)
+                return fail(MOE_ERR_INVALID_ARG, "tile-block weights run on the tiled kernels only "
+                                                 "(MOE_FLAG_FORCE_SKINNY)");
+            if (moe::tile_blocks_expert_bytes(0, I, H) >= ((int64_t)1 << 31) ||
+                moe::tile_blocks_expert_bytes(1, I, H) >= ((int64_t)1 << 31))
+                return fail(MOE_ERR_UNSUPPORTED, "one expert's tile blocks exceed 2^31 bytes");
+        }
     }
     return MOE_OK;
 }
@@ -148,6 +160,7 @@ Sched schedule(int64_t T, int32_t k, int64_t E, const moe_opts *opts)
     const uint32_t flags = opts ? opts->flags : 0;
     if (opts && opts->weight_format != MOE_WEIGHTS_NATIVE) return Sched::SKINNY;  // low-precision weights
     if (opts && opts->dtype == MOE_F32) return Sched::SKINNY;  // the fp32 kernels (one schedule)
+    if (opts && opts->weight_layout == MOE_LAYOUT_TILE_BLOCKS) return Sched::TILED;  // the blocks' only reader
     if (flags & MOE_FLAG_FORCE_SKINNY) return Sched::SKINNY;
     if (flags & MOE_FLAG_FORCE_TILED) return Sched::TILED;
     if (T * k > 32 * E) return Sched::TILED;  // more than about 32 rows per expert
@@ -319,14 +332,15 @@ static int forward_impl(const void *hidden, const void *router_w, const void *ga
         return fail(MOE_ERR_ALIGNMENT, "gate_up_scale / down_scale not 4-byte aligned");
     const uint64_t es = opts->dtype == MOE_BF16 ? 2 : 4;
     const uint64_t wes2 = w4 ? 1 : w8 ? 2 : 2 * es;  // twice the bytes per routed expert weight
+    const bool blocks = opts->weight_layout == MOE_LAYOUT_TILE_BLOCKS;
     const uint64_t out_bytes = (uint64_t)T * H * es;
     struct Range {
         const void *p;
         uint64_t n;
     } ins[] = {{hidden, (uint64_t)T * H * es},
                {router_w, (uint64_t)E * H * es},
-               {gate_up, (uint64_t)E * 2 * I * H * wes2 / 2},
-               {down, (uint64_t)E * H * I * wes2 / 2},
+               {gate_up, blocks ? (uint64_t)E * moe::tile_blocks_expert_bytes(0, I, H) : (uint64_t)E * 2 * I * H * wes2 / 2},
+               {down, blocks ? (uint64_t)E * moe::tile_blocks_expert_bytes(1, I, H) : (uint64_t)E * H * I * wes2 / 2},
                {opts->gate_up_scale, w8 ? (uint64_t)E * 2 * I * 4 : 0},
                {opts->down_scale, w8 ? (uint64_t)E * H * 4 : 0},
                {opts->gate_up_block_scale, w4 ? (uint64_t)E * 2 * I * (H / 32) : 0},
@@ -462,6 +476,10 @@ static int forward_impl(const void *hidden, const void *router_w, const void *ga
     gu.cus = cus;
     gu.a_rows_total = T;
     gu.skinny_max_rows = sched == Sched::MIXED ? moe::kSkinnyMaxRows : 0;
+    if (blocks) {
+        gu.w_blocks = true;
+        gu.w_expert_stride = moe::tile_blocks_expert_bytes(0, I, H) / 2;
+    }
 
     moe::GemmProblem dn = gu;
     dn.A = ws.h;
@@ -469,7 +487,7 @@ static int forward_impl(const void *hidden, const void *router_w, const void *ga
     dn.W = down;
     dn.w_scale = w8 ? opts->down_scale : nullptr;
     dn.w_bscale = w4 ? opts->down_block_scale : nullptr;
-    dn.w_expert_stride = H * I;
+    dn.w_expert_stride = blocks ? moe::tile_blocks_expert_bytes(1, I, H) / 2 : H * I;
     dn.K = I;
     dn.N = H;
     dn.C = ws.slot;
@@ -499,6 +517,7 @@ static int forward_impl(const void *hidden, const void *router_w, const void *ga
         sg.W = opts->shared_gate_up;
         sg.w_scale = nullptr;  // the shared expert keeps opts->dtype
         sg.w_bscale = nullptr;
+        sg.w_blocks = false;  // and MOE_LAYOUT_ROWS
         sg.w_expert_stride = 0;
         sg.N = opts->shared_I;
         sg.C = ws.sh_h;
@@ -565,6 +584,36 @@ int moe_forward_noalloc(const void *hidden, const void *router_w, const void *ga
     o.workspace = ptr;
     o.workspace_bytes = kScratchBytes;
     return forward_impl(hidden, router_w, gate_up, down, T, H, I, E, k, &o, out);
+}
+
+int64_t moe_tile_blocks_bytes(int32_t which, int64_t E, int64_t I, int64_t H)
+{
+    g_err[0] = 0;
+    if (which != MOE_PACK_GATE_UP && which != MOE_PACK_DOWN)
+        return fail(MOE_ERR_INVALID_ARG, "which = %d: MOE_PACK_GATE_UP or MOE_PACK_DOWN", which);
+    if (E < 1 || E > moe::kMaxExperts)
+        return fail(MOE_ERR_INVALID_ARG, "E = %lld outside [1, %d]", (long long)E, moe::kMaxExperts);
+    if (H < 8 || H % 8) return fail(MOE_ERR_INVALID_ARG, "H = %lld must be a positive multiple of 8", (long long)H);
+    if (I < 8 || I % 8) return fail(MOE_ERR_INVALID_ARG, "I = %lld must be a positive multiple of 8", (long long)I);
+    if (H > (1 << 24) || I > (1 << 24))
+        return fail(MOE_ERR_UNSUPPORTED, "H = %lld or I = %lld above 2^24", (long long)H, (long long)I);
+    const int64_t per = moe::tile_blocks_expert_bytes(which, I, H);
+    if (per >= ((int64_t)1 << 31)) return fail(MOE_ERR_UNSUPPORTED, "one expert's tile blocks exceed 2^31 bytes");
+    return E * per;
+}
+
+int moe_pack_tile_blocks(int32_t which, const void *w, int64_t E, int64_t I, int64_t H, void *out, void *stream)
+{
+    const int64_t n = moe_tile_blocks_bytes(which, E, I, H);  // argument checks
+    if (n < 0) return (int)n;
+    if (!w || !out) return fail(MOE_ERR_INVALID_ARG, "w and out must be non-NULL");
+    if (!aligned(w, 16) || !aligned(out, 16)) return fail(MOE_ERR_ALIGNMENT, "w and out must be 16-byte aligned");
+    const uint64_t wbytes = (uint64_t)E * (which == MOE_PACK_GATE_UP ? 2 * I * H : H * I) * 2;
+    if (overlaps(out, (uint64_t)n, w, wbytes)) return fail(MOE_ERR_INVALID_ARG, "out overlaps w");
+    hipError_t err = moe::launch_pack_tile_blocks(which, w, E, I, H, out, (hipStream_t)stream);
+    if (err == hipSuccess && debug_sync()) err = hipStreamSynchronize((hipStream_t)stream);
+    if (err != hipSuccess) return fail(MOE_ERR_HIP, "pack_tile_blocks failed: %s", hipGetErrorString(err));
+    return MOE_OK;
 }
 
 int moe_quantize_fp8_rows(const void *w, int64_t rows, int64_t cols, void *q, float *scale, void *stream)

@@ -160,7 +160,21 @@ struct GemmProblem {
     int cus = 0;             // compute units of the device (persistent grids)
     int64_t a_rows_total = 0;  // rows of A (gate_up: tokens; down: assignments or tokens)
     int skinny_max_rows = 0;   // > 0: the weight-streaming launch leaves experts with more rows to the tiled one
+    bool w_blocks = false;     // routed weights in tile blocks (MOE_LAYOUT_TILE_BLOCKS; tiled kernels only)
 };
+
+// Tile blocks (MOE_LAYOUT_TILE_BLOCKS): 256 weight rows x 32 columns per block.
+constexpr int kBlockRows = 256;
+constexpr int kBlockCols = 32;
+// Bytes of one expert's tile blocks (which: MOE_PACK_GATE_UP / MOE_PACK_DOWN).
+inline int64_t tile_blocks_expert_bytes(int which, int64_t I, int64_t H)
+{
+    const int64_t nb = which == 0 ? (I + 127) / 128 : (H + kBlockRows - 1) / kBlockRows;
+    const int64_t nk = which == 0 ? (H + kBlockCols - 1) / kBlockCols : (I + kBlockCols - 1) / kBlockCols;
+    return nb * nk * kBlockRows * kBlockCols * 2;
+}
+hipError_t launch_pack_tile_blocks(int which, const void *w, int64_t E, int64_t I, int64_t H, void *out,
+                                   hipStream_t st);
 
 // Largest T*k for which the weight-streaming kernels route directly from the ids.
 constexpr int kSkinnyDirectMax = 1024;

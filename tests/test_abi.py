@@ -433,3 +433,80 @@ def test_workspace_of_each_schedule():
     forced = moe.workspace_bytes(256, 4096, 6400, 16, 2, flags=moe.FLAG_FORCE_SKINNY)
     assert mixed - forced >= split
     assert mixed <= moe.NOALLOC_SCRATCH_BYTES
+
+
+def blocks_opts():
+    o = good_opts(nbytes=100)  # too small: a valid call stops at the workspace check
+    o.weight_layout = moe.LAYOUT_TILE_BLOCKS
+    return o
+
+
+def test_tile_blocks_bytes_follow_the_header():
+    # E * ceil(I/128) * ceil(H/32) * 16 KB (gate_up), E * ceil(H/256) * ceil(I/32) * 16 KB (down)
+    for E, I, H in ((16, 6400, 4096), (4, 200, 328), (1, 8, 8), (64, 1024, 2048), (3, 136, 264)):
+        gu = moe.tile_blocks_bytes(moe.PACK_GATE_UP, E, I, H)
+        dn = moe.tile_blocks_bytes(moe.PACK_DOWN, E, I, H)
+        assert gu == E * (-(-I // 128)) * (-(-H // 32)) * 256 * 32 * 2
+        assert dn == E * (-(-H // 256)) * (-(-I // 32)) * 256 * 32 * 2
+        # never smaller than the nn.Linear layout; equal when the blocks tile it exactly
+        assert gu >= E * 2 * I * H * 2 and dn >= E * H * I * 2
+    assert moe.tile_blocks_bytes(moe.PACK_GATE_UP, 16, 6400, 4096) == 16 * 2 * 6400 * 4096 * 2
+    lib = moe.load_library()
+    assert lib.moe_tile_blocks_bytes(2, 4, 32, 64) == -1          # which
+    assert lib.moe_tile_blocks_bytes(0, 0, 32, 64) == -1          # E
+    assert lib.moe_tile_blocks_bytes(0, 4, 36, 64) == -1          # I not a multiple of 8
+    assert lib.moe_tile_blocks_bytes(1, 4, 32, 0) == -1           # H
+    assert lib.moe_tile_blocks_bytes(0, 4, 8, 1 << 24) == -2      # one expert's blocks past 2^31 bytes
+
+
+def test_pack_tile_blocks_checks_arguments():
+    lib = moe.load_library()
+    vp = ctypes.c_void_p
+    base = 1 << 40
+    w, out = vp(base), vp(base + (1 << 30))
+    assert lib.moe_pack_tile_blocks(3, w, 4, 32, 64, out, None) == -1
+    assert lib.moe_pack_tile_blocks(0, None, 4, 32, 64, out, None) == -1
+    assert lib.moe_pack_tile_blocks(0, w, 4, 32, 64, None, None) == -1
+    assert lib.moe_pack_tile_blocks(0, vp(base + 8), 4, 32, 64, out, None) == -4
+    assert lib.moe_pack_tile_blocks(1, w, 4, 32, 64, vp(base + 4096), None) == -1  # out overlaps w
+    assert "overlaps" in moe.last_error()
+
+
+def test_tile_block_layout_options_are_checked():
+    rc, msg = call(opts=blocks_opts())  # valid apart from the fake addresses: reaches the workspace check
+    assert rc == -3, msg
+    o = blocks_opts()
+    o.weight_layout = 5
+    rc, msg = call(opts=o)
+    assert rc == -1 and "weight_layout" in msg
+    o = blocks_opts()
+    o.dtype = 1
+    assert call(opts=o)[0] == -2
+    o = blocks_opts()
+    o.weight_format = moe.WEIGHTS_FP8_E4M3
+    o.gate_up_scale = (1 << 40) + (5 << 30)
+    o.down_scale = (1 << 40) + (6 << 30)
+    assert call(opts=o)[0] == -2
+    o = blocks_opts()
+    o.flags = moe.FLAG_FORCE_SKINNY
+    rc, msg = call(opts=o)
+    assert rc == -1 and "tiled" in msg
+    # the blocks are larger than the rows when the tiles overhang (I = 200: two
+    # 128-row halves per expert): out just past the rows' end but inside the blocks
+    E, I, H = 4, 200, 328
+    rows_end = (1 << 40) + (2 << 30) + E * 2 * I * H * 2
+    rc, msg = call(T=4, H=H, I=I, E=E, opts=blocks_opts(), out=rows_end + 256)
+    assert rc == -1 and "overlaps" in msg
+    rc, _ = call(T=4, H=H, I=I, E=E, opts=good_opts(nbytes=100), out=rows_end + 256)
+    assert rc == -3  # the row layout ends before out
+
+
+def test_tile_blocks_take_the_tiled_schedule_at_any_size():
+    # the blocks are read by the tiled kernels only: a decode-sized call sizes
+    # the split-K buffer of the tiled schedule
+    o = moe.new_opts()
+    o.weight_layout = moe.LAYOUT_TILE_BLOCKS
+    lib = moe.load_library()
+    blocks = lib.moe_workspace_bytes(32, 4096, 6400, 16, 2, ctypes.byref(o))
+    tiled = moe.workspace_bytes(32, 4096, 6400, 16, 2, flags=moe.FLAG_FORCE_TILED)
+    assert blocks == tiled > moe.workspace_bytes(32, 4096, 6400, 16, 2)
