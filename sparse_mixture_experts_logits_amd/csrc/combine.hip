@@ -11,6 +11,17 @@ namespace moe {
 
 namespace {
 
+// Slots and the shared output are read once: non-temporal loads keep them
+// from displacing what the next launches reuse (skewed workload: 128 ->
+// 108 us for 0.54 GB of slots; the Instella-style layer's next gate_up also
+// ran 4% faster).
+__device__ __forceinline__ float4 ld4(const float *p)
+{
+    typedef float f4v __attribute__((ext_vector_type(4)));
+    const f4v v = __builtin_nontemporal_load(reinterpret_cast<const f4v *>(p));
+    return make_float4(v.x, v.y, v.z, v.w);
+}
+
 template <bool BF16OUT>
 __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ slot,
                                                       const float *__restrict__ sh_y, int64_t T,
@@ -21,13 +32,13 @@ __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ 
         const int64_t t = idx / (H / 4);
         const int64_t c = (idx - t * (H / 4)) * 4;
         const float *s = slot + (t * k) * H + c;
-        float4 acc = *reinterpret_cast<const float4 *>(s);
+        float4 acc = ld4(s);
         for (int j = 1; j < k; j++) {
-            const float4 v = *reinterpret_cast<const float4 *>(s + (int64_t)j * H);
+            const float4 v = ld4(s + (int64_t)j * H);
             acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
         }
         if (sh_y) {
-            const float4 v = *reinterpret_cast<const float4 *>(sh_y + t * H + c);
+            const float4 v = ld4(sh_y + t * H + c);
             acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
         }
         if (BF16OUT) {

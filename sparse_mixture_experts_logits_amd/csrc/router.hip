@@ -93,8 +93,8 @@ __device__ __forceinline__ bool ranks_before(float va, int ia, float vb, int ib)
 // takes TG tokens x 4 experts at a time so every loaded slice of hidden and
 // router weights feeds several dot products, and all loads of a 512-element
 // chunk are issued before its fmas.
-template <typename Tin, int RT>
-__global__ __launch_bounds__(256) void router_topk_kernel(
+template <typename Tin, int RT, int NW>
+__global__ __launch_bounds__(NW * 64) void router_topk_kernel(
     const Tin *__restrict__ X, const Tin *__restrict__ Wr, const float *__restrict__ bias, int T,
     int H, int E, int k, float routed_scale, int32_t *__restrict__ ids, float *__restrict__ wts,
     int32_t *__restrict__ ids_out, float *__restrict__ wts_out, float *__restrict__ logits_out,
@@ -124,14 +124,14 @@ __global__ __launch_bounds__(256) void router_topk_kernel(
     const int tblk = blockIdx.x * RT;
     const bool stats = blk_prob != nullptr;
 
-    for (int e = threadIdx.x; e < E; e += 256) {
+    for (int e = threadIdx.x; e < E; e += NW * 64) {
         s_hist[e] = 0;
         s_mhist[e] = 0;
     }
     if (threadIdx.x == 0) s_ntok = 0;
 
     // ---- logits
-    const int epw = (E + 3) / 4;
+    const int epw = (E + NW - 1) / NW;
     const int e_lo = wave * epw;
     const int e_hi = min(E, e_lo + epw);
     const int nchunk = (H + 511) / 512;
@@ -215,7 +215,7 @@ __global__ __launch_bounds__(256) void router_topk_kernel(
 
     // ---- optional logits output
     if (logits_out) {
-        for (int idx = threadIdx.x; idx < RT * E; idx += 256) {
+        for (int idx = threadIdx.x; idx < RT * E; idx += NW * 64) {
             const int j = idx / E, e = idx - j * E;
             const int t = tblk + j;
             if (t < T) logits_out[(int64_t)t * E + e] = s_logit[j][e];
@@ -223,7 +223,7 @@ __global__ __launch_bounds__(256) void router_topk_kernel(
     }
 
     // ---- top-k per token: k rounds of a wave-wide arg-max under the ranking rule
-    for (int j = wave; j < RT; j += 4) {
+    for (int j = wave; j < RT; j += NW) {  // RT <= 4 with NW = 8: waves 4..7 route no token
         const int t = tblk + j;
         if (t >= T) break;  // wave-uniform
         const float *lrow = s_logit[j];
@@ -412,10 +412,10 @@ __global__ __launch_bounds__(256) void router_topk_kernel(
         __builtin_amdgcn_wave_barrier();
     }
     __syncthreads();
-    for (int e = threadIdx.x; e < E; e += 256) blk_counts[(int64_t)blockIdx.x * E + e] = s_hist[e];
+    for (int e = threadIdx.x; e < E; e += NW * 64) blk_counts[(int64_t)blockIdx.x * E + e] = s_hist[e];
     if (stats) {
         const int nt = min(RT, T - tblk);
-        for (int e = threadIdx.x; e < E; e += 256) {
+        for (int e = threadIdx.x; e < E; e += NW * 64) {
             float ps = 0.0f;
             for (int j = 0; j < nt; j++) ps += s_prob[j][e];  // token order
             blk_prob[(int64_t)blockIdx.x * E + e] = ps;
@@ -616,20 +616,28 @@ hipError_t launch_router_topk(const Shape &s, const void *X, const void *Wr, con
                               float routed_scale, float *logits_out, int32_t *ids_out, float *wts_out,
                               const RouterStats &rs, const RouterCfg &rc, const Workspace &ws, hipStream_t st)
 {
-    dim3 grid(s.nblk), block(256);
+    dim3 grid(s.nblk);
     float *bp = rs.on() ? ws.blk_prob : nullptr;
-#define MOE_ROUTER_LAUNCH(TIN, RT)                                                                      \
-    hipLaunchKernelGGL((router_topk_kernel<TIN, RT>), grid, block, 0, st, (const TIN *)X, (const TIN *)Wr, \
+#define MOE_ROUTER_LAUNCH(TIN, RT, NW)                                                                  \
+    hipLaunchKernelGGL((router_topk_kernel<TIN, RT, NW>), grid, dim3(NW * 64), 0, st, (const TIN *)X, (const TIN *)Wr, \
                        bias, (int)s.T, (int)s.H, (int)s.E, s.k, routed_scale, ws.ids, ws.wts, ids_out,  \
                        wts_out, logits_out, ws.blk_counts, rs.mask, bp, ws.blk_mcnt, ws.blk_ntok,     \
                        rc.score_func, rc.sel_bias, rc.n_group, rc.topk_group, rc.jitter_eps)
     static_assert(kRouterMaxTokensPerBlock == 4, "router blocks of 1 or 4 tokens");
+    // 32 experts or more: 8 waves share a block's experts (each wave's chain of
+    // chunk loads half as long); fewer: 4 waves
+    const bool wide = s.E >= 32;
     if (s.dtype == 0) {
-        if (s.rtok == 1) MOE_ROUTER_LAUNCH(__bf16, 1);
-        else MOE_ROUTER_LAUNCH(__bf16, 4);
+        if (s.rtok == 1) {
+            if (wide) MOE_ROUTER_LAUNCH(__bf16, 1, 8);
+            else MOE_ROUTER_LAUNCH(__bf16, 1, 4);
+        } else {
+            if (wide) MOE_ROUTER_LAUNCH(__bf16, 4, 8);
+            else MOE_ROUTER_LAUNCH(__bf16, 4, 4);
+        }
     } else {
-        if (s.rtok == 1) MOE_ROUTER_LAUNCH(float, 1);
-        else MOE_ROUTER_LAUNCH(float, 4);
+        if (s.rtok == 1) MOE_ROUTER_LAUNCH(float, 1, 4);
+        else MOE_ROUTER_LAUNCH(float, 4, 4);
     }
 #undef MOE_ROUTER_LAUNCH
     return hipGetLastError();
