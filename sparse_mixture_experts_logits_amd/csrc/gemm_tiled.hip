@@ -117,10 +117,10 @@ __device__ __forceinline__ void band_order(int local, int nte, int NB, int &mt, 
     mt = mbase + (within - nb * sm);
 }
 
-// tile id -> (expert, N-block, first row, rows)
+// tile id -> (expert, N-block, first row, rows, index in the M-tile list)
 template <int BM>
 __device__ __forceinline__ void decode_tile(const TiledParams &p, int id, int n_mtiles, int &e, int &nb, int &row0,
-                                            int &rows)
+                                            int &rows, int &tix)
 {
     if (p.tiles) {
         const int32_t *s_ts = p.tile_start;
@@ -132,47 +132,125 @@ __device__ __forceinline__ void decode_tile(const TiledParams &p, int id, int n_
         e = lo;
         int mt;
         band_order(id - s_ts[e] * p.NB, s_ts[e + 1] - s_ts[e], p.NB, mt, nb);
-        const MTile t = p.tiles[s_ts[e] + mt];
+        tix = s_ts[e] + mt;
+        const MTile t = p.tiles[tix];
         row0 = t.row0;
         rows = t.rows;
     } else {
         e = 0;
         int mt;
         band_order(id, n_mtiles, p.NB, mt, nb);
+        tix = mt;
         row0 = mt * BM;
         rows = min(BM, p.dense_rows - row0);
+    }
+}
+
+// Stores 16 bf16 values of h: column c0 + lane % 32 (c0 a wave-uniform
+// multiple of 32), rows rbase + 8 (q / 4) + 4 (lane / 32) + q % 4 of M-tile
+// tix (first row row0), skipping rows past the tile's and columns past N.
+// Rows are row-major, or in the h row blocks of the tile list, where the
+// block of the 32 columns is wave-uniform (one scalar base per block).
+template <bool HB>
+__device__ __forceinline__ void store_h16(const TiledParams &p, int tix, int row0, int rows, int c0, int rbase,
+                                          int lane, const uint32_t (&v)[16])
+{
+    static_assert(kBlockCols == 32, "column block of 32");
+    const int c = c0 + (lane & 31);
+    uint16_t *h = reinterpret_cast<uint16_t *>(p.C);
+    if (HB) {
+        // the block through a buffer resource (scalar registers) and one
+        // 32-bit offset a lane: no per-element 64-bit addresses
+        const int nkb = (p.N + kBlockCols - 1) / kBlockCols;
+        uint16_t *hb = h + ((int64_t)tix * nkb + (c0 >> 5)) * (kHBlockRows * kBlockCols);
+        const __amdgpu_buffer_rsrc_t r =
+            __builtin_amdgcn_make_buffer_rsrc(hb, 0, kHBlockRows * kBlockCols * 2, 0x00020000);
+#pragma unroll
+        for (int q = 0; q < 16; q++) {
+            const int rr = rbase + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
+            if (rr < rows && c < p.N)
+                __builtin_amdgcn_raw_buffer_store_b16((uint16_t)v[q], r, (rr * kBlockCols + (lane & 31)) * 2, 0, 0);
+        }
+    } else {
+#pragma unroll
+        for (int q = 0; q < 16; q++) {
+            const int rr = rbase + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
+            if (rr < rows && c < p.N) h[(int64_t)(row0 + rr) * p.N + c] = (uint16_t)v[q];
+        }
     }
 }
 
 // Epilogue of one tile from the accumulators of wave (wm, wn): h = silu(gate)
 // * up as bf16 (gate_up) or the weighted fp32 slot rows (down). xg: LDS for
 // the gate halves of the extra rows (gate_up with XT > 0).
-template <int BM, int BN, int WM, int WN, bool GATEUP, int XT>
+template <int BM, int BN, int WM, int WN, bool GATEUP, int XT, bool HB>
 __device__ __forceinline__ void tile_epilogue(const TiledParams &p, const f32x16_t (&acc)[BM / WM / 32][BN / WN / 32],
                                               const f32x16_t &accx, int wm, int wn, int lane, int row0, int rows,
-                                              int nb, bool xtra, float *xgs)
+                                              int nb, bool xtra, float *xgs, int tix, uint16_t *stage)
 {
     constexpr int RM = BM / WM / 32;
     constexpr int RN = BN / WN / 32;
     const int jx = GATEUP ? (wm >> 1) + (RN / 2) * (wm & 1) : wm;
-    if (GATEUP) {
+    if constexpr (GATEUP && HB) {
+        // h row blocks: the tile's h goes through LDS (the idle stage ring) in
+        // block order, then out in 16-byte pieces, each 32-column block of
+        // the tile one contiguous run of its rows
         constexpr int HW = BN / 2 / WN;
-        __bf16 *H = reinterpret_cast<__bf16 *>(p.C);
+        constexpr int NCB = BN / 2 / kBlockCols;  // column blocks of the tile
+        constexpr int NT = WM * WN * 64;
+        __syncthreads();  // every wave is done with the stage ring
 #pragma unroll
         for (int i = 0; i < RM; i++)
 #pragma unroll
             for (int j = 0; j < RN / 2; j++) {
-                const int c = nb * (BN / 2) + wn * HW + j * 32 + (lane & 31);
+                const int cb = (wn * HW + j * 32) / kBlockCols;  // wave-uniform
 #pragma unroll
                 for (int q = 0; q < 16; q++) {
                     const int rr = wm * (BM / WM) + i * 32 + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
-                    if (rr < rows && c < p.N) {
-                        const float g = acc[i][j][q];
-                        const float u = acc[i][j + RN / 2][q];
-                        const uint32_t hb = f32_to_bf16_bits(silu_f32(g) * u);
-                        reinterpret_cast<uint16_t *>(H)[(int64_t)(row0 + rr) * p.N + c] = (uint16_t)hb;
-                    }
+                    stage[(cb * kHBlockRows + rr) * kBlockCols + (lane & 31)] =
+                        (uint16_t)f32_to_bf16_bits(silu_f32(acc[i][j][q]) * acc[i][j + RN / 2][q]);
                 }
+            }
+        if (XT > 0 && xtra) {
+            float *xg = xgs + (wn * 2 + (wm >> 1)) * (16 * 64);
+            if ((wm & 1) == 0) {
+#pragma unroll
+                for (int q = 0; q < 16; q++) xg[q * 64 + lane] = accx[q];
+            }
+            __syncthreads();
+            if (wm & 1) {
+                const int cb = (wn * HW + (wm >> 1) * 32) / kBlockCols;
+#pragma unroll
+                for (int q = 0; q < 16; q++) {
+                    const int rr = BM + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
+                    stage[(cb * kHBlockRows + rr) * kBlockCols + (lane & 31)] =
+                        (uint16_t)f32_to_bf16_bits(silu_f32(xg[q * 64 + lane]) * accx[q]);
+                }
+            }
+        }
+        __syncthreads();
+        const int nkb = (p.N + kBlockCols - 1) / kBlockCols;
+        const u32x4 *src = reinterpret_cast<const u32x4 *>(stage);
+        u32x4 *dst = reinterpret_cast<u32x4 *>(p.C);
+        constexpr int PIECES = kBlockCols * 2 / 16;  // 16-byte pieces per block row
+        for (int ch = threadIdx.x; ch < NCB * kHBlockRows * PIECES; ch += NT) {
+            const int cb = ch / (kHBlockRows * PIECES);
+            const int r = (ch / PIECES) % kHBlockRows;
+            if (r < rows && (nb * NCB + cb) * kBlockCols < p.N)
+                dst[(((int64_t)tix * nkb + nb * NCB + cb) * kHBlockRows + r) * PIECES + ch % PIECES] = src[ch];
+        }
+        return;
+    }
+    if (GATEUP) {
+        constexpr int HW = BN / 2 / WN;
+#pragma unroll
+        for (int i = 0; i < RM; i++)
+#pragma unroll
+            for (int j = 0; j < RN / 2; j++) {
+                uint32_t v[16];
+#pragma unroll
+                for (int q = 0; q < 16; q++) v[q] = f32_to_bf16_bits(silu_f32(acc[i][j][q]) * acc[i][j + RN / 2][q]);
+                store_h16<HB>(p, tix, row0, rows, nb * (BN / 2) + wn * HW + j * 32, wm * (BM / WM) + i * 32, lane, v);
             }
         if (XT > 0 && xtra) {
             // gate blocks (even wm) to LDS; the up waves (odd wm) combine
@@ -183,15 +261,10 @@ __device__ __forceinline__ void tile_epilogue(const TiledParams &p, const f32x16
             }
             __syncthreads();
             if (wm & 1) {
-                const int c = nb * (BN / 2) + wn * HW + (wm >> 1) * 32 + (lane & 31);
+                uint32_t v[16];
 #pragma unroll
-                for (int q = 0; q < 16; q++) {
-                    const int rr = BM + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
-                    if (rr < rows && c < p.N) {
-                        const uint32_t hb = f32_to_bf16_bits(silu_f32(xg[q * 64 + lane]) * accx[q]);
-                        reinterpret_cast<uint16_t *>(H)[(int64_t)(row0 + rr) * p.N + c] = (uint16_t)hb;
-                    }
-                }
+                for (int q = 0; q < 16; q++) v[q] = f32_to_bf16_bits(silu_f32(xg[q * 64 + lane]) * accx[q]);
+                store_h16<HB>(p, tix, row0, rows, nb * (BN / 2) + wn * HW + (wm >> 1) * 32, BM, lane, v);
             }
         }
     } else {
@@ -289,12 +362,14 @@ __device__ __forceinline__ uint32_t lds_addr(const void *p) { return (uint32_t)(
 // gate_up: the four waves of a column half take the gate and the up block of
 // its two output column blocks, and the gate blocks reach the matching up
 // waves through LDS in the epilogue.
-template <int BM, int BN, int WM, int WN, int OCC, bool GATEUP, int XT, int BK, int STAGES, bool WPACK>
+template <int BM, int BN, int WM, int WN, int OCC, bool GATEUP, int XT, int BK, int STAGES, bool WPACK, bool HB>
 __global__ __launch_bounds__(WM *WN * 64, OCC) void tiled_gemm_kernel(TiledParams p)
 {
     // WPACK: the weights are in tile blocks (one stage of one N-block = 256
     // rows x 32 columns, contiguous; zero-filled past N and K)
     static_assert(!WPACK || (BN == kBlockRows && BK == kBlockCols), "tile blocks are 256 x 32");
+    // a routed down launch may read h row blocks: one tile's rows, 32 columns a stage
+    static_assert(GATEUP || XT == 0 || (BM + XT == kHBlockRows && BK == kBlockCols), "h row blocks are 288 x 32");
     constexpr int CH = BK / 8;    // 16-byte chunks per row of a stage
     constexpr int RPI = 64 / CH;  // rows filled by one 64-lane copy instruction
     static_assert(CH == 4 || CH == 8, "stage rows of 64 or 128 bytes");
@@ -371,7 +446,8 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void tiled_gemm_kernel(TiledParam
 
         // ---- decode tile id -> (expert, M-tile, N-block)
         int e, nb, row0, rows;
-        decode_tile<BM>(p, id, n_mtiles, e, nb, row0, rows);
+        int tix;
+        decode_tile<BM>(p, id, n_mtiles, e, nb, row0, rows, tix);
         const bool xtra = XT > 0 && rows > BM;  // tile-uniform
 
         // ---- per-lane DMA sources (rows past the tile repeat row 0; dropped
@@ -381,13 +457,21 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void tiled_gemm_kernel(TiledParam
         auto chunk_of = [&](int rr) { return (lane % CH) ^ lds_swz<CH>(rr); };
         const uint32_t krow = (uint32_t)p.K * 2u;  // bytes per row
         const i32x4_t ra = buf_rsrc(p.A, p.a_bytes);
+        // A in h row blocks (down after a tiled gate_up): row rc of the tile's
+        // block for stage kt at ((tix * nk_all + kt) * kHBlockRows + rc) * 64
+        constexpr bool ablk = !GATEUP && HB;
+        const uint32_t ablock0 = (uint32_t)(tix * nk_all + ks) * (uint32_t)kHBlockRows;
         uint32_t aoff[A_INS];
 #pragma unroll
         for (int i = 0; i < A_INS; i++) {
             const int rr = RPI * (wave * A_INS + i) + drow;
             const int rc = rr < rows ? rr : 0;
-            const uint32_t src = p.a_rows ? (uint32_t)p.a_rows[row0 + rc] : (uint32_t)(row0 + rc);
-            aoff[i] = src * krow + (uint32_t)kbase * 2u + (uint32_t)chunk_of(rr) * 16u;
+            if (ablk) {
+                aoff[i] = (ablock0 + (uint32_t)rc) * (BK * 2u) + (uint32_t)chunk_of(rr) * 16u;
+            } else {
+                const uint32_t src = p.a_rows ? (uint32_t)p.a_rows[row0 + rc] : (uint32_t)(row0 + rc);
+                aoff[i] = src * krow + (uint32_t)kbase * 2u + (uint32_t)chunk_of(rr) * 16u;
+            }
         }
         // extra rows BM + XR*wave + lane/CH, lanes below XR*CH (rows past the
         // tile repeat row BM)
@@ -396,8 +480,12 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void tiled_gemm_kernel(TiledParam
         const int xrr = BM + XR * wave + (xlane ? drow : 0);
         if (XT > 0 && xtra) {
             const int rc = xrr < rows ? xrr : BM;
-            const uint32_t src = p.a_rows ? (uint32_t)p.a_rows[row0 + rc] : (uint32_t)(row0 + rc);
-            xoff = src * krow + (uint32_t)kbase * 2u + (uint32_t)chunk_of(xrr) * 16u;
+            if (ablk) {
+                xoff = (ablock0 + (uint32_t)rc) * (BK * 2u) + (uint32_t)chunk_of(xrr) * 16u;
+            } else {
+                const uint32_t src = p.a_rows ? (uint32_t)p.a_rows[row0 + rc] : (uint32_t)(row0 + rc);
+                xoff = src * krow + (uint32_t)kbase * 2u + (uint32_t)chunk_of(xrr) * 16u;
+            }
         }
         const i32x4_t rb = buf_rsrc(p.W + (int64_t)e * p.w_expert_stride,
                                     WPACK ? (uint32_t)p.w_expert_stride * 2u : (uint32_t)(GATEUP ? 2 * p.N : p.N) * krow);
@@ -425,8 +513,10 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void tiled_gemm_kernel(TiledParam
         // partial stage (K not a multiple of BK) masks lanes; they zero-fill.
         // stage kt's offset into the weights: BK columns of a row, or one tile block
         auto wstage = [&](int kt) { return WPACK ? (uint32_t)kt * (BN * BK * 2u) : (uint32_t)(kt * BK) * 2u; };
+        // and into A: BK columns of a row, or one block of the h row blocks
+        auto astage = [&](int kt) { return ablk ? (uint32_t)kt * (kHBlockRows * BK * 2u) : (uint32_t)(kt * BK) * 2u; };
         auto issue = [&](int kt, int b) {
-            const uint32_t k0 = (uint32_t)(kt * BK) * 2u;
+            const uint32_t k0 = astage(kt);
 #pragma unroll
             for (int i = 0; i < A_INS; i++) dma16(ra, aoff[i], k0, lds_addr(&sA[b][(wave * A_INS + i) * 64]));
 #pragma unroll
@@ -435,7 +525,7 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void tiled_gemm_kernel(TiledParam
         };
         auto issue_tail = [&](int kt, int b) {
             const int k0 = kt * BK;
-            const uint32_t k0b = (uint32_t)k0 * 2u;
+            const uint32_t k0b = astage(kt);
 #pragma unroll
             for (int i = 0; i < A_INS; i++) {
                 u32x4 *dst = &sA[b][(wave * A_INS + i) * 64];
@@ -497,7 +587,7 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void tiled_gemm_kernel(TiledParam
 
         // copy instruction q (A rows, then B rows, then the extra rows) of stage kt into buffer b
         auto issue_one = [&](int kt, int b, int q) {
-            const uint32_t k0 = (uint32_t)(kt * BK) * 2u;
+            const uint32_t k0 = astage(kt);
             if (q < A_INS) dma16(ra, aoff[q], k0, lds_addr(&sA[b][(wave * A_INS + q) * 64]));
             else if (q < LOADS) dma16(rb, boff[q - A_INS], wstage(kt), lds_addr(&sB[b][(wave * B_INS + q - A_INS) * 64]));
             else if (xlane) dma16(ra, xoff, k0, lds_addr(&sA[b][(BM + XR * wave) * CH]));
@@ -628,7 +718,10 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void tiled_gemm_kernel(TiledParam
                 for (int q = 0; q < 16; q++) pp[(RM * RN) * 1024 + q * 64] = accx[q];
             }
         } else {
-            tile_epilogue<BM, BN, WM, WN, GATEUP, XT>(p, acc, accx, wm, wn, lane, row0, rows, nb, xtra, &s_xg[0][0]);
+            static_assert(!(GATEUP && HB) || (BN / 2 / kBlockCols) * kHBlockRows * kBlockCols * 2 <= (int)sizeof(sA),
+                          "the tile's h row blocks fit the stage ring");
+            tile_epilogue<BM, BN, WM, WN, GATEUP, XT, HB>(p, acc, accx, wm, wn, lane, row0, rows, nb, xtra, &s_xg[0][0],
+                                                      tix, reinterpret_cast<uint16_t *>(&sA[0][0]));
         }
     }
 }
@@ -639,7 +732,7 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void tiled_gemm_kernel(TiledParam
 // the tile as the main kernel's epilogue would (the extra rows go with row
 // block 0; for gate_up an up wave sums its gate partner's partials as well). The split plan is recomputed from the
 // same inputs as the main kernel's.
-template <int BM, int BN, int WM, int WN, bool GATEUP, int XT, int BK>
+template <int BM, int BN, int WM, int WN, bool GATEUP, int XT, int BK, bool HB>
 __global__ __launch_bounds__(64) void tiled_split_finish_kernel(TiledParams p)
 {
     constexpr int NWAVE = WM * WN;
@@ -660,7 +753,8 @@ __global__ __launch_bounds__(64) void tiled_split_finish_kernel(TiledParams p)
     const int wm = wave / WN;
     const int wn = wave - wm * WN;
     int e, nb, row0, rows;
-    decode_tile<BM>(p, sp.full + t, n_mtiles, e, nb, row0, rows);
+    int tix;
+    decode_tile<BM>(p, sp.full + t, n_mtiles, e, nb, row0, rows, tix);
     (void)e;
     const bool xtra = XT > 0 && rows > BM;
 
@@ -686,32 +780,25 @@ __global__ __launch_bounds__(64) void tiled_split_finish_kernel(TiledParams p)
 
     if (GATEUP) {
         constexpr int HW = BN / 2 / WN;
-        uint16_t *H = reinterpret_cast<uint16_t *>(p.C);
 #pragma unroll
             for (int j = 0; j < RN / 2; j++) {
                 f32x16_t g, u;
                 sum_block(wave, i * RN + j, g);
                 sum_block(wave, i * RN + j + RN / 2, u);
-                const int c = nb * (BN / 2) + wn * HW + j * 32 + (lane & 31);
+                uint32_t v[16];
 #pragma unroll
-                for (int q = 0; q < 16; q++) {
-                    const int rr = wm * (BM / WM) + i * 32 + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
-                    if (rr < rows && c < p.N)
-                        H[(int64_t)(row0 + rr) * p.N + c] = (uint16_t)f32_to_bf16_bits(silu_f32(g[q]) * u[q]);
-                }
+                for (int q = 0; q < 16; q++) v[q] = f32_to_bf16_bits(silu_f32(g[q]) * u[q]);
+                store_h16<HB>(p, tix, row0, rows, nb * (BN / 2) + wn * HW + j * 32, wm * (BM / WM) + i * 32, lane, v);
             }
         if (XT > 0 && xtra && (wm & 1) && i == 0) {
             // up block of the extra rows; its gate block is in wave (wm - 1, wn)
             f32x16_t g, u;
             sum_block(wave - WN, RM * RN, g);
             sum_block(wave, RM * RN, u);
-            const int c = nb * (BN / 2) + wn * HW + (wm >> 1) * 32 + (lane & 31);
+            uint32_t v[16];
 #pragma unroll
-            for (int q = 0; q < 16; q++) {
-                const int rr = BM + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
-                if (rr < rows && c < p.N)
-                    H[(int64_t)(row0 + rr) * p.N + c] = (uint16_t)f32_to_bf16_bits(silu_f32(g[q]) * u[q]);
-            }
+            for (int q = 0; q < 16; q++) v[q] = f32_to_bf16_bits(silu_f32(g[q]) * u[q]);
+            store_h16<HB>(p, tix, row0, rows, nb * (BN / 2) + wn * HW + (wm >> 1) * 32, BM, lane, v);
         }
     } else {
         float *Y = reinterpret_cast<float *>(p.C);
@@ -779,11 +866,14 @@ TiledParams make_params(const GemmProblem &g, int NB)
     t.part = nullptr;
     t.G = 0;
     t.cap = 0;
-    t.a_bytes = (uint32_t)std::min<int64_t>(g.a_rows_total * g.K * 2, 0xFFFFFFFFll);
+    // down reads A from the h row blocks when they are in use
+    const int64_t abytes = (g.h_blocks && g.dense_rows == 0 && g.a_rows == nullptr) ? g.h_bytes : g.a_rows_total * g.K * 2;
+    t.a_bytes = (uint32_t)std::min<int64_t>(abytes, 0xFFFFFFFFll);
     return t;
 }
 
-template <int BM, int BN, int WM, int WN, int OCC, bool GATEUP, int XT, int BK, int STAGES, bool WPACK = false>
+template <int BM, int BN, int WM, int WN, int OCC, bool GATEUP, int XT, int BK, int STAGES, bool WPACK = false,
+          bool HB = false>
 hipError_t launch_cfg(const GemmProblem &g, hipStream_t st)
 {
     const int cols = GATEUP ? BN / 2 : BN;  // output columns per N-block
@@ -799,11 +889,11 @@ hipError_t launch_cfg(const GemmProblem &g, hipStream_t st)
         const int total = (int)((g.dense_rows + BM - 1) / BM) * t.NB;
         if (split_plan(total, t.G, t.cap, (int)((g.K + BK - 1) / BK), true).split < 2) t.part = nullptr;
     }
-    hipLaunchKernelGGL((tiled_gemm_kernel<BM, BN, WM, WN, OCC, GATEUP, XT, BK, STAGES, WPACK>), dim3(t.G),
+    hipLaunchKernelGGL((tiled_gemm_kernel<BM, BN, WM, WN, OCC, GATEUP, XT, BK, STAGES, WPACK, HB>), dim3(t.G),
                        dim3(WM * WN * 64), 0, st, t);
     if (t.part) {
         // at most cap / 2 tiles are split (two pieces or more each)
-        hipLaunchKernelGGL((tiled_split_finish_kernel<BM, BN, WM, WN, GATEUP, XT, BK>),
+        hipLaunchKernelGGL((tiled_split_finish_kernel<BM, BN, WM, WN, GATEUP, XT, BK, HB>),
                            dim3(t.cap / 2 * WM * WN * (BM / WM / 32)), dim3(64), 0, st, t);
     }
     return hipGetLastError();
@@ -884,14 +974,22 @@ int tiled_tail_m() { return MOE_TILED_TAIL; }
 hipError_t launch_gate_up_tiled(const GemmProblem &g, hipStream_t st)
 {
     if (g.dense_rows > 0) return MOE_DENSE_GATE_UP_CFG(g, st);
-    if (g.w_blocks) return launch_cfg<256, 256, 4, 2, 1, true, MOE_TILED_TAIL, kBlockCols, kRoutedStages, true>(g, st);
+    if (g.w_blocks) {
+        if (g.h_blocks) return launch_cfg<256, 256, 4, 2, 1, true, MOE_TILED_TAIL, kBlockCols, kRoutedStages, true, true>(g, st);
+        return launch_cfg<256, 256, 4, 2, 1, true, MOE_TILED_TAIL, kBlockCols, kRoutedStages, true>(g, st);
+    }
+    if (g.h_blocks) return launch_cfg<256, 256, 4, 2, 1, true, MOE_TILED_TAIL, kRoutedBK, kRoutedStages, false, true>(g, st);
     return launch_cfg<256, 256, 4, 2, 1, true, MOE_TILED_TAIL, kRoutedBK, kRoutedStages>(g, st);
 }
 
 hipError_t launch_down_tiled(const GemmProblem &g, hipStream_t st)
 {
     if (g.dense_rows > 0) return MOE_DENSE_DOWN_CFG(g, st);
-    if (g.w_blocks) return launch_cfg<256, 256, 4, 2, 1, false, MOE_TILED_TAIL, kBlockCols, kRoutedStages, true>(g, st);
+    if (g.w_blocks) {
+        if (g.h_blocks) return launch_cfg<256, 256, 4, 2, 1, false, MOE_TILED_TAIL, kBlockCols, kRoutedStages, true, true>(g, st);
+        return launch_cfg<256, 256, 4, 2, 1, false, MOE_TILED_TAIL, kBlockCols, kRoutedStages, true>(g, st);
+    }
+    if (g.h_blocks) return launch_cfg<256, 256, 4, 2, 1, false, MOE_TILED_TAIL, kRoutedBK, kRoutedStages, false, true>(g, st);
     return launch_cfg<256, 256, 4, 2, 1, false, MOE_TILED_TAIL, kRoutedBK, kRoutedStages>(g, st);
 }
 

@@ -191,6 +191,8 @@ moe::Shape make_shape(int64_t T, int64_t H, int64_t I, int64_t E, int32_t k, con
     // the few tiles of the mixed schedule's large experts, spreads them over
     // every CU along K)
     s.partBytes = (s.dtype == MOE_BF16 && sc != Sched::SKINNY) ? moe::tiled_split_bytes() : 0;
+    // every routed row on the tiled kernels: h lives in row blocks of the tile list
+    s.hBlocks = s.dtype == MOE_BF16 && sc == Sched::TILED;
     return s;
 }
 
@@ -226,7 +228,7 @@ int64_t workspace_layout(const Shape &s, void *base, Workspace *ws)
     w.row_token = (int32_t *)take(TK * 4);
     w.row_weight = (float *)take(TK * 4);
     w.row_expert = (int32_t *)take(TK * 4);
-    w.h = take(TK * s.I * es);
+    w.h = take(s.hBlocks ? h_blocks_bytes(s.maxTiles, s.I) : TK * s.I * es);
     w.slot = (float *)take(TK * s.H * 4);
     w.sh_h = s.sharedI > 0 ? take(s.T * s.sharedI * es) : nullptr;
     w.sh_y = s.sharedI > 0 ? (float *)take(s.T * s.H * 4) : nullptr;
@@ -480,6 +482,8 @@ static int forward_impl(const void *hidden, const void *router_w, const void *ga
         gu.w_blocks = true;
         gu.w_expert_stride = moe::tile_blocks_expert_bytes(0, I, H) / 2;
     }
+    gu.h_blocks = s.hBlocks;
+    gu.h_bytes = s.hBlocks ? moe::h_blocks_bytes(s.maxTiles, I) : 0;
 
     moe::GemmProblem dn = gu;
     dn.A = ws.h;
@@ -518,6 +522,7 @@ static int forward_impl(const void *hidden, const void *router_w, const void *ga
         sg.w_scale = nullptr;  // the shared expert keeps opts->dtype
         sg.w_bscale = nullptr;
         sg.w_blocks = false;  // and MOE_LAYOUT_ROWS
+        sg.h_blocks = false;
         sg.w_expert_stride = 0;
         sg.N = opts->shared_I;
         sg.C = ws.sh_h;

@@ -83,6 +83,10 @@ struct Workspace {
     float *part;           // large-M schedule: partial sums of split tiles (or null)
 };
 
+// Tile blocks (MOE_LAYOUT_TILE_BLOCKS): 256 weight rows x 32 columns per block.
+constexpr int kBlockRows = 256;
+constexpr int kBlockCols = 32;
+
 struct Shape {
     int64_t T, H, I, E;
     int k;
@@ -95,7 +99,19 @@ struct Shape {
     int tileMinRows; // experts with fewer rows get no M-tile (mixed schedule; 0: every expert)
     int64_t maxTiles;
     int64_t partBytes;  // partial-sum buffer (0 unless the large-M schedule may run)
+    bool hBlocks;       // h in row blocks of the tile list (bf16 tiled schedule, see below)
 };
+
+// h in row blocks (bf16, tiled schedule only): gate_up's tile i writes its
+// rows as [i][kt][kHBlockRows][kBlockCols], one contiguous 18 KB run per
+// 32-column stage, so that every copy of the down GEMM's token rows reads
+// 1 KB contiguous. Rows past the tile's own and columns past I are never
+// written (the down copies clamp the rows and mask the columns).
+constexpr int kHBlockRows = 288;  // rows of an M-tile with its extra rows
+inline int64_t h_blocks_bytes(int64_t tiles, int64_t I)
+{
+    return tiles * ((I + kBlockCols - 1) / kBlockCols) * kHBlockRows * kBlockCols * 2;
+}
 
 // Byte layout of the workspace; returns total bytes, fills ws when base != null.
 int64_t workspace_layout(const Shape &s, void *base, Workspace *ws);
@@ -161,11 +177,10 @@ struct GemmProblem {
     int64_t a_rows_total = 0;  // rows of A (gate_up: tokens; down: assignments or tokens)
     int skinny_max_rows = 0;   // > 0: the weight-streaming launch leaves experts with more rows to the tiled one
     bool w_blocks = false;     // routed weights in tile blocks (MOE_LAYOUT_TILE_BLOCKS; tiled kernels only)
+    bool h_blocks = false;     // tiled routed launches: gate_up writes C, down reads A, as h row blocks
+    int64_t h_bytes = 0;       // bytes of the h row blocks (their buffer resource bound)
 };
 
-// Tile blocks (MOE_LAYOUT_TILE_BLOCKS): 256 weight rows x 32 columns per block.
-constexpr int kBlockRows = 256;
-constexpr int kBlockCols = 32;
 // Bytes of one expert's tile blocks (which: MOE_PACK_GATE_UP / MOE_PACK_DOWN).
 inline int64_t tile_blocks_expert_bytes(int which, int64_t I, int64_t H)
 {
