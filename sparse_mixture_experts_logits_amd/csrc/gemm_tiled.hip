@@ -902,11 +902,15 @@ hipError_t launch_cfg(const GemmProblem &g, hipStream_t st)
 #ifndef MOE_TILED_TAIL
 #define MOE_TILED_TAIL 32
 #endif
+// Dense problems (the shared expert over all T rows): one tile per CU for a
+// few thousand rows, so each tile takes 8 waves (two per SIMD) to keep the
+// MFMA pipe fed while a wave waits: gate_up waves 2 x 4 (64 rows x 32 gate +
+// 32 up columns each), down waves 4 x 2 (32 rows x 64 columns each).
 #ifndef MOE_DENSE_GATE_UP_CFG
-#define MOE_DENSE_GATE_UP_CFG launch_cfg<128, 256, 2, 2, 1, true, 0, 64, 3>
+#define MOE_DENSE_GATE_UP_CFG launch_cfg<128, 256, 2, 4, 1, true, 0, 64, 3>
 #endif
 #ifndef MOE_DENSE_DOWN_CFG
-#define MOE_DENSE_DOWN_CFG launch_cfg<128, 128, 2, 2, 1, false, 0, 64, 4>
+#define MOE_DENSE_DOWN_CFG launch_cfg<128, 128, 4, 2, 1, false, 0, 64, 4>
 #endif
 
 // Tile blocks from the nn.Linear layout: one thread per 16 bytes (8 columns)
