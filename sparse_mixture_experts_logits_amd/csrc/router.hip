@@ -462,12 +462,12 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(
     if (g < G) {
         int s = 0;
         int b = b0;
-        for (; b + 8 <= b1; b += 8) {  // eight independent loads per step
-            int v[8];
+        for (; b + 16 <= b1; b += 16) {  // sixteen independent loads per step
+            int v[16];
 #pragma unroll
-            for (int u = 0; u < 8; u++) v[u] = blk_counts[(int64_t)(b + u) * E + e];
+            for (int u = 0; u < 16; u++) v[u] = blk_counts[(int64_t)(b + u) * E + e];
 #pragma unroll
-            for (int u = 0; u < 8; u++) s += v[u];
+            for (int u = 0; u < 16; u++) s += v[u];
         }
         for (; b < b1; b++) s += blk_counts[(int64_t)b * E + e];
         s_part[g * E + e] = s;
@@ -483,24 +483,47 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(
         s_cnt[tid] = run;
     }
     __syncthreads();
+    // expert offsets and first tiles: inclusive prefix sums of the counts and
+    // tile counts over the experts, log2(E) doubling steps (integer sums, so
+    // the same values as a serial pass)
+    __shared__ int s_scan[2][2][kMaxExperts];
+    if (tid < E) {
+        s_scan[0][0][tid] = s_cnt[tid];
+        s_scan[0][1][tid] = n_tiles(s_cnt[tid]);
+    }
+    __syncthreads();
+    int src = 0;
+    for (int d = 1; d < E; d <<= 1) {
+        if (tid < E) {
+            int a = s_scan[src][0][tid], t = s_scan[src][1][tid];
+            if (tid >= d) {
+                a += s_scan[src][0][tid - d];
+                t += s_scan[src][1][tid - d];
+            }
+            s_scan[src ^ 1][0][tid] = a;
+            s_scan[src ^ 1][1][tid] = t;
+        }
+        src ^= 1;
+        __syncthreads();
+    }
+    if (tid < E) {
+        s_off[tid + 1] = s_scan[src][0][tid];
+        s_ts[tid + 1] = s_scan[src][1][tid];
+    }
     if (tid == 0) {
         s_off[0] = 0;
         s_ts[0] = 0;
-        for (int x = 0; x < E; x++) {
-            s_off[x + 1] = s_off[x] + s_cnt[x];
-            s_ts[x + 1] = s_ts[x] + n_tiles(s_cnt[x]);
-        }
     }
     __syncthreads();
     if (g < G) {
         int base = s_off[e] + s_part[g * E + e];
         int b = b0;
-        for (; b + 8 <= b1; b += 8) {
-            int v[8];
+        for (; b + 16 <= b1; b += 16) {
+            int v[16];
 #pragma unroll
-            for (int u = 0; u < 8; u++) v[u] = blk_counts[(int64_t)(b + u) * E + e];
+            for (int u = 0; u < 16; u++) v[u] = blk_counts[(int64_t)(b + u) * E + e];
 #pragma unroll
-            for (int u = 0; u < 8; u++) {
+            for (int u = 0; u < 16; u++) {
                 blk_base[(int64_t)(b + u) * E + e] = base;
                 base += v[u];
             }
@@ -513,17 +536,25 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(
     if (tid < E) {
         counts[tid] = s_cnt[tid];
         if (counts_out) counts_out[tid] = s_cnt[tid];
-        const int nt = n_tiles(s_cnt[tid]);
-        for (int i = 0; i < nt; i++) {
-            MTile m;
-            int r0, rows;
-            tile_rows(s_cnt[tid], nt, i, r0, rows);
-            m.expert = tid;
-            m.row0 = s_off[tid] + r0;
-            m.rows = rows;
-            m.pad = 0;
-            tiles[s_ts[tid] + i] = m;
+    }
+    // the tile list, one thread per tile: its expert is the last one whose
+    // first tile is at or before it (binary search over the first tiles)
+    for (int idx = tid; idx < s_ts[E]; idx += 1024) {
+        int lo = 0, hi = E;  // s_ts[lo] <= idx < s_ts[hi]
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (s_ts[mid] <= idx) lo = mid;
+            else hi = mid;
         }
+        const int nt = s_ts[lo + 1] - s_ts[lo];
+        MTile m;
+        int r0, rows;
+        tile_rows(s_cnt[lo], nt, idx - s_ts[lo], r0, rows);
+        m.expert = lo;
+        m.row0 = s_off[lo] + r0;
+        m.rows = rows;
+        m.pad = 0;
+        tiles[idx] = m;
     }
     if (tid <= E) {
         offsets[tid] = s_off[tid];
