@@ -60,6 +60,7 @@ struct TiledParams {
     int G;      // workgroups of the persistent launch
     int cap;    // pieces the partial-sum buffer holds for this tile shape
     uint32_t a_bytes;  // bytes of A the rows may reach (buffer resource bound)
+    int kgran;         // k-stages of a split piece are a multiple of this (2: A copied in pairs of stages)
 };
 
 // The last, partial round of a persistent launch leaves most CUs idle when
@@ -78,14 +79,14 @@ struct SplitPlan {
     int nwork;  // work items of the persistent loop
 };
 
-__host__ __device__ __forceinline__ SplitPlan split_plan(int total, int G, int cap, int nk, bool enabled)
+__host__ __device__ __forceinline__ SplitPlan split_plan(int total, int G, int cap, int nk, bool enabled, int gran)
 {
     SplitPlan sp{total, 1, nk, total};
     cap = std::min(G, cap);
     const int rem = total % G;
     if (!enabled || rem == 0 || 2 * rem > cap || nk < 2) return sp;
     int split = std::min(std::min(cap / rem, kMaxSplit), nk);
-    const int nks = (nk + split - 1) / split;
+    const int nks = ((nk + split - 1) / split + gran - 1) / gran * gran;
     split = (nk + nks - 1) / nks;  // every piece holds at least one stage
     if (split < 2) return sp;
     sp.full = total - rem;
@@ -362,9 +363,18 @@ __device__ __forceinline__ uint32_t lds_addr(const void *p) { return (uint32_t)(
 // gate_up: the four waves of a column half take the gate and the up block of
 // its two output column blocks, and the gate blocks reach the matching up
 // waves through LDS in the epilogue.
-template <int BM, int BN, int WM, int WN, int OCC, bool GATEUP, int XT, int BK, int STAGES, bool WPACK, bool HB>
+// AP (gate_up, 32-wide stages, 4-deep ring, K a multiple of 64): the token
+// rows are copied for two stages at once, 8 rows x 128 bytes per copy
+// instruction instead of 16 rows x 64 bytes (half the copies, each at the
+// address unit's full rate); a pair buffer is two ring slots of A seen as
+// rows of 8 chunks, swizzled like 128-byte stage rows. The weights keep
+// their 32-wide 4-deep ring. Pair q + 1 is copied during stage 2q, into the
+// pair buffer that stages 2q - 2 and 2q - 1 used.
+template <int BM, int BN, int WM, int WN, int OCC, bool GATEUP, int XT, int BK, int STAGES, bool WPACK, bool HB,
+          bool AP>
 __global__ __launch_bounds__(WM *WN * 64, OCC) void tiled_gemm_kernel(TiledParams p)
 {
+    static_assert(!AP || (GATEUP && BK == 32 && STAGES == 4), "A in pairs of 32-wide stages, 4-deep ring");
     // WPACK: the weights are in tile blocks (one stage of one N-block = 256
     // rows x 32 columns, contiguous; zero-filled past N and K)
     static_assert(!WPACK || (BN == kBlockRows && BK == kBlockCols), "tile blocks are 256 x 32");
@@ -425,7 +435,7 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void tiled_gemm_kernel(TiledParam
     // RPI*(wave*INS + i) + lane/CH, chunk slot lane%CH (logical chunk lc below)
     const int drow = lane / CH;
 
-    const SplitPlan sp = split_plan(total, G, p.cap, nk_all, p.part != nullptr);
+    const SplitPlan sp = split_plan(total, G, p.cap, nk_all, p.part != nullptr, p.kgran);
 
     for (int r = 0;; r++) {
         const int wid = r * G + xcd * nx + li;
@@ -485,6 +495,30 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void tiled_gemm_kernel(TiledParam
             } else {
                 const uint32_t src = p.a_rows ? (uint32_t)p.a_rows[row0 + rc] : (uint32_t)(row0 + rc);
                 xoff = src * krow + (uint32_t)kbase * 2u + (uint32_t)chunk_of(xrr) * 16u;
+            }
+        }
+        // AP: the pair copies' sources (the same rows, 8 rows x 8 chunks a copy)
+        constexpr int CHA = 8;
+        constexpr int RPIA = 64 / CHA;
+        constexpr int A_INSA = AP ? BM / RPIA / NWAVE : 1;
+        static_assert(!AP || (A_INSA * RPIA * NWAVE == BM && XR * CHA <= 64), "pair copy geometry");
+        auto chunk_a = [&](int rr) { return (lane % CHA) ^ lds_swz<CHA>(rr); };
+        uint32_t aoffa[A_INSA];
+        uint32_t xoffa = 0;
+        const bool xlanea = lane < XR * CHA;
+        if constexpr (AP) {
+#pragma unroll
+            for (int i = 0; i < A_INSA; i++) {
+                const int rr = RPIA * (wave * A_INSA + i) + lane / CHA;
+                const int rc = rr < rows ? rr : 0;
+                const uint32_t src = p.a_rows ? (uint32_t)p.a_rows[row0 + rc] : (uint32_t)(row0 + rc);
+                aoffa[i] = src * krow + (uint32_t)kbase * 2u + (uint32_t)chunk_a(rr) * 16u;
+            }
+            if (XT > 0 && xtra) {
+                const int xr = BM + XR * wave + (xlanea ? lane / CHA : 0);
+                const int rc = xr < rows ? xr : BM;
+                const uint32_t src = p.a_rows ? (uint32_t)p.a_rows[row0 + rc] : (uint32_t)(row0 + rc);
+                xoffa = src * krow + (uint32_t)kbase * 2u + (uint32_t)chunk_a(xr) * 16u;
             }
         }
         const i32x4_t rb = buf_rsrc(p.W + (int64_t)e * p.w_expert_stride,
@@ -555,6 +589,18 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void tiled_gemm_kernel(TiledParam
         auto issue_any = [&](int kt, int b) {
             if (ragged && kt == nk - 1) issue_tail(kt, b);
             else issue(kt, b);
+        };
+        // AP: copy q of A pair pr (stages 2pr, 2pr + 1) into pair buffer pb
+        // (q < A_INSA: token rows; q == A_INSA: this wave's extra rows), and
+        // copy q of weight stage kt alone
+        auto issue_pair = [&](int pr, int pb, int q) {
+            u32x4 *base = &sA[2 * pb][0];
+            const uint32_t k0 = (uint32_t)pr * (2u * BK * 2u);
+            if (q < A_INSA) dma16(ra, aoffa[q], k0, lds_addr(base + (wave * A_INSA + q) * 64));
+            else if (xlanea) dma16(ra, xoffa, k0, lds_addr(base + (BM + XR * wave) * CHA));
+        };
+        auto issue_w = [&](int kt, int b, int q) {
+            dma16(rb, boff[q], wstage(kt), lds_addr(&sB[b][(wave * B_INS + q) * 64]));
         };
 
         f32x16_t acc[RM][RN];
@@ -652,11 +698,92 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void tiled_gemm_kernel(TiledParam
             }
         };
 
+        // AP: fragment offsets into a pair buffer, half h (stage 2q + h) and
+        // k-step kk: row l32 of 8 chunks, logical chunk 4h + 2kk + lane / 32
+        int vaa[2][KSTEPS], vxaa[2][KSTEPS];
+#pragma unroll
+        for (int h = 0; h < 2; h++)
+#pragma unroll
+            for (int kk = 0; kk < KSTEPS; kk++) {
+                const int lo = l32 * CHA + ((h * 4 + kk * 2 + (lane >> 5)) ^ lds_swz<CHA>(l32));
+                vaa[h][kk] = wm * (BM / WM) * CHA + lo;
+                vxaa[h][kk] = BM * CHA + lo;
+            }
+        // AP: consume weight buffer b and half h of pair buffer pb; with CP,
+        // spread between the MFMAs the copies of weight stage nkt into buffer
+        // nbuf and (CA) before them those of pair npr into pair buffer npb
+        auto compute_stage_ap = [&](auto nbc, auto exc, auto cpc, auto cac, auto hc, int b, int pb, int nkt, int nbuf,
+                                    int npr, int npb) {
+            constexpr int NB = decltype(nbc)::value;
+            constexpr bool EX = decltype(exc)::value;
+            constexpr bool CP = decltype(cpc)::value;
+            constexpr bool CA = decltype(cac)::value;
+            constexpr int H = decltype(hc)::value;
+            constexpr int LA = CA ? A_INSA + (EX ? 1 : 0) : 0;
+            constexpr int LX = LA + B_INS;
+            constexpr int NMMA = (BK / 16) * (RM * RN + (EX ? 1 : 0));
+            constexpr int PER = NMMA / LX > 0 ? NMMA / LX : 1;
+            static_assert(PER * LX <= NMMA, "every copy finds an MFMA slot");
+            auto copy = [&](int q) {
+                if (q < LA) issue_pair(npr, npb, q);
+                else issue_w(nkt, nbuf, q - LA);
+            };
+            const u32x4 *A = &sA[2 * pb][0];
+            const u32x4 *Bw = &sB[b][0];
+#pragma unroll
+            for (int kk = 0; kk < BK / 16; kk++) {
+                bf16x8_t af[RM], bf[RN], ax, bx;
+#pragma unroll
+                for (int i = 0; i < NB; i++) af[i] = as_bf16x8(A[vaa[H][kk] + i * 32 * CHA]);
+                if (EX) {
+                    ax = as_bf16x8(A[vxaa[H][kk]]);
+                    bx = as_bf16x8(Bw[vxb[kk]]);
+                }
+#pragma unroll
+                for (int j = 0; j < RN; j++) {
+                    if (NB == 0) break;
+                    const int row = GATEUP ? ((j < RN / 2) ? j * 32 : BN / 2 + (j - RN / 2) * 32) : j * 32;
+                    bf[j] = as_bf16x8(Bw[vb[kk] + row * CH]);
+                }
+                auto slot = [&](int mi) {
+                    if (CP && (mi + 1) % PER == 0 && (mi + 1) / PER - 1 < LX) copy((mi + 1) / PER - 1);
+                };
+#pragma unroll
+                for (int i = 0; i < RM; i++)
+#pragma unroll
+                    for (int j = 0; j < RN; j++) {
+                        if (i < NB)
+                            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
+                        slot((kk * (RM * RN + (EX ? 1 : 0)) + i * RN + j));
+                    }
+                if (EX) {
+                    accx = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ax, bx, accx, 0, 0, 0);
+                    slot(kk * (RM * RN + 1) + RM * RN);
+                }
+            }
+        };
+
         // all waves are done with the previous tile's stages before refilling them
         wait_vm_barrier<0>();
+        if constexpr (AP) {
+            // weight stages 0, 1, 2 and pair 0, in the order the waits count:
+            // W0, A0, W1, W2 (nk is even)
 #pragma unroll
-        for (int s = 0; s < STAGES - 1; s++)
-            if (s < nk) issue_any(s, s);
+            for (int q = 0; q < B_INS; q++) issue_w(0, 0, q);
+#pragma unroll
+            for (int q = 0; q < A_INSA + (XT > 0 ? 1 : 0); q++)
+                if (q < A_INSA || xtra) issue_pair(0, 0, q);
+#pragma unroll
+            for (int q = 0; q < B_INS; q++) issue_w(1, 1, q);
+            if (2 < nk) {
+#pragma unroll
+                for (int q = 0; q < B_INS; q++) issue_w(2, 2, q);
+            }
+        } else {
+#pragma unroll
+            for (int s = 0; s < STAGES - 1; s++)
+                if (s < nk) issue_any(s, s);
+        }
 
         // Steady state: stage kt is consumed while stages kt+1, kt+2 are in
         // flight and stage kt+3 is issued into the buffer stage kt-1 used.
@@ -688,6 +815,59 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void tiled_gemm_kernel(TiledParam
                 compute_stage(nbc, exc, NOCP{}, b % STAGES, 0, 0);
             }
         };
+        // AP: stage s needs weight stage s and pair s / 2. Copies go out in
+        // the order W(s + 3) at stage s, with pair s / 2 + 1 before it at even
+        // s, so at even s the copies after pair s / 2 are W(s + 1) and
+        // W(s + 2), and at odd s those after W(s) are W(s + 1), pair
+        // (s + 1) / 2 and W(s + 2) (each only if it exists).
+        auto kloop_ap = [&](auto nbc, auto exc) {
+            constexpr bool EXv = decltype(exc)::value;
+            constexpr int LW = B_INS;
+            constexpr int LA = A_INSA + (EXv ? 1 : 0);
+            using CP = std::integral_constant<bool, true>;
+            using NOCP = std::integral_constant<bool, false>;
+            using CA = std::integral_constant<bool, true>;
+            using NOCA = std::integral_constant<bool, false>;
+            using H0 = std::integral_constant<int, 0>;
+            using H1 = std::integral_constant<int, 1>;
+            int kt = 0;
+            for (; kt + 2 * STAGES - 1 <= nk; kt += STAGES) {
+                const int pr = kt / 2;  // even: the pair of stages kt, kt + 1 lives in pair buffer 0
+                wait_vm_barrier<2 * LW>();
+                compute_stage_ap(nbc, exc, CP{}, CA{}, H0{}, 0, 0, kt + 3, 3, pr + 1, 1);
+                wait_vm_barrier<2 * LW + LA>();
+                compute_stage_ap(nbc, exc, CP{}, NOCA{}, H1{}, 1, 0, kt + 4, 0, 0, 0);
+                wait_vm_barrier<2 * LW>();
+                compute_stage_ap(nbc, exc, CP{}, CA{}, H0{}, 2, 1, kt + 5, 1, pr + 2, 0);
+                wait_vm_barrier<2 * LW + LA>();
+                compute_stage_ap(nbc, exc, CP{}, NOCA{}, H1{}, 3, 1, kt + 6, 2, 0, 0);
+            }
+#pragma unroll
+            for (int b = 0; b < 2 * STAGES - 1; b++) {
+                const int st = kt + b;
+                if (st >= nk) break;
+                const bool a1 = st + 1 < nk, a2 = st + 2 < nk;
+                if (b % 2 == 0) {
+                    if (a2) wait_vm_barrier<2 * LW>();
+                    else if (a1) wait_vm_barrier<LW>();
+                    else wait_vm_barrier<0>();
+                    if (st + 2 < nk) {
+#pragma unroll
+                        for (int q = 0; q < LA; q++) issue_pair(st / 2 + 1, (b / 2 + 1) % 2, q);
+                    }
+                } else {
+                    if (a2) wait_vm_barrier<2 * LW + LA>();
+                    else if (a1) wait_vm_barrier<LW + LA>();
+                    else wait_vm_barrier<0>();
+                }
+                if (st + 3 < nk) {
+#pragma unroll
+                    for (int q = 0; q < LW; q++) issue_w(st + 3, (b + 3) % STAGES, q);
+                }
+                if (b % 2 == 0) compute_stage_ap(nbc, exc, NOCP{}, NOCA{}, H0{}, b % STAGES, (b / 2) % 2, 0, 0, 0, 0);
+                else compute_stage_ap(nbc, exc, NOCP{}, NOCA{}, H1{}, b % STAGES, (b / 2) % 2, 0, 0, 0, 0);
+            }
+        };
         // 32-row blocks of this wave that hold rows of the tile (wave-uniform);
         // one copy of the loop per case
         const int nvb = max(0, min(RM, (rows - wm * (BM / WM) + 31) / 32));
@@ -697,10 +877,17 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void tiled_gemm_kernel(TiledParam
         using IRM = std::integral_constant<int, RM>;
         using F = std::integral_constant<bool, false>;
         using T = std::integral_constant<bool, true>;
-        if (XT > 0 && xtra) kloop(IRM{}, std::integral_constant<bool, XT != 0>{});
-        else if (nvb >= RM) kloop(IRM{}, F{});
-        else if (nvb == 1) kloop(I1{}, F{});
-        else kloop(I0{}, F{});
+        if constexpr (AP) {
+            if (XT > 0 && xtra) kloop_ap(IRM{}, std::integral_constant<bool, XT != 0>{});
+            else if (nvb >= RM) kloop_ap(IRM{}, F{});
+            else if (nvb == 1) kloop_ap(I1{}, F{});
+            else kloop_ap(I0{}, F{});
+        } else {
+            if (XT > 0 && xtra) kloop(IRM{}, std::integral_constant<bool, XT != 0>{});
+            else if (nvb >= RM) kloop(IRM{}, F{});
+            else if (nvb == 1) kloop(I1{}, F{});
+            else kloop(I0{}, F{});
+        }
         (void)T{};
 
         // ---- epilogue, or the partial sums of a piece of a split tile
@@ -743,7 +930,7 @@ __global__ __launch_bounds__(64) void tiled_split_finish_kernel(TiledParams p)
     const int n_mtiles = p.tiles ? p.tile_start[p.E] : (p.dense_rows + BM - 1) / BM;
     const int total = n_mtiles * p.NB;
     const int nk_all = (p.K + BK - 1) / BK;
-    const SplitPlan sp = split_plan(total, p.G, p.cap, nk_all, p.part != nullptr);
+    const SplitPlan sp = split_plan(total, p.G, p.cap, nk_all, p.part != nullptr, p.kgran);
     const int t = blockIdx.x / (NWAVE * RM);
     const int wave = (blockIdx.x / RM) % NWAVE;
     const int i = blockIdx.x % RM;  // this workgroup's 32-row block
@@ -869,16 +1056,18 @@ TiledParams make_params(const GemmProblem &g, int NB)
     // down reads A from the h row blocks when they are in use
     const int64_t abytes = (g.h_blocks && g.dense_rows == 0 && g.a_rows == nullptr) ? g.h_bytes : g.a_rows_total * g.K * 2;
     t.a_bytes = (uint32_t)std::min<int64_t>(abytes, 0xFFFFFFFFll);
+    t.kgran = 1;
     return t;
 }
 
 template <int BM, int BN, int WM, int WN, int OCC, bool GATEUP, int XT, int BK, int STAGES, bool WPACK = false,
-          bool HB = false>
+          bool HB = false, bool AP = false>
 hipError_t launch_cfg(const GemmProblem &g, hipStream_t st)
 {
     const int cols = GATEUP ? BN / 2 : BN;  // output columns per N-block
     TiledParams t = make_params(g, (int)((g.N + cols - 1) / cols));
     t.G = persistent_grid(g.cus, OCC);
+    t.kgran = AP ? 2 : 1;  // pairs of stages never straddle two split pieces
     // pieces of this tile shape that fit the buffer (sized for kSplitPieces
     // routed 256x256 pieces), at most one round of the launch
     constexpr int64_t piece_bytes = (int64_t)WM * WN * ((BM / WM / 32) * (BN / WN / 32) + (XT > 0 ? 1 : 0)) * 1024 * 4;
@@ -887,9 +1076,9 @@ hipError_t launch_cfg(const GemmProblem &g, hipStream_t st)
     // a dense problem's tile count is known here: no second launch when no tile is split
     if (t.part && g.dense_rows > 0) {
         const int total = (int)((g.dense_rows + BM - 1) / BM) * t.NB;
-        if (split_plan(total, t.G, t.cap, (int)((g.K + BK - 1) / BK), true).split < 2) t.part = nullptr;
+        if (split_plan(total, t.G, t.cap, (int)((g.K + BK - 1) / BK), true, t.kgran).split < 2) t.part = nullptr;
     }
-    hipLaunchKernelGGL((tiled_gemm_kernel<BM, BN, WM, WN, OCC, GATEUP, XT, BK, STAGES, WPACK, HB>), dim3(t.G),
+    hipLaunchKernelGGL((tiled_gemm_kernel<BM, BN, WM, WN, OCC, GATEUP, XT, BK, STAGES, WPACK, HB, AP>), dim3(t.G),
                        dim3(WM * WN * 64), 0, st, t);
     if (t.part) {
         // at most cap / 2 tiles are split (two pieces or more each)
@@ -901,6 +1090,9 @@ hipError_t launch_cfg(const GemmProblem &g, hipStream_t st)
 
 #ifndef MOE_TILED_TAIL
 #define MOE_TILED_TAIL 32
+#endif
+#ifndef MOE_TILED_APAIR
+#define MOE_TILED_APAIR 1
 #endif
 // Dense problems (the shared expert over all T rows): one tile per CU for a
 // few thousand rows, so each tile takes 8 waves (two per SIMD) to keep the
@@ -978,6 +1170,14 @@ int tiled_tail_m() { return MOE_TILED_TAIL; }
 hipError_t launch_gate_up_tiled(const GemmProblem &g, hipStream_t st)
 {
     if (g.dense_rows > 0) return MOE_DENSE_GATE_UP_CFG(g, st);
+    // Token rows copied in pairs of stages when K holds whole pairs: on the
+    // tiled schedule (h in row blocks) with row-layout weights, whose
+    // 16-row weight copies keep the address unit busiest (prefill gate_up
+    // 0.85 -> 0.82 ms); with tile-block weights it measured even to 1% slower
+    // on prefill and skewed batches, so those keep single stages, and so do
+    // the mixed schedule's few tiles.
+    if (MOE_TILED_APAIR && kRoutedBK == 32 && kRoutedStages == 4 && g.K % 64 == 0 && g.h_blocks && !g.w_blocks)
+        return launch_cfg<256, 256, 4, 2, 1, true, MOE_TILED_TAIL, 32, 4, false, true, true>(g, st);
     if (g.w_blocks) {
         if (g.h_blocks) return launch_cfg<256, 256, 4, 2, 1, true, MOE_TILED_TAIL, kBlockCols, kRoutedStages, true, true>(g, st);
         return launch_cfg<256, 256, 4, 2, 1, true, MOE_TILED_TAIL, kBlockCols, kRoutedStages, true>(g, st);
