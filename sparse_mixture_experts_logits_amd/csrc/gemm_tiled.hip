@@ -363,18 +363,19 @@ __device__ __forceinline__ uint32_t lds_addr(const void *p) { return (uint32_t)(
 // gate_up: the four waves of a column half take the gate and the up block of
 // its two output column blocks, and the gate blocks reach the matching up
 // waves through LDS in the epilogue.
-// AP (gate_up, 32-wide stages, 4-deep ring, K a multiple of 64): the token
-// rows are copied for two stages at once, 8 rows x 128 bytes per copy
-// instruction instead of 16 rows x 64 bytes (half the copies, each at the
-// address unit's full rate); a pair buffer is two ring slots of A seen as
-// rows of 8 chunks, swizzled like 128-byte stage rows. The weights keep
-// their 32-wide 4-deep ring. Pair q + 1 is copied during stage 2q, into the
-// pair buffer that stages 2q - 2 and 2q - 1 used.
+// AP (32-wide stages, 4-deep ring, K a multiple of 64): one operand is
+// copied for two stages at once, 8 rows x 128 bytes per copy instruction
+// instead of 16 rows x 64 bytes (half the copies, each at the address unit's
+// full rate): gate_up's token rows, or down's row-layout weights. A pair
+// buffer is two ring slots of that operand seen as rows of 8 chunks,
+// swizzled like 128-byte stage rows; the other operand keeps its 32-wide
+// 4-deep ring. Pair q + 1 is copied during stage 2q, into the pair buffer
+// that stages 2q - 2 and 2q - 1 used.
 template <int BM, int BN, int WM, int WN, int OCC, bool GATEUP, int XT, int BK, int STAGES, bool WPACK, bool HB,
           bool AP>
 __global__ __launch_bounds__(WM *WN * 64, OCC) void tiled_gemm_kernel(TiledParams p)
 {
-    static_assert(!AP || (GATEUP && BK == 32 && STAGES == 4), "A in pairs of 32-wide stages, 4-deep ring");
+    static_assert(!AP || (BK == 32 && STAGES == 4 && (GATEUP || !WPACK)), "pairs of 32-wide stages, 4-deep ring");
     // WPACK: the weights are in tile blocks (one stage of one N-block = 256
     // rows x 32 columns, contiguous; zero-filled past N and K)
     static_assert(!WPACK || (BN == kBlockRows && BK == kBlockCols), "tile blocks are 256 x 32");
@@ -497,28 +498,38 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void tiled_gemm_kernel(TiledParam
                 xoff = src * krow + (uint32_t)kbase * 2u + (uint32_t)chunk_of(xrr) * 16u;
             }
         }
-        // AP: the pair copies' sources (the same rows, 8 rows x 8 chunks a copy)
+        // AP: the pair copies' sources (the same rows, 8 rows x 8 chunks a
+        // copy): gate_up's token rows (and extra rows), or down's weight rows
         constexpr int CHA = 8;
         constexpr int RPIA = 64 / CHA;
-        constexpr int A_INSA = AP ? BM / RPIA / NWAVE : 1;
-        static_assert(!AP || (A_INSA * RPIA * NWAVE == BM && XR * CHA <= 64), "pair copy geometry");
+        constexpr int P_INS = AP ? (GATEUP ? BM : BN) / RPIA / NWAVE : 1;
+        static_assert(!AP || (P_INS * RPIA * NWAVE == (GATEUP ? BM : BN) && XR * CHA <= 64), "pair copy geometry");
         auto chunk_a = [&](int rr) { return (lane % CHA) ^ lds_swz<CHA>(rr); };
-        uint32_t aoffa[A_INSA];
+        uint32_t poff[P_INS];
         uint32_t xoffa = 0;
         const bool xlanea = lane < XR * CHA;
-        if constexpr (AP) {
+        if constexpr (AP && GATEUP) {
 #pragma unroll
-            for (int i = 0; i < A_INSA; i++) {
-                const int rr = RPIA * (wave * A_INSA + i) + lane / CHA;
+            for (int i = 0; i < P_INS; i++) {
+                const int rr = RPIA * (wave * P_INS + i) + lane / CHA;
                 const int rc = rr < rows ? rr : 0;
                 const uint32_t src = p.a_rows ? (uint32_t)p.a_rows[row0 + rc] : (uint32_t)(row0 + rc);
-                aoffa[i] = src * krow + (uint32_t)kbase * 2u + (uint32_t)chunk_a(rr) * 16u;
+                poff[i] = src * krow + (uint32_t)kbase * 2u + (uint32_t)chunk_a(rr) * 16u;
             }
             if (XT > 0 && xtra) {
                 const int xr = BM + XR * wave + (xlanea ? lane / CHA : 0);
                 const int rc = xr < rows ? xr : BM;
                 const uint32_t src = p.a_rows ? (uint32_t)p.a_rows[row0 + rc] : (uint32_t)(row0 + rc);
                 xoffa = src * krow + (uint32_t)kbase * 2u + (uint32_t)chunk_a(xr) * 16u;
+            }
+        }
+        if constexpr (AP && !GATEUP) {
+#pragma unroll
+            for (int i = 0; i < P_INS; i++) {
+                const int rr = RPIA * (wave * P_INS + i) + lane / CHA;
+                const int n = nb * BN + rr;
+                const uint32_t wrow = (uint32_t)(n < p.N ? n : 0);
+                poff[i] = wrow * krow + (uint32_t)kbase * 2u + (uint32_t)chunk_a(rr) * 16u;
             }
         }
         const i32x4_t rb = buf_rsrc(p.W + (int64_t)e * p.w_expert_stride,
@@ -590,17 +601,23 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void tiled_gemm_kernel(TiledParam
             if (ragged && kt == nk - 1) issue_tail(kt, b);
             else issue(kt, b);
         };
-        // AP: copy q of A pair pr (stages 2pr, 2pr + 1) into pair buffer pb
-        // (q < A_INSA: token rows; q == A_INSA: this wave's extra rows), and
-        // copy q of weight stage kt alone
+        // AP: copy q of pair pr (stages 2pr, 2pr + 1) into pair buffer pb
+        // (q < P_INS: rows; q == P_INS: gate_up's extra rows for this wave),
+        // and copy q of the other operand's stage kt alone (gate_up: weight
+        // rows; down: h rows, then the extra rows)
         auto issue_pair = [&](int pr, int pb, int q) {
-            u32x4 *base = &sA[2 * pb][0];
+            u32x4 *base = GATEUP ? &sA[2 * pb][0] : &sB[2 * pb][0];
             const uint32_t k0 = (uint32_t)pr * (2u * BK * 2u);
-            if (q < A_INSA) dma16(ra, aoffa[q], k0, lds_addr(base + (wave * A_INSA + q) * 64));
+            if (q < P_INS) dma16(GATEUP ? ra : rb, poff[q], k0, lds_addr(base + (wave * P_INS + q) * 64));
             else if (xlanea) dma16(ra, xoffa, k0, lds_addr(base + (BM + XR * wave) * CHA));
         };
-        auto issue_w = [&](int kt, int b, int q) {
-            dma16(rb, boff[q], wstage(kt), lds_addr(&sB[b][(wave * B_INS + q) * 64]));
+        auto issue_single = [&](int kt, int b, int q) {
+            if (GATEUP) {
+                dma16(rb, boff[q], wstage(kt), lds_addr(&sB[b][(wave * B_INS + q) * 64]));
+            } else {
+                if (q < A_INS) dma16(ra, aoff[q], astage(kt), lds_addr(&sA[b][(wave * A_INS + q) * 64]));
+                else if (xlane) dma16(ra, xoff, astage(kt), lds_addr(&sA[b][(BM + XR * wave) * CH]));
+            }
         };
 
         f32x16_t acc[RM][RN];
@@ -700,17 +717,17 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void tiled_gemm_kernel(TiledParam
 
         // AP: fragment offsets into a pair buffer, half h (stage 2q + h) and
         // k-step kk: row l32 of 8 chunks, logical chunk 4h + 2kk + lane / 32
-        int vaa[2][KSTEPS], vxaa[2][KSTEPS];
+        int vpa[2][KSTEPS], vpx[2][KSTEPS];
 #pragma unroll
         for (int h = 0; h < 2; h++)
 #pragma unroll
             for (int kk = 0; kk < KSTEPS; kk++) {
                 const int lo = l32 * CHA + ((h * 4 + kk * 2 + (lane >> 5)) ^ lds_swz<CHA>(l32));
-                vaa[h][kk] = wm * (BM / WM) * CHA + lo;
-                vxaa[h][kk] = BM * CHA + lo;
+                vpa[h][kk] = (GATEUP ? wm * (BM / WM) : wn * HWB) * CHA + lo;
+                vpx[h][kk] = (GATEUP ? BM : xrow - l32) * CHA + lo;
             }
-        // AP: consume weight buffer b and half h of pair buffer pb; with CP,
-        // spread between the MFMAs the copies of weight stage nkt into buffer
+        // AP: consume single-stage buffer b and half h of pair buffer pb; with
+        // CP, spread between the MFMAs the copies of stage nkt into buffer
         // nbuf and (CA) before them those of pair npr into pair buffer npb
         auto compute_stage_ap = [&](auto nbc, auto exc, auto cpc, auto cac, auto hc, int b, int pb, int nkt, int nbuf,
                                     int npr, int npb) {
@@ -719,31 +736,37 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void tiled_gemm_kernel(TiledParam
             constexpr bool CP = decltype(cpc)::value;
             constexpr bool CA = decltype(cac)::value;
             constexpr int H = decltype(hc)::value;
-            constexpr int LA = CA ? A_INSA + (EX ? 1 : 0) : 0;
-            constexpr int LX = LA + B_INS;
+            constexpr int LA = CA ? P_INS + (GATEUP && EX ? 1 : 0) : 0;
+            constexpr int LX = LA + (GATEUP ? B_INS : A_INS + (EX ? 1 : 0));
             constexpr int NMMA = (BK / 16) * (RM * RN + (EX ? 1 : 0));
             constexpr int PER = NMMA / LX > 0 ? NMMA / LX : 1;
             static_assert(PER * LX <= NMMA, "every copy finds an MFMA slot");
             auto copy = [&](int q) {
                 if (q < LA) issue_pair(npr, npb, q);
-                else issue_w(nkt, nbuf, q - LA);
+                else issue_single(nkt, nbuf, q - LA);
             };
-            const u32x4 *A = &sA[2 * pb][0];
-            const u32x4 *Bw = &sB[b][0];
+            const u32x4 *A = GATEUP ? &sA[2 * pb][0] : &sA[b][0];
+            const u32x4 *Bw = GATEUP ? &sB[b][0] : &sB[2 * pb][0];
+            constexpr int CHAv = GATEUP ? CHA : CH;  // chunks per row of A's buffer
+            constexpr int CHBv = GATEUP ? CH : CHA;  // and of B's
 #pragma unroll
             for (int kk = 0; kk < BK / 16; kk++) {
+                const int oa = GATEUP ? vpa[H][kk] : va[kk];
+                const int oxa = GATEUP ? vpx[H][kk] : vxa[kk];
+                const int ob = GATEUP ? vb[kk] : vpa[H][kk];
+                const int oxb = GATEUP ? vxb[kk] : vpx[H][kk];
                 bf16x8_t af[RM], bf[RN], ax, bx;
 #pragma unroll
-                for (int i = 0; i < NB; i++) af[i] = as_bf16x8(A[vaa[H][kk] + i * 32 * CHA]);
+                for (int i = 0; i < NB; i++) af[i] = as_bf16x8(A[oa + i * 32 * CHAv]);
                 if (EX) {
-                    ax = as_bf16x8(A[vxaa[H][kk]]);
-                    bx = as_bf16x8(Bw[vxb[kk]]);
+                    ax = as_bf16x8(A[oxa]);
+                    bx = as_bf16x8(Bw[oxb]);
                 }
 #pragma unroll
                 for (int j = 0; j < RN; j++) {
                     if (NB == 0) break;
                     const int row = GATEUP ? ((j < RN / 2) ? j * 32 : BN / 2 + (j - RN / 2) * 32) : j * 32;
-                    bf[j] = as_bf16x8(Bw[vb[kk] + row * CH]);
+                    bf[j] = as_bf16x8(Bw[ob + row * CHBv]);
                 }
                 auto slot = [&](int mi) {
                     if (CP && (mi + 1) % PER == 0 && (mi + 1) / PER - 1 < LX) copy((mi + 1) / PER - 1);
@@ -766,18 +789,23 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void tiled_gemm_kernel(TiledParam
         // all waves are done with the previous tile's stages before refilling them
         wait_vm_barrier<0>();
         if constexpr (AP) {
-            // weight stages 0, 1, 2 and pair 0, in the order the waits count:
-            // W0, A0, W1, W2 (nk is even)
+            // single stages 0, 1, 2 and pair 0, in the order the waits count:
+            // S0, P0, S1, S2 (nk is even)
+            constexpr int LS0 = GATEUP ? B_INS : A_INS + (XT > 0 ? 1 : 0);
+            constexpr int LP0 = P_INS + (GATEUP && XT > 0 ? 1 : 0);
 #pragma unroll
-            for (int q = 0; q < B_INS; q++) issue_w(0, 0, q);
+            for (int q = 0; q < LS0; q++)
+                if (GATEUP || q < A_INS || xtra) issue_single(0, 0, q);
 #pragma unroll
-            for (int q = 0; q < A_INSA + (XT > 0 ? 1 : 0); q++)
-                if (q < A_INSA || xtra) issue_pair(0, 0, q);
+            for (int q = 0; q < LP0; q++)
+                if (!GATEUP || q < P_INS || xtra) issue_pair(0, 0, q);
 #pragma unroll
-            for (int q = 0; q < B_INS; q++) issue_w(1, 1, q);
+            for (int q = 0; q < LS0; q++)
+                if (GATEUP || q < A_INS || xtra) issue_single(1, 1, q);
             if (2 < nk) {
 #pragma unroll
-                for (int q = 0; q < B_INS; q++) issue_w(2, 2, q);
+                for (int q = 0; q < LS0; q++)
+                    if (GATEUP || q < A_INS || xtra) issue_single(2, 2, q);
             }
         } else {
 #pragma unroll
@@ -815,15 +843,15 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void tiled_gemm_kernel(TiledParam
                 compute_stage(nbc, exc, NOCP{}, b % STAGES, 0, 0);
             }
         };
-        // AP: stage s needs weight stage s and pair s / 2. Copies go out in
-        // the order W(s + 3) at stage s, with pair s / 2 + 1 before it at even
-        // s, so at even s the copies after pair s / 2 are W(s + 1) and
-        // W(s + 2), and at odd s those after W(s) are W(s + 1), pair
-        // (s + 1) / 2 and W(s + 2) (each only if it exists).
+        // AP: stage s needs single stage s and pair s / 2. Copies go out in
+        // the order S(s + 3) at stage s, with pair s / 2 + 1 before it at even
+        // s, so at even s the copies after pair s / 2 are S(s + 1) and
+        // S(s + 2), and at odd s those after S(s) are S(s + 1), pair
+        // (s + 1) / 2 and S(s + 2) (each only if it exists).
         auto kloop_ap = [&](auto nbc, auto exc) {
             constexpr bool EXv = decltype(exc)::value;
-            constexpr int LW = B_INS;
-            constexpr int LA = A_INSA + (EXv ? 1 : 0);
+            constexpr int LW = GATEUP ? B_INS : A_INS + (EXv ? 1 : 0);  // single-stage copies
+            constexpr int LA = P_INS + (GATEUP && EXv ? 1 : 0);         // pair copies
             using CP = std::integral_constant<bool, true>;
             using NOCP = std::integral_constant<bool, false>;
             using CA = std::integral_constant<bool, true>;
@@ -862,7 +890,7 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void tiled_gemm_kernel(TiledParam
                 }
                 if (st + 3 < nk) {
 #pragma unroll
-                    for (int q = 0; q < LW; q++) issue_w(st + 3, (b + 3) % STAGES, q);
+                    for (int q = 0; q < LW; q++) issue_single(st + 3, (b + 3) % STAGES, q);
                 }
                 if (b % 2 == 0) compute_stage_ap(nbc, exc, NOCP{}, NOCA{}, H0{}, b % STAGES, (b / 2) % 2, 0, 0, 0, 0);
                 else compute_stage_ap(nbc, exc, NOCP{}, NOCA{}, H1{}, b % STAGES, (b / 2) % 2, 0, 0, 0, 0);
@@ -1067,7 +1095,11 @@ hipError_t launch_cfg(const GemmProblem &g, hipStream_t st)
     const int cols = GATEUP ? BN / 2 : BN;  // output columns per N-block
     TiledParams t = make_params(g, (int)((g.N + cols - 1) / cols));
     t.G = persistent_grid(g.cus, OCC);
-    t.kgran = AP ? 2 : 1;  // pairs of stages never straddle two split pieces
+    // Split pieces hold whole 64-column pairs of 32-wide stages whenever K
+    // has them, with or without paired copies (AP needs it), so the pieces,
+    // and with them the rounding of the summed partials, are the same for
+    // every kernel variant of a shape.
+    t.kgran = (BK == 32 && g.K % 64 == 0) ? 2 : 1;
     // pieces of this tile shape that fit the buffer (sized for kSplitPieces
     // routed 256x256 pieces), at most one round of the launch
     constexpr int64_t piece_bytes = (int64_t)WM * WN * ((BM / WM / 32) * (BN / WN / 32) + (XT > 0 ? 1 : 0)) * 1024 * 4;
@@ -1093,6 +1125,9 @@ hipError_t launch_cfg(const GemmProblem &g, hipStream_t st)
 #endif
 #ifndef MOE_TILED_APAIR
 #define MOE_TILED_APAIR 1
+#endif
+#ifndef MOE_TILED_APAIR_DN
+#define MOE_TILED_APAIR_DN MOE_TILED_APAIR
 #endif
 // Dense problems (the shared expert over all T rows): one tile per CU for a
 // few thousand rows, so each tile takes 8 waves (two per SIMD) to keep the
@@ -1189,6 +1224,10 @@ hipError_t launch_gate_up_tiled(const GemmProblem &g, hipStream_t st)
 hipError_t launch_down_tiled(const GemmProblem &g, hipStream_t st)
 {
     if (g.dense_rows > 0) return MOE_DENSE_DOWN_CFG(g, st);
+    // row-layout weights copied in pairs of stages (the h rows are 1 KB
+    // runs already), on the tiled schedule when K holds whole pairs
+    if (MOE_TILED_APAIR_DN && kRoutedBK == 32 && kRoutedStages == 4 && g.K % 64 == 0 && g.h_blocks && !g.w_blocks)
+        return launch_cfg<256, 256, 4, 2, 1, false, MOE_TILED_TAIL, 32, 4, false, true, true>(g, st);
     if (g.w_blocks) {
         if (g.h_blocks) return launch_cfg<256, 256, 4, 2, 1, false, MOE_TILED_TAIL, kBlockCols, kRoutedStages, true, true>(g, st);
         return launch_cfg<256, 256, 4, 2, 1, false, MOE_TILED_TAIL, kBlockCols, kRoutedStages, true>(g, st);
