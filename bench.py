@@ -19,7 +19,11 @@ step with FP8 (E4M3, per-row scaled) and MXFP4 (E2M1, E8M0 scale per 32)
 expert weights under ``decode_fp8`` and ``decode_mxfp4``, and the prefill,
 skewed and Instella-style workloads with their bf16 routed weights packed in
 tile blocks under ``<workload>_tile_blocks`` (other weight storage, so never
-the headline value). Each carries a ``roofline`` of its
+the headline value), and with other routing rules under
+``<workload>_<router>``: the Instella-style layer with sigmoid scores, a
+selection-only bias and group-limited top-k (``noaux_groups``), the prefill
+with PhiMoE's sparsemixer selection (``sparsemixer``) and with the router
+statistics and load-balancing loss computed (``router_stats``). Each carries a ``roofline`` of its
 dominant kernel, bound by max(FLOP / MFMA peak, bytes / HBM bandwidth). A
 short untimed pilot with events at every stage boundary finds the dominant
 kernel; every timed call then records HIP events around that kernel on the
@@ -360,7 +364,18 @@ class TimingEvent:
         if self.cuda_event and self._hip is not None:
             self._hip.hipEventDestroy(self.cuda_event)
 
-def run_workload(name, steps, warmup, weights="bf16"):
+# Routing rules other than the default softmax top-k, for the nested lines:
+# extra moe_forward options (the selection bias is drawn from its own seed).
+ROUTER_VARIANTS = {
+    "noaux_groups": dict(score_func="sigmoid", n_group=8, topk_group=4, selection_bias=True),
+    "sparsemixer": dict(score_func="sparsemixer"),
+    "router_stats": dict(router_stats=True),
+}
+ROUTER_NESTED = (("instella_fine", "noaux_groups"), ("phimoe_prefill", "sparsemixer"),
+                 ("phimoe_prefill", "router_stats"))
+
+
+def run_workload(name, steps, warmup, weights="bf16", router=None):
     import torch
     import numpy as np
     import sparse_mixture_experts_logits_amd as moe
@@ -398,6 +413,12 @@ def run_workload(name, steps, warmup, weights="bf16"):
         sgu, sdn = d(gu), d(dn)
     bias = None if inp.bias is None else torch.from_numpy(inp.bias).to(dev)
     kw = dict(routed_scale=wl.routed_scale, router_bias=bias, shared_gate_up=sgu, shared_down=sdn, **scales)
+    if router:
+        rv = dict(ROUTER_VARIANTS[router])
+        if rv.pop("selection_bias", False):
+            rng = np.random.default_rng(np.random.SeedSequence([0, 100]))
+            rv["selection_bias"] = torch.from_numpy(rng.normal(0.0, 0.1, wl.E).astype(np.float32)).to(dev)
+        kw.update(rv)
 
     out = torch.empty((wl.T, wl.H), dtype=hidden.dtype, device=dev)
     need = moe.workspace_bytes(wl.T, wl.H, wl.I, wl.E, wl.k, shared_I=sgu.shape[0] // 2 if sgu is not None else 0,
@@ -461,7 +482,7 @@ def run_workload(name, steps, warmup, weights="bf16"):
     stages = dict(zip(moe.STAGES, stage_ms.tolist()))
     stages[moe.STAGES[dom]] = dom_ms  # live value from the timed region
     return dict(wl=wl, counts=counts, wall_s=wall, gpu_ms=gpu_ms, steps=steps, warmup=warmup, stages=stages,
-                dominant=moe.STAGES[dom], inp=inp, weights=weights, schedule=schedule_of(wl, weights))
+                dominant=moe.STAGES[dom], inp=inp, weights=weights, schedule=schedule_of(wl, weights), router=router)
 
 
 _INPUT_CACHE = {}
@@ -612,6 +633,9 @@ def nested_line(res):
              roofline=roof, layer=layer_summary(res, w))
     if res["weights"] != "bf16":
         d["weights"] = WEIGHT_FORMATS[res["weights"]]
+    if res.get("router"):
+        d["router"] = {k: (v if not isinstance(v, bool) or k != "selection_bias" else "N(0, 0.1) per expert")
+                       for k, v in ROUTER_VARIANTS[res["router"]].items()}
     return d
 
 
@@ -621,6 +645,8 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="phimoe_decode")
+    ap.add_argument("--router", choices=sorted(ROUTER_VARIANTS), default=None,
+                    help="routing rule of the main workload (default: softmax top-k)")
     ap.add_argument("--only", action="store_true", help="measure the main workload only (no nested lines)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--skip", nargs="*", default=[], help="nested lines to leave out (workload names, "
@@ -664,7 +690,7 @@ def main(argv=None):
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
 
-    res = run_workload(args.workload, args.steps, args.warmup, weights=args.weights)
+    res = run_workload(args.workload, args.steps, args.warmup, weights=args.weights, router=args.router)
     roof, w = roofline_of(res)
     lay = layer_summary(res, w)
     wl = res["wl"]
@@ -684,7 +710,8 @@ def main(argv=None):
         "config": {"workload": wl.name, "T": wl.T, "H": wl.H, "I": wl.I, "E": wl.E, "k": wl.k,
                    "routed_scale": wl.routed_scale, "shared_I": wl.n_shared * wl.shared_I,
                    "parallelism": "single GPU",
-                   **({"expert_weights": WEIGHT_FORMATS[args.weights]} if args.weights != "bf16" else {})},
+                   **({"expert_weights": WEIGHT_FORMATS[args.weights]} if args.weights != "bf16" else {}),
+                   **({"router": args.router} if args.router else {})},
         "roofline": roof,
         "layer": lay,
     }
@@ -705,6 +732,12 @@ def main(argv=None):
             key = name + "_tile_blocks"
             if key not in args.skip:
                 line[key] = nested_line(run_workload(name, args.steps, args.warmup, weights="tile_blocks"))
+                log(f"[bench] {key}: {line[key]['layer']['ms_per_step']} ms per step")
+        # and with other routing rules
+        for name, rv in ROUTER_NESTED:
+            key = f"{name}_{rv}"
+            if key not in args.skip:
+                line[key] = nested_line(run_workload(name, args.steps, args.warmup, router=rv))
                 log(f"[bench] {key}: {line[key]['layer']['ms_per_step']} ms per step")
     print(json.dumps(line), flush=True)
     return 0

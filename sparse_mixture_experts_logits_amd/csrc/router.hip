@@ -570,9 +570,25 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(
     __shared__ float s_load[kMaxExperts];
     __shared__ float s_prob[kMaxExperts];
     if (g < G) {
+        // sixteen blocks' loads in flight per step, summed in block order
         float ps = 0.0f;
         int ms = 0;
-        for (int b = b0; b < b1; b++) {
+        int b = b0;
+        for (; b + 16 <= b1; b += 16) {
+            float pv[16];
+            int mv[16];
+#pragma unroll
+            for (int u = 0; u < 16; u++) {
+                pv[u] = blk_prob[(int64_t)(b + u) * E + e];
+                mv[u] = blk_mcnt[(int64_t)(b + u) * E + e];
+            }
+#pragma unroll
+            for (int u = 0; u < 16; u++) {
+                ps += pv[u];
+                ms += mv[u];
+            }
+        }
+        for (; b < b1; b++) {
             ps += blk_prob[(int64_t)b * E + e];
             ms += blk_mcnt[(int64_t)b * E + e];
         }

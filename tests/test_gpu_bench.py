@@ -43,3 +43,7 @@ def test_bench_prints_one_json_line_with_roofline_and_cpu_baseline(capsys):
         assert sub["steps"] == 5 and sub["warmup"] == 1, sec
     assert d["tiny_f32"]["dtype"] == "f32" and d["tiny_f32"]["layer"]["tokens_per_s"] > 0
     assert 0 <= d["phimoe_skewed"]["roofline"]["padded_flop_frac"] < 0.2
+    # the other routing rules: their own lines, naming the rule
+    for sec, rule in (("instella_fine_noaux_groups", "sigmoid"), ("phimoe_prefill_sparsemixer", "sparsemixer")):
+        assert d[sec]["router"]["score_func"] == rule and d[sec]["layer"]["tokens_per_s"] > 0, sec
+    assert d["phimoe_prefill_router_stats"]["router"]["router_stats"] is True
