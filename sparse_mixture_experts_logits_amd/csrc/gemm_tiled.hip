@@ -1123,6 +1123,9 @@ hipError_t launch_cfg(const GemmProblem &g, hipStream_t st)
 #ifndef MOE_TILED_TAIL
 #define MOE_TILED_TAIL 32
 #endif
+// Copies in pairs of stages (AP) for the routed gate_up (token rows) and
+// down (row-layout weights) on the tiled schedule: compile-time switches, on
+// by default; off, every launch copies single stages (same results).
 #ifndef MOE_TILED_APAIR
 #define MOE_TILED_APAIR 1
 #endif
