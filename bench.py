@@ -23,7 +23,11 @@ the headline value), and with other routing rules under
 ``<workload>_<router>``: the Instella-style layer with sigmoid scores, a
 selection-only bias and group-limited top-k (``noaux_groups``), the prefill
 with PhiMoE's sparsemixer selection (``sparsemixer``) and with the router
-statistics and load-balancing loss computed (``router_stats``). Each carries a ``roofline`` of its
+statistics and load-balancing loss computed (``router_stats``), and one GPU's
+share of the prefill chunk split over 8 GPUs: ``phimoe_prefill_tp8`` (tensor
+parallel, I/8 = 800 columns of every expert, all tokens) and
+``phimoe_prefill_ep8`` (expert parallel: the GEMMs of 2 experts with 512 rows
+each). Each carries a ``roofline`` of its
 dominant kernel, bound by max(FLOP / MFMA peak, bytes / HBM bandwidth). A
 short untimed pilot with events at every stage boundary finds the dominant
 kernel; every timed call then records HIP events around that kernel on the
@@ -620,7 +624,8 @@ def cpu_baseline(res, max_tokens, min_seconds=10.0):
 # ------------------------------------------------------------------ main
 
 # PhiMoE-shaped workloads first: they share one set of device weights
-NESTED = ("phimoe_prefill", "phimoe_skewed", "phimoe_skewed_small", "instella_fine", "tiny_f32")
+NESTED = ("phimoe_prefill", "phimoe_skewed", "phimoe_skewed_small", "instella_fine", "tiny_f32",
+          "phimoe_prefill_tp8", "phimoe_prefill_ep8")
 TILE_BLOCK_NESTED = ("phimoe_prefill", "phimoe_skewed", "instella_fine")
 
 

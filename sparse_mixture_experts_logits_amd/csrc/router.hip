@@ -454,7 +454,10 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(
     };
 
     const int tid = threadIdx.x;
-    const int G = 1024 / E;  // E <= 256 so G >= 4
+    // G groups of threads split the router blocks per expert; E <= 256 so
+    // G >= 4, and at most 64 so that the serial pass over the groups below
+    // stays short when there are few experts
+    const int G = min(1024 / E, 64);
     const int g = tid / E, e = tid - (tid / E) * E;
     const int chunk = (nblk + G - 1) / G;
     const int b0 = g * chunk;

@@ -356,8 +356,8 @@ def test_mixed_schedule(kw):
 
 # ------------------------------------------------------------------ full-size workloads
 
-FULL = ["phimoe_decode", "phimoe_prefill", "instella_fine", "phimoe_skewed"]
-EVERY_TOKEN = {"phimoe_decode", "phimoe_prefill", "instella_fine"}
+FULL = ["phimoe_decode", "phimoe_prefill", "instella_fine", "phimoe_skewed", "phimoe_prefill_tp8", "phimoe_prefill_ep8"]
+EVERY_TOKEN = {"phimoe_decode", "phimoe_prefill", "instella_fine", "phimoe_prefill_tp8", "phimoe_prefill_ep8"}
 
 
 def full_size_tokens(name, inp, ref):

@@ -82,6 +82,20 @@ WORKLOADS = [
              bias=((0, 6.0), (13, -30.0), (14, -30.0), (15, -30.0)),
              description="a decode-sized batch with the skewed router bias: about 32 rows per expert on "
                          "average, nearly every token on expert 0"),
+    # One GPU's share of the prefill chunk when the layer is split over 8 GPUs.
+    # Tensor parallel: each rank holds I/8 = 800 gate, up and down columns of
+    # every expert and routes all tokens (the prefill's hidden stream and the
+    # same router draw, so the same routing); its output is a partial sum.
+    Workload("phimoe_prefill_tp8", 2, T=4096, H=4096, I=800, E=16, k=2, dtype="bf16",
+             description="one rank of 8-way tensor parallelism over the prefill chunk: I/8 = 800"),
+    # Expert parallel: each rank holds 2 of the 16 experts, which receive
+    # about 2 * 8192 / 16 = 1024 of the chunk's assignments, 512 each. Here
+    # 512 tokens each pick both of 2 experts, so the expert GEMMs are exactly
+    # that share (2 experts, 512 rows each); the router and the combine run
+    # over 512 tokens instead of the rank's 4096.
+    Workload("phimoe_prefill_ep8", 6, T=512, H=4096, I=6400, E=2, k=2, dtype="bf16",
+             description="the expert GEMMs of one rank of 8-way expert parallelism over the prefill chunk: "
+                         "2 experts, 512 rows each"),
 ]
 BY_NAME = {w.name: w for w in WORKLOADS}
 
