@@ -27,7 +27,9 @@
  *   - All tensor pointers are DEVICE pointers owned by the caller; the
  *     library never allocates or frees memory on the call path and keeps no
  *     mutable global state (calls on different streams may overlap as long
- *     as their buffers do not).
+ *     as their buffers do not). The one exception is moe_forward_noalloc:
+ *     its per-GPU scratch array, and that array's address, looked up once
+ *     per device (thread-safe) and then only read.
  *   - Tensors are dense, row-major, with the shapes stated; base pointers
  *     must be 16-byte aligned; H, I and shared_I must be multiples of 8.
  *   - Every argument check runs before any HIP call; a rejected call has
